@@ -1,0 +1,204 @@
+"""Seeded synthetic inputs for the DeepSeek Sparse Attention (DSA) decode/prefill path.
+
+This module is shared by the oracle side (tests, the CPU baseline) and the HIP side
+(tests, bench).  It only draws random numbers and lays them out in the paged cache
+format; it contains none of the method's arithmetic (no scoring, no selection, no
+attention).
+
+Workloads follow the shapes the GLM-5.x pages describe for DSA: a multi-head
+lightning indexer (64 heads x 128 dims) over a single-head key cache, top-k = 2048,
+and absorbed-mode MLA with 64 query heads over a 512 latent + 64 rope row
+[Inside GLM-5.3 (SemiAnalysis), §Lightning Indexer, §Sparse MLA, §MLA changes].
+Integer-valued indexer inputs make every fp32 indexer score exact, so scores and
+selected index sets can be compared bit for bit.
+
+Random numbers come from torch generators seeded per (config seed, tensor id,
+layer); tensors are drawn directly on the target device so multi-GB pools are
+cheap to build.  The oracle receives host copies of exactly the same values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import torch
+
+BLOCK = 64  # tokens per page of every paged cache
+
+# tensor ids used to derive independent generator seeds
+_T_QIDX, _T_W, _T_KPOOL, _T_Q, _T_KV, _T_PERM, _T_LENS = range(7)
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """One synthetic workload.
+
+    ctx            : context length of every request (already includes the query token)
+    ctx_range      : if set, lengths are drawn uniformly from [lo, hi] (inclusive)
+    extra_dense    : extra requests appended after the main batch, each with this context
+    prefill_tokens : >0 selects a causal prefill chunk of that many query tokens
+                     ending at position ctx-1 of a single request
+    layers         : DSA layers sharing one indexer (IndexShare group); 1 = plain DSA
+    identity_pages : physical block i holds logical block i (else a random permutation)
+    """
+    name: str
+    seed: int
+    batch: int
+    ctx: int
+    Hi: int
+    Di: int
+    H: int
+    Dl: int
+    Dr: int
+    k: int
+    dtype: torch.dtype
+    idx_range: int        # q_idx / k_idx are integers uniform in [-idx_range, idx_range]
+    w_max: int            # w are integers uniform in [0, w_max]
+    sm_scale: float
+    ctx_range: Optional[tuple] = None
+    extra_dense: tuple = ()
+    prefill_tokens: int = 0
+    layers: int = 1
+    identity_pages: bool = False
+
+    @property
+    def row_dim(self) -> int:
+        return self.Dl + self.Dr
+
+
+def _cfgs() -> Dict[str, Config]:
+    bf = torch.bfloat16
+    big = dict(Hi=64, Di=128, H=64, Dl=512, Dr=64, k=2048, dtype=bf, idx_range=4, w_max=3,
+               sm_scale=1.0 / math.sqrt(576.0))
+    return {
+        # tiny fp32 parity case: 1 token, L=256, 4x32 indexer, k=64, 8 heads of 64+16
+        "tiny_fp32": Config("tiny_fp32", seed=0, batch=1, ctx=256, Hi=4, Di=32, H=8, Dl=64, Dr=16,
+                            k=64, dtype=torch.float32, idx_range=3, w_max=2,
+                            sm_scale=1.0 / math.sqrt(80.0), identity_pages=True),
+        # single-layer decode, batch 1 at 32K context
+        "decode_b1_32k": Config("decode_b1_32k", seed=1, batch=1, ctx=32768, **big),
+        # batched decode: 64 requests with L uniform in [4096, 65536], random page permutation
+        "decode_b64_paged": Config("decode_b64_paged", seed=2, batch=64, ctx=65536,
+                                   ctx_range=(4096, 65536), **big),
+        # prefill chunk: 4096 causal queries at positions 126976..131071 of a 131072 context
+        "prefill_4096_at_128k": Config("prefill_4096_at_128k", seed=3, batch=1, ctx=131072,
+                                       prefill_tokens=4096, identity_pages=True, **big),
+        # IndexShare decode: 4 layers, 32 requests at 131072 + 8 dense requests at 1500
+        "indexshare_decode_4layer": Config("indexshare_decode_4layer", seed=4, batch=32,
+                                           ctx=131072, extra_dense=(1500,) * 8, layers=4, **big),
+    }
+
+
+CONFIGS: Dict[str, Config] = _cfgs()
+
+
+def shrink(cfg: Config, **over) -> Config:
+    """A smaller variant of a config (same dims and distributions) for fast tests."""
+    return dataclasses.replace(cfg, **over)
+
+
+def _gen(cfg: Config, tensor_id: int, layer: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    # distinct, reproducible stream per (config seed, tensor, layer)
+    g.manual_seed((cfg.seed * 1_000_003 + tensor_id * 10_007 + layer * 101 + 17) & 0x7FFFFFFFFFFF)
+    return g
+
+
+def _chunked(shape, draw, dtype, device, rows_per_chunk=1 << 14):
+    """Fill a [n, ...] tensor chunk by chunk (keeps fp32 temporaries small)."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    n = shape[0]
+    for s in range(0, n, rows_per_chunk):
+        e = min(n, s + rows_per_chunk)
+        out[s:e] = draw((e - s,) + tuple(shape[1:])).to(dtype)
+    return out
+
+
+def _ints(cfg, tid, layer, shape, lo, hi, dtype, device):
+    g = _gen(cfg, tid, layer, device)
+    return _chunked(shape, lambda sh: torch.randint(lo, hi + 1, sh, generator=g, device=device,
+                                                    dtype=torch.int32), dtype, device)
+
+
+def _normal(cfg, tid, layer, shape, dtype, device):
+    g = _gen(cfg, tid, layer, device)
+    return _chunked(shape, lambda sh: torch.randn(sh, generator=g, device=device,
+                                                  dtype=torch.float32), dtype, device)
+
+
+def context_lengths(cfg: Config) -> List[int]:
+    """Context length (including the query token) of every request, main batch first."""
+    if cfg.ctx_range is not None:
+        g = _gen(cfg, _T_LENS, 0, "cpu")
+        lo, hi = cfg.ctx_range
+        lens = torch.randint(lo, hi + 1, (cfg.batch,), generator=g).tolist()
+    else:
+        lens = [cfg.ctx] * cfg.batch
+    return lens + list(cfg.extra_dense)
+
+
+def page_table(cfg: Config, lens: List[int]):
+    """block_table [B][max_blocks] int32 (unused slots -1) and the pool size.
+
+    Physical blocks are handed out from one random permutation of all blocks (or in
+    order when identity_pages is set), so consecutive logical blocks of a request sit at
+    unrelated physical addresses.
+    """
+    nblk = [(n + BLOCK - 1) // BLOCK for n in lens]
+    total = sum(nblk)
+    max_blocks = max(nblk)
+    if cfg.identity_pages:
+        perm = torch.arange(total, dtype=torch.int32)
+    else:
+        perm = torch.randperm(total, generator=_gen(cfg, _T_PERM, 0, "cpu")).to(torch.int32)
+    bt = torch.full((len(lens), max_blocks), -1, dtype=torch.int32)
+    off = 0
+    for b, nb in enumerate(nblk):
+        bt[b, :nb] = perm[off:off + nb]
+        off += nb
+    return bt, total
+
+
+def make_inputs(cfg: Config, device="cpu") -> dict:
+    """All inputs of one step of the path, resident on `device`.
+
+    Returns a dict with
+      seq_len      int32 [B]            context length per request (query token included)
+      block_table  int32 [B][max_blocks]
+      k_pool       [nblk][64][Di]       single-head indexer keys (cfg.dtype)
+      q_idx        [T][Hi][Di]          indexer queries (cfg.dtype)
+      w            float32 [T][Hi]      indexer head weights
+      kv_pools     list over layers of [nblk][64][Dl+Dr] latent rows (cfg.dtype)
+      q            list over layers of [T][H][Dl+Dr] absorbed queries (cfg.dtype)
+      q_row, q_pos int32 [T]            request and position of each query token
+    Decode: T = B, query t belongs to request t at position seq_len[t]-1.
+    Prefill: T = prefill_tokens, all of request 0, positions ctx-T .. ctx-1.
+    """
+    lens = context_lengths(cfg)
+    bt, nblk = page_table(cfg, lens)
+    B = len(lens)
+    if cfg.prefill_tokens:
+        T = cfg.prefill_tokens
+        q_row = torch.zeros(T, dtype=torch.int32)
+        q_pos = torch.arange(cfg.ctx - T, cfg.ctx, dtype=torch.int32)
+    else:
+        T = B
+        q_row = torch.arange(B, dtype=torch.int32)
+        q_pos = torch.tensor(lens, dtype=torch.int32) - 1
+    r = cfg.idx_range
+    inp = {
+        "cfg": cfg,
+        "seq_len": torch.tensor(lens, dtype=torch.int32, device=device),
+        "block_table": bt.to(device),
+        "q_row": q_row.to(device),
+        "q_pos": q_pos.to(device),
+        "k_pool": _ints(cfg, _T_KPOOL, 0, (nblk, BLOCK, cfg.Di), -r, r, cfg.dtype, device),
+        "q_idx": _ints(cfg, _T_QIDX, 0, (T, cfg.Hi, cfg.Di), -r, r, cfg.dtype, device),
+        "w": _ints(cfg, _T_W, 0, (T, cfg.Hi), 0, cfg.w_max, torch.float32, device),
+        "kv_pools": [_normal(cfg, _T_KV, l, (nblk, BLOCK, cfg.row_dim), cfg.dtype, device)
+                     for l in range(cfg.layers)],
+        "q": [_normal(cfg, _T_Q, l, (T, cfg.H, cfg.row_dim), cfg.dtype, device)
+              for l in range(cfg.layers)],
+    }
+    return inp

@@ -1,0 +1,59 @@
+"""Drive the CPU oracle over a set of generated inputs.
+
+TEST INFRASTRUCTURE ONLY (tests, the smoke check and the benchmark's CPU-baseline leg).
+
+Inputs arrive as the torch tensors produced by `dsa_inputs.make_inputs` (on any
+device); torch is used here only to copy exact values to the host.  bfloat16 tensors
+are copied as raw bits and decoded by the oracle's own bit shift.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import dsa_oracle as O
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(t.view(torch.int16).numpy())
+    return t.double().numpy()
+
+
+def request_rows(pool: torch.Tensor, block_table_row: np.ndarray, n: int) -> np.ndarray:
+    """Logical rows 0..n-1 of one request.
+
+    Only the blocks the request owns are copied to the host (pools can be many GB); the
+    page translation itself is the oracle's `logical_rows` over that copied sub-pool."""
+    nb = (n + O.BLOCK - 1) // O.BLOCK
+    phys = np.asarray(block_table_row[:nb], dtype=np.int64)
+    sub = to_f64(pool[torch.as_tensor(phys, device=pool.device)])       # [nb][64][D]
+    return O.logical_rows(sub, np.arange(nb), n)
+
+
+def expected_token(inp: dict, t: int, layers=None) -> dict:
+    """Oracle results for query token t of an input set (decode or prefill).
+
+    Returns dict(scores f32 [n], idx int32 [k], out list of f64 [H][Dl], lse list [H], n)."""
+    cfg = inp["cfg"]
+    layers = range(cfg.layers) if layers is None else layers
+    b = int(inp["q_row"][t])
+    n = int(inp["q_pos"][t]) + 1
+    bt = inp["block_table"][b].cpu().numpy()
+    keys = request_rows(inp["k_pool"], bt, n)
+    scores = O.indexer_scores(to_f64(inp["q_idx"][t]), to_f64(inp["w"][t]), keys)
+    idx = O.topk_positions(scores, n, cfg.k)
+    sel = idx[idx >= 0]
+    outs, lses = [], []
+    for l in layers:
+        rows = request_rows(inp["kv_pools"][l], bt, n)
+        o, s = O.mla_absorbed(to_f64(inp["q"][l][t]), rows[sel], cfg.Dl, cfg.sm_scale)
+        outs.append(o)
+        lses.append(s)
+    return dict(scores=scores, idx=idx, out=outs, lse=lses, n=n)
+
+
+def expected_topk(scores: np.ndarray, n_valid: np.ndarray, k: int) -> np.ndarray:
+    """Top-k of every row of a score matrix [rows][ld] (fp32)."""
+    return np.stack([O.topk_positions(scores[r], int(n_valid[r]), k) for r in range(scores.shape[0])])
