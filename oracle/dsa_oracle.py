@@ -37,14 +37,21 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def logical_rows(pool: np.ndarray, block_table_row: np.ndarray, n: int) -> np.ndarray:
-    """Rows of logical positions 0..n-1 of one request from a paged pool.
+def page_slots(block_table_row: np.ndarray, positions: np.ndarray):
+    """Physical (block, slot) of logical positions of one request.
 
     Position s lives in physical block block_table_row[s // 64] at slot s % 64 (the
     page mapping that serving engines keep for sparse attention; remio.ai GLM-5.3
-    explainer, §HiSparse).  pool: [num_blocks][64][row_dim]."""
-    s = np.arange(n)
-    return pool[block_table_row[s // BLOCK], s % BLOCK]
+    explainer, §HiSparse)."""
+    positions = np.asarray(positions, dtype=np.int64)
+    return np.asarray(block_table_row, dtype=np.int64)[positions // BLOCK], positions % BLOCK
+
+
+def logical_rows(pool: np.ndarray, block_table_row: np.ndarray, n: int) -> np.ndarray:
+    """Rows of logical positions 0..n-1 of one request from a paged pool
+    pool: [num_blocks][64][row_dim]."""
+    blk, slot = page_slots(block_table_row, np.arange(n))
+    return pool[blk, slot]
 
 
 # --------------------------------------------------------------------------- indexer

@@ -32,23 +32,37 @@ def request_rows(pool: torch.Tensor, block_table_row: np.ndarray, n: int) -> np.
     return O.logical_rows(sub, np.arange(nb), n)
 
 
-def expected_token(inp: dict, t: int, layers=None) -> dict:
+def selected_rows(pool: torch.Tensor, block_table_row: np.ndarray, positions: np.ndarray) -> np.ndarray:
+    """Rows of the given logical positions: the oracle maps each position to its
+    (block, slot); only those rows are copied to the host."""
+    blk, slot = O.page_slots(block_table_row, positions)
+    dev = pool.device
+    return to_f64(pool[torch.as_tensor(blk, device=dev), torch.as_tensor(slot, device=dev)])
+
+
+def expected_token(inp: dict, t: int, layers=None, key_cache: dict = None) -> dict:
     """Oracle results for query token t of an input set (decode or prefill).
 
+    key_cache (optional) keeps each request's logical key rows between calls.
     Returns dict(scores f32 [n], idx int32 [k], out list of f64 [H][Dl], lse list [H], n)."""
     cfg = inp["cfg"]
     layers = range(cfg.layers) if layers is None else layers
     b = int(inp["q_row"][t])
     n = int(inp["q_pos"][t]) + 1
     bt = inp["block_table"][b].cpu().numpy()
-    keys = request_rows(inp["k_pool"], bt, n)
-    scores = O.indexer_scores(to_f64(inp["q_idx"][t]), to_f64(inp["w"][t]), keys)
+    if key_cache is not None and b in key_cache and key_cache[b].shape[0] >= n:
+        keys = key_cache[b]
+    else:
+        keys = request_rows(inp["k_pool"], bt, n)
+        if key_cache is not None:
+            key_cache[b] = keys
+    scores = O.indexer_scores(to_f64(inp["q_idx"][t]), to_f64(inp["w"][t]), keys[:n])
     idx = O.topk_positions(scores, n, cfg.k)
     sel = idx[idx >= 0]
     outs, lses = [], []
     for l in layers:
-        rows = request_rows(inp["kv_pools"][l], bt, n)
-        o, s = O.mla_absorbed(to_f64(inp["q"][l][t]), rows[sel], cfg.Dl, cfg.sm_scale)
+        rows = selected_rows(inp["kv_pools"][l], bt, sel)
+        o, s = O.mla_absorbed(to_f64(inp["q"][l][t]), rows, cfg.Dl, cfg.sm_scale)
         outs.append(o)
         lses.append(s)
     return dict(scores=scores, idx=idx, out=outs, lse=lses, n=n)

@@ -1,0 +1,86 @@
+"""ctypes binding of libdsa.so (the C ABI declared in include/dsa.h).
+
+Argument marshalling only: torch tensors are turned into device pointers, sizes and the
+current HIP stream; every computation happens in the library's kernels.  The library
+must have been built (python -m sparse_attention_19_amd.build); importing this module
+without it raises ImportError -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_STALE_INDEX, DSA_ERR_HIP = range(6)
+DSA_F32, DSA_BF16 = 0, 1
+DSA_OP_TOPK, DSA_OP_MLA = 0, 1
+DSA_BLOCK = 64
+DSA_MAX_K = 2048
+
+EXPORTS = [
+    "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+    "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
+    "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
+]
+
+
+class DsaPool(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
+                ("block_size", ctypes.c_int32), ("row_dim", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class DsaPageTable(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+
+
+class DsaIndexCache(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("group", ctypes.c_int32), ("valid", ctypes.c_int32),
+                ("step", ctypes.c_uint64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_19_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    pool_p, pt_p, cache_p = ctypes.POINTER(DsaPool), ctypes.POINTER(DsaPageTable), ctypes.POINTER(DsaIndexCache)
+    sig = {
+        "dsa_indexer_scores": [P, P, pool_p, pt_p, P, P, I32, I32, I32, P, I64, P],
+        "dsa_topk": [P, I64, P, I32, I32, I32, P, I64, P, SZ, P],
+        "dsa_sparse_mla_decode": [P, pool_p, pt_p, P, I64, I32, I32, I32, I32, F, P, P, P, SZ, P],
+        "dsa_sparse_mla_prefill": [P, pool_p, pt_p, P, P, P, I64, I32, I32, I32, I32, I32, F, P, P, P, SZ, P],
+        "dsa_index_cache_init": [cache_p, P, I64, I32, I32, I32],
+        "dsa_index_cache_publish": [cache_p, ctypes.c_uint64],
+        "dsa_index_cache_get": [cache_p, ctypes.c_uint64, I32, ctypes.POINTER(ctypes.c_void_p)],
+        "dsa_workspace_bytes": [I32, I32, I64, I32, I32, I32],
+        "dsa_status_string": [ctypes.c_int],
+        "dsa_last_error": [],
+        "dsa_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.dsa_workspace_bytes.restype = ctypes.c_size_t
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_version.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{LIB.dsa_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def check(status: int) -> None:
+    if status != DSA_OK:
+        raise DsaError(status, LIB.dsa_last_error().decode())

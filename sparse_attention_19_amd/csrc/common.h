@@ -1,0 +1,66 @@
+// Device helpers shared by the gfx950 kernels of the DSA path (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBlock = 64;  // positions per page
+constexpr int kWave = 64;   // CDNA wavefront width
+
+#define DSA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.
+// A: lane l holds row l%16, 8 k-values; B: lane l holds column l%16, 8 k-values (the
+// same 8 k-slots as A for lanes of the same l/16 group).  C: lane l holds
+// rows 4*(l/16) + j (j = 0..3) of column l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 bf16 MFMA.  A: lane l holds row l%32; B: column l%32; 8 k-values each.
+// C: lane l, slot j holds row 8*(j/4) + 4*(l/32) + (j%4) of column l%32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int mfma32_row(int lane, int j) {
+  return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+}
+
+// Transposed LDS read of 16-bit data (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives in slot j the element (i % 4) of the 4-element (8-byte) run
+// addressed by lane 4*j + i/4 of the same group.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(DSA_LDS(s16x4, const_cast<void*>(lds_addr)));
+}
+
+__device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+__device__ __forceinline__ bf16x8 as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f2bf_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf_bits2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Compiler-level ordering point for LDS traffic exchanged between lanes of one wave
+// (LDS operations of a wave execute in order in hardware).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+}  // namespace dsa

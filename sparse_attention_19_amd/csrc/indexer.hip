@@ -1,0 +1,266 @@
+// Lightning indexer for gfx950.
+//
+// score[t][s] = sum_j w[t][j] * max(0, q_idx[t][j] . key_s)      (SemiAnalysis, "Inside
+// GLM-5.3: How Sparse Attention Affects DRAM Memory TAM", §Lightning Indexer: multi-head
+// indexer queries, a single-head key, ReLU of the dot product, weighted sum over heads).
+//
+// bf16 instance (64 heads x 128 dims): a GEMM  C[head][key] = Q[head][:] . K[key][:]  on
+// 32x32x16 MFMA with the ReLU and the head-weighted reduction fused into the epilogue, so
+// the per-head logits never leave registers.  Keys stream from the paged pool through a
+// double-buffered LDS tile of 128 keys (2 pages):
+//   decode  : one query token per workgroup; the 4 waves split each key tile (32 keys each)
+//             -> the key cache is read exactly once (HBM-bound streaming)
+//   prefill : 8 query tokens per workgroup (one per wave of 8); every wave consumes the whole
+//             key tile -> each key tile fetched from L2/MALL once per 8 tokens (MFMA-bound)
+// The contraction order over the 128 dims is permuted identically for Q and K (lane half h
+// of k-step s holds dims 64h + 8s .. 64h + 8s + 7), which lets every lane fetch its 8 steps
+// as one contiguous 128-byte run.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kHi = 64, kDi = 128;
+constexpr int kTileKeys = 128;                 // keys per LDS tile (2 pages)
+constexpr int kRowBytes = kDi * 2;             // 256 B per key row
+constexpr int kLdsRow = kRowBytes + 16;        // padded LDS row (conflict-free b128 reads)
+constexpr int kTileBytes = kTileKeys * kLdsRow;
+
+// Loads one 128-key tile (2 pages) of a request starting at logical key `key0` (a
+// multiple of 128) into registers: thread t fetches 16-byte chunks t, t+kThreads, ...
+// (fully coalesced within each page).  Pages at or beyond n, and block-table entries
+// outside the pool, read as zeros.
+template <int kThreads>
+struct TileRegs { uint4 v[kTileKeys * 16 / kThreads]; };
+
+template <int kThreads>
+__device__ __forceinline__ void load_tile(TileRegs<kThreads>& r, const uint8_t* pool,
+                                          int64_t num_blocks, const int* bt_row, int key0, int n) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kTileKeys * 16 / kThreads; ++i) {
+    const int id = tid + kThreads * i;           // 16-byte chunk id in the 32 KB tile
+    const int key = id >> 4;                     // 0..127
+    const int lblk = (key0 + key) >> 6;
+    int64_t phys = -1;
+    if (key0 + (key & ~63) < n) phys = bt_row[lblk];
+    if (phys >= 0 && phys < num_blocks) {
+      const int64_t off = ((phys * kBlock + ((key0 + key) & 63)) * kRowBytes) + (id & 15) * 16;
+      r.v[i] = *reinterpret_cast<const uint4*>(pool + off);
+    } else {
+      r.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int kThreads>
+__device__ __forceinline__ void store_tile(const TileRegs<kThreads>& r, uint8_t* lds) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kTileKeys * 16 / kThreads; ++i) {
+    const int id = tid + kThreads * i;
+    *reinterpret_cast<uint4*>(lds + (id >> 4) * kLdsRow + (id & 15) * 16) = r.v[i];
+  }
+}
+
+// A-operand fragments of one query token (64 heads) for the 32x32x16 MFMA:
+// a[i][s] = Q[32i + l%32][64*(l/32) + 8s .. +8]
+struct QFrag { bf16x8 a[2][8]; float w[2][16]; };
+
+__device__ __forceinline__ void load_qfrag(QFrag& f, const uint8_t* q_tok, const float* w_tok) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint4* src = reinterpret_cast<const uint4*>(q_tok + (32 * i + (lane & 31)) * kRowBytes +
+                                                      (lane >> 5) * 128);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f.a[i][s] = as_bf8(src[s]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) f.w[i][j] = w_tok[32 * i + mfma32_row(lane, j)];
+  }
+}
+
+// Scores of 32 keys (LDS rows r0..r0+31) for one token; result valid in lanes 0..31
+// (lane = key).
+__device__ __forceinline__ float score32(const QFrag& f, const uint8_t* lds, int r0) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* base = lds + (r0 + (lane & 31)) * kLdsRow + (lane >> 5) * 128;
+  f32x16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const bf16x8 b = as_bf8(*reinterpret_cast<const uint4*>(base + 16 * s));
+    c0 = mfma32(f.a[0][s], b, c0);
+    c1 = mfma32(f.a[1][s], b, c1);
+  }
+  float p = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    p = fmaf(f.w[0][j], fmaxf(c0[j], 0.f), p);
+    p = fmaf(f.w[1][j], fmaxf(c1[j], 0.f), p);
+  }
+  p += __shfl_xor(p, 32, kWave);
+  return p + 0.0f;   // canonical +0.0
+}
+
+// grid.x: key chunks of `tiles_per_wg` tiles; grid.y: token groups.
+//   decode : 4 waves, 1 token per workgroup, wave w scores keys 32w..32w+31 of each tile
+//   prefill: 8 waves, 8 tokens per workgroup (token t0 + w in wave w), every wave scores
+//            all 128 keys of each tile
+template <bool kDecode>
+__global__ __launch_bounds__(kDecode ? 256 : 512) void indexer_bf16_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ pool,
+    int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
+    int max_blocks, int batch, const int* __restrict__ q_row, const int* __restrict__ q_pos, int T,
+    int tiles_per_wg, float* __restrict__ scores, int64_t ld) {
+  constexpr int kThreads = kDecode ? 256 : 512;
+  constexpr int kTPG = kDecode ? 1 : kThreads / kWave;   // tokens per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTileBytes];
+  __shared__ int s_req[kTPG];
+  __shared__ int s_n[kTPG];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.y * kTPG;
+  if (tid < kTPG) {
+    const int t = t0 + tid;
+    int b = -1, n = 0;
+    if (t < T) {
+      b = q_row ? q_row[t] : t;
+      if (b < 0 || b >= batch) {
+        b = -1;                                   // token of no request: nothing to score
+      } else {
+        n = q_pos ? q_pos[t] + 1 : seq_len[b];
+        n = max(0, min(n, max_blocks * kBlock));
+      }
+    }
+    s_req[tid] = b;
+    s_n[tid] = n;
+  }
+  __syncthreads();
+
+  const int key_begin = blockIdx.x * tiles_per_wg * kTileKeys;
+
+  // Process each distinct request among this group's tokens (normally exactly one).
+  for (int u = 0; u < kTPG; ++u) {
+    const int b = s_req[u];
+    bool seen = (b < 0);
+    for (int v = 0; v < u; ++v) seen |= (s_req[v] == b);
+    if (seen) continue;                                   // uniform across the workgroup
+    int nmax = 0;
+    for (int v = 0; v < kTPG; ++v) if (s_req[v] == b) nmax = max(nmax, s_n[v]);
+    const int key_end = min(nmax, key_begin + tiles_per_wg * kTileKeys);
+    if (key_begin >= key_end) continue;
+    const int* bt_row = block_table + (int64_t)b * max_blocks;
+
+    // this wave's token, if it belongs to request b
+    const int slot = kDecode ? 0 : wave;
+    const int tok = (s_req[slot] == b) ? t0 + slot : -1;
+    const int tn = (tok >= 0) ? s_n[slot] : 0;
+    QFrag f;
+    if (tok >= 0) load_qfrag(f, q_idx + (int64_t)tok * kHi * kRowBytes, w + (int64_t)tok * kHi);
+
+    TileRegs<kThreads> regs;
+    load_tile<kThreads>(regs, pool, num_blocks, bt_row, key_begin, nmax);
+    int buf = 0;
+    for (int key0 = key_begin; key0 < key_end; key0 += kTileKeys) {
+      store_tile<kThreads>(regs, lds[buf]);
+      __syncthreads();
+      if (key0 + kTileKeys < key_end)
+        load_tile<kThreads>(regs, pool, num_blocks, bt_row, key0 + kTileKeys, nmax);
+      if (tok >= 0) {
+        if (kDecode) {
+          const float p = score32(f, lds[buf], wave * 32);
+          const int s = key0 + wave * 32 + lane;
+          if (lane < 32 && s < tn) scores[(int64_t)tok * ld + s] = p;
+        } else {
+          for (int part = 0; part < kTileKeys / 32; ++part) {
+            if (key0 + part * 32 >= tn) break;
+            const float p = score32(f, lds[buf], part * 32);
+            const int s = key0 + part * 32 + lane;
+            if (lane < 32 && s < tn) scores[(int64_t)tok * ld + s] = p;
+          }
+        }
+      }
+      buf ^= 1;
+    }
+    __syncthreads();   // LDS reuse by the next request's tiles
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32 instance (small dims: Hi <= 64, Di <= 128): plain VALU, one key per thread.
+constexpr int kF32Keys = 256;
+
+__global__ __launch_bounds__(256) void indexer_f32_kernel(
+    const float* __restrict__ q_idx, const float* __restrict__ w, const float* __restrict__ pool,
+    int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
+    int max_blocks, int batch, const int* __restrict__ q_row, const int* __restrict__ q_pos, int Hi,
+    int Di, float* __restrict__ scores, int64_t ld) {
+  __shared__ float sq[64 * 128];
+  __shared__ float sw[64];
+  const int t = blockIdx.y;
+  const int b = q_row ? q_row[t] : t;
+  if (b < 0 || b >= batch) return;
+  int n = q_pos ? q_pos[t] + 1 : seq_len[b];
+  n = min(n, max_blocks * kBlock);
+  const int s = blockIdx.x * kF32Keys + threadIdx.x;
+  if (blockIdx.x * kF32Keys >= n) return;
+  for (int i = threadIdx.x; i < Hi * Di; i += blockDim.x) sq[i] = q_idx[(int64_t)t * Hi * Di + i];
+  for (int i = threadIdx.x; i < Hi; i += blockDim.x) sw[i] = w[(int64_t)t * Hi + i];
+  __syncthreads();
+  if (s >= n) return;
+  const int64_t phys = block_table[(int64_t)b * max_blocks + (s >> 6)];
+  float acc = 0.f;
+  if (phys >= 0 && phys < num_blocks) {
+    const float* key = pool + (phys * kBlock + (s & 63)) * Di;
+    for (int j = 0; j < Hi; ++j) {
+      float d = 0.f;
+      for (int c = 0; c < Di; c += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(key + c);
+        d = fmaf(sq[j * Di + c], kv.x, d);
+        d = fmaf(sq[j * Di + c + 1], kv.y, d);
+        d = fmaf(sq[j * Di + c + 2], kv.z, d);
+        d = fmaf(sq[j * Di + c + 3], kv.w, d);
+      }
+      acc = fmaf(sw[j], fmaxf(d, 0.f), acc);
+    }
+  }
+  scores[(int64_t)t * ld + s] = acc + 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
+  const int max_keys = a.max_blocks * kBlock;
+  if (a.bf16) {
+    if (a.prefill) {
+      // key chunks of 64 tiles (8192 keys) per workgroup, 8 tokens per workgroup
+      const int tiles = (max_keys + kTileKeys - 1) / kTileKeys;
+      const int per = 64;
+      dim3 grid((tiles + per - 1) / per, (a.T + 7) / 8);
+      hipLaunchKernelGGL(indexer_bf16_kernel<false>, grid, dim3(512), 0, stream,
+                         (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool, a.num_blocks,
+                         a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.T, per,
+                         a.scores, a.ld);
+    } else {
+      // aim for >= ~2048 workgroups over the batch; at most 8 tiles (1024 keys) each
+      const int tiles = (max_keys + kTileKeys - 1) / kTileKeys;
+      int per = 8;
+      while (per > 1 && (int64_t)a.T * ((tiles + per - 1) / per) < 2048) per >>= 1;
+      dim3 grid((tiles + per - 1) / per, a.T);
+      hipLaunchKernelGGL(indexer_bf16_kernel<true>, grid, dim3(256), 0, stream,
+                         (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool, a.num_blocks,
+                         a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.T, per,
+                         a.scores, a.ld);
+    }
+  } else {
+    dim3 grid((max_keys + kF32Keys - 1) / kF32Keys, a.T);
+    hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), 0, stream, (const float*)a.q_idx, a.w,
+                       (const float*)a.pool, a.num_blocks, a.block_table, a.seq_len, a.max_blocks,
+                       a.batch, a.q_row, a.q_pos, a.Hi, a.Di, a.scores, a.ld);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

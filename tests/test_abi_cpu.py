@@ -1,0 +1,192 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry point that
+include/dsa.h declares, and rejects invalid arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_19_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: every call below is rejected
+FAKE2 = 0x20000
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 11
+    assert sorted(L.EXPORTS) == names
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert L.LIB.dsa_status_string(L.DSA_OK) == b"DSA_OK"
+    assert L.LIB.dsa_status_string(L.DSA_ERR_STALE_INDEX) == b"DSA_ERR_STALE_INDEX"
+    assert L.LIB.dsa_status_string(99) == b"DSA_ERR_UNKNOWN"
+    assert L.LIB.dsa_version().startswith(b"dsa-gfx950")
+
+
+def pool(dtype=L.DSA_BF16, row=128, nblk=10, data=FAKE, bs=64):
+    return L.DsaPool(data, nblk, bs, row, dtype)
+
+
+def pt(batch=2, max_blocks=4):
+    return L.DsaPageTable(FAKE, FAKE2, batch, max_blocks)
+
+
+def idx_call(**kw):
+    a = dict(q_idx=FAKE, w=FAKE, pool=pool(), pt=pt(), q_row=None, q_pos=None, T=2, Hi=64, Di=128,
+             scores=FAKE, ld=256)
+    a.update(kw)
+    return L.LIB.dsa_indexer_scores(a["q_idx"], a["w"], ctypes.byref(a["pool"]) if a["pool"] else None,
+                                    ctypes.byref(a["pt"]) if a["pt"] else None, a["q_row"], a["q_pos"],
+                                    a["T"], a["Hi"], a["Di"], a["scores"], a["ld"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_idx=None), L.DSA_ERR_INVALID),
+    (dict(w=None), L.DSA_ERR_INVALID),
+    (dict(scores=None), L.DSA_ERR_INVALID),
+    (dict(pool=None), L.DSA_ERR_INVALID),
+    (dict(pt=None), L.DSA_ERR_INVALID),
+    (dict(pool=pool(data=None)), L.DSA_ERR_INVALID),
+    (dict(pool=pool(bs=32)), L.DSA_ERR_UNSUPPORTED),
+    (dict(pool=pool(nblk=0)), L.DSA_ERR_INVALID),
+    (dict(pool=pool(row=64)), L.DSA_ERR_INVALID),
+    (dict(pool=pool(dtype=7)), L.DSA_ERR_UNSUPPORTED),
+    (dict(pool=pool(data=FAKE + 4)), L.DSA_ERR_INVALID),
+    (dict(T=3), L.DSA_ERR_INVALID),                       # decode: T must equal batch
+    (dict(q_row=FAKE), L.DSA_ERR_INVALID),                # q_row without q_pos
+    (dict(ld=255), L.DSA_ERR_INVALID),                    # ld < max_blocks * 64
+    (dict(Hi=32), L.DSA_ERR_UNSUPPORTED),                 # bf16 instance is 64 x 128
+    (dict(Hi=8, Di=32, pool=pool(L.DSA_F32, row=32)), L.DSA_OK),   # fp32 small dims are fine ...
+    (dict(Hi=8, Di=30, pool=pool(L.DSA_F32, row=30)), L.DSA_ERR_UNSUPPORTED),
+    (dict(Hi=65, Di=32, pool=pool(L.DSA_F32, row=32)), L.DSA_ERR_UNSUPPORTED),
+    (dict(pt=L.DsaPageTable(None, FAKE2, 2, 4)), L.DSA_ERR_INVALID),
+    (dict(pt=L.DsaPageTable(FAKE, FAKE2, 0, 4)), L.DSA_ERR_INVALID),
+    (dict(pt=L.DsaPageTable(FAKE, FAKE2, 2, 0)), L.DSA_ERR_INVALID),
+])
+def test_indexer_rejects(kw, status):
+    if status == L.DSA_OK:
+        # valid shape: only check it is not rejected for shape reasons -- with T = 0 no launch
+        kw = dict(kw, T=0, q_row=FAKE, q_pos=FAKE)
+    got = idx_call(**kw)
+    assert got == status, L.LIB.dsa_last_error()
+    if status != L.DSA_OK:
+        assert L.LIB.dsa_last_error()
+
+
+def topk_call(**kw):
+    a = dict(scores=FAKE, ld=1000, n_valid=FAKE2, n_add=0, rows=3, k=64, idx=FAKE, ld_idx=64, ws=None, wsb=0)
+    a.update(kw)
+    return L.LIB.dsa_topk(a["scores"], a["ld"], a["n_valid"], a["n_add"], a["rows"], a["k"], a["idx"],
+                          a["ld_idx"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(scores=None), L.DSA_ERR_INVALID),
+    (dict(n_valid=None), L.DSA_ERR_INVALID),
+    (dict(idx=None), L.DSA_ERR_INVALID),
+    (dict(k=0), L.DSA_ERR_UNSUPPORTED),
+    (dict(k=2049, ld_idx=4096), L.DSA_ERR_UNSUPPORTED),
+    (dict(ld_idx=63), L.DSA_ERR_INVALID),
+    (dict(ld=0), L.DSA_ERR_INVALID),
+    (dict(n_add=2), L.DSA_ERR_INVALID),
+    (dict(rows=-1), L.DSA_ERR_INVALID),
+    (dict(rows=0), L.DSA_OK),                             # empty: nothing enqueued
+    (dict(rows=0, scores=None, idx=None), L.DSA_OK),      # ... and may pass NULL data
+    (dict(ld=40000), L.DSA_ERR_WORKSPACE),                # long rows need the merge workspace
+])
+def test_topk_rejects(kw, status):
+    assert topk_call(**kw) == status
+
+
+def mla_call(prefill=False, **kw):
+    a = dict(q=FAKE, pool=pool(row=576), pt=pt(), idx=FAKE, ld_idx=2048, k=2048, H=64, Dl=512, Dr=64,
+             scale=0.04, out=FAKE, lse=None, ws=FAKE2, wsb=1 << 40, q_row=FAKE, q_pos=FAKE, T=2)
+    a.update(kw)
+    pp = ctypes.byref(a["pool"]) if a["pool"] else None
+    tp = ctypes.byref(a["pt"]) if a["pt"] else None
+    if prefill:
+        return L.LIB.dsa_sparse_mla_prefill(a["q"], pp, tp, a["q_row"], a["q_pos"], a["idx"], a["ld_idx"],
+                                            a["T"], a["k"], a["H"], a["Dl"], a["Dr"], a["scale"], a["out"],
+                                            a["lse"], a["ws"], a["wsb"], None)
+    return L.LIB.dsa_sparse_mla_decode(a["q"], pp, tp, a["idx"], a["ld_idx"], a["k"], a["H"], a["Dl"],
+                                       a["Dr"], a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), L.DSA_ERR_INVALID),
+    (dict(out=None), L.DSA_ERR_INVALID),
+    (dict(idx=None), L.DSA_ERR_INVALID),
+    (dict(pool=None), L.DSA_ERR_INVALID),
+    (dict(pt=None), L.DSA_ERR_INVALID),
+    (dict(pool=pool(row=512)), L.DSA_ERR_INVALID),
+    (dict(H=32), L.DSA_ERR_UNSUPPORTED),
+    (dict(Dl=256, Dr=320), L.DSA_ERR_UNSUPPORTED),
+    (dict(k=4096, ld_idx=4096), L.DSA_ERR_UNSUPPORTED),
+    (dict(ld_idx=100), L.DSA_ERR_INVALID),
+    (dict(scale=float("inf")), L.DSA_ERR_INVALID),
+    (dict(ws=None), L.DSA_ERR_WORKSPACE),
+    (dict(wsb=16), L.DSA_ERR_WORKSPACE),
+    (dict(out=FAKE + 2), L.DSA_ERR_INVALID),
+    (dict(pool=pool(L.DSA_F32, row=80), H=65, Dl=64, Dr=16), L.DSA_ERR_UNSUPPORTED),
+    (dict(pool=pool(L.DSA_F32, row=1028), H=8, Dl=1024, Dr=4), L.DSA_ERR_UNSUPPORTED),
+])
+def test_mla_rejects(prefill, kw, status):
+    assert mla_call(prefill, **kw) == status
+
+
+def test_mla_f32_small_dims_accepted_without_workspace():
+    # an empty prefill chunk passes every check and enqueues nothing
+    assert mla_call(True, T=0, pool=pool(L.DSA_F32, row=80), H=8, Dl=64, Dr=16, k=64, ld_idx=64,
+                    ws=None, wsb=0) == L.DSA_OK
+
+
+def test_prefill_requires_positions():
+    assert mla_call(True, q_row=None) == L.DSA_ERR_INVALID
+    assert mla_call(True, q_pos=None) == L.DSA_ERR_INVALID
+    assert mla_call(True, T=-1) == L.DSA_ERR_INVALID
+
+
+def test_workspace_sizes():
+    # decode of 1 token splits the 2048-entry list 32 ways; a 4096-token prefill does not split
+    one = L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 1, 0, 2048, 64, 512)
+    assert one == 32 * 64 * (512 + 2) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 4096, 0, 2048, 64, 512) == 0
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 0, 0, 2048, 64, 512) == 0
+    # rows of at most 32768 positions are selected in one workgroup: no workspace
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 64, 32768, 2048, 0, 0) == 0
+    # longer rows: per-chunk (key, position) lists and counts
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 40, 131072, 2048, 0, 0) == 40 * 4 * (2048 * 8 + 4)
+
+
+def test_index_cache_host_logic():
+    c = L.DsaIndexCache()
+    lib = L.LIB
+    assert lib.dsa_index_cache_init(ctypes.byref(c), FAKE, 2048, 40, 2048, 4) == L.DSA_OK
+    out = ctypes.c_void_p()
+    assert lib.dsa_index_cache_get(ctypes.byref(c), 0, 1, ctypes.byref(out)) == L.DSA_ERR_STALE_INDEX
+    assert lib.dsa_index_cache_publish(ctypes.byref(c), 7) == L.DSA_OK
+    for layer in (1, 2, 3):
+        out = ctypes.c_void_p()
+        assert lib.dsa_index_cache_get(ctypes.byref(c), 7, layer, ctypes.byref(out)) == L.DSA_OK
+        assert out.value == FAKE
+    assert lib.dsa_index_cache_get(ctypes.byref(c), 7, 0, ctypes.byref(out)) == L.DSA_ERR_STALE_INDEX
+    assert lib.dsa_index_cache_get(ctypes.byref(c), 7, 4, ctypes.byref(out)) == L.DSA_ERR_STALE_INDEX
+    assert lib.dsa_index_cache_get(ctypes.byref(c), 8, 1, ctypes.byref(out)) == L.DSA_ERR_STALE_INDEX
+    assert lib.dsa_index_cache_publish(ctypes.byref(c), 8) == L.DSA_OK
+    assert lib.dsa_index_cache_get(ctypes.byref(c), 7, 1, ctypes.byref(out)) == L.DSA_ERR_STALE_INDEX
+    assert lib.dsa_index_cache_init(ctypes.byref(c), FAKE, 100, 40, 2048, 4) == L.DSA_ERR_INVALID
+    assert lib.dsa_index_cache_init(ctypes.byref(c), FAKE, 2048, 40, 2048, 1) == L.DSA_ERR_INVALID
+    assert lib.dsa_index_cache_init(ctypes.byref(c), None, 2048, 40, 2048, 4) == L.DSA_ERR_INVALID

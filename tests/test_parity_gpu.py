@@ -1,0 +1,315 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Bars: indexer scores and top-k index sets bit-exact; attention outputs within the
+normwise relative error 1e-5 (fp32) / 2e-2 (bf16) per (token, head) row:
+max_c |out - ref| / max_c |ref|; lse within 1e-5 relative (fp32) / 2e-3 absolute (bf16).
+Small cases check every token; the full-size workloads (the launch configuration the
+benchmark times) check sampled tokens, each computed one by one by the oracle.
+"""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as I
+from oracle import dsa_oracle as O
+from oracle import run as R
+
+pytestmark = pytest.mark.gpu
+
+import sparse_attention_19_amd as D  # noqa: E402  (fails loudly if the library is missing)
+from sparse_attention_19_amd import pipeline as P  # noqa: E402
+
+DEV = "cuda"
+OUT_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def rel_rows(got: np.ndarray, ref: np.ndarray) -> float:
+    num = np.abs(got - ref).max(axis=1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((num / den).max())
+
+
+def check_token(inp, buf, t, layers=None, key_cache=None, check_scores=True):
+    cfg = inp["cfg"]
+    exp = R.expected_token(inp, t, layers, key_cache)
+    n = exp["n"]
+    if check_scores:
+        got = buf.scores[t, :n].cpu().numpy()
+        bad = np.nonzero(got.view(np.int32) != exp["scores"].view(np.int32))[0]
+        assert bad.size == 0, f"token {t}: {bad.size} score mismatches, first at {bad[:5]}"
+    gidx = buf.idx[t].cpu().numpy()
+    assert np.array_equal(gidx, exp["idx"]), f"token {t}: top-k differs (n={n})"
+    layers = range(cfg.layers) if layers is None else layers
+    for li, l in enumerate(layers):
+        out = R.to_f64(buf.outs[l][t])
+        e = rel_rows(out, exp["out"][li])
+        assert e <= OUT_TOL[cfg.dtype], f"token {t} layer {l}: out rel err {e:.3g}"
+        lse = buf.lses[l][t].cpu().double().numpy()
+        if cfg.dtype == torch.float32:
+            assert np.allclose(lse, exp["lse"][li], rtol=1e-5, atol=1e-5)
+        else:
+            assert np.abs(lse - exp["lse"][li]).max() <= 2e-3, np.abs(lse - exp["lse"][li]).max()
+    return exp
+
+
+def run_cfg(cfg, **over):
+    if over:
+        cfg = I.shrink(cfg, **over)
+    log(f"[gpu] inputs {cfg.name} {over}")
+    inp = I.make_inputs(cfg, DEV)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    return inp, buf
+
+
+# ------------------------------------------------------------------ small cases, every token
+
+def test_tiny_fp32_full_path():
+    inp, buf = run_cfg(I.CONFIGS["tiny_fp32"])
+    check_token(inp, buf, 0)
+
+
+def test_tiny_fp32_dense_and_ragged():
+    # several requests, lengths around k = 64 and not multiples of the page size
+    cfg = I.shrink(I.CONFIGS["tiny_fp32"], batch=7, ctx_range=(1, 300), identity_pages=False)
+    inp = I.make_inputs(cfg, DEV)
+    lens = inp["seq_len"].tolist()
+    log(f"[gpu] tiny ragged lens {lens}")
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in range(len(lens)):
+        check_token(inp, buf, t)
+
+
+def test_bf16_decode_ragged_batch():
+    # lengths straddle k = 2048 (dense and sparse rows), ragged last pages, random pages
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=6, ctx_range=(1, 6000))
+    inp = I.make_inputs(cfg, DEV)
+    lens = inp["seq_len"].tolist()
+    log(f"[gpu] bf16 ragged lens {lens}")
+    assert min(lens) <= 2048 < max(lens)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in range(len(lens)):
+        check_token(inp, buf, t)
+
+
+def test_bf16_decode_edge_lengths():
+    # n = 1, n = k, n = k + 1, n a multiple of 64, n = 64k + 1
+    lens = [1, 2048, 2049, 4096, 4097, 63, 65, 2047]
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=len(lens), ctx_range=None)
+    inp = I.make_inputs(cfg, DEV)
+    # override lengths: block tables are sized for cfg.ctx so any length <= ctx is valid
+    inp["seq_len"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    inp["q_pos"] = inp["seq_len"] - 1
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in range(len(lens)):
+        check_token(inp, buf, t)
+
+
+def test_bf16_prefill_small_multi_request():
+    # a chunk whose tokens cross n = k, plus tokens of a second request in the same chunk
+    cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], ctx=2100, prefill_tokens=100)
+    inp = I.make_inputs(cfg, DEV)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    kc = {}
+    for t in list(range(0, 100, 7)) + [47, 48, 49, 99]:
+        check_token(inp, buf, t, key_cache=kc)
+    # mixed requests: same pools, two requests with different page tables
+    cfg2 = I.shrink(I.CONFIGS["decode_b64_paged"], batch=2, ctx_range=None, ctx=3000)
+    inp2 = I.make_inputs(cfg2, DEV)
+    T = 24
+    q_row = torch.tensor([i % 2 for i in range(T)], dtype=torch.int32)
+    q_pos = torch.tensor([2990 - 100 * i if i % 3 else 2000 + i for i in range(T)], dtype=torch.int32)
+    inp2["q_row"], inp2["q_pos"] = q_row.to(DEV), q_pos.to(DEV)
+    inp2["q_idx"] = inp2["q_idx"][:1].repeat(T, 1, 1).contiguous()
+    inp2["q_idx"] = (inp2["q_idx"] + torch.arange(T, device=DEV).view(T, 1, 1).remainder(3)
+                     .to(inp2["q_idx"].dtype) - 1).contiguous()
+    inp2["w"] = inp2["w"][:1].repeat(T, 1).contiguous()
+    g = torch.Generator(device=DEV).manual_seed(7)
+    inp2["q"] = [torch.randn(T, 64, 576, device=DEV, generator=g).to(torch.bfloat16)]
+    inp2["cfg"] = I.shrink(cfg2, prefill_tokens=T)
+    buf2 = P.run_inputs(inp2)
+    torch.cuda.synchronize()
+    for t in range(T):
+        check_token(inp2, buf2, t)
+
+
+def test_mla_alternative_scale():
+    # the 1/16 = 1/sqrt(256) reading of the softmax scale (GLM-5 SDPA head dim)
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=3, ctx_range=(1000, 9000), sm_scale=1.0 / 16)
+    inp, buf = run_cfg(cfg)
+    for t in range(3):
+        check_token(inp, buf, t)
+
+
+# ------------------------------------------------------------------ top-k in isolation
+
+def _topk_case(scores: np.ndarray, n_valid, k):
+    rows, ld = scores.shape
+    s = torch.from_numpy(scores.astype(np.float32)).to(DEV)
+    nv = torch.tensor(n_valid, dtype=torch.int32, device=DEV)
+    idx = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    D.dsa_topk(s, nv, k, idx, ws=D.workspace(D.DSA_OP_TOPK, rows, ld, k, 0, 0, DEV))
+    torch.cuda.synchronize()
+    exp = R.expected_topk(scores.astype(np.float32), np.array(n_valid), k)
+    got = idx.cpu().numpy()
+    for r in range(rows):
+        assert np.array_equal(got[r], exp[r]), f"row {r} n={n_valid[r]} k={k}"
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 2048])
+def test_topk_adversarial(k):
+    rng = np.random.default_rng(k)
+    ld = 40000
+    rows = []
+    nv = []
+    rows.append(np.full(ld, 3.0)); nv.append(ld)                                  # all equal
+    rows.append(rng.integers(0, 2, ld).astype(np.float64)); nv.append(ld)         # two values
+    r = rng.standard_normal(ld); r[rng.integers(0, ld, 500)] = 0.0
+    r[rng.integers(0, ld, 500)] = -0.0; nv.append(ld); rows.append(r)             # signed zeros
+    rows.append(rng.integers(-3, 4, ld).astype(np.float64)); nv.append(k)        # n = k
+    rows.append(rng.integers(-3, 4, ld).astype(np.float64)); nv.append(k + 1)    # n = k + 1
+    rows.append(rng.integers(-3, 4, ld).astype(np.float64)); nv.append(max(0, k - 1))
+    rows.append(rng.integers(-3, 4, ld).astype(np.float64)); nv.append(0)         # empty
+    rows.append(rng.integers(0, 50, ld).astype(np.float64)); nv.append(32768)    # cache edge
+    rows.append(rng.integers(0, 50, ld).astype(np.float64)); nv.append(32769)
+    rows.append(-np.abs(rng.standard_normal(ld)) * 1e30); nv.append(ld)          # huge negatives
+    rows.append(np.where(np.arange(ld) > ld - k - 3, 5.0, 1.0)); nv.append(ld)   # winners at the end
+    _topk_case(np.stack(rows), nv, k)
+
+
+def test_topk_long_rows_ties():
+    rng = np.random.default_rng(5)
+    ld = 131072
+    sc = np.stack([rng.integers(0, 300, ld).astype(np.float64), np.full(ld, 1.0),
+                   rng.integers(0, 4, ld) * 1000.0])
+    _topk_case(sc, [ld, ld, 100000], 2048)
+
+
+def test_topk_prefill_offset():
+    # n_add = 1: row r considers q_pos[r] + 1 positions
+    rng = np.random.default_rng(9)
+    sc = rng.integers(0, 100, (5, 5000)).astype(np.float32)
+    q_pos = [0, 99, 2047, 2048, 4999]
+    s = torch.from_numpy(sc).to(DEV)
+    idx = torch.empty((5, 2048), dtype=torch.int32, device=DEV)
+    D.dsa_topk(s, torch.tensor(q_pos, dtype=torch.int32, device=DEV), 2048, idx, n_add=1)
+    exp = R.expected_topk(sc, np.array(q_pos) + 1, 2048)
+    assert np.array_equal(idx.cpu().numpy(), exp)
+
+
+# ------------------------------------------------------------------ layout and determinism
+
+def test_paged_layout_invariance_and_determinism():
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=4, ctx_range=(3000, 9000))
+    inp = I.make_inputs(cfg, DEV)
+    a = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    snap = [a.scores.clone(), a.idx.clone(), a.outs[0].clone(), a.lses[0].clone()]
+    b = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    lens = inp["seq_len"].tolist()
+    for t, n in enumerate(lens):           # run-to-run bit identical (scores past n are unwritten)
+        assert torch.equal(snap[0][t, :n], b.scores[t, :n])
+    for x, y in zip(snap[1:], [b.idx, b.outs[0], b.lses[0]]):
+        assert torch.equal(x, y)
+    # same logical rows laid out with an identity page table
+    bt = inp["block_table"]
+    ident = torch.full_like(bt, -1)
+    kp = torch.empty_like(inp["k_pool"])
+    kvp = torch.empty_like(inp["kv_pools"][0])
+    off = 0
+    for r, n in enumerate(lens):
+        nb = (n + 63) // 64
+        phys = bt[r, :nb].long()
+        ident[r, :nb] = torch.arange(off, off + nb, dtype=torch.int32, device=DEV)
+        kp[off:off + nb] = inp["k_pool"][phys]
+        kvp[off:off + nb] = inp["kv_pools"][0][phys]
+        off += nb
+    inp2 = dict(inp, block_table=ident, k_pool=kp, kv_pools=[kvp])
+    c = P.run_inputs(inp2)
+    torch.cuda.synchronize()
+    for t, n in enumerate(lens):
+        assert torch.equal(c.scores[t, :n], snap[0][t, :n])
+    assert torch.equal(c.idx, snap[1])
+    assert torch.equal(c.outs[0], snap[2])
+    assert torch.equal(c.lses[0], snap[3])
+
+
+def test_indexshare_reuses_first_layer_selection():
+    cfg = I.shrink(I.CONFIGS["indexshare_decode_4layer"], batch=3, ctx=5000, extra_dense=(1500, 700))
+    inp, buf = run_cfg(cfg)
+    for t in range(5):
+        check_token(inp, buf, t)
+    # the shared layers' outputs equal a plain decode of that layer with layer 0's idx
+    cache = buf.cache
+    with pytest.raises(D.DsaError):
+        cache.get(step=1, layer_in_group=1)
+    with pytest.raises(D.DsaError):
+        cache.get(step=0, layer_in_group=4)
+    idx = cache.get(0, 2)
+    out = torch.empty_like(buf.outs[2])
+    lse = torch.empty_like(buf.lses[2])
+    ws = D.workspace(D.DSA_OP_MLA, 5, 0, cfg.k, cfg.H, cfg.Dl, DEV)
+    D.dsa_sparse_mla_decode(inp["q"][2], inp["kv_pools"][2], inp["block_table"], inp["seq_len"], idx,
+                            cfg.k, cfg.sm_scale, out, lse, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, buf.outs[2]) and torch.equal(lse, buf.lses[2])
+
+
+def test_empty_prefill_chunk_is_a_noop():
+    cfg = I.CONFIGS["decode_b1_32k"]
+    z = torch.zeros((0,), dtype=torch.int32, device=DEV)
+    kv = torch.zeros((1, 64, 576), dtype=torch.bfloat16, device=DEV)
+    bt = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    sl = torch.ones((1,), dtype=torch.int32, device=DEV)
+    q = torch.zeros((0, 64, 576), dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros((0, 64, 512), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((0, 2048), dtype=torch.int32, device=DEV)
+    D.dsa_sparse_mla_prefill(q, kv, bt, sl, z, z, idx, 2048, cfg.sm_scale, out)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def test_full_decode_b1_32k():
+    inp, buf = run_cfg(I.CONFIGS["decode_b1_32k"])
+    check_token(inp, buf, 0)
+
+
+def test_full_decode_b64_paged_sampled():
+    inp, buf = run_cfg(I.CONFIGS["decode_b64_paged"])
+    lens = inp["seq_len"].tolist()
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 17, 40})
+    for t in pick:
+        log(f"[gpu] decode_b64 token {t} n={lens[t]}")
+        check_token(inp, buf, t)
+
+
+def test_full_indexshare_sampled():
+    inp, buf = run_cfg(I.CONFIGS["indexshare_decode_4layer"])
+    for t in (0, 19, 31, 32, 39):
+        log(f"[gpu] indexshare token {t}")
+        check_token(inp, buf, t)
+
+
+def test_full_prefill_sampled():
+    inp, buf = run_cfg(I.CONFIGS["prefill_4096_at_128k"])
+    kc = {}
+    random.seed(3)
+    for t in sorted({0, 1, 2047, 4094, 4095, *random.sample(range(4096), 3)}):
+        log(f"[gpu] prefill token {t}")
+        check_token(inp, buf, t, key_cache=kc)
