@@ -63,4 +63,20 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
+#define DSA_VMCNT(n) (((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
+#define DSA_LGKMCNT0 0xc07f
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load (vmcnt(0)), which would drain loads that are deliberately left
+// in flight across the barrier (prefetched tiles).  This waits only for the wave's own
+// LDS operations; asynchronous global->LDS copies must be waited for explicitly (vmcnt)
+// by the wave that issued them before it reaches the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace dsa

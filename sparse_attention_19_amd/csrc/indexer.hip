@@ -6,12 +6,17 @@
 //
 // bf16 instance (64 heads x 128 dims): a GEMM  C[head][key] = Q[head][:] . K[key][:]  on
 // 32x32x16 MFMA with the ReLU and the head-weighted reduction fused into the epilogue, so
-// the per-head logits never leave registers.  Keys stream from the paged pool through a
-// double-buffered LDS tile of 128 keys (2 pages):
-//   decode  : one query token per workgroup; the 4 waves split each key tile (32 keys each)
-//             -> the key cache is read exactly once (HBM-bound streaming)
-//   prefill : 8 query tokens per workgroup (one per wave of 8); every wave consumes the whole
-//             key tile -> each key tile fetched from L2/MALL once per 8 tokens (MFMA-bound)
+// the per-head logits never leave registers.
+//   decode  : HBM-bound streaming of the key cache, read exactly once.  Each workgroup is a
+//             single wave that owns a range of one request's keys and streams it in 32-key
+//             slices (8 KB) through a 3-slot LDS ring filled by global_load_lds_dwordx4
+//             (no staging registers; two slices in flight while the third is consumed).
+//             Rows land XOR-swizzled (16-byte chunk c of row r at chunk c ^ (r % 16)) so
+//             the MFMA operand reads are bank-conflict-free; scores collect in LDS and
+//             leave in one coalesced burst.
+//   prefill : 8 query tokens per workgroup (one per wave of 8) share a double-buffered
+//             128-key LDS tile -> each key tile is fetched from L2/MALL once per 8 tokens
+//             (MFMA-bound).
 // The contraction order over the 128 dims is permuted identically for Q and K (lane half h
 // of k-step s holds dims 64h + 8s .. 64h + 8s + 7), which lets every lane fetch its 8 steps
 // as one contiguous 128-byte run.
@@ -189,6 +194,100 @@ __global__ __launch_bounds__(kDecode ? 256 : 512) void indexer_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
+// decode: one wave per workgroup, grid (key ranges of `range` keys, T)
+constexpr int kSlice = 32;                       // keys per slice
+constexpr int kSliceBytes = kSlice * kRowBytes;  // 8 KB
+constexpr int kRing = 3;
+constexpr int kMaxRange = 1024;
+
+__device__ __forceinline__ float score32_swz(const QFrag& f, const uint8_t* slice) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, h = lane >> 5;
+  const uint8_t* row = slice + n * kRowBytes;
+  f32x16 c0 = {}, c1 = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int chunk = (8 * h + s) ^ (n & 15);
+    const bf16x8 b = as_bf8(*reinterpret_cast<const uint4*>(row + 16 * chunk));
+    c0 = mfma32(f.a[0][s], b, c0);
+    c1 = mfma32(f.a[1][s], b, c1);
+  }
+  float p = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    p = fmaf(f.w[0][j], fmaxf(c0[j], 0.f), p);
+    p = fmaf(f.w[1][j], fmaxf(c1[j], 0.f), p);
+  }
+  p += __shfl_xor(p, 32, kWave);
+  return p + 0.0f;   // canonical +0.0
+}
+
+__global__ __launch_bounds__(64) void indexer_decode_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ pool,
+    int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
+    int max_blocks, int batch, const int* __restrict__ q_row, const int* __restrict__ q_pos,
+    int range, float* __restrict__ scores, int64_t ld) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kSliceBytes];
+  __shared__ float sc[kMaxRange];
+  const int lane = threadIdx.x;
+  const int t = blockIdx.y;
+  const int b = q_row ? q_row[t] : t;
+  if (b < 0 || b >= batch) return;
+  int n = q_pos ? q_pos[t] + 1 : seq_len[b];
+  n = max(0, min(n, max_blocks * kBlock));
+  const int key0 = blockIdx.x * range;
+  if (key0 >= n) return;
+  const int key_end = min(n, key0 + range);
+  const int ns = (key_end - key0 + kSlice - 1) / kSlice;
+
+  // physical block of each page of the range (lane i holds page i); one round trip
+  const int blk0 = key0 / kBlock;
+  const int nbk = (key_end - key0 + kBlock - 1) / kBlock;
+  int my_phys = -1;
+  if (lane < nbk) my_phys = block_table[(int64_t)b * max_blocks + blk0 + lane];
+  const bool my_ok = my_phys >= 0 && my_phys < num_blocks;
+
+  QFrag f;
+  load_qfrag(f, q_idx + (int64_t)t * kHi * kRowBytes, w + (int64_t)t * kHi);
+
+  // issue the 8 loads of slice sl into ring slot sl % 3; lane l of load i fills
+  // (row 4i + l/16, LDS chunk l%16) with global chunk (l%16) ^ (row % 16)
+  auto issue = [&](int sl) {
+    const int page = (sl * kSlice) / kBlock;
+    const int phys = __shfl(my_phys, page, kWave);
+    const bool ok = __shfl((int)my_ok, page, kWave) != 0;
+    // an unusable page reads block 0 (always valid memory); its scores are zeroed below
+    const uint8_t* base = pool + ((int64_t)(ok ? phys : 0) * kBlock + (key0 + sl * kSlice) % kBlock) *
+                                     kRowBytes;
+    uint8_t* dst = ring[sl % kRing];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      __builtin_amdgcn_global_load_lds(base + r * kRowBytes + 16 * c,
+                                       DSA_LDS(void, dst + 1024 * i), 16, 0, 0);
+    }
+  };
+  for (int sl = 0; sl < kRing && sl < ns; ++sl) issue(sl);
+  for (int sl = 0; sl < ns; ++sl) {
+    if (sl + 2 < ns) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(16));
+    else if (sl + 1 < ns) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(8));
+    else __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
+    float p = score32_swz(f, ring[sl % kRing]);
+    const int page = (sl * kSlice) / kBlock;
+    if (__shfl((int)my_ok, page, kWave) == 0) p = 0.f;   // empty row: score 0
+    if (lane < kSlice) sc[sl * kSlice + lane] = p;
+    if (sl + kRing < ns) {
+      __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);   // the slot's operand reads are done
+      issue(sl + kRing);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
+  float* dst = scores + (int64_t)t * ld + key0;
+  for (int i = lane; i < key_end - key0; i += kWave) dst[i] = sc[i];
+}
+
+// ---------------------------------------------------------------------------------------
 // fp32 instance (small dims: Hi <= 64, Di <= 128): plain VALU, one key per thread.
 constexpr int kF32Keys = 256;
 
@@ -244,15 +343,13 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
                          a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.T, per,
                          a.scores, a.ld);
     } else {
-      // aim for >= ~2048 workgroups over the batch; at most 8 tiles (1024 keys) each
-      const int tiles = (max_keys + kTileKeys - 1) / kTileKeys;
-      int per = 8;
-      while (per > 1 && (int64_t)a.T * ((tiles + per - 1) / per) < 2048) per >>= 1;
-      dim3 grid((tiles + per - 1) / per, a.T);
-      hipLaunchKernelGGL(indexer_bf16_kernel<true>, grid, dim3(256), 0, stream,
-                         (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool, a.num_blocks,
-                         a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.T, per,
-                         a.scores, a.ld);
+      // key ranges of 128..1024 keys: at least ~2048 single-wave workgroups over the batch
+      int range = kMaxRange;
+      while (range > 128 && (int64_t)a.T * ((max_keys + range - 1) / range) < 2048) range >>= 1;
+      dim3 grid((max_keys + range - 1) / range, a.T);
+      hipLaunchKernelGGL(indexer_decode_kernel, grid, dim3(64), 0, stream, (const uint8_t*)a.q_idx, a.w,
+                         (const uint8_t*)a.pool, a.num_blocks, a.block_table, a.seq_len, a.max_blocks,
+                         a.batch, a.q_row, a.q_pos, range, a.scores, a.ld);
     }
   } else {
     dim3 grid((max_keys + kF32Keys - 1) / kF32Keys, a.T);

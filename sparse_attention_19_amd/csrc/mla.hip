@@ -32,43 +32,24 @@ namespace {
 
 constexpr int kH = 64, kDl = 512, kRow = 576;
 constexpr int kRowBytes = kRow * 2;             // 1152
-constexpr int kMT = 32;                         // rows per tile
-constexpr int kLdsRowBytes = 1184;              // padded: 296 dwords == 8 (mod 64) banks
-constexpr int kTileBytes = kMT * kLdsRowBytes;  // 37888
 constexpr int kChunks = kRowBytes / 16;         // 72 x 16 B per row
-constexpr int kThreads = 256;
-constexpr int kGatherPer = kMT * kChunks / kThreads;   // 9
+constexpr int kMT = 32;                         // rows per tile
+constexpr int kRowSlots = kChunks + 1;          // LDS row stride: 73 chunks (odd)
+constexpr int kTileSlots = kMT * kRowSlots;     // 2336
+constexpr int kTileBytes = kTileSlots * 16;     // 37376
+constexpr int kTileLoads = (kTileSlots + 63) / 64;   // 37 direct-to-LDS loads of 1 KB
+constexpr int kRing = 3;                        // LDS tile slots: 2 tiles in flight
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxLoadsPerWave = (kTileLoads + kWaves - 1) / kWaves;   // 5 (waves 0-4), 4 (5-7)
 constexpr int kMaxList = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;            // log2 units a running max may lag behind
 
-struct Gather { uint4 v[kGatherPer]; };
-
-__device__ __forceinline__ void gather_tile(Gather& g, const uint8_t* pool, const int* rowid,
-                                            int e0, int nent) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < kGatherPer; ++j) {
-    const int id = tid + kThreads * j;
-    const int row = id / kChunks, ch = id - row * kChunks;
-    const int e = e0 + row;
-    const int rid = e < nent ? rowid[e] : -1;
-    if (rid >= 0)
-      g.v[j] = *reinterpret_cast<const uint4*>(pool + (int64_t)rid * kRowBytes + ch * 16);
-    else
-      g.v[j] = make_uint4(0, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void stash_tile(const Gather& g, uint8_t* lds) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < kGatherPer; ++j) {
-    const int id = tid + kThreads * j;
-    const int row = id / kChunks, ch = id - row * kChunks;
-    *reinterpret_cast<uint4*>(lds + row * kLdsRowBytes + ch * 16) = g.v[j];
-  }
-}
+// LDS placement of 16-byte chunk `ch` of tile row `row`: rows 73 chunks apart, so the 16
+// rows of one MFMA operand fetch fall on 16 different 16-byte bank groups (9r mod 16).
+__device__ __forceinline__ int tile_slot(int row, int ch) { return row * kRowSlots + ch; }
 
 // Resolve the token's (request, n) and this split's slice [i0, i0 + nent) of the
 // selected list; fills rowid[] with global row ids (phys * 64 + slot) or -1.
@@ -102,99 +83,189 @@ __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const in
   }
 }
 
+// Direct-to-LDS gather of one tile (rows e0 .. e0+31 of the list): load m of wave w fills
+// tile slots 64*(w + 8m) + lane.  The (row, chunk) each lane fetches is fixed for the whole
+// kernel and precomputed; lanes on a row's pad slot stay idle.  Rows without a valid
+// position read row 0 of the pool (always valid memory); their logits are masked.
+struct TileLoads {
+  int row[kMaxLoadsPerWave];
+  int off[kMaxLoadsPerWave];   // byte offset of the chunk within its row
+  uint32_t active;             // bit m: load m is issued by this wave and this lane
+  int count;                   // loads this wave issues per tile
+};
+
+__device__ __forceinline__ TileLoads plan_tile_loads() {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  TileLoads tl;
+  tl.active = 0;
+  tl.count = (kTileLoads - wave + kWaves - 1) / kWaves;
+#pragma unroll
+  for (int m = 0; m < kMaxLoadsPerWave; ++m) {
+    const int s = 64 * (wave + kWaves * m) + lane;
+    const int row = s / kRowSlots, ch = s - row * kRowSlots;
+    tl.row[m] = row < kMT ? row : 0;
+    tl.off[m] = 16 * ch;
+    if (m < tl.count && row < kMT && ch < kChunks) tl.active |= 1u << m;
+  }
+  return tl;
+}
+
+// Row ids of this lane's loads of the tile starting at list entry e0 (-1: none).
+__device__ __forceinline__ void tile_rowids(const TileLoads& tl, const int* rowid, int e0, int nent,
+                                            int (&rid)[kMaxLoadsPerWave]) {
+#pragma unroll
+  for (int m = 0; m < kMaxLoadsPerWave; ++m) {
+    const int e = e0 + tl.row[m];
+    rid[m] = (m < tl.count && e < nent) ? rowid[e] : -1;
+  }
+}
+
+__device__ __forceinline__ void issue_tile(const TileLoads& tl, const uint8_t* pool,
+                                           const int (&rid)[kMaxLoadsPerWave], uint8_t* dst) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < kMaxLoadsPerWave; ++m) {
+    if (m >= tl.count) break;                      // uniform per wave
+    const uint8_t* src = pool + (int64_t)(rid[m] >= 0 ? rid[m] : 0) * kRowBytes + tl.off[m];
+    if (tl.active & (1u << m))
+      __builtin_amdgcn_global_load_lds(src, DSA_LDS(void, dst + 1024 * (wave + kWaves * m)), 16, 0, 0);
+  }
+}
+
+// 8 waves: wave w = (head group hg = w % 4: heads 16hg..16hg+15, half dh = w / 4).
+//   logits : wave (hg, dh) contracts dims 288dh .. 288dh+287 of all 32 keys of the tile
+//            against its 16 heads; the two partial logits of a head group are summed
+//            through LDS, leaving all 32 logits per head in the A-operand layout of P.V
+//   P.V    : wave (hg, dh) accumulates O[16 heads][dims 256dh .. 256dh+255]
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
     const int* __restrict__ block_table, const int* __restrict__ seq_len, int max_blocks, int batch,
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
     int64_t ld_idx, int k, float scale_log2, int splits, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv[2][kTileBytes];
+  constexpr int kSteps = kRow / 32 / 2;      // 9 k-steps of 32 dims per half
+  __shared__ __attribute__((aligned(16))) uint8_t kv[kRing][kTileBytes];
   __shared__ int rowid[kMaxList];
+  __shared__ f32x4 xch[kWaves][2][64];       // partial logits (keys 0-15, 16-31) per wave
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hg = wave & 3, dh = wave >> 2;
   const int g = lane >> 4, c16 = lane & 15;
   const int t = blockIdx.y, sp = blockIdx.x;
 
-  // Q^T fragments (B operand): head 16*wave + c16, dims 32*st + 8*g .. +8; issued first so
-  // their latency overlaps the index / page-table lookups
-  bf16x8 qf[kRow / 32];
+  // Q^T fragments (B operand): head 16*hg + c16, dims 288dh + 32*st + 8*g .. +8; issued
+  // first so their latency overlaps the index / page-table lookups
+  bf16x8 qf[kSteps];
   {
     const uint4* src = reinterpret_cast<const uint4*>(
-        q + ((int64_t)t * kH + 16 * wave + c16) * kRowBytes + 16 * g);
+        q + ((int64_t)t * kH + 16 * hg + c16) * kRowBytes + 576 * dh + 16 * g);
 #pragma unroll
-    for (int st = 0; st < kRow / 32; ++st) qf[st] = as_bf8(src[4 * st]);
+    for (int st = 0; st < kSteps; ++st) qf[st] = as_bf8(src[4 * st]);
   }
+  const TileLoads tl = plan_tile_loads();
   int nent;
   resolve_rows(t, sp, splits, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos,
                idx, ld_idx, k, rowid, nent);
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[kDl / 16];
+  f32x4 o[kDl / 32];
 #pragma unroll
-  for (int dt = 0; dt < kDl / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < kDl / 32; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int ka = 16 * tile_slot(c16, g) + 576 * dh;                       // + 64 st
+  const int vb = 16 * tile_slot(4 * g + (c16 >> 2), 0) + 8 * (c16 & 3) + 512 * dh;  // + 32 dt
   const int ntiles = (nent + kMT - 1) / kMT;
-  Gather gt;
-  if (ntiles > 0) gather_tile(gt, pool, rowid, 0, nent);
+  int rid[kMaxLoadsPerWave];
+  if (ntiles > 0) {
+    tile_rowids(tl, rowid, 0, nent, rid);
+    issue_tile(tl, pool, rid, kv[0]);
+  }
+  if (ntiles > 1) {
+    tile_rowids(tl, rowid, kMT, nent, rid);
+    issue_tile(tl, pool, rid, kv[1]);
+  }
   for (int tile = 0; tile < ntiles; ++tile) {
-    uint8_t* kb = kv[tile & 1];
-    stash_tile(gt, kb);
-    __syncthreads();
-    if (tile + 1 < ntiles) gather_tile(gt, pool, rowid, (tile + 1) * kMT, nent);
+    const int e0 = tile * kMT;
+    // LDS lookups for this iteration, issued before the waits so they resolve meanwhile:
+    // row ids of the tile to prefetch and the validity of this tile's rows
+    tile_rowids(tl, rowid, e0 + 2 * kMT, nent, rid);
+    const int er = e0 + (lane & 31);
+    const int vr = er < nent ? rowid[er] : -1;
+    // this wave's loads of `tile` done (the next tile's may still fly), then everyone's
+    if (tile + 1 < ntiles) {
+      if (tl.count == 5) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(5));
+      else __builtin_amdgcn_s_waitcnt(DSA_VMCNT(4));
+    } else {
+      __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
+    }
+    lds_barrier();
+    // every wave finished tile-1, so its slot takes tile+2
+    if (tile + 2 < ntiles) issue_tile(tl, pool, rid, kv[(tile + 2) % kRing]);
+    const uint8_t* kb = kv[tile % kRing];
+    // valid rows of the tile as a bit mask (row r -> bit r)
+    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);
 
-    // logits for keys 4g+j (s0) and 16+4g+j (s1), head c16
+    // partial logits over this wave's 288 dims: keys 4g+j (s0) and 16+4g+j (s1), head c16
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* ka = kb + c16 * kLdsRowBytes + 16 * g;
 #pragma unroll
-    for (int st = 0; st < kRow / 32; ++st) {
-      const bf16x8 a0 = as_bf8(*reinterpret_cast<const uint4*>(ka + 64 * st));
-      const bf16x8 a1 = as_bf8(*reinterpret_cast<const uint4*>(ka + 16 * kLdsRowBytes + 64 * st));
+    for (int st = 0; st < kSteps; ++st) {
+      const bf16x8 a0 = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 64 * st));
+      const bf16x8 a1 = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 16 * 16 * kRowSlots + 64 * st));
       s0 = mfma16(a0, qf[st], s0);
       s1 = mfma16(a1, qf[st], s1);
     }
+    xch[wave][0][lane] = s0;
+    xch[wave][1][lane] = s1;
+    lds_barrier();
+    const f32x4 p0 = xch[wave ^ 4][0][lane], p1 = xch[wave ^ 4][1][lane];
+
     float x[8];
-    const int e0 = tile * kMT;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int ea = e0 + 4 * g + j, eb = e0 + 16 + 4 * g + j;
-      x[j] = (ea < nent && rowid[ea] >= 0) ? s0[j] * scale_log2 : -INFINITY;
-      x[4 + j] = (eb < nent && rowid[eb] >= 0) ? s1[j] * scale_log2 : -INFINITY;
+      // both waves of the head group add the same two partials (commutative: same bits)
+      const float la = dh ? p0[j] + s0[j] : s0[j] + p0[j];
+      const float lb = dh ? p1[j] + s1[j] : s1[j] + p1[j];
+      x[j] = (vmask >> (4 * g + j)) & 1u ? la * scale_log2 : -INFINITY;
+      x[4 + j] = (vmask >> (16 + 4 * g + j)) & 1u ? lb * scale_log2 : -INFINITY;
     }
     float tmax = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
+    // the running max only moves when a logit exceeds it by more than the slack, so
+    // exp2(x - m) stays <= 2^8 and the O rescale is rare
+    const bool grow = tmax > m_run + kRescaleSlack;
+    const float m_new = grow ? tmax : m_run;
     const bool none = (m_new == -INFINITY);
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
     float psum = 0.f;
     bf16x8 pa;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = none ? 0.f : exp2f(x[j] - m_new);
+      const float p = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
       psum += p;
       pa[j] = (__bf16)p;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (__ballot(alpha != 1.f)) {               // rescale O rows (heads 4g + j) by their alpha
+      float ar[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ar[j] = __shfl(alpha, 4 * g + j, kWave);
+#pragma unroll
+      for (int dt = 0; dt < kDl / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[dt][j] *= ar[j];
+    }
 
-    // rescale O rows (heads 4g + j of this wave) by their alpha
-    float ar[4];
+    // P.V: B operand rows 4g + j (slots 0..3) and 16 + 4g + j (slots 4..7), dims
+    // 256dh + 16dt + c16; lane (g, c16) addresses 4 dims (8 bytes) of row 4g + c16/4
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ar[j] = __shfl(alpha, 4 * g + j, kWave);
-#pragma unroll
-    for (int dt = 0; dt < kDl / 16; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[dt][j] *= ar[j];
-
-    // P.V: B operand rows 4g + j (slots 0..3) and 16 + 4g + j (slots 4..7), dims 16dt + c16
-    const uint8_t* vb = kb + (4 * g + (c16 >> 2)) * kLdsRowBytes + 8 * (c16 & 3);
-#pragma unroll
-    for (int dt = 0; dt < kDl / 16; ++dt) {
-      const s16x4 lo = lds_read_tr16(vb + 32 * dt);
-      const s16x4 hi = lds_read_tr16(vb + 16 * kLdsRowBytes + 32 * dt);
+    for (int dt = 0; dt < kDl / 32; ++dt) {
+      const s16x4 lo = lds_read_tr16(kb + vb + 32 * dt);
+      const s16x4 hi = lds_read_tr16(kb + vb + 16 * 16 * kRowSlots + 32 * dt);
       const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
                                                              hi[0], hi[1], hi[2], hi[3]};
       o[dt] = mfma16(pa, __builtin_bit_cast(bf16x8, v8), o[dt]);
@@ -207,29 +278,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   float lr[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) lr[j] = __shfl(l_tot, 4 * g + j, kWave);
-  const int head0 = 16 * wave + 4 * g;   // rows of o[dt][j]: head0 + j
+  const int head0 = 16 * hg + 4 * g;   // rows of o[dt][j]: head0 + j
+  const int dim0 = 256 * dh + c16;     // column of o[dt][*]: dim0 + 16 dt
   if (splits == 1) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float inv = lr[j] > 0.f ? 1.f / lr[j] : 0.f;
-      uint16_t* dst = out + ((int64_t)t * kH + head0 + j) * kDl + c16;
+      uint16_t* dst = out + ((int64_t)t * kH + head0 + j) * kDl + dim0;
 #pragma unroll
-      for (int dt = 0; dt < kDl / 16; ++dt) dst[16 * dt] = f2bf_bits(o[dt][j] * inv);
+      for (int dt = 0; dt < kDl / 32; ++dt) dst[16 * dt] = f2bf_bits(o[dt][j] * inv);
     }
-    if (lse && g == 0)
-      lse[(int64_t)t * kH + 16 * wave + c16] =
+    if (lse && g == 0 && dh == 0)
+      lse[(int64_t)t * kH + 16 * hg + c16] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     const int64_t base = ((int64_t)t * splits + sp) * kH;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float* dst = ws_o + (base + head0 + j) * kDl + c16;
+      float* dst = ws_o + (base + head0 + j) * kDl + dim0;
 #pragma unroll
-      for (int dt = 0; dt < kDl / 16; ++dt) dst[16 * dt] = o[dt][j];
+      for (int dt = 0; dt < kDl / 32; ++dt) dst[16 * dt] = o[dt][j];
     }
-    if (g == 0) {
-      ws_ml[(base + 16 * wave + c16) * 2 + 0] = m_run;
-      ws_ml[(base + 16 * wave + c16) * 2 + 1] = l_tot;
+    if (g == 0 && dh == 0) {
+      ws_ml[(base + 16 * hg + c16) * 2 + 0] = m_run;
+      ws_ml[(base + 16 * hg + c16) * 2 + 1] = l_tot;
     }
   }
 }
@@ -345,13 +417,14 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(
 
 }  // namespace
 
-// Splits of the selected list per token: enough (token, split) workgroups to cover the
-// 256 CUs once, at most 32, and never more than the list has tiles.
+// Splits of the selected list per token: as many (token, split) workgroups as fit in one
+// round on the 256 CUs (one workgroup per CU), at most 32 and never more than the list has
+// tiles.
 int mla_splits(int T, int k, bool bf16) {
   if (!bf16 || T <= 0) return 1;
   const int tiles = (k + kMT - 1) / kMT;
-  int s = 1;
-  while (s < 32 && (int64_t)T * s < 256) s <<= 1;
+  int s = 256 / T;
+  s = s < 1 ? 1 : (s > 32 ? 32 : s);
   return s < tiles ? s : tiles;
 }
 
