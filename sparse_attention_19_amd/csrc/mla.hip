@@ -132,35 +132,48 @@ __device__ __forceinline__ void issue_tile(const TileLoads& tl, const uint8_t* p
   }
 }
 
-// 8 waves: wave w = (head group hg = w % 4: heads 16hg..16hg+15, half dh = w / 4).
-//   logits : wave (hg, dh) contracts dims 288dh .. 288dh+287 of all 32 keys of the tile
-//            against its 16 heads; the two partial logits of a head group are summed
-//            through LDS, leaving all 32 logits per head in the A-operand layout of P.V
-//   P.V    : wave (hg, dh) accumulates O[16 heads][dims 256dh .. 256dh+255]
+// Per 32-row tile, 8 waves split the work three ways so that every tile byte is read from
+// LDS as few times as the register budget allows (2 waves per SIMD):
+//   logits  : wave w = (hg = w & 1: heads 32hg..32hg+31, dh = (w >> 1) & 1: dims
+//             288dh..288dh+287, kh = w >> 2: keys 16kh..16kh+15) computes partial
+//             S^T[key][head]; each K fragment read from LDS feeds two MFMAs (two head
+//             tiles).  Partials go to LDS.
+//   softmax : wave w owns heads 8w..8w+7 over all 32 keys: sums the two partials, applies
+//             the online-softmax update, writes P (bf16) and the per-head O rescale.
+//   P.V     : wave w owns output dims 64w..64w+63 of all 64 heads; each V fragment (read
+//             once from LDS with the transposing ds_read_b64_tr_b16) feeds four MFMAs.
+constexpr int kSRow = 36;          // partial-logit row stride (floats): conflict-free 16-byte writes
+constexpr int kPRow = 40;          // P row stride (bf16): 80 bytes, conflict-free operand reads
+
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
     const int* __restrict__ block_table, const int* __restrict__ seq_len, int max_blocks, int batch,
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
     int64_t ld_idx, int k, float scale_log2, int splits, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  constexpr int kSteps = kRow / 32 / 2;      // 9 k-steps of 32 dims per half
+  constexpr int kSteps = kRow / 32 / 2;      // 9 k-steps of 32 dims per dim half
   __shared__ __attribute__((aligned(16))) uint8_t kv[kRing][kTileBytes];
   __shared__ int rowid[kMaxList];
-  __shared__ f32x4 xch[kWaves][2][64];       // partial logits (keys 0-15, 16-31) per wave
+  __shared__ __attribute__((aligned(16))) float spart[2][kH][kSRow];   // [dh][head][key]
+  __shared__ __attribute__((aligned(16))) uint16_t pmat[kH][kPRow];    // P[head][key] bf16
+  __shared__ __attribute__((aligned(16))) float s_alpha[kH];
+  __shared__ float s_ml[kH][2];
+  __shared__ __attribute__((aligned(16))) int s_grow[kWaves];   // owner wave rescales a head
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hg = wave & 3, dh = wave >> 2;
+  const int hg = wave & 1, dh = (wave >> 1) & 1, kh = wave >> 2;
   const int g = lane >> 4, c16 = lane & 15;
   const int t = blockIdx.y, sp = blockIdx.x;
 
-  // Q^T fragments (B operand): head 16*hg + c16, dims 288dh + 32*st + 8*g .. +8; issued
-  // first so their latency overlaps the index / page-table lookups
-  bf16x8 qf[kSteps];
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(
-        q + ((int64_t)t * kH + 16 * hg + c16) * kRowBytes + 576 * dh + 16 * g);
+  // Q^T fragments (B operand) of head tiles ht = 0, 1: head 32hg + 16ht + c16,
+  // dims 288dh + 32st + 8g .. +8; issued first so their latency overlaps the lookups
+  bf16x8 qf[2][kSteps];
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) qf[st] = as_bf8(src[4 * st]);
+  for (int ht = 0; ht < 2; ++ht) {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        q + ((int64_t)t * kH + 32 * hg + 16 * ht + c16) * kRowBytes + 576 * dh + 16 * g);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) qf[ht][st] = as_bf8(src[4 * st]);
   }
   const TileLoads tl = plan_tile_loads();
   int nent;
@@ -168,13 +181,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
                idx, ld_idx, k, rowid, nent);
   __syncthreads();
 
+  // softmax state of the owned head (lanes 8i..8i+7 hold head 8w + i)
+  const int sm_head = 8 * wave + (lane >> 3);
+  const int sm_key = 4 * (lane & 7);
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[kDl / 32];
-#pragma unroll
-  for (int dt = 0; dt < kDl / 32; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ka = 16 * tile_slot(c16, g) + 576 * dh;                       // + 64 st
-  const int vb = 16 * tile_slot(4 * g + (c16 >> 2), 0) + 8 * (c16 & 3) + 512 * dh;  // + 32 dt
+  f32x4 o[4][4];                              // [head tile][dim tile]
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ka = 16 * tile_slot(16 * kh + c16, 36 * dh + g);           // + 64 st
+  const int vb = 16 * tile_slot(8 * g + (c16 >> 2), 0) + 8 * (c16 & 3) + 128 * wave;  // + 32 dt
   const int ntiles = (nent + kMT - 1) / kMT;
   int rid[kMaxLoadsPerWave];
   if (ntiles > 0) {
@@ -187,8 +206,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   }
   for (int tile = 0; tile < ntiles; ++tile) {
     const int e0 = tile * kMT;
-    // LDS lookups for this iteration, issued before the waits so they resolve meanwhile:
-    // row ids of the tile to prefetch and the validity of this tile's rows
     tile_rowids(tl, rowid, e0 + 2 * kMT, nent, rid);
     const int er = e0 + (lane & 31);
     const int vr = er < nent ? rowid[er] : -1;
@@ -203,105 +220,124 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     // every wave finished tile-1, so its slot takes tile+2
     if (tile + 2 < ntiles) issue_tile(tl, pool, rid, kv[(tile + 2) % kRing]);
     const uint8_t* kb = kv[tile % kRing];
-    // valid rows of the tile as a bit mask (row r -> bit r)
-    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);
+    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // row r valid -> bit r
 
-    // partial logits over this wave's 288 dims: keys 4g+j (s0) and 16+4g+j (s1), head c16
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- partial logits: keys 16kh + 4g + j, heads 32hg + 16ht + c16, dims of half dh
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      const bf16x8 a0 = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 64 * st));
-      const bf16x8 a1 = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 16 * 16 * kRowSlots + 64 * st));
-      s0 = mfma16(a0, qf[st], s0);
-      s1 = mfma16(a1, qf[st], s1);
+      const bf16x8 a = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 64 * st));
+      sacc[0] = mfma16(a, qf[0][st], sacc[0]);
+      sacc[1] = mfma16(a, qf[1][st], sacc[1]);
     }
-    xch[wave][0][lane] = s0;
-    xch[wave][1][lane] = s1;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+      *reinterpret_cast<f32x4*>(&spart[dh][32 * hg + 16 * ht + c16][16 * kh + 4 * g]) = sacc[ht];
     lds_barrier();
-    const f32x4 p0 = xch[wave ^ 4][0][lane], p1 = xch[wave ^ 4][1][lane];
 
-    float x[8];
+    // ---- softmax of the owned head over the tile's 32 keys (8 lanes x 4 keys)
+    {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&spart[0][sm_head][sm_key]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&spart[1][sm_head][sm_key]);
+      float x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // both waves of the head group add the same two partials (commutative: same bits)
-      const float la = dh ? p0[j] + s0[j] : s0[j] + p0[j];
-      const float lb = dh ? p1[j] + s1[j] : s1[j] + p1[j];
-      x[j] = (vmask >> (4 * g + j)) & 1u ? la * scale_log2 : -INFINITY;
-      x[4 + j] = (vmask >> (16 + 4 * g + j)) & 1u ? lb * scale_log2 : -INFINITY;
+      for (int j = 0; j < 4; ++j)
+        x[j] = (vmask >> (sm_key + j)) & 1u ? (a0[j] + a1[j]) * scale_log2 : -INFINITY;
+      float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 1));
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 2));
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 4));
+      // the running max only moves when a logit exceeds it by more than the slack, so
+      // exp2(x - m) stays <= 2^8 and the O rescale is rare
+      const bool grow = tmax > m_run + kRescaleSlack;
+      const float m_new = grow ? tmax : m_run;
+      const bool none = (m_new == -INFINITY);
+      const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      float p[4], psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
+        psum += p[j];
+      }
+      psum += shfl_xor_f(psum, 1);
+      psum += shfl_xor_f(psum, 2);
+      psum += shfl_xor_f(psum, 4);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
+      const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
+      *reinterpret_cast<uint2*>(&pmat[sm_head][sm_key]) = make_uint2(lo, hi);
+      if ((lane & 7) == 0) s_alpha[sm_head] = alpha;
+      if (lane == 0) s_grow[wave] = __ballot(alpha != 1.f) != 0;
     }
-    float tmax = x[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    // the running max only moves when a logit exceeds it by more than the slack, so
-    // exp2(x - m) stays <= 2^8 and the O rescale is rare
-    const bool grow = tmax > m_run + kRescaleSlack;
-    const float m_new = grow ? tmax : m_run;
-    const bool none = (m_new == -INFINITY);
-    const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-    float psum = 0.f;
-    bf16x8 pa;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
-      psum += p;
-      pa[j] = (__bf16)p;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {               // rescale O rows (heads 4g + j) by their alpha
-      float ar[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ar[j] = __shfl(alpha, 4 * g + j, kWave);
-#pragma unroll
-      for (int dt = 0; dt < kDl / 32; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[dt][j] *= ar[j];
-    }
+    lds_barrier();
 
-    // P.V: B operand rows 4g + j (slots 0..3) and 16 + 4g + j (slots 4..7), dims
-    // 256dh + 16dt + c16; lane (g, c16) addresses 4 dims (8 bytes) of row 4g + c16/4
+    // ---- O[64 heads][dims 64w + 16dt + c16] += P . V
+    const int4 gr0 = *reinterpret_cast<const int4*>(&s_grow[0]);
+    const int4 gr1 = *reinterpret_cast<const int4*>(&s_grow[4]);
+    if (gr0.x | gr0.y | gr0.z | gr0.w | gr1.x | gr1.y | gr1.z | gr1.w) {
 #pragma unroll
-    for (int dt = 0; dt < kDl / 32; ++dt) {
+      for (int ht = 0; ht < 4; ++ht) {
+        const f32x4 al = *reinterpret_cast<const f32x4*>(&s_alpha[16 * ht + 4 * g]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[ht][dt][j] *= al[j];
+      }
+    }
+    bf16x8 pa[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+      pa[ht] = as_bf8(*reinterpret_cast<const uint4*>(&pmat[16 * ht + c16][8 * g]));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
       const s16x4 lo = lds_read_tr16(kb + vb + 32 * dt);
-      const s16x4 hi = lds_read_tr16(kb + vb + 16 * 16 * kRowSlots + 32 * dt);
+      const s16x4 hi = lds_read_tr16(kb + vb + 16 * 4 * kRowSlots + 32 * dt);
       const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
                                                              hi[0], hi[1], hi[2], hi[3]};
-      o[dt] = mfma16(pa, __builtin_bit_cast(bf16x8, v8), o[dt]);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) o[ht][dt] = mfma16(pa[ht], vf, o[ht][dt]);
     }
   }
 
-  // per-head totals: l over the 4 lanes sharing head c16
-  float l_tot = l_run + shfl_xor_f(l_run, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
-  float lr[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lr[j] = __shfl(l_tot, 4 * g + j, kWave);
-  const int head0 = 16 * hg + 4 * g;   // rows of o[dt][j]: head0 + j
-  const int dim0 = 256 * dh + c16;     // column of o[dt][*]: dim0 + 16 dt
+  // ---- epilogue: per-head (m, l) from the softmax owners
+  if ((lane & 7) == 0) {
+    s_ml[sm_head][0] = m_run;
+    s_ml[sm_head][1] = l_run;
+  }
+  __syncthreads();
   if (splits == 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float inv = lr[j] > 0.f ? 1.f / lr[j] : 0.f;
-      uint16_t* dst = out + ((int64_t)t * kH + head0 + j) * kDl + dim0;
+    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int dt = 0; dt < kDl / 32; ++dt) dst[16 * dt] = f2bf_bits(o[dt][j] * inv);
+      for (int j = 0; j < 4; ++j) {
+        const int head = 16 * ht + 4 * g + j;
+        const float l = s_ml[head][1];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* dst = out + ((int64_t)t * kH + head) * kDl + 64 * wave + c16;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dst[16 * dt] = f2bf_bits(o[ht][dt][j] * inv);
+      }
+    if (lse && tid < kH) {
+      const float m = s_ml[tid][0], l = s_ml[tid][1];
+      lse[(int64_t)t * kH + tid] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
-    if (lse && g == 0 && dh == 0)
-      lse[(int64_t)t * kH + 16 * hg + c16] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     const int64_t base = ((int64_t)t * splits + sp) * kH;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float* dst = ws_o + (base + head0 + j) * kDl + dim0;
+    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int dt = 0; dt < kDl / 32; ++dt) dst[16 * dt] = o[dt][j];
-    }
-    if (g == 0 && dh == 0) {
-      ws_ml[(base + 16 * hg + c16) * 2 + 0] = m_run;
-      ws_ml[(base + 16 * hg + c16) * 2 + 1] = l_tot;
+      for (int j = 0; j < 4; ++j) {
+        float* dst = ws_o + (base + 16 * ht + 4 * g + j) * kDl + 64 * wave + c16;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dst[16 * dt] = o[ht][dt][j];
+      }
+    if (tid < kH) {
+      ws_ml[(base + tid) * 2 + 0] = s_ml[tid][0];
+      ws_ml[(base + tid) * 2 + 1] = s_ml[tid][1];
     }
   }
 }
