@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the DSA decode hot path on one MI355X.
+"""Benchmark of the DSA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_b1_32k]
 
@@ -9,55 +9,130 @@ inputs already resident in HBM.  Consecutive steps rotate over several independe
 copies of the inputs whose total size exceeds the 256 MB Infinity Cache, so every step
 streams its key cache and latent rows from HBM as a multi-layer model would.
 
-Prints one JSON line (rank 0): tokens/s, the step's algorithmic HBM bandwidth, the
-roofline of the dominant kernel (timed with HIP events on the stream it runs on) and
-the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: tokens/s, the step's algorithmic HBM bandwidth, the roofline of
+the dominant kernel (its launches timed with HIP events recorded on the kernel's own
+stream by the library, dsa_timing_start/collect) and the CPU oracle timed on a bounded
+sample of the same workload.
+
+Two helper modes turn rocprofv3 output into the text summaries kept under profiles/:
+    --copy-calibration MIB      only copies MIB MiB device-to-device (--steps times),
+                                the reference for scaling FETCH_SIZE / WRITE_SIZE
+    --summarize-trace DIR       per-kernel table of a --kernel-trace --stats run
+    --summarize-traffic ...     HBM bytes per dispatch of one kernel from --pmc runs
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
+import sqlite3
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "sparse_attention_19_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 MFMA
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 MALL_BYTES = 256 << 20
 METRIC = "DSA decode tokens/s at 32K–128K ctx + achieved HBM GB/s fraction"
 
+# kernel -> source file that defines it (its hash decides whether stored counters still apply)
+KERNEL_SRC = {
+    "indexer_decode_kernel": "indexer.hip", "indexer_bf16_kernel": "indexer.hip",
+    "indexer_f32_kernel": "indexer.hip", "topk_chunk_kernel": "topk.hip", "topk_merge_kernel": "topk.hip",
+    "mla_bf16_kernel": "mla.hip", "mla_combine_kernel": "mla.hip", "mla_f32_kernel": "mla.hip",
+}
 
-def algorithmic_bytes(cfg, lens, T):
-    """Bytes each op must move at minimum (inputs read once, outputs written once).
 
-    indexer : keys 2*Di B per visible position + q_idx + w + fp32 scores written
-    topk    : fp32 scores read + int32 indices written
-    mla     : 2*(Dl+Dr) B per selected row and layer + q + out (+ idx read per layer)
+def kernel_source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SRC[kernel], "common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def workload_sizes(cfg):
+    """Token-level sizes of a workload: (T, per-token visible n, unique keys read)."""
+    import dsa_inputs as I
+    lens = I.context_lengths(cfg)
+    if cfg.prefill_tokens:
+        T = cfg.prefill_tokens
+        n_tok = [cfg.ctx - T + i + 1 for i in range(T)]
+        uniq = cfg.ctx
+    else:
+        T = len(lens)
+        n_tok = list(lens)
+        uniq = sum(lens)
+    return T, n_tok, uniq
+
+
+def algorithmic(cfg, kernels_seen=()):
+    """Algorithmic bytes (each input read once, each output written once) and FLOPs per
+    launch of each kernel, and the bound that applies to it.
+
+    indexer  keys 2*Di B per cached position (once), q_idx + w per token, fp32 score per
+             visible (token, position) pair; 2*Hi*Di FLOP per pair
+    top-k    the fp32 scores read, k int32 indices written per token (split between the
+             chunk and merge kernels when both run)
+    MLA      2*(Dl+Dr) B per selected row per token (one layer per launch), q, idx, and
+             out + lse per token; 2*H*(2*Dl+Dr) FLOP per selected row
     """
-    eb = 4 if cfg.dtype.itemsize == 4 else 2
-    n_tot = sum(lens)
-    sel = sum(min(n, cfg.k) for n in lens)
-    idx_b = {
-        "indexer": n_tot * (cfg.Di * eb + 4) + T * (cfg.Hi * cfg.Di * eb + cfg.Hi * 4),
-        "topk": n_tot * 4 + T * cfg.k * 4,
-        "mla": cfg.layers * (sel * cfg.row_dim * eb + T * cfg.H * (cfg.row_dim + cfg.Dl) * eb
-                             + T * cfg.k * 4 + T * cfg.H * 4),
+    T, n_tok, uniq = workload_sizes(cfg)
+    eb = cfg.dtype.itemsize
+    n_tot = sum(n_tok)
+    sel = sum(min(n, cfg.k) for n in n_tok)
+    prefill = bool(cfg.prefill_tokens)
+    mfma_ok = eb == 2
+    ix_b = uniq * cfg.Di * eb + n_tot * 4 + T * (cfg.Hi * cfg.Di * eb + cfg.Hi * 4)
+    ix_f = 2 * n_tot * cfg.Hi * cfg.Di
+    tk_in, tk_out = n_tot * 4, T * cfg.k * 4
+    mla_in = sel * cfg.row_dim * eb + T * cfg.H * cfg.row_dim * eb + T * cfg.k * 4
+    mla_out = T * cfg.H * (cfg.Dl * eb + 4)
+    mla_f = 2 * sel * cfg.H * (cfg.row_dim + cfg.Dl)
+    merge = "topk_merge_kernel" in kernels_seen
+    combine = "mla_combine_kernel" in kernels_seen
+    ix_bound = "mfma" if (prefill and mfma_ok) else "hbm"
+    mla_bound = "mfma" if (prefill and mfma_ok) else "hbm"
+    out = {
+        "indexer_decode_kernel": (ix_b, ix_f, "hbm"),
+        "indexer_bf16_kernel": (ix_b, ix_f, ix_bound),
+        "indexer_f32_kernel": (ix_b, ix_f, "hbm"),
+        "topk_chunk_kernel": (tk_in + (0 if merge else tk_out), 0, "hbm"),
+        "topk_merge_kernel": (tk_out, 0, "hbm"),
+        "mla_bf16_kernel": (mla_in + (0 if combine else mla_out), mla_f, mla_bound),
+        "mla_combine_kernel": (mla_out, 0, "hbm"),
+        "mla_f32_kernel": (mla_in + mla_out, mla_f, "hbm"),
     }
-    return idx_b
+    # a step's HBM bytes: in prefill the tokens' selections overlap, and each latent row
+    # is fetched from HBM once (later visits hit the caches), so count unique rows there
+    rows_hbm = min(uniq, sel) if prefill else sel
+    mla_step = rows_hbm * cfg.row_dim * eb + T * cfg.H * cfg.row_dim * eb + T * cfg.k * 4 + mla_out
+    step = {"indexer": ix_b, "topk": tk_in + tk_out, "mla": cfg.layers * mla_step}
+    return out, step
 
 
-def algorithmic_flops(cfg, lens):
-    n_tot = sum(lens)
-    sel = sum(min(n, cfg.k) for n in lens)
-    return {
-        "indexer": 2 * n_tot * cfg.Hi * cfg.Di,
-        "mla": cfg.layers * 2 * sel * cfg.H * (cfg.row_dim + cfg.Dl),
-    }
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed --pmc summary, if the kernel is unchanged."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("JSON "):
+                rec = json.loads(line[5:])
+                if rec.get("source_sha") == kernel_source_sha(kernel):
+                    return rec["traffic_bytes_per_dispatch"]
+    return None
 
 
 def cpu_baseline(inp, budget_s=12.0):
     """The oracle (numpy float64) on whole tokens of the same workload, ~budget_s of CPU work."""
-    import numpy as np
     from oracle import dsa_oracle as O
     from oracle import run as R
     try:
@@ -66,7 +141,6 @@ def cpu_baseline(inp, budget_s=12.0):
     except Exception:
         threads = os.cpu_count() or 1
     cfg = inp["cfg"]
-    T = inp["q_idx"].shape[0]
     t = 0
     b = int(inp["q_row"][t])
     n = int(inp["q_pos"][t]) + 1
@@ -87,10 +161,184 @@ def cpu_baseline(inp, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or done >= 10000:
             break
+    kind = "prefill" if cfg.prefill_tokens else "decode"
     return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} whole decode tokens (request 0 of {cfg.name}, n={n}, "
-                      f"{cfg.layers} layer(s)) in {el:.1f} s; batch size does not change the "
-                      f"per-token oracle work"}
+            "sample": f"{done} whole {kind} tokens (token 0 of {cfg.name}, n={n}, {cfg.layers} "
+                      f"layer(s): indexer, stable-sort top-k, attention) in {el:.1f} s; the oracle's "
+                      f"work per token grows with its n"}
+
+
+# --------------------------------------------------------------------------- benchmark
+
+def run_bench(args):
+    import torch
+    import dsa_inputs as I
+    import sparse_attention_19_amd as D
+    from sparse_attention_19_amd import pipeline as P
+
+    cfg = I.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, n_tok, _ = workload_sizes(cfg)
+    _, step_parts = algorithmic(cfg)
+    step_bytes = sum(step_parts.values())
+    copies = args.copies or max(1, min(64, -(-2 * MALL_BYTES // step_bytes)))
+
+    inputs = [I.make_inputs(I.shrink(cfg, seed=cfg.seed + 1000 * c), dev) for c in range(copies)]
+    buf = P.run_inputs(inputs[0])
+    torch.cuda.synchronize()
+
+    def step(i):
+        P.run_inputs(inputs[i % copies], buf, step=i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps back to back, no per-kernel instrumentation
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # per-kernel durations: the library brackets each launch with HIP events on its stream
+    K2 = max(20, min(args.steps, 100))
+    D.dsa_timing_start(K2 * (8 + 2 * cfg.layers))
+    for i in range(K2):
+        step(args.warmup + args.steps + i)
+    launches = D.dsa_timing_collect()
+    per = {}
+    for name, t in launches:
+        c = per.setdefault(name, [0, 0.0])
+        c[0] += 1
+        c[1] += t
+    kern = {n: {"launches_per_step": c[0] / K2, "avg_ms": c[1] / c[0], "ms_per_step": c[1] / K2}
+            for n, c in per.items()}
+    alg, _ = algorithmic(cfg, kernels_seen=set(per))
+    dom = max(kern, key=lambda n: kern[n]["ms_per_step"])
+    a_bytes, a_flops, bound = alg[dom]
+    avg_s = kern[dom]["avg_ms"] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = a_flops / avg_s / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"
+    else:
+        achieved, peak, unit = a_bytes / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(dom, cfg.name), "kernel": dom,
+            "avg_launch_ms": round(kern[dom]["avg_ms"], 5),
+            "algorithmic_bytes_per_launch": a_bytes, "algorithmic_flops_per_launch": a_flops}
+
+    value = T / (ms * 1e-3)
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype.itemsize == 2 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "requests": len(I.context_lengths(cfg)), "ctx": cfg.ctx,
+                   "query_tokens": T, "k": cfg.k, "indexer_heads_x_dim": f"{cfg.Hi}x{cfg.Di}",
+                   "mla_heads_x_dim": f"{cfg.H}x({cfg.Dl}+{cfg.Dr})", "layers": cfg.layers,
+                   "rotated_input_copies": copies},
+        "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_gbs": round(step_gbs, 1),
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "kernels": {n: {k: round(v, 5) for k, v in d.items()} for n, d in sorted(kern.items())},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inputs[0])
+    print(json.dumps(res), flush=True)
+
+
+def run_copy_calibration(args):
+    """Device-to-device copies of a known size: FETCH_SIZE / WRITE_SIZE of these dispatches
+    against the bytes moved give the scale factors applied to the path's kernels."""
+    import torch
+    n = args.copy_calibration << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": args.steps}), flush=True)
+
+
+# --------------------------------------------------------------------------- rocprofv3 summaries
+
+def _db(d):
+    dbs = glob.glob(os.path.join(d, "**", "*results.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 results database under {d}")
+    return sqlite3.connect(dbs[0])
+
+
+def _short(name):
+    m = re.search(r"dsa::.*?(\w+_kernel)\b", name or "")
+    return m.group(1) if m else (name or "")[:40]
+
+
+def summarize_trace(args):
+    c = _db(args.summarize_trace)
+    rows = list(c.execute("select name, total_calls, average, total_duration, percentage from top_kernels"))
+    print(f"# rocprofv3 kernel trace: {args.title}")
+    print(f"# profiled with : {args.command}")
+    print(f"# summarised by : python bench.py --summarize-trace <output dir>")
+    print("# avg_us and total_ms are per-dispatch GPU durations; the path's kernels are dsa::*")
+    print(f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+    for name, calls, avg, total, pct in rows:
+        print(f"{_short(name):40s} {calls:6d} {avg:10.3f} {total / 1000.0:10.3f} {pct:6.2f}")
+
+
+def _counter_per_dispatch(d, counter, pick):
+    c = _db(d)
+    per = {}
+    for kname, disp, cname, val in c.execute(
+            "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+        if cname != counter or not pick(kname or ""):
+            continue
+        per[disp] = per.get(disp, 0.0) + val
+    if not per:
+        raise SystemExit(f"{d}: no {counter} values for the selected kernel")
+    return per
+
+
+def summarize_traffic(args):
+    import dsa_inputs as I
+    kernel, cfg = args.kernel, I.CONFIGS[args.workload]
+    is_k = lambda n: _short(n) == kernel  # noqa: E731
+    fetch = _counter_per_dispatch(args.fetch, "FETCH_SIZE", is_k)
+    write = _counter_per_dispatch(args.write, "WRITE_SIZE", is_k)
+    exp_kib = args.copy_mib * 1024.0
+    big = lambda n: "copy" in n.lower() or "elementwise" in n.lower()  # noqa: E731
+    cf = [v for v in _counter_per_dispatch(args.copy_fetch, "FETCH_SIZE", big).values() if v > 0.5 * exp_kib]
+    cw = [v for v in _counter_per_dispatch(args.copy_write, "WRITE_SIZE", big).values() if v > 0.5 * exp_kib]
+    if not cf or not cw:
+        raise SystemExit("copy calibration dispatches not found")
+    f_fac = exp_kib / (sum(cf) / len(cf))
+    w_fac = exp_kib / (sum(cw) / len(cw))
+    f_kib = sum(fetch.values()) / len(fetch)
+    w_kib = sum(write.values()) / len(write)
+    traffic = (f_kib * f_fac + w_kib * w_fac) * 1024.0
+    alg, _ = algorithmic(cfg, kernels_seen={"mla_combine_kernel"} if args.combine else set())
+    rec = {"kernel": kernel, "workload": cfg.name, "source_sha": kernel_source_sha(kernel),
+           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "dispatches": len(fetch), "copy_fetch_factor": round(f_fac, 4), "copy_write_factor": round(w_fac, 4),
+           "traffic_bytes_per_dispatch": int(traffic), "algorithmic_bytes_per_dispatch": alg[kernel][0]}
+    print(f"# HBM traffic of {kernel} on {cfg.name} (rocprofv3 --pmc, one counter per pass)")
+    print(f"# FETCH_SIZE pass : {args.fetch_command}")
+    print(f"# WRITE_SIZE pass : {args.write_command}")
+    print(f"# copy calibration: the same two passes over `python bench.py --copy-calibration {args.copy_mib}`")
+    print(f"# summarised by   : python bench.py --summarize-traffic (arguments: the four output dirs)")
+    print(f"FETCH_SIZE  {f_kib:14.1f} KiB/dispatch  x {f_fac:.4f} (copy of {args.copy_mib} MiB read "
+          f"{sum(cf) / len(cf):.0f} KiB)")
+    print(f"WRITE_SIZE  {w_kib:14.1f} KiB/dispatch  x {w_fac:.4f} (copy of {args.copy_mib} MiB wrote "
+          f"{sum(cw) / len(cw):.0f} KiB)")
+    print(f"traffic     {traffic / 1e6:14.3f} MB/dispatch; algorithmic {alg[kernel][0] / 1e6:.3f} MB "
+          f"(ratio {traffic / max(1, alg[kernel][0]):.3f})")
+    print("JSON " + json.dumps(rec))
 
 
 def main():
@@ -101,129 +349,34 @@ def main():
     ap.add_argument("--config", default="decode_b1_32k")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-traffic", action="store_true")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--kernel")
+    ap.add_argument("--workload")
+    ap.add_argument("--combine", action="store_true", help="the MLA ran with its combine kernel")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--fetch-command", default="")
+    ap.add_argument("--write-command", default="")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_traffic:
+        return summarize_traffic(args)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              f"sharding of this path is described in DESIGN.md, not run.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures "
+              f"the path on one MI355X; how it would shard over several is described, not run.",
+              file=sys.stderr)
         sys.exit(2)
-
-    import torch
-    import dsa_inputs as I
-    import sparse_attention_19_amd as D
-    from sparse_attention_19_amd import pipeline as P
-
-    cfg = I.CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    lens = I.context_lengths(cfg)
-    T = cfg.prefill_tokens or len(lens)
-    if cfg.prefill_tokens:
-        lens = [cfg.ctx - T + i + 1 for i in range(T)]
-    ab = algorithmic_bytes(cfg, lens, T)
-    af = algorithmic_flops(cfg, lens)
-    step_bytes = sum(ab.values())
-    copies = args.copies or max(1, min(64, -(-2 * MALL_BYTES // step_bytes)))
-
-    inputs = []
-    for c in range(copies):
-        inputs.append(I.make_inputs(I.shrink(cfg, seed=cfg.seed + 1000 * c), dev))
-    bufs = [P.run_inputs(inputs[0])]
-    for c in range(1, copies):
-        bufs.append(bufs[0])             # outputs may be shared: steps are stream-ordered
-    torch.cuda.synchronize()
-
-    def step(i, ev=None):
-        inp = inputs[i % copies]
-        buf = bufs[0]
-        c = inp["cfg"]
-        if ev is not None:
-            ev[0].record()
-        if c.prefill_tokens:
-            D.dsa_indexer_scores(inp["q_idx"], inp["w"], inp["k_pool"], inp["block_table"], inp["seq_len"],
-                                 buf.scores, q_row=inp["q_row"], q_pos=inp["q_pos"])
-        else:
-            D.dsa_indexer_scores(inp["q_idx"], inp["w"], inp["k_pool"], inp["block_table"], inp["seq_len"],
-                                 buf.scores)
-        if ev is not None:
-            ev[1].record()
-        if c.prefill_tokens:
-            D.dsa_topk(buf.scores, inp["q_pos"], c.k, buf.idx, n_add=1, ws=buf.ws_topk)
-        else:
-            D.dsa_topk(buf.scores, inp["seq_len"], c.k, buf.idx, n_add=0, ws=buf.ws_topk)
-        if buf.cache is not None:
-            buf.cache.publish(i)
-        if ev is not None:
-            ev[2].record()
-        for layer in range(c.layers):
-            idx = buf.idx if layer == 0 else buf.cache.get(i, layer)
-            if c.prefill_tokens:
-                D.dsa_sparse_mla_prefill(inp["q"][layer], inp["kv_pools"][layer], inp["block_table"],
-                                         inp["seq_len"], inp["q_row"], inp["q_pos"], idx, c.k, c.sm_scale,
-                                         buf.outs[layer], buf.lses[layer], ws=buf.ws_mla)
-            else:
-                D.dsa_sparse_mla_decode(inp["q"][layer], inp["kv_pools"][layer], inp["block_table"],
-                                        inp["seq_len"], idx, c.k, c.sm_scale, buf.outs[layer],
-                                        buf.lses[layer], ws=buf.ws_mla)
-        if ev is not None:
-            ev[3].record()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps back to back
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-
-    # per-op durations: HIP events recorded on the stream the kernels are launched on
-    K2 = max(20, args.steps // 2)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K2)]
-    for i in range(K2):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    op_ms = {
-        "indexer": sum(e[0].elapsed_time(e[1]) for e in evs) / K2,
-        "topk": sum(e[1].elapsed_time(e[2]) for e in evs) / K2,
-        "mla": sum(e[2].elapsed_time(e[3]) for e in evs) / K2,
-    }
-    dom = max(op_ms, key=op_ms.get)
-    bound = "mfma" if (cfg.prefill_tokens and dom in af) else "hbm"
-    if bound == "hbm":
-        achieved = ab[dom] / (op_ms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
-                "algorithmic_bytes_per_launch": ab[dom], "avg_ms": round(op_ms[dom], 5)}
-    else:
-        achieved = af[dom] / (op_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None, "kernel": dom,
-                "algorithmic_flops_per_launch": af[dom], "avg_ms": round(op_ms[dom], 5)}
-
-    tok_per_step = T
-    value = tok_per_step / (ms * 1e-3)
-    step_gbs = step_bytes / (ms * 1e-3) / 1e9
-    res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
-        if cfg.dtype.itemsize == 2 else "f32", "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": len(I.context_lengths(cfg)), "ctx": cfg.ctx,
-                   "query_tokens": T, "k": cfg.k, "indexer": f"{cfg.Hi}x{cfg.Di}",
-                   "mla": f"{cfg.H}x({cfg.Dl}+{cfg.Dr})", "layers": cfg.layers, "rotated_copies": copies},
-        "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_gbs": round(step_gbs, 1),
-                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-        "op_ms": {k: round(v, 5) for k, v in op_ms.items()},
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inputs[0])
-    print(json.dumps(res), flush=True)
+    if args.copy_calibration:
+        return run_copy_calibration(args)
+    run_bench(args)
 
 
 if __name__ == "__main__":

@@ -197,6 +197,23 @@ const char* dsa_last_error(void);
 /* Library version string. */
 const char* dsa_version(void);
 
+/*
+ * Per-kernel timing, for benchmarks and profilers (not part of the method).
+ * dsa_timing_start(capacity) creates 2*capacity HIP events; from then on each of the
+ * first `capacity` kernels the library enqueues (from any thread) carries a start/stop
+ * event pair in its own dispatch (hipExtLaunchKernel), so their elapsed time is that
+ * kernel's execution alone.  It fails with DSA_ERR_INVALID if capacity is outside
+ * [1, 1<<20] or timing is already on, and with DSA_ERR_HIP if the events cannot be
+ * created.
+ * dsa_timing_collect(names, ms, cap) waits for the recorded events, writes up to `cap`
+ * (kernel name, milliseconds) pairs in launch order (names are static strings; either
+ * array may be NULL when cap is 0), destroys the events, turns timing off and returns
+ * the number of timed launches (which may exceed cap), or -1 if timing was off or a
+ * HIP call failed (see dsa_last_error).
+ */
+dsa_status dsa_timing_start(int32_t capacity);
+int32_t dsa_timing_collect(const char** names, float* ms, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

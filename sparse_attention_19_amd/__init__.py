@@ -13,12 +13,13 @@ from typing import Optional
 
 import torch
 
-from ._lib import (DSA_BF16, DSA_BLOCK, DSA_F32, DSA_MAX_K, DSA_OP_MLA, DSA_OP_TOPK, LIB, LIB_PATH,
-                   DsaError, DsaIndexCache, DsaPageTable, DsaPool, check)
+from ._lib import (DSA_BF16, DSA_BLOCK, DSA_ERR_INVALID, DSA_F32, DSA_MAX_K, DSA_OP_MLA, DSA_OP_TOPK, LIB,
+                   LIB_PATH, DsaError, DsaIndexCache, DsaPageTable, DsaPool, check)
 
 __all__ = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
     "IndexCache", "dsa_workspace_bytes", "workspace", "DsaError", "LIB_PATH", "DSA_OP_TOPK", "DSA_OP_MLA",
+    "dsa_timing_start", "dsa_timing_collect",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
@@ -137,3 +138,18 @@ class IndexCache:
         check(LIB.dsa_index_cache_get(ctypes.byref(self.c), step, layer_in_group, ctypes.byref(p)))
         assert p.value == self.idx.data_ptr()
         return self.idx
+
+
+def dsa_timing_start(capacity: int) -> None:
+    """Time every kernel the library enqueues from now on (first `capacity` launches)."""
+    check(LIB.dsa_timing_start(capacity))
+
+
+def dsa_timing_collect(cap: int = 1 << 16):
+    """Wait for the timed launches and return [(kernel name, ms)] in launch order."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = LIB.dsa_timing_collect(names, ms, cap)
+    if n < 0:
+        raise DsaError(DSA_ERR_INVALID, LIB.dsa_last_error().decode())
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]

@@ -2,7 +2,7 @@
 
 Argument marshalling only: torch tensors are turned into device pointers, sizes and the
 current HIP stream; every computation happens in the library's kernels.  The library
-must have been built (python -m sparse_attention_19_amd.build); importing this module
+must have been built (python sparse_attention_19_amd/build.py); importing this module
 without it raises ImportError -- there is no fallback path.
 """
 from __future__ import annotations
@@ -23,6 +23,7 @@ EXPORTS = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
     "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
     "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
+    "dsa_timing_start", "dsa_timing_collect",
 ]
 
 
@@ -44,7 +45,7 @@ class DsaIndexCache(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_19_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_attention_19_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     pool_p, pt_p, cache_p = ctypes.POINTER(DsaPool), ctypes.POINTER(DsaPageTable), ctypes.POINTER(DsaIndexCache)
@@ -60,7 +61,13 @@ def _load() -> ctypes.CDLL:
         "dsa_status_string": [ctypes.c_int],
         "dsa_last_error": [],
         "dsa_version": [],
+        "dsa_timing_start": [I32],
+        "dsa_timing_collect": [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(F), I32],
     }
+    missing = [n for n in sig if not hasattr(lib, n)]
+    if missing:
+        raise ImportError(f"{LIB_PATH} is stale (no {', '.join(missing)}): rebuild it with "
+                          f"`python sparse_attention_19_amd/build.py`")
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args

@@ -1,7 +1,9 @@
 """Build step of the HIP library: compiles csrc/*.hip + csrc/dsa_abi.cpp for gfx950 into
 sparse_attention_19_amd/libdsa.so (in-tree, so it travels with the source tree).
 
-    python -m sparse_attention_19_amd.build
+    python sparse_attention_19_amd/build.py
+
+(Run as a file, not with -m: importing the package loads the library this builds.)
 """
 from __future__ import annotations
 

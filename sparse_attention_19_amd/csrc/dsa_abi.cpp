@@ -6,7 +6,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "launch.h"
@@ -106,7 +108,44 @@ dsa_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// Per-kernel timing state (dsa_timing_start / dsa_timing_collect), shared by all threads.
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  int capacity = 0;
+  int used = 0;                    // launches seen while on (may exceed capacity)
+  std::vector<hipEvent_t> events;  // [2 * capacity]: start, stop
+  std::vector<const char*> names;  // [capacity]
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+void destroy_events(Timing& t) {
+  for (hipEvent_t e : t.events) (void)hipEventDestroy(e);
+  t.events.clear();
+  t.names.clear();
+  t.on = false;
+  t.capacity = t.used = 0;
+}
+
 }  // namespace
+
+namespace dsa {
+
+KernelEvents::KernelEvents(const char* name) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (!t.on) return;
+  const int s = t.used++;
+  if (s >= t.capacity) return;
+  t.names[s] = name;
+  start = t.events[2 * s];
+  stop = t.events[2 * s + 1];
+}
+
+}  // namespace dsa
 
 extern "C" {
 
@@ -242,5 +281,60 @@ const char* dsa_status_string(dsa_status s) {
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
 const char* dsa_version(void) { return "dsa-gfx950 0.1.0"; }
+
+dsa_status dsa_timing_start(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20))
+    return fail(DSA_ERR_INVALID, "timing capacity %d outside [1, %d]", capacity, 1 << 20);
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (t.on) return fail(DSA_ERR_INVALID, "timing is already on");
+  t.events.reserve(2 * (size_t)capacity);
+  for (int i = 0; i < 2 * capacity; ++i) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      destroy_events(t);
+      return fail(DSA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+    t.events.push_back(e);
+  }
+  t.names.assign(capacity, nullptr);
+  t.capacity = capacity;
+  t.used = 0;
+  t.on = true;
+  return ok();
+}
+
+int32_t dsa_timing_collect(const char** names, float* ms, int32_t cap) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (!t.on) {
+    fail(DSA_ERR_INVALID, "timing is off");
+    return -1;
+  }
+  if (cap > 0 && (!names || !ms)) {
+    fail(DSA_ERR_INVALID, "names/ms is NULL");
+    return -1;
+  }
+  const int n = t.used < t.capacity ? t.used : t.capacity;
+  for (int i = 0; i < n; ++i) {
+    hipError_t err = hipEventSynchronize(t.events[2 * i + 1]);
+    float v = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&v, t.events[2 * i], t.events[2 * i + 1]);
+    if (err != hipSuccess) {
+      fail(DSA_ERR_HIP, "timing event %d: %s", i, hipGetErrorString(err));
+      destroy_events(t);
+      return -1;
+    }
+    if (i < cap) {
+      names[i] = t.names[i];
+      ms[i] = v;
+    }
+  }
+  const int used = t.used;
+  destroy_events(t);
+  ok();
+  return used;
+}
 
 }  // extern "C"

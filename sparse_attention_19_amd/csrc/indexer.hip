@@ -338,24 +338,35 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
       const int tiles = (max_keys + kTileKeys - 1) / kTileKeys;
       const int per = 64;
       dim3 grid((tiles + per - 1) / per, (a.T + 7) / 8);
-      hipLaunchKernelGGL(indexer_bf16_kernel<false>, grid, dim3(512), 0, stream,
-                         (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool, a.num_blocks,
-                         a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.T, per,
-                         a.scores, a.ld);
+      {
+        const KernelEvents ev("indexer_bf16_kernel");
+        hipExtLaunchKernelGGL(indexer_bf16_kernel<false>, grid, dim3(512), 0, stream, ev.start,
+                              ev.stop, 0, (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool,
+                              a.num_blocks, a.block_table, a.seq_len, a.max_blocks, a.batch,
+                              a.q_row, a.q_pos, a.T, per, a.scores, a.ld);
+      }
     } else {
       // key ranges of 128..1024 keys: at least ~2048 single-wave workgroups over the batch
       int range = kMaxRange;
       while (range > 128 && (int64_t)a.T * ((max_keys + range - 1) / range) < 2048) range >>= 1;
       dim3 grid((max_keys + range - 1) / range, a.T);
-      hipLaunchKernelGGL(indexer_decode_kernel, grid, dim3(64), 0, stream, (const uint8_t*)a.q_idx, a.w,
-                         (const uint8_t*)a.pool, a.num_blocks, a.block_table, a.seq_len, a.max_blocks,
-                         a.batch, a.q_row, a.q_pos, range, a.scores, a.ld);
+      {
+        const KernelEvents ev("indexer_decode_kernel");
+        hipExtLaunchKernelGGL(indexer_decode_kernel, grid, dim3(64), 0, stream, ev.start, ev.stop,
+                              0, (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool, a.num_blocks,
+                              a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos,
+                              range, a.scores, a.ld);
+      }
     }
   } else {
     dim3 grid((max_keys + kF32Keys - 1) / kF32Keys, a.T);
-    hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), 0, stream, (const float*)a.q_idx, a.w,
-                       (const float*)a.pool, a.num_blocks, a.block_table, a.seq_len, a.max_blocks,
-                       a.batch, a.q_row, a.q_pos, a.Hi, a.Di, a.scores, a.ld);
+    {
+      const KernelEvents ev("indexer_f32_kernel");
+      hipExtLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), 0, stream, ev.start, ev.stop, 0,
+                            (const float*)a.q_idx, a.w, (const float*)a.pool, a.num_blocks,
+                            a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.Hi,
+                            a.Di, a.scores, a.ld);
+    }
   }
   return hipGetLastError();
 }

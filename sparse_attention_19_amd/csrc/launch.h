@@ -2,11 +2,21 @@
 // Arguments arrive here already validated.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dsa {
+
+// Start/stop events for one kernel launch while per-kernel timing (dsa_timing_start) is
+// on, else null.  They go into the dispatch itself (hipExtLaunchKernelGGL), so the
+// elapsed time between them is the kernel's own execution.
+struct KernelEvents {
+  explicit KernelEvents(const char* name);
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
 
 struct IndexerArgs {
   const void* q_idx;

@@ -475,19 +475,27 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
     const int splits = mla_splits(a.T, a.k, true);
     float* ws_o = (float*)a.ws;
     float* ws_ml = ws_o ? ws_o + (size_t)a.T * splits * kH * kDl : nullptr;
-    hipLaunchKernelGGL(mla_bf16_kernel, dim3(splits, a.T), dim3(kThreads), 0, stream,
-                       (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks, a.block_table,
-                       a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k,
-                       a.sm_scale * kLog2e, splits, (uint16_t*)a.out, a.lse, ws_o, ws_ml);
+    {
+      const KernelEvents ev("mla_bf16_kernel");
+      hipExtLaunchKernelGGL(mla_bf16_kernel, dim3(splits, a.T), dim3(kThreads), 0, stream, ev.start,
+                            ev.stop, 0, (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks,
+                            a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos,
+                            a.idx, a.ld_idx, a.k, a.sm_scale * kLog2e, splits, (uint16_t*)a.out,
+                            a.lse, ws_o, ws_ml);
+    }
     if (splits > 1) {
-      hipLaunchKernelGGL(mla_combine_kernel, dim3(a.T, kH), dim3(64), 0, stream, ws_o, ws_ml, splits,
-                         kH, kDl, (uint16_t*)a.out, a.lse);
+      const KernelEvents ev("mla_combine_kernel");
+      hipExtLaunchKernelGGL(mla_combine_kernel, dim3(a.T, kH), dim3(64), 0, stream, ev.start,
+                            ev.stop, 0, ws_o, ws_ml, splits, kH, kDl, (uint16_t*)a.out, a.lse);
     }
   } else {
-    hipLaunchKernelGGL(mla_f32_kernel, dim3(a.T, a.H), dim3(256), 0, stream, (const float*)a.q,
-                       (const float*)a.pool, a.num_blocks, a.block_table, a.seq_len, a.max_blocks,
-                       a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k, a.H, a.Dl, a.Dr,
-                       a.sm_scale * kLog2e, (float*)a.out, a.lse);
+    {
+      const KernelEvents ev("mla_f32_kernel");
+      hipExtLaunchKernelGGL(mla_f32_kernel, dim3(a.T, a.H), dim3(256), 0, stream, ev.start, ev.stop,
+                            0, (const float*)a.q, (const float*)a.pool, a.num_blocks, a.block_table,
+                            a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx,
+                            a.k, a.H, a.Dl, a.Dr, a.sm_scale * kLog2e, (float*)a.out, a.lse);
+    }
   }
   return hipGetLastError();
 }

@@ -438,11 +438,17 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     ws_pos = (int*)(ws_key + (size_t)a.rows * mc * a.k);
     ws_cnt = ws_pos + (size_t)a.rows * mc * a.k;
   }
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3(a.rows, mc), dim3(kThreads), 0, stream, a.scores, a.ld,
-                     a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, ws_key, ws_pos, ws_cnt, mc);
+  {
+    const KernelEvents ev("topk_chunk_kernel");
+    hipExtLaunchKernelGGL(topk_chunk_kernel, dim3(a.rows, mc), dim3(kThreads), 0, stream, ev.start,
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx,
+                          ws_key, ws_pos, ws_cnt, mc);
+  }
   if (mc > 1) {
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(a.rows), dim3(kThreads), 0, stream, a.ld, a.n_valid,
-                       a.n_add, a.k, a.idx, a.ld_idx, ws_key, ws_pos, ws_cnt, mc);
+    const KernelEvents ev("topk_merge_kernel");
+    hipExtLaunchKernelGGL(topk_merge_kernel, dim3(a.rows), dim3(kThreads), 0, stream, ev.start,
+                          ev.stop, 0, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, ws_key,
+                          ws_pos, ws_cnt, mc);
   }
   return hipGetLastError();
 }

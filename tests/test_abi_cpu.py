@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -190,3 +190,11 @@ def test_index_cache_host_logic():
     assert lib.dsa_index_cache_init(ctypes.byref(c), FAKE, 100, 40, 2048, 4) == L.DSA_ERR_INVALID
     assert lib.dsa_index_cache_init(ctypes.byref(c), FAKE, 2048, 40, 2048, 1) == L.DSA_ERR_INVALID
     assert lib.dsa_index_cache_init(ctypes.byref(c), None, 2048, 40, 2048, 4) == L.DSA_ERR_INVALID
+
+
+def test_timing_rejects_before_any_hip_call():
+    assert L.LIB.dsa_timing_start(0) == L.DSA_ERR_INVALID
+    assert L.LIB.dsa_timing_start((1 << 20) + 1) == L.DSA_ERR_INVALID
+    # never started: collect reports -1 and says why
+    assert L.LIB.dsa_timing_collect(None, None, 0) == -1
+    assert b"off" in L.LIB.dsa_last_error()
