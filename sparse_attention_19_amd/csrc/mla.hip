@@ -9,18 +9,21 @@
 // Affects DRAM Memory TAM", §Sparse MLA: DSA uses MLA's MQA mode; §MLA changes: d = 512,
 // r = 64, the roofline algebra of that mode).
 //
-// bf16 instance (64 heads, 512 + 64): a workgroup of 4 waves handles one (token, split)
-// pair; wave w owns heads 16w..16w+15.  Per tile of 32 selected rows:
-//   gather   : page-translate each position, fetch the 1152-byte rows (coalesced 16-byte
-//              chunks) into registers one tile ahead, then into a padded LDS tile
-//   logits   : S^T[key][head] = K[key][:] . Q^T on 16x16x32 MFMA, Q held in registers
-//   softmax  : online (running max / sum per head, exp2 with the log2(e) folded into the
-//              scale); the resulting P is already in the A-operand layout of the next MFMA
-//   P.V      : O[head][dim] += P[head][key] . V[key][dim]; the V operand is read from the
-//              same LDS tile with the transposing ds_read_b64_tr_b16, so the row tile is
-//              fetched from HBM exactly once for both products
-// Splits of the selected list run in parallel workgroups and are merged by a combine
-// kernel (log-sum-exp weighting) when there are few tokens.
+// bf16 instance (64 heads, 512 + 64): a workgroup of 8 waves handles one (token, split)
+// pair and walks its slice of the selected list in tiles of 32 rows:
+//   gather   : page-translate each position once into an LDS row-id list; every tile's
+//              1152-byte rows stream straight into a padded LDS tile with
+//              global_load_lds_dwordx4 (no staging registers), two tiles ahead through a
+//              3-slot ring, so the rows are fetched from HBM exactly once
+//   logits   : S^T[key][head] = K[key][:] . Q^T on 16x16x32 MFMA, Q held in registers;
+//              the 8 waves split heads, dims and keys and exchange partials through LDS
+//   softmax  : online (running max / sum per head, exp2 with log2(e) folded into the
+//              scale, rescale of O only when the max grows by more than 2^8); P to LDS
+//   P.V      : O[head][dim] += P[head][key] . V[key][dim], each wave 64 output dims of all
+//              heads; the V operand comes from the same LDS tile through the transposing
+//              ds_read_b64_tr_b16
+// When there are few tokens, splits of the selected list run in parallel workgroups and a
+// combine kernel merges their partial (O, max, sum) with log-sum-exp weights.
 #include <math.h>
 
 #include "common.h"
