@@ -63,6 +63,79 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// Wave-wide scans and reductions on DPP (VALU lane moves, no LDS round trip): row_shr
+// steps scan each 16-lane row, then row_bcast:15 / row_bcast:31 carry the row totals
+// into the rows above.  Out-of-row sources read as 0 (bound_ctrl), the identity of both
+// add and unsigned max.  All 64 lanes must be active.
+#define DSA_DPP(v, ctrl, rows, bc) \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), (rows), 0xf, (bc)))
+
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+  v += DSA_DPP(v, 0x111, 0xf, true);   // row_shr:1
+  v += DSA_DPP(v, 0x112, 0xf, true);   // row_shr:2
+  v += DSA_DPP(v, 0x114, 0xf, true);   // row_shr:4
+  v += DSA_DPP(v, 0x118, 0xf, true);   // row_shr:8
+  v += DSA_DPP(v, 0x142, 0xa, false);  // row_bcast:15 into rows 1 and 3
+  v += DSA_DPP(v, 0x143, 0xc, false);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Maximum over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, DSA_DPP(v, 0x111, 0xf, true));
+  v = max(v, DSA_DPP(v, 0x112, 0xf, true));
+  v = max(v, DSA_DPP(v, 0x114, 0xf, true));
+  v = max(v, DSA_DPP(v, 0x118, 0xf, true));
+  v = max(v, DSA_DPP(v, 0x142, 0xa, false));
+  v = max(v, DSA_DPP(v, 0x143, 0xc, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Reductions over each group of 8 consecutive lanes, result in all 8: quad_perm swaps
+// (xor 1, xor 2) combine each quad, row_half_mirror (lane i <-> 7 - i within 8) the two
+// quads of the group.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                               0xf, 0xf, true));
+}
+__device__ __forceinline__ float group8_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));       // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));       // quad_perm [2,3,0,1]
+  return fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+}
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  return v + dpp_f<0x141>(v);
+}
+
+// Minimum over the wave, in every lane (min a = ~max ~a keeps 0 the identity).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// One global_load_lds_dwordx4: the 16 bytes at each lane's `gptr` land in LDS at
+// lds_base + 16 * lane (lds_base is wave-uniform and is passed in M0).
+// Issued from inline asm on purpose: for the builtin, the compiler treats every later LDS
+// access as possibly aliasing any load still in flight into LDS and drains all of them
+// first (s_waitcnt vmcnt(0)), which serialises a prefetch ring.  Every caller waits for
+// its own loads with an explicit s_waitcnt vmcnt(n) before the destination is read.  The
+// instruction writes no VGPR (its data goes to LDS) and reads its address VGPRs when it
+// issues, so no register the compiler reuses is left in flight; the s_nop covers the
+// M0-write-to-LDS-DMA wait state.
+__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)DSA_LDS(void, const_cast<void*>(lds_base)));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+}
+
+// Makes `v` available in registers at this point: its loads complete here rather than
+// wherever the scheduler would sink them (e.g. into a loop whose waits it would then
+// count against loads issued outside its view).
+template <typename T>
+__device__ __forceinline__ void settle(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
 #define DSA_VMCNT(n) (((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 #define DSA_LGKMCNT0 0xc07f

@@ -222,6 +222,40 @@ __device__ __forceinline__ float score32_swz(const QFrag& f, const uint8_t* slic
   return p + 0.0f;   // canonical +0.0
 }
 
+// The 8 direct-to-LDS loads of one 32-key slice (8 KB) into a ring slot.
+__device__ __forceinline__ void issue_slice(const uint8_t* base, uint8_t* dst) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    lds_dma16(base + r * kRowBytes + 16 * c, dst + 1024 * i);
+  }
+}
+
+// One step of the ring: request the slice two ahead into `next` (when `ahead`), wait for
+// this slice's own loads, score its 32 keys from `cur` and park the scores in `sc`.
+// `cur`, `next` and `sc` are distinct LDS regions; declaring them __restrict__ lets the
+// compiler see that the loads still landing in other ring slots do not feed the reads of
+// `cur`, so it does not drain them before reading (the wait below is for this slice only).
+__device__ __forceinline__ void slice_step(const QFrag& f, const uint8_t* __restrict__ cur,
+                                           uint8_t* __restrict__ next, const uint8_t* src, bool ahead,
+                                           bool more, float* __restrict__ sc, bool zero) {
+  const int lane = threadIdx.x & 63;
+  if (ahead) {
+    issue_slice(src, next);
+    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(16));   // slices +1 and +2 may still fly
+  } else if (more) {
+    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(8));
+  } else {
+    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
+  }
+  asm volatile("" ::: "memory");
+  float p = score32_swz(f, cur);
+  if (zero) p = 0.f;                               // empty row: score 0
+  if (lane < kSlice) sc[lane] = p;
+}
+
 __global__ __launch_bounds__(64) void indexer_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ pool,
     int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
@@ -250,37 +284,37 @@ __global__ __launch_bounds__(64) void indexer_decode_kernel(
   QFrag f;
   load_qfrag(f, q_idx + (int64_t)t * kHi * kRowBytes, w + (int64_t)t * kHi);
 
-  // issue the 8 loads of slice sl into ring slot sl % 3; lane l of load i fills
-  // (row 4i + l/16, LDS chunk l%16) with global chunk (l%16) ^ (row % 16)
-  auto issue = [&](int sl) {
+  // lane l of load i of a slice fills (row 4i + l/16, LDS chunk l%16) with global chunk
+  // (l%16) ^ (row % 16); an unusable page reads block 0 (always valid memory) and its
+  // scores are zeroed
+  auto slice_src = [&](int sl) {
     const int page = (sl * kSlice) / kBlock;
     const int phys = __shfl(my_phys, page, kWave);
     const bool ok = __shfl((int)my_ok, page, kWave) != 0;
-    // an unusable page reads block 0 (always valid memory); its scores are zeroed below
-    const uint8_t* base = pool + ((int64_t)(ok ? phys : 0) * kBlock + (key0 + sl * kSlice) % kBlock) *
-                                     kRowBytes;
-    uint8_t* dst = ring[sl % kRing];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);
-      __builtin_amdgcn_global_load_lds(base + r * kRowBytes + 16 * c,
-                                       DSA_LDS(void, dst + 1024 * i), 16, 0, 0);
-    }
+    return pool + ((int64_t)(ok ? phys : 0) * kBlock + (key0 + sl * kSlice) % kBlock) * kRowBytes;
   };
-  for (int sl = 0; sl < kRing && sl < ns; ++sl) issue(sl);
+  // Q and the page lookups are in registers from here on: the loop below then waits only
+  // for its own slices' loads
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) settle(f.a[h][i]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) settle(f.w[h][j]);
+  }
+  settle(my_phys);
+  __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
+  // always two slices: the second of a one-slice range lies in the same 64-key page, so
+  // it reads valid memory (into a slot nobody reads) and the load count stays fixed
+  issue_slice(slice_src(0), ring[0]);
+  issue_slice(slice_src(1), ring[1]);
   for (int sl = 0; sl < ns; ++sl) {
-    if (sl + 2 < ns) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(16));
-    else if (sl + 1 < ns) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(8));
-    else __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
-    float p = score32_swz(f, ring[sl % kRing]);
+    const bool ahead = sl + 2 < ns;
+    const uint8_t* src = ahead ? slice_src(sl + 2) : pool;
     const int page = (sl * kSlice) / kBlock;
-    if (__shfl((int)my_ok, page, kWave) == 0) p = 0.f;   // empty row: score 0
-    if (lane < kSlice) sc[sl * kSlice + lane] = p;
-    if (sl + kRing < ns) {
-      __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);   // the slot's operand reads are done
-      issue(sl + kRing);
-    }
+    const bool zero = __shfl((int)my_ok, page, kWave) == 0;
+    slice_step(f, ring[sl % kRing], ring[(sl + 2) % kRing], src, ahead, sl + 1 < ns,
+               sc + sl * kSlice, zero);
   }
   __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
   float* dst = scores + (int64_t)t * ld + key0;

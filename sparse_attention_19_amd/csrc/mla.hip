@@ -131,7 +131,7 @@ __device__ __forceinline__ void issue_tile(const TileLoads& tl, const uint8_t* p
     if (m >= tl.count) break;                      // uniform per wave
     const uint8_t* src = pool + (int64_t)(rid[m] >= 0 ? rid[m] : 0) * kRowBytes + tl.off[m];
     if (tl.active & (1u << m))
-      __builtin_amdgcn_global_load_lds(src, DSA_LDS(void, dst + 1024 * (wave + kWaves * m)), 16, 0, 0);
+      lds_dma16(src, dst + 1024 * (wave + kWaves * m));
   }
 }
 
@@ -147,6 +147,120 @@ __device__ __forceinline__ void issue_tile(const TileLoads& tl, const uint8_t* p
 //             once from LDS with the transposing ds_read_b64_tr_b16) feeds four MFMAs.
 constexpr int kSRow = 36;          // partial-logit row stride (floats): conflict-free 16-byte writes
 constexpr int kPRow = 40;          // P row stride (bf16): 80 bytes, conflict-free operand reads
+
+// One 32-row tile of the list: wait for this wave's loads of the tile, request tile + 2
+// into `next`, then logits, online softmax and P.V from `kb`.  The LDS regions (the tile's
+// slot, the slot being filled, the row-id list and the exchange buffers) are distinct and
+// passed __restrict__, which tells the compiler that the loads still landing in `next`
+// and the other slot do not feed any of these reads; otherwise it drains every
+// outstanding global->LDS load before the first read and the prefetch never overlaps.
+__device__ __forceinline__ void mla_tile(const uint8_t* __restrict__ kb, uint8_t* __restrict__ next,
+                                         const int* __restrict__ rowid, float* __restrict__ spart,
+                                         uint16_t* __restrict__ pmat, float* __restrict__ s_alpha,
+                                         int* __restrict__ s_grow, const uint8_t* pool,
+                                         const TileLoads& tl, int tile, int ntiles, int nent,
+                                         const bf16x8 (&qf)[2][kRow / 64], int ka, int vb,
+                                         float scale_log2, f32x4 (&o)[4][4], float& m_run,
+                                         float& l_run) {
+  constexpr int kSteps = kRow / 64;          // 9 k-steps of 32 dims per dim half
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hg = wave & 1, dh = (wave >> 1) & 1, kh = wave >> 2;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int sm_head = 8 * wave + (lane >> 3);
+  const int sm_key = 4 * (lane & 7);
+  int rid[kMaxLoadsPerWave];
+  const int e0 = tile * kMT;
+  tile_rowids(tl, rowid, e0 + 2 * kMT, nent, rid);
+  const int er = e0 + (lane & 31);
+  const int vr = er < nent ? rowid[er] : -1;
+  // this wave's loads of `tile` done (the next tile's may still fly), then everyone's
+  if (tile + 1 < ntiles) {
+    if (tl.count == 5) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(5));
+    else __builtin_amdgcn_s_waitcnt(DSA_VMCNT(4));
+  } else {
+    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
+  }
+  lds_barrier();
+  // every wave finished tile-1, so its slot takes tile+2
+  if (tile + 2 < ntiles) issue_tile(tl, pool, rid, next);
+  const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // row r valid -> bit r
+
+  // ---- partial logits: keys 16kh + 4g + j, heads 32hg + 16ht + c16, dims of half dh
+  f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    const bf16x8 a = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 64 * st));
+    sacc[0] = mfma16(a, qf[0][st], sacc[0]);
+    sacc[1] = mfma16(a, qf[1][st], sacc[1]);
+  }
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+    *reinterpret_cast<f32x4*>(&spart[(dh * kH + 32 * hg + 16 * ht + c16) * kSRow + 16 * kh + 4 * g]) =
+        sacc[ht];
+  lds_barrier();
+
+  // ---- softmax of the owned head over the tile's 32 keys (8 lanes x 4 keys)
+  {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&spart[sm_head * kSRow + sm_key]);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&spart[(kH + sm_head) * kSRow + sm_key]);
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[j] = (vmask >> (sm_key + j)) & 1u ? (a0[j] + a1[j]) * scale_log2 : -INFINITY;
+    const float tmax = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    // the running max only moves when a logit exceeds it by more than the slack, so
+    // exp2(x - m) stays <= 2^8 and the O rescale is rare
+    const bool grow = tmax > m_run + kRescaleSlack;
+    const float m_new = grow ? tmax : m_run;
+    const bool none = (m_new == -INFINITY);
+    const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    float p[4], psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
+      psum += p[j];
+    }
+    psum = group8_sum(psum);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
+    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
+    *reinterpret_cast<uint2*>(&pmat[sm_head * kPRow + sm_key]) = make_uint2(lo, hi);
+    if ((lane & 7) == 0) s_alpha[sm_head] = alpha;
+    if (lane == 0) s_grow[wave] = __ballot(alpha != 1.f) != 0;
+  }
+  lds_barrier();
+
+  // ---- O[64 heads][dims 64w + 16dt + c16] += P . V
+  const int4 gr0 = *reinterpret_cast<const int4*>(&s_grow[0]);
+  const int4 gr1 = *reinterpret_cast<const int4*>(&s_grow[4]);
+  if (gr0.x | gr0.y | gr0.z | gr0.w | gr1.x | gr1.y | gr1.z | gr1.w) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const f32x4 al = *reinterpret_cast<const f32x4*>(&s_alpha[16 * ht + 4 * g]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[ht][dt][j] *= al[j];
+    }
+  }
+  bf16x8 pa[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+    pa[ht] = as_bf8(*reinterpret_cast<const uint4*>(&pmat[(16 * ht + c16) * kPRow + 8 * g]));
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const s16x4 lo = lds_read_tr16(kb + vb + 32 * dt);
+    const s16x4 hi = lds_read_tr16(kb + vb + 16 * 4 * kRowSlots + 32 * dt);
+    const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
+                                                           hi[0], hi[1], hi[2], hi[3]};
+    const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) o[ht][dt] = mfma16(pa[ht], vf, o[ht][dt]);
+  }
+}
 
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
@@ -198,113 +312,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   const int ka = 16 * tile_slot(16 * kh + c16, 36 * dh + g);           // + 64 st
   const int vb = 16 * tile_slot(8 * g + (c16 >> 2), 0) + 8 * (c16 & 3) + 128 * wave;  // + 32 dt
   const int ntiles = (nent + kMT - 1) / kMT;
-  int rid[kMaxLoadsPerWave];
+  // Q and the lookups are in registers from here on: the loop below then waits only for
+  // its own tiles' loads
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) settle(qf[ht][st]);
+  __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
   if (ntiles > 0) {
+    // always two tiles: rows past the list read row 0 of the pool (valid memory) into a
+    // slot nobody reads, and the load count stays fixed
+    int rid[kMaxLoadsPerWave];
     tile_rowids(tl, rowid, 0, nent, rid);
     issue_tile(tl, pool, rid, kv[0]);
-  }
-  if (ntiles > 1) {
     tile_rowids(tl, rowid, kMT, nent, rid);
     issue_tile(tl, pool, rid, kv[1]);
   }
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int e0 = tile * kMT;
-    tile_rowids(tl, rowid, e0 + 2 * kMT, nent, rid);
-    const int er = e0 + (lane & 31);
-    const int vr = er < nent ? rowid[er] : -1;
-    // this wave's loads of `tile` done (the next tile's may still fly), then everyone's
-    if (tile + 1 < ntiles) {
-      if (tl.count == 5) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(5));
-      else __builtin_amdgcn_s_waitcnt(DSA_VMCNT(4));
-    } else {
-      __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
-    }
-    lds_barrier();
-    // every wave finished tile-1, so its slot takes tile+2
-    if (tile + 2 < ntiles) issue_tile(tl, pool, rid, kv[(tile + 2) % kRing]);
-    const uint8_t* kb = kv[tile % kRing];
-    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // row r valid -> bit r
-
-    // ---- partial logits: keys 16kh + 4g + j, heads 32hg + 16ht + c16, dims of half dh
-    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const bf16x8 a = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 64 * st));
-      sacc[0] = mfma16(a, qf[0][st], sacc[0]);
-      sacc[1] = mfma16(a, qf[1][st], sacc[1]);
-    }
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-      *reinterpret_cast<f32x4*>(&spart[dh][32 * hg + 16 * ht + c16][16 * kh + 4 * g]) = sacc[ht];
-    lds_barrier();
-
-    // ---- softmax of the owned head over the tile's 32 keys (8 lanes x 4 keys)
-    {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&spart[0][sm_head][sm_key]);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&spart[1][sm_head][sm_key]);
-      float x[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[j] = (vmask >> (sm_key + j)) & 1u ? (a0[j] + a1[j]) * scale_log2 : -INFINITY;
-      float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 1));
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 2));
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 4));
-      // the running max only moves when a logit exceeds it by more than the slack, so
-      // exp2(x - m) stays <= 2^8 and the O rescale is rare
-      const bool grow = tmax > m_run + kRescaleSlack;
-      const float m_new = grow ? tmax : m_run;
-      const bool none = (m_new == -INFINITY);
-      const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      float p[4], psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
-        psum += p[j];
-      }
-      psum += shfl_xor_f(psum, 1);
-      psum += shfl_xor_f(psum, 2);
-      psum += shfl_xor_f(psum, 4);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
-      const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
-      *reinterpret_cast<uint2*>(&pmat[sm_head][sm_key]) = make_uint2(lo, hi);
-      if ((lane & 7) == 0) s_alpha[sm_head] = alpha;
-      if (lane == 0) s_grow[wave] = __ballot(alpha != 1.f) != 0;
-    }
-    lds_barrier();
-
-    // ---- O[64 heads][dims 64w + 16dt + c16] += P . V
-    const int4 gr0 = *reinterpret_cast<const int4*>(&s_grow[0]);
-    const int4 gr1 = *reinterpret_cast<const int4*>(&s_grow[4]);
-    if (gr0.x | gr0.y | gr0.z | gr0.w | gr1.x | gr1.y | gr1.z | gr1.w) {
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const f32x4 al = *reinterpret_cast<const f32x4*>(&s_alpha[16 * ht + 4 * g]);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[ht][dt][j] *= al[j];
-      }
-    }
-    bf16x8 pa[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-      pa[ht] = as_bf8(*reinterpret_cast<const uint4*>(&pmat[16 * ht + c16][8 * g]));
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const s16x4 lo = lds_read_tr16(kb + vb + 32 * dt);
-      const s16x4 hi = lds_read_tr16(kb + vb + 16 * 4 * kRowSlots + 32 * dt);
-      const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
-                                                             hi[0], hi[1], hi[2], hi[3]};
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) o[ht][dt] = mfma16(pa[ht], vf, o[ht][dt]);
-    }
-  }
+  for (int tile = 0; tile < ntiles; ++tile)
+    mla_tile(kv[tile % kRing], kv[(tile + 2) % kRing], rowid, &spart[0][0][0], &pmat[0][0], s_alpha,
+             s_grow, pool, tl, tile, ntiles, nent, qf, ka, vb, scale_log2, o, m_run, l_run);
 
   // ---- epilogue: per-head (m, l) from the softmax owners
   if ((lane & 7) == 0) {
@@ -346,15 +372,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 }
 
 // Merge split partials: m = max m_s, L = sum l_s 2^(m_s - m), O = sum O_s 2^(m_s - m) / L.
-// grid (T, H); one wave per (token, head): lane s first turns split s's (m_s, l_s) into
-// its weight, then every lane accumulates 8 output dims over all splits with independent
-// (unrolled) 32-byte loads.  Requires splits <= 64 and Dl == 512.
+// grid (T, H, Z); one wave per (token, head) and 1/Z of the output dims, in passes of 64
+// dims (kPasses / Z of them).  Lane s first turns split s's (m_s, l_s) into its weight;
+// then lane 16a + c accumulates dims 4c..4c+3 of every pass over the splits a, a + 4, ...
+// with independent 16-byte loads (all in flight together), and the four split groups are
+// summed through LDS.  Requires splits <= 64 and Dl == 64 * kPasses.
+constexpr int kPasses = kDl / 64;
+
 __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict__ ws_o,
                                                          const float* __restrict__ ws_ml, int splits,
-                                                         int H, int Dl, uint16_t* __restrict__ out,
+                                                         int H, uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
   __shared__ float wgt[64];
+  __shared__ float4 part[4][kPasses][16];
   const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int npass = kPasses / gridDim.z, pass0 = blockIdx.z * npass;
   float ms = -INFINITY, ls = 0.f;
   if (lane < splits) {
     const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (((int64_t)t * splits + lane) * H + h) * 2);
@@ -371,25 +403,47 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
   const float inv = L > 0.f ? 1.f / L : 0.f;
   wgt[lane] = f * inv;
   __syncthreads();
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const float* src = ws_o + ((int64_t)t * splits * H + h) * Dl + lane * 8;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) {
-    const float ws = wgt[s];
-    const float4 a = *reinterpret_cast<const float4*>(src + (int64_t)s * H * Dl);
-    const float4 b = *reinterpret_cast<const float4*>(src + (int64_t)s * H * Dl + 4);
-    acc[0] = fmaf(ws, a.x, acc[0]); acc[1] = fmaf(ws, a.y, acc[1]);
-    acc[2] = fmaf(ws, a.z, acc[2]); acc[3] = fmaf(ws, a.w, acc[3]);
-    acc[4] = fmaf(ws, b.x, acc[4]); acc[5] = fmaf(ws, b.y, acc[5]);
-    acc[6] = fmaf(ws, b.z, acc[6]); acc[7] = fmaf(ws, b.w, acc[7]);
-  }
-  uint32_t packed[4];
+  const int a = lane >> 4, c = lane & 15;
+  const float* src = ws_o + ((int64_t)t * splits * H + h) * kDl + 64 * pass0 + 4 * c;
+  float4 acc[kPasses];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    packed[i] = (uint32_t)f2bf_bits(acc[2 * i]) | ((uint32_t)f2bf_bits(acc[2 * i + 1]) << 16);
-  *reinterpret_cast<uint4*>(out + ((int64_t)t * H + h) * Dl + lane * 8) =
-      make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  if (lse && lane == 0) lse[(int64_t)t * H + h] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
+  for (int p = 0; p < kPasses; ++p) acc[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = a; s < splits; s += 4) {
+    const float w = wgt[s];
+    const float* row = src + (int64_t)s * H * kDl;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      if (p < npass) {
+        const float4 v = *reinterpret_cast<const float4*>(row + 64 * p);
+        acc[p].x = fmaf(w, v.x, acc[p].x);
+        acc[p].y = fmaf(w, v.y, acc[p].y);
+        acc[p].z = fmaf(w, v.z, acc[p].z);
+        acc[p].w = fmaf(w, v.w, acc[p].w);
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p)
+    if (p < npass) part[a][p][c] = acc[p];
+  __syncthreads();
+  for (int i = lane; i < 16 * npass; i += 64) {
+    const int p = i >> 4, cc = i & 15;
+    float4 r = part[0][p][cc];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+      const float4 q = part[g][p][cc];
+      r.x += q.x;
+      r.y += q.y;
+      r.z += q.z;
+      r.w += q.w;
+    }
+    const uint32_t lo = (uint32_t)f2bf_bits(r.x) | ((uint32_t)f2bf_bits(r.y) << 16);
+    const uint32_t hi = (uint32_t)f2bf_bits(r.z) | ((uint32_t)f2bf_bits(r.w) << 16);
+    *reinterpret_cast<uint2*>(out + ((int64_t)t * H + h) * kDl + 64 * (pass0 + p) + 4 * cc) =
+        make_uint2(lo, hi);
+  }
+  if (lse && blockIdx.z == 0 && lane == 0)
+    lse[(int64_t)t * H + h] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -487,9 +541,12 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
                             a.lse, ws_o, ws_ml);
     }
     if (splits > 1) {
+      // split the output dims over Z workgroups per (token, head) until ~2048 are in flight
+      int Z = 1;
+      while (Z < kPasses && (int64_t)a.T * kH * Z < 2048) Z *= 2;
       const KernelEvents ev("mla_combine_kernel");
-      hipExtLaunchKernelGGL(mla_combine_kernel, dim3(a.T, kH), dim3(64), 0, stream, ev.start,
-                            ev.stop, 0, ws_o, ws_ml, splits, kH, kDl, (uint16_t*)a.out, a.lse);
+      hipExtLaunchKernelGGL(mla_combine_kernel, dim3(a.T, kH, Z), dim3(64), 0, stream, ev.start,
+                            ev.stop, 0, ws_o, ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
     }
   } else {
     {

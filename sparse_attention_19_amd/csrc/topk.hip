@@ -10,15 +10,20 @@
 // workgroup holds a chunk of up to 32768 keys in registers (32 consecutive keys per
 // thread, staged through a bank-conflict-free padded LDS copy) and selects in three steps:
 //   1. pruning : the key tau of a fixed rank among 1024 evenly spaced samples bounds the
-//                answer from below; the keys >= tau (about 2k + 768 of them) are
-//                compacted, in position order, into an LDS candidate list.  If that list
-//                would hold fewer than k or more than 8192 keys, all keys stay candidates.
+//                answer from below (one wave selects it on its own, 8-bit radix levels
+//                in a private 256-bin histogram); the keys >= tau (about 2k + 768 of
+//                them) are compacted, in position order, into an LDS candidate list.  If
+//                that list would hold fewer than k or more than 8192 keys, all keys stay
+//                candidates.
 //   2. select  : the exact k-th largest key theta, by radix levels of 12 bits over the
-//                range [lowest candidate, highest key] (at most 3 levels) with a shared
-//                4096-bin LDS histogram; lanes of a wave that fall in one bin add once.
+//                range [lowest candidate, highest key] (at most 3 levels) with two
+//                alternating 4096-bin LDS histograms (one is cleared while the other
+//                fills, so a level costs three barriers); lanes of a wave that fall in
+//                one bin add once.
 //   3. compact : per-thread counts of (> theta, == theta), one packed block scan, and the
 //                first need_eq ties in position order give every selected position its
 //                output slot -- ascending and independent of scheduling.
+// Wave scans and reductions run on DPP lane moves; block scans take one barrier each.
 // Rows longer than 32768 run that procedure per 32768-key chunk (grid rows x chunks),
 // writing each chunk's top-k (key, position) list to the workspace; a merge kernel then
 // selects the row's top-k from those lists in batches of at most 8192 candidates.  This
@@ -38,58 +43,49 @@ constexpr int kPadWords = kChunk + kChunk / 32; // padded LDS copy: item e at e 
 constexpr int kCap = 8192;                      // candidate list capacity
 constexpr int kCR = kCap / kThreads;            // 8 candidates per thread
 constexpr int kBins = 4096;
+constexpr int kHistWords = kBins + kWave;       // + one dummy word per lane
+constexpr int kSampleBins = 256;                // wave-private histogram of the sample select
 constexpr int kSampleMargin = 768;              // candidates aimed for above 2k
 constexpr int kMaxK = 2048;
+static_assert(kThreads * 4 == kBins, "one uint4 of bins per thread");
+static_assert(kChunk / 32 + 2 * kHistWords <= kPadWords, "histogram fits in the free pad area");
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
-
 struct Smem {
-  uint32_t hist[kBins + kWave];     // + one dummy word per lane
-  uint32_t wsum[kWaves];
-  uint32_t wred[2][kWaves];
-  uint32_t sel[2];
+  uint32_t wsum[3][kWaves];   // block-scan partials (levels alternate 0/1; the lists use 2)
+  uint32_t wred[2][kWaves];   // block min / max partials
+  uint32_t sel[2][2];         // per radix level: (bin, count above it), alternating
+  uint32_t tau;
 };
 
-// Exclusive scan of one value per thread; *total receives the block sum.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, Smem& sm, uint32_t* total) {
+// Exclusive scan of one value per thread over the block; *total receives the sum.  One
+// barrier: `wsum` must not be written again before every thread has returned.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) sm.wsum[wave] = incl;
+  const uint32_t incl = wave_incl_add(v);
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    const uint32_t x = sm.wsum[w];
+    const uint32_t x = wsum[w];
     before += (w < wave) ? x : 0u;
     tot += x;
   }
-  __syncthreads();
   *total = tot;
   return before + incl - v;
 }
 
-// Block-wide min and max of one value per thread.
+// Block-wide min and max (one barrier; Smem::wred is reused only after further barriers).
 __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, Smem& sm, uint32_t* mn,
                                              uint32_t* mx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, kWave));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, kWave));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane == 0) {
     sm.wred[0][wave] = lo;
     sm.wred[1][wave] = hi;
@@ -101,26 +97,97 @@ __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, Smem& sm,
     a = min(a, sm.wred[0][w]);
     b = max(b, sm.wred[1][w]);
   }
-  __syncthreads();
   *mn = a;
   *mx = b;
+}
+
+// rank-th largest (1-based, rank <= number of nonzero entries) of the 1024 entries of
+// `v` (LDS), zero entries ignored, computed by one wave alone: 8-bit radix levels over
+// [min, max] with a private histogram `hs` (LDS, kSampleBins words, 16-byte aligned).
+__device__ __forceinline__ uint32_t wave_select_rank(const uint32_t* v, uint32_t rank, uint32_t* hs) {
+  const int lane = threadIdx.x & 63;
+  uint32_t s[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 x = reinterpret_cast<const uint4*>(v)[4 * lane + i];
+    s[4 * i] = x.x;
+    s[4 * i + 1] = x.y;
+    s[4 * i + 2] = x.z;
+    s[4 * i + 3] = x.w;
+  }
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    mn = min(mn, s[r] ? s[r] : 0xFFFFFFFFu);
+    mx = max(mx, s[r]);
+  }
+  uint32_t L = wave_min_u32(mn);
+  const uint32_t hi = wave_max_u32(mx);
+  int W = (hi <= L) ? 0 : 32 - __clz(hi - L);
+  uint32_t remaining = rank;
+  while (W > 0) {
+    const int shift = W > 8 ? W - 8 : 0;
+    reinterpret_cast<uint4*>(hs)[lane] = make_uint4(0, 0, 0, 0);
+    wave_lds_fence();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t d = s[r] - L;
+      if (s[r] != 0u && s[r] >= L && (W >= 32 || d < (1u << W))) atomicAdd(&hs[d >> shift], 1u);
+    }
+    wave_lds_fence();
+    // lane l owns bins 255-4l .. 252-4l (descending)
+    const uint4 c4 = reinterpret_cast<const uint4*>(hs)[kSampleBins / 4 - 1 - lane];
+    const uint32_t c[4] = {c4.w, c4.z, c4.y, c4.x};
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_add(local);
+    const uint32_t excl = incl - local;
+    const uint64_t hit = __ballot(excl < remaining && remaining <= incl);
+    const int f = __ffsll((unsigned long long)hit) - 1;
+    uint32_t bin = 0, above = 0;
+    if (lane == f) {
+      uint32_t run = excl;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!found && run + c[q] >= remaining) {
+          bin = (uint32_t)(kSampleBins - 1 - 4 * lane - q);
+          above = run;
+          found = true;
+        }
+        if (!found) run += c[q];
+      }
+    }
+    bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, f);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)above, f);
+    remaining -= above;
+    L += bin << shift;
+    W = shift;
+    wave_lds_fence();
+  }
+  return L;
 }
 
 // Exact `rank`-th largest (1-based, rank <= number of valid keys) of the keys of all
 // threads, every valid key lying in [lo, hi] with lo >= 1 (key 0 marks an empty slot).
 // Returns theta and the number of keys equal to theta that belong to the top `rank`.
+// hist_a must be zero (cleared before a barrier that precedes the call); both histograms
+// (kHistWords words, 16-byte aligned) are left dirty.
 template <int R>
-__device__ __forceinline__ void select_rank(const uint32_t (&key)[R], uint32_t lo,
-                                            uint32_t hi, uint32_t rank, Smem& sm,
-                                            uint32_t* theta, uint32_t* need_eq) {
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ void select_rank(const uint32_t (&key)[R], uint32_t lo, uint32_t hi,
+                                            uint32_t rank, uint32_t* hist_a, uint32_t* hist_b,
+                                            Smem& sm, uint32_t* theta, uint32_t* need_eq) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t L = lo;
   int W = (hi <= lo) ? 0 : 32 - __clz(hi - lo);
   uint32_t remaining = rank;
+  uint32_t* cur = hist_a;
+  uint32_t* nxt = hist_b;
+  int level = 0;
   while (W > 0) {
     const int shift = W > 12 ? W - 12 : 0;
-    for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
-    __syncthreads();
+    // the other buffer feeds the next level; its last reads were before the previous
+    // level's final barrier
+    reinterpret_cast<uint4*>(nxt)[tid] = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       // branch-free: lanes outside the range add to a private dummy word; lanes sharing
@@ -133,35 +200,37 @@ __device__ __forceinline__ void select_rank(const uint32_t (&key)[R], uint32_t l
       const bool in0 = bin == b0;
       const uint32_t addr = in0 ? (lane == 0 ? b0 : (uint32_t)(kBins + lane)) : bin;
       const uint32_t inc = in0 ? (lane == 0 ? (uint32_t)__popcll(same) : 0u) : 1u;
-      atomicAdd(&sm.hist[addr], inc);
+      atomicAdd(&cur[addr], inc);
     }
     __syncthreads();
     // thread t owns bins 4095-4t .. 4092-4t (descending)
-    uint32_t c[4], local = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = sm.hist[kBins - 1 - 4 * tid - q];
-      local += c[q];
-    }
+    const uint4 c4 = reinterpret_cast<const uint4*>(cur)[kBins / 4 - 1 - tid];
+    const uint32_t c[4] = {c4.w, c4.z, c4.y, c4.x};
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
     uint32_t total;
-    const uint32_t excl = block_excl_scan(local, sm, &total);
+    const uint32_t excl = block_excl_scan(local, sm.wsum[level & 1], &total);
     if (excl < remaining && remaining <= excl + local) {
       uint32_t run = excl;
+      bool found = false;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (run + c[q] >= remaining) {
-          sm.sel[0] = (uint32_t)(kBins - 1 - 4 * tid - q);
-          sm.sel[1] = run;
-          break;
+        if (!found && run + c[q] >= remaining) {
+          sm.sel[level & 1][0] = (uint32_t)(kBins - 1 - 4 * tid - q);
+          sm.sel[level & 1][1] = run;
+          found = true;
         }
-        run += c[q];
+        if (!found) run += c[q];
       }
     }
     __syncthreads();
-    remaining -= sm.sel[1];
-    L += sm.sel[0] << shift;
+    remaining -= sm.sel[level & 1][1];
+    L += sm.sel[level & 1][0] << shift;
     W = shift;
-    __syncthreads();
+    uint32_t* t = cur;
+    cur = nxt;
+    nxt = t;
+    ++level;
+    (void)wave;
   }
   *theta = L;
   *need_eq = remaining;
@@ -172,7 +241,7 @@ __device__ __forceinline__ void select_rank(const uint32_t (&key)[R], uint32_t l
 // emit(r, slot) for every selected entry; slot = its rank in list order.
 template <int R, typename Emit>
 __device__ __forceinline__ void compact(const uint32_t (&key)[R], uint32_t theta,
-                                        uint32_t need_eq, Smem& sm, Emit emit) {
+                                        uint32_t need_eq, uint32_t* wsum, Emit emit) {
   static_assert(R <= 32, "selection masks are 32-bit");
   uint32_t gtm = 0, eqm = 0;      // per-entry flags as bit masks (bit r = entry r)
 #pragma unroll
@@ -182,7 +251,7 @@ __device__ __forceinline__ void compact(const uint32_t (&key)[R], uint32_t theta
   }
   const uint32_t gt = __popc(gtm), eq = __popc(eqm);
   uint32_t total;
-  const uint32_t before = block_excl_scan(gt | (eq << 16), sm, &total);
+  const uint32_t before = block_excl_scan(gt | (eq << 16), wsum, &total);
   // ties taken by earlier threads, then by this one (its first entries equal to theta).
   // Clamping before subtracting keeps every difference non-negative (no guarded
   // subtraction that an optimiser could hoist out of its guard).
@@ -200,11 +269,15 @@ __device__ __forceinline__ void compact(const uint32_t (&key)[R], uint32_t theta
 // Top-k of a list held as R consecutive entries per thread (entry (t, r) = item R*t + r),
 // with count > k items in total; entries past the list hold key 0.  Valid keys are never 0
 // (0 is the key of a NaN, and NaN scores are not supported).
-// emit(item, key, slot) for each selected item.  cand_key / cand_item: LDS scratch of
-// kCap entries each.
+// emit(item, key, slot) for each selected item.  Scratch (LDS): hist_a (zero on entry),
+// hist_b, and for R > kCR the samples (kThreads words), the candidate list (kCap keys and
+// kCap items) -- none of it overlapping the others.  Every thread must have finished any
+// earlier use of hist_b / the candidate area before it enters (the first barrier here
+// orders all later writes to them).
 template <int R, typename Emit>
 __device__ __forceinline__ void topk_of_list(const uint32_t (&key)[R], int count, uint32_t k,
-                                             Smem& sm, uint32_t* cand_key, uint32_t* cand_item,
+                                             Smem& sm, uint32_t* hist_a, uint32_t* hist_b,
+                                             uint32_t* samp, uint32_t* cand_key, uint32_t* cand_item,
                                              Emit emit) {
   const int tid = threadIdx.x;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -213,26 +286,29 @@ __device__ __forceinline__ void topk_of_list(const uint32_t (&key)[R], int count
     mn = min(mn, key[r] ? key[r] : 0xFFFFFFFFu);
     mx = max(mx, key[r]);
   }
+  const bool try_prune = R > kCR && count > kCap;
+  if (try_prune) samp[tid] = key[R / 2];              // sample = item R*t + R/2
   uint32_t kmin, kmax;
   block_minmax(mn, mx, sm, &kmin, &kmax);
 
   bool pruned = false;
-  if (R > kCR && count > kCap) {
-    // 1. lower bound tau: a fixed rank among evenly spaced samples (item R*t + R/2)
-    uint32_t sk[1] = {key[R / 2]};
-    uint32_t smin, smax, ns;
-    block_minmax(sk[0] ? sk[0] : 0xFFFFFFFFu, sk[0], sm, &smin, &smax);
-    (void)block_excl_scan(sk[0] ? 1u : 0u, sm, &ns);
+  if (try_prune) {
+    // 1. lower bound tau: a fixed rank among the valid samples (threads holding > R/2 items)
+    const int ns = count > R / 2 ? min(kThreads, (count - R / 2 - 1) / R + 1) : 0;
     const uint64_t want = 2ull * k + kSampleMargin;
-    const uint32_t rank = (uint32_t)((want * ns + (uint64_t)count - 1) / (uint64_t)count);
-    if (rank >= 1 && rank < ns) {
-      uint32_t tau, unused;
-      select_rank<1>(sk, smin, smax, rank, sm, &tau, &unused);
+    const uint32_t rank = (uint32_t)((want * (uint64_t)ns + (uint64_t)count - 1) / (uint64_t)count);
+    if (rank >= 1 && rank < (uint32_t)ns) {
+      if (tid < kWave) {
+        const uint32_t tau = wave_select_rank(samp, rank, hist_b);
+        if (tid == 0) sm.tau = tau;
+      }
+      __syncthreads();
+      const uint32_t tau = sm.tau;
       uint32_t cm = 0;
 #pragma unroll
       for (int r = 0; r < R; ++r) cm |= (key[r] >= tau ? 1u : 0u) << r;
       uint32_t ctot;
-      const uint32_t off = block_excl_scan((uint32_t)__popc(cm), sm, &ctot);
+      const uint32_t off = block_excl_scan((uint32_t)__popc(cm), sm.wsum[2], &ctot);
       if (ctot >= k && ctot <= (uint32_t)kCap) {
         pruned = true;
 #pragma unroll
@@ -250,8 +326,8 @@ __device__ __forceinline__ void topk_of_list(const uint32_t (&key)[R], int count
           ck[r] = (uint32_t)(kCR * tid + r) < ctot ? v : 0u;
         }
         uint32_t theta, need_eq;
-        select_rank<kCR>(ck, tau, kmax, k, sm, &theta, &need_eq);          // 2.
-        compact<kCR>(ck, theta, need_eq, sm, [&](int r, uint32_t slot) {       // 3.
+        select_rank<kCR>(ck, tau, kmax, k, hist_a, hist_b, sm, &theta, &need_eq);   // 2.
+        compact<kCR>(ck, theta, need_eq, sm.wsum[2], [&](int r, uint32_t slot) {       // 3.
           emit(cand_item[kCR * tid + r], ck[r], slot);
         });
       }
@@ -259,8 +335,8 @@ __device__ __forceinline__ void topk_of_list(const uint32_t (&key)[R], int count
   }
   if (!pruned) {
     uint32_t theta, need_eq;
-    select_rank<R>(key, kmin, kmax, k, sm, &theta, &need_eq);
-    compact<R>(key, theta, need_eq, sm,
+    select_rank<R>(key, kmin, kmax, k, hist_a, hist_b, sm, &theta, &need_eq);
+    compact<R>(key, theta, need_eq, sm.wsum[2],
                [&](int r, uint32_t slot) { emit((uint32_t)(R * tid + r), key[r], slot); });
   }
 }
@@ -273,11 +349,15 @@ __device__ __forceinline__ int row_len(const int* n_valid, int n_add, int64_t ld
 // Stage 1, grid (rows, chunks): rows with n <= k get 0..n-1 and -1 padding; rows with
 // k < n <= 32768 get their final top-k; longer rows write each chunk's top-k as
 // (key, position) lists: ws_key / ws_pos [row][chunk][k], ws_cnt [row][chunk].
+// LDS: the padded chunk copy; once every thread holds its keys in registers it becomes
+// the candidate list (words 0 .. 2*kCap) and the second histogram (after that).
 __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
     int* __restrict__ idx, int64_t ld_idx, uint32_t* __restrict__ ws_key, int* __restrict__ ws_pos,
     int* __restrict__ ws_cnt, int max_chunks) {
-  __shared__ uint32_t pad[kPadWords];      // padded chunk copy, later the candidate list
+  __shared__ __attribute__((aligned(16))) uint32_t pad[kPadWords];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_a[kHistWords];
+  __shared__ __attribute__((aligned(16))) uint32_t samp[kThreads];
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int row = blockIdx.x, chunk = blockIdx.y;
@@ -293,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   const int cnt = min(kChunk, n - c0);
   const bool multi = n > kChunk;
 
+  reinterpret_cast<uint4*>(hist_a)[tid] = make_uint4(0, 0, 0, 0);   // zero for select_rank
   // coalesced 16-byte loads into the padded LDS copy
   const float* src = scores + (int64_t)row * ld + c0;
   if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
@@ -338,11 +419,12 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     const uint32_t v = pad[33 * tid + r];          // in bounds: 33 * 1023 + 31 < kPadWords
     key[r] = r < nv ? v : 0u;
   }
-  __syncthreads();    // the LDS copy now becomes the candidate list
-
+  // (topk_of_list's first barrier comes after every thread has read its keys, so pad is
+  // free from there on)
   uint32_t* cand_key = pad;
   uint32_t* cand_item = pad + kCap;
-  topk_of_list<kR>(key, cnt, (uint32_t)k, sm, cand_key, cand_item,
+  uint32_t* hist_b = pad + 2 * kCap;
+  topk_of_list<kR>(key, cnt, (uint32_t)k, sm, hist_a, hist_b, samp, cand_key, cand_item,
                    [&](uint32_t item, uint32_t kv, uint32_t slot) {
                      if (slot >= (uint32_t)k) return;
                      if (!multi) {
@@ -363,10 +445,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     int64_t ld, const int* __restrict__ n_valid, int n_add, int k, int* __restrict__ idx,
     int64_t ld_idx, const uint32_t* __restrict__ ws_key, const int* __restrict__ ws_pos,
     const int* __restrict__ ws_cnt, int max_chunks) {
-  __shared__ uint32_t lkey[kCap];
+  __shared__ __attribute__((aligned(16))) uint32_t lkey[kCap];
   __shared__ int lpos[kCap];
   __shared__ uint32_t nkey[kMaxK];
   __shared__ int npos[kMaxK];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_a[kHistWords];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_b[kHistWords];
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -387,6 +471,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
       fill += m;
       ++c;
     }
+    reinterpret_cast<uint4*>(hist_a)[tid] = make_uint4(0, 0, 0, 0);
     __syncthreads();
     if (fill > k) {
       uint32_t ck[kCR];
@@ -395,8 +480,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         const uint32_t v = lkey[kCR * tid + r];      // in bounds: kCR * 1024 == kCap
         ck[r] = kCR * tid + r < fill ? v : 0u;
       }
-      // 8 entries per thread: topk_of_list does no pruning, so it needs no candidate scratch
-      topk_of_list<kCR>(ck, fill, (uint32_t)k, sm, nullptr, nullptr,
+      // 8 entries per thread: topk_of_list does no pruning, so it needs no sample or
+      // candidate scratch
+      topk_of_list<kCR>(ck, fill, (uint32_t)k, sm, hist_a, hist_b, nullptr, nullptr, nullptr,
                         [&](uint32_t item, uint32_t kv, uint32_t slot) {
                           if (slot < (uint32_t)k) {
                             nkey[slot] = kv;
