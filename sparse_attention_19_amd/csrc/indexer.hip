@@ -197,7 +197,6 @@ __global__ __launch_bounds__(kDecode ? 256 : 512) void indexer_bf16_kernel(
 // decode: one wave per workgroup, grid (key ranges of `range` keys, T)
 constexpr int kSlice = 32;                       // keys per slice
 constexpr int kSliceBytes = kSlice * kRowBytes;  // 8 KB
-constexpr int kRing = 3;
 constexpr int kMaxRange = 1024;
 
 __device__ __forceinline__ float score32_swz(const QFrag& f, const uint8_t* slice) {
@@ -222,38 +221,26 @@ __device__ __forceinline__ float score32_swz(const QFrag& f, const uint8_t* slic
   return p + 0.0f;   // canonical +0.0
 }
 
-// The 8 direct-to-LDS loads of one 32-key slice (8 KB) into a ring slot.
-__device__ __forceinline__ void issue_slice(const uint8_t* base, uint8_t* dst) {
+// One 32-key slice (8 KB, 32 consecutive rows of one page) in registers: load i of lane
+// l holds row 4i + l/16, 16-byte chunk l%16 -- each load reads 1 KB contiguous.
+struct SliceRegs {
+  u32x4 v[8];
+};
+
+__device__ __forceinline__ void load_slice(SliceRegs& r, const uint8_t* rows) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.v[i] = *reinterpret_cast<const u32x4*>(rows + 1024 * i + 16 * lane);
+}
+
+// Into an LDS slot with the XOR swizzle score32_swz reads: chunk c of row r at c ^ (r % 16).
+__device__ __forceinline__ void store_slice(const SliceRegs& r, uint8_t* dst) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    lds_dma16(base + r * kRowBytes + 16 * c, dst + 1024 * i);
+    const int row = 4 * i + (lane >> 4);
+    *reinterpret_cast<u32x4*>(dst + row * kRowBytes + 16 * ((lane & 15) ^ (row & 15))) = r.v[i];
   }
-}
-
-// One step of the ring: request the slice two ahead into `next` (when `ahead`), wait for
-// this slice's own loads, score its 32 keys from `cur` and park the scores in `sc`.
-// `cur`, `next` and `sc` are distinct LDS regions; declaring them __restrict__ lets the
-// compiler see that the loads still landing in other ring slots do not feed the reads of
-// `cur`, so it does not drain them before reading (the wait below is for this slice only).
-__device__ __forceinline__ void slice_step(const QFrag& f, const uint8_t* __restrict__ cur,
-                                           uint8_t* __restrict__ next, const uint8_t* src, bool ahead,
-                                           bool more, float* __restrict__ sc, bool zero) {
-  const int lane = threadIdx.x & 63;
-  if (ahead) {
-    issue_slice(src, next);
-    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(16));   // slices +1 and +2 may still fly
-  } else if (more) {
-    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(8));
-  } else {
-    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
-  }
-  asm volatile("" ::: "memory");
-  float p = score32_swz(f, cur);
-  if (zero) p = 0.f;                               // empty row: score 0
-  if (lane < kSlice) sc[lane] = p;
 }
 
 __global__ __launch_bounds__(64) void indexer_decode_kernel(
@@ -261,7 +248,7 @@ __global__ __launch_bounds__(64) void indexer_decode_kernel(
     int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
     int max_blocks, int batch, const int* __restrict__ q_row, const int* __restrict__ q_pos,
     int range, float* __restrict__ scores, int64_t ld) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kSliceBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2][kSliceBytes];
   __shared__ float sc[kMaxRange];
   const int lane = threadIdx.x;
   const int t = blockIdx.y;
@@ -284,17 +271,21 @@ __global__ __launch_bounds__(64) void indexer_decode_kernel(
   QFrag f;
   load_qfrag(f, q_idx + (int64_t)t * kHi * kRowBytes, w + (int64_t)t * kHi);
 
-  // lane l of load i of a slice fills (row 4i + l/16, LDS chunk l%16) with global chunk
-  // (l%16) ^ (row % 16); an unusable page reads block 0 (always valid memory) and its
-  // scores are zeroed
-  auto slice_src = [&](int sl) {
+  // rows of slice sl (an unusable page reads block 0 -- always valid memory -- and its
+  // scores are zeroed)
+  auto slice_rows = [&](int sl) {
     const int page = (sl * kSlice) / kBlock;
     const int phys = __shfl(my_phys, page, kWave);
     const bool ok = __shfl((int)my_ok, page, kWave) != 0;
     return pool + ((int64_t)(ok ? phys : 0) * kBlock + (key0 + sl * kSlice) % kBlock) * kRowBytes;
   };
-  // Q and the page lookups are in registers from here on: the loop below then waits only
-  // for its own slices' loads
+  auto score_slice = [&](int sl) {
+    float p = score32_swz(f, ring[sl & 1]);
+    const int page = (sl * kSlice) / kBlock;
+    if (__shfl((int)my_ok, page, kWave) == 0) p = 0.f;   // empty row: score 0
+    if (lane < kSlice) sc[sl * kSlice + lane] = p;
+  };
+  // Q and the page lookups are in registers from here on
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -303,18 +294,28 @@ __global__ __launch_bounds__(64) void indexer_decode_kernel(
     for (int j = 0; j < 16; ++j) settle(f.w[h][j]);
   }
   settle(my_phys);
-  __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
-  // always two slices: the second of a one-slice range lies in the same 64-key page, so
-  // it reads valid memory (into a slot nobody reads) and the load count stays fixed
-  issue_slice(slice_src(0), ring[0]);
-  issue_slice(slice_src(1), ring[1]);
-  for (int sl = 0; sl < ns; ++sl) {
-    const bool ahead = sl + 2 < ns;
-    const uint8_t* src = ahead ? slice_src(sl + 2) : pool;
-    const int page = (sl * kSlice) / kBlock;
-    const bool zero = __shfl((int)my_ok, page, kWave) == 0;
-    slice_step(f, ring[sl % kRing], ring[(sl + 2) % kRing], src, ahead, sl + 1 < ns,
-               sc + sl * kSlice, zero);
+  // Slices stream through registers two ahead and a 2-slot LDS ring: at step sl the
+  // registers of slice sl+1 go to slot (sl+1)&1 (which held slice sl-1) and are reloaded
+  // with slice sl+3, then slice sl is scored from slot sl&1.  The second slice of a
+  // one-slice range lies in the same 64-key page, so it reads valid memory.
+  SliceRegs ra, rb;
+  load_slice(ra, slice_rows(0));
+  load_slice(rb, slice_rows(1));
+  store_slice(ra, ring[0]);
+  if (ns > 2) load_slice(ra, slice_rows(2));
+  for (int sl = 0; sl < ns; sl += 2) {
+    if (sl + 1 < ns) {
+      store_slice(rb, ring[1]);
+      if (sl + 3 < ns) load_slice(rb, slice_rows(sl + 3));
+    }
+    score_slice(sl);
+    if (sl + 1 < ns) {
+      if (sl + 2 < ns) {
+        store_slice(ra, ring[0]);
+        if (sl + 4 < ns) load_slice(ra, slice_rows(sl + 4));
+      }
+      score_slice(sl + 1);
+    }
   }
   __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
   float* dst = scores + (int64_t)t * ld + key0;
@@ -380,9 +381,11 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
                               a.q_row, a.q_pos, a.T, per, a.scores, a.ld);
       }
     } else {
-      // key ranges of 128..1024 keys: at least ~2048 single-wave workgroups over the batch
+      // key ranges of 64..1024 keys, halved until there are ~8192 single-wave workgroups:
+      // about four rounds of the 2048 that the 256 CUs hold at once, so the last round
+      // is not left half empty
       int range = kMaxRange;
-      while (range > 128 && (int64_t)a.T * ((max_keys + range - 1) / range) < 2048) range >>= 1;
+      while (range > 64 && (int64_t)a.T * ((max_keys + range - 1) / range) < 8192) range >>= 1;
       dim3 grid((max_keys + range - 1) / range, a.T);
       {
         const KernelEvents ev("indexer_decode_kernel");

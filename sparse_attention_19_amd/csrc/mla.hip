@@ -11,17 +11,18 @@
 //
 // bf16 instance (64 heads, 512 + 64): a workgroup of 8 waves handles one (token, split)
 // pair and walks its slice of the selected list in tiles of 32 rows:
-//   gather   : page-translate each position once into an LDS row-id list; every tile's
-//              1152-byte rows stream straight into a padded LDS tile with
-//              global_load_lds_dwordx4 (no staging registers), two tiles ahead through a
-//              3-slot ring, so the rows are fetched from HBM exactly once
+//   gather   : page-translate each position once into an LDS row-id list; each tile's
+//              1152-byte rows are fetched with coalesced 16-byte register loads one step
+//              ahead and written into a 3-slot LDS ring (rows padded to 73 chunks and
+//              placed so that both operand reads below are free of bank conflicts), so
+//              every row is read from HBM exactly once
 //   logits   : S^T[key][head] = K[key][:] . Q^T on 16x16x32 MFMA, Q held in registers;
 //              the 8 waves split heads, dims and keys and exchange partials through LDS
 //   softmax  : online (running max / sum per head, exp2 with log2(e) folded into the
 //              scale, rescale of O only when the max grows by more than 2^8); P to LDS
 //   P.V      : O[head][dim] += P[head][key] . V[key][dim], each wave 64 output dims of all
 //              heads; the V operand comes from the same LDS tile through the transposing
-//              ds_read_b64_tr_b16
+//              ds_read_b64_tr_b16; it runs in the same phase as the next tile's logits
 // When there are few tokens, splits of the selected list run in parallel workgroups and a
 // combine kernel merges their partial (O, max, sum) with log-sum-exp weights.
 #include <math.h>
@@ -40,11 +41,10 @@ constexpr int kMT = 32;                         // rows per tile
 constexpr int kRowSlots = kChunks + 1;          // LDS row stride: 73 chunks (odd)
 constexpr int kTileSlots = kMT * kRowSlots;     // 2336
 constexpr int kTileBytes = kTileSlots * 16;     // 37376
-constexpr int kTileLoads = (kTileSlots + 63) / 64;   // 37 direct-to-LDS loads of 1 KB
-constexpr int kRing = 3;                        // LDS tile slots: 2 tiles in flight
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxLoadsPerWave = (kTileLoads + kWaves - 1) / kWaves;   // 5 (waves 0-4), 4 (5-7)
+constexpr int kTileChunks = kMT * kChunks;      // 2304 16-byte chunks per tile
+constexpr int kLoads = (kTileChunks + kThreads - 1) / kThreads;   // 5 per thread (the last partial)
 constexpr int kMaxList = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -86,52 +86,45 @@ __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const in
   }
 }
 
-// Direct-to-LDS gather of one tile (rows e0 .. e0+31 of the list): load m of wave w fills
-// tile slots 64*(w + 8m) + lane.  The (row, chunk) each lane fetches is fixed for the whole
-// kernel and precomputed; lanes on a row's pad slot stay idle.  Rows without a valid
-// position read row 0 of the pool (always valid memory); their logits are masked.
-struct TileLoads {
-  int row[kMaxLoadsPerWave];
-  int off[kMaxLoadsPerWave];   // byte offset of the chunk within its row
-  uint32_t active;             // bit m: load m is issued by this wave and this lane
-  int count;                   // loads this wave issues per tile
+// LDS row of list entry k of a tile: within each group of 8 the entries go to rows
+// 0,2,4,6,1,3,5,7.  With the 73-chunk row stride this keeps both operand reads free of
+// bank conflicts: the logits read 16 consecutive entries at one chunk (rows 4 banks
+// apart), the transposing V read takes 4 consecutive entries per 16-lane group (now 8
+// banks apart).
+__device__ __forceinline__ int lds_row(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
+
+// Register-staged gather of one tile (list entries e0 .. e0+31): thread t fetches chunks
+// q = t + 512 m (entry q / 72, chunk q % 72), so each wave reads one or two whole rows
+// per load -- contiguous 1152-byte runs.  Entries without a valid position read row 0 of
+// the pool (always valid memory, finite data); their logits are masked.
+struct TileRegs {
+  u32x4 v[kLoads];
 };
 
-__device__ __forceinline__ TileLoads plan_tile_loads() {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  TileLoads tl;
-  tl.active = 0;
-  tl.count = (kTileLoads - wave + kWaves - 1) / kWaves;
+__device__ __forceinline__ void load_tile(TileRegs& r, const uint8_t* pool, const int* rowid, int e0,
+                                          int nent) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int m = 0; m < kMaxLoadsPerWave; ++m) {
-    const int s = 64 * (wave + kWaves * m) + lane;
-    const int row = s / kRowSlots, ch = s - row * kRowSlots;
-    tl.row[m] = row < kMT ? row : 0;
-    tl.off[m] = 16 * ch;
-    if (m < tl.count && row < kMT && ch < kChunks) tl.active |= 1u << m;
-  }
-  return tl;
-}
-
-// Row ids of this lane's loads of the tile starting at list entry e0 (-1: none).
-__device__ __forceinline__ void tile_rowids(const TileLoads& tl, const int* rowid, int e0, int nent,
-                                            int (&rid)[kMaxLoadsPerWave]) {
-#pragma unroll
-  for (int m = 0; m < kMaxLoadsPerWave; ++m) {
-    const int e = e0 + tl.row[m];
-    rid[m] = (m < tl.count && e < nent) ? rowid[e] : -1;
+  for (int m = 0; m < kLoads; ++m) {
+    const int q = tid + kThreads * m;
+    if (q < kTileChunks) {
+      const int key = q / kChunks, ch = q - key * kChunks;
+      const int e = e0 + key;
+      const int rid = e < nent ? rowid[e] : -1;
+      r.v[m] = *reinterpret_cast<const u32x4*>(pool + (int64_t)(rid >= 0 ? rid : 0) * kRowBytes + 16 * ch);
+    }
   }
 }
 
-__device__ __forceinline__ void issue_tile(const TileLoads& tl, const uint8_t* pool,
-                                           const int (&rid)[kMaxLoadsPerWave], uint8_t* dst) {
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void store_tile(const TileRegs& r, uint8_t* dst) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int m = 0; m < kMaxLoadsPerWave; ++m) {
-    if (m >= tl.count) break;                      // uniform per wave
-    const uint8_t* src = pool + (int64_t)(rid[m] >= 0 ? rid[m] : 0) * kRowBytes + tl.off[m];
-    if (tl.active & (1u << m))
-      lds_dma16(src, dst + 1024 * (wave + kWaves * m));
+  for (int m = 0; m < kLoads; ++m) {
+    const int q = tid + kThreads * m;
+    if (q < kTileChunks) {
+      const int key = q / kChunks, ch = q - key * kChunks;
+      *reinterpret_cast<u32x4*>(dst + 16 * tile_slot(lds_row(key), ch)) = r.v[m];
+    }
   }
 }
 
@@ -147,49 +140,18 @@ __device__ __forceinline__ void issue_tile(const TileLoads& tl, const uint8_t* p
 //             once from LDS with the transposing ds_read_b64_tr_b16) feeds four MFMAs.
 constexpr int kSRow = 36;          // partial-logit row stride (floats): conflict-free 16-byte writes
 constexpr int kPRow = 40;          // P row stride (bf16): 80 bytes, conflict-free operand reads
+constexpr int kSteps = kRow / 64;  // 9 k-steps of 32 dims per dim half
 
-// One 32-row tile of the list: wait for this wave's loads of the tile, request tile + 2
-// into `next`, then logits, online softmax and P.V from `kb`.  The LDS regions (the tile's
-// slot, the slot being filled, the row-id list and the exchange buffers) are distinct and
-// passed __restrict__, which tells the compiler that the loads still landing in `next`
-// and the other slot do not feed any of these reads; otherwise it drains every
-// outstanding global->LDS load before the first read and the prefetch never overlaps.
-__device__ __forceinline__ void mla_tile(const uint8_t* __restrict__ kb, uint8_t* __restrict__ next,
-                                         const int* __restrict__ rowid, float* __restrict__ spart,
-                                         uint16_t* __restrict__ pmat, float* __restrict__ s_alpha,
-                                         int* __restrict__ s_grow, const uint8_t* pool,
-                                         const TileLoads& tl, int tile, int ntiles, int nent,
-                                         const bf16x8 (&qf)[2][kRow / 64], int ka, int vb,
-                                         float scale_log2, f32x4 (&o)[4][4], float& m_run,
-                                         float& l_run) {
-  constexpr int kSteps = kRow / 64;          // 9 k-steps of 32 dims per dim half
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// Partial logits of one tile (slot `kb`) into spart[dh][head][key].
+__device__ __forceinline__ void logits_phase(const uint8_t* kb, int ka, const bf16x8 (&qf)[2][kSteps],
+                                             float* spart) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hg = wave & 1, dh = (wave >> 1) & 1, kh = wave >> 2;
   const int g = lane >> 4, c16 = lane & 15;
-  const int sm_head = 8 * wave + (lane >> 3);
-  const int sm_key = 4 * (lane & 7);
-  int rid[kMaxLoadsPerWave];
-  const int e0 = tile * kMT;
-  tile_rowids(tl, rowid, e0 + 2 * kMT, nent, rid);
-  const int er = e0 + (lane & 31);
-  const int vr = er < nent ? rowid[er] : -1;
-  // this wave's loads of `tile` done (the next tile's may still fly), then everyone's
-  if (tile + 1 < ntiles) {
-    if (tl.count == 5) __builtin_amdgcn_s_waitcnt(DSA_VMCNT(5));
-    else __builtin_amdgcn_s_waitcnt(DSA_VMCNT(4));
-  } else {
-    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
-  }
-  lds_barrier();
-  // every wave finished tile-1, so its slot takes tile+2
-  if (tile + 2 < ntiles) issue_tile(tl, pool, rid, next);
-  const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // row r valid -> bit r
-
-  // ---- partial logits: keys 16kh + 4g + j, heads 32hg + 16ht + c16, dims of half dh
   f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int st = 0; st < kSteps; ++st) {
-    const bf16x8 a = as_bf8(*reinterpret_cast<const uint4*>(kb + ka + 64 * st));
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + ka + 64 * st);
     sacc[0] = mfma16(a, qf[0][st], sacc[0]);
     sacc[1] = mfma16(a, qf[1][st], sacc[1]);
   }
@@ -197,43 +159,53 @@ __device__ __forceinline__ void mla_tile(const uint8_t* __restrict__ kb, uint8_t
   for (int ht = 0; ht < 2; ++ht)
     *reinterpret_cast<f32x4*>(&spart[(dh * kH + 32 * hg + 16 * ht + c16) * kSRow + 16 * kh + 4 * g]) =
         sacc[ht];
-  lds_barrier();
+}
 
-  // ---- softmax of the owned head over the tile's 32 keys (8 lanes x 4 keys)
-  {
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&spart[sm_head * kSRow + sm_key]);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&spart[(kH + sm_head) * kSRow + sm_key]);
-    float x[4];
+// Online-softmax update of the owned head over one tile's 32 keys (8 lanes x 4 keys):
+// P (bf16) to pmat, the O rescale factor to s_alpha, and whether any head of this wave
+// rescales to s_grow.
+__device__ __forceinline__ void softmax_phase(const float* spart, uint16_t* pmat, float* s_alpha,
+                                              int* s_grow, uint32_t vmask, float scale_log2,
+                                              float& m_run, float& l_run) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sm_head = 8 * wave + (lane >> 3);
+  const int sm_key = 4 * (lane & 7);
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(&spart[sm_head * kSRow + sm_key]);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(&spart[(kH + sm_head) * kSRow + sm_key]);
+  float x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      x[j] = (vmask >> (sm_key + j)) & 1u ? (a0[j] + a1[j]) * scale_log2 : -INFINITY;
-    const float tmax = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    // the running max only moves when a logit exceeds it by more than the slack, so
-    // exp2(x - m) stays <= 2^8 and the O rescale is rare
-    const bool grow = tmax > m_run + kRescaleSlack;
-    const float m_new = grow ? tmax : m_run;
-    const bool none = (m_new == -INFINITY);
-    const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-    float p[4], psum = 0.f;
+  for (int j = 0; j < 4; ++j)
+    x[j] = (vmask >> (sm_key + j)) & 1u ? (a0[j] + a1[j]) * scale_log2 : -INFINITY;
+  const float tmax = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  // the running max only moves when a logit exceeds it by more than the slack, so
+  // exp2(x - m) stays <= 2^8 and the O rescale is rare
+  const bool grow = tmax > m_run + kRescaleSlack;
+  const float m_new = grow ? tmax : m_run;
+  const bool none = (m_new == -INFINITY);
+  const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+  float p[4], psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
-      psum += p[j];
-    }
-    psum = group8_sum(psum);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
-    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
-    *reinterpret_cast<uint2*>(&pmat[sm_head * kPRow + sm_key]) = make_uint2(lo, hi);
-    if ((lane & 7) == 0) s_alpha[sm_head] = alpha;
-    if (lane == 0) s_grow[wave] = __ballot(alpha != 1.f) != 0;
+  for (int j = 0; j < 4; ++j) {
+    p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
+    psum += p[j];
   }
-  lds_barrier();
+  psum = group8_sum(psum);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
+  const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
+  *reinterpret_cast<uint2*>(&pmat[sm_head * kPRow + sm_key]) = make_uint2(lo, hi);
+  if ((lane & 7) == 0) s_alpha[sm_head] = alpha;
+  if (lane == 0) s_grow[wave] = __ballot(alpha != 1.f) != 0;
+}
 
-  // ---- O[64 heads][dims 64w + 16dt + c16] += P . V
+// O[64 heads][dims 64w + 16dt + c16] = alpha * O + P . V for one tile (slot `kb`).
+__device__ __forceinline__ void pv_phase(const uint8_t* kb, int vlo, int vhi, const uint16_t* pmat,
+                                         const float* s_alpha, const int* s_grow, f32x4 (&o)[4][4]) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
   const int4 gr0 = *reinterpret_cast<const int4*>(&s_grow[0]);
   const int4 gr1 = *reinterpret_cast<const int4*>(&s_grow[4]);
   if (gr0.x | gr0.y | gr0.z | gr0.w | gr1.x | gr1.y | gr1.z | gr1.w) {
@@ -249,11 +221,11 @@ __device__ __forceinline__ void mla_tile(const uint8_t* __restrict__ kb, uint8_t
   bf16x8 pa[4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
-    pa[ht] = as_bf8(*reinterpret_cast<const uint4*>(&pmat[(16 * ht + c16) * kPRow + 8 * g]));
+    pa[ht] = *reinterpret_cast<const bf16x8*>(&pmat[(16 * ht + c16) * kPRow + 8 * g]);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    const s16x4 lo = lds_read_tr16(kb + vb + 32 * dt);
-    const s16x4 hi = lds_read_tr16(kb + vb + 16 * 4 * kRowSlots + 32 * dt);
+    const s16x4 lo = lds_read_tr16(kb + vlo + 32 * dt);
+    const s16x4 hi = lds_read_tr16(kb + vhi + 32 * dt);
     const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
                                                            hi[0], hi[1], hi[2], hi[3]};
     const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
@@ -268,8 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
     int64_t ld_idx, int k, float scale_log2, int splits, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  constexpr int kSteps = kRow / 32 / 2;      // 9 k-steps of 32 dims per dim half
-  __shared__ __attribute__((aligned(16))) uint8_t kv[kRing][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kv[3][kTileBytes];
   __shared__ int rowid[kMaxList];
   __shared__ __attribute__((aligned(16))) float spart[2][kH][kSRow];   // [dh][head][key]
   __shared__ __attribute__((aligned(16))) uint16_t pmat[kH][kPRow];    // P[head][key] bf16
@@ -292,7 +263,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) qf[ht][st] = as_bf8(src[4 * st]);
   }
-  const TileLoads tl = plan_tile_loads();
   int nent;
   resolve_rows(t, sp, splits, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos,
                idx, ld_idx, k, rowid, nent);
@@ -309,28 +279,37 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ka = 16 * tile_slot(16 * kh + c16, 36 * dh + g);           // + 64 st
-  const int vb = 16 * tile_slot(8 * g + (c16 >> 2), 0) + 8 * (c16 & 3) + 128 * wave;  // + 32 dt
+  // operand addresses: K of entry 16kh + c16 at chunk 36dh + g (+ 4 per k-step); V of
+  // entries 8g + c16/4 (lo) and 8g + 4 + c16/4 (hi), bytes 8 (c16 % 4) of dims 64w..
+  const int ka = 16 * tile_slot(lds_row(16 * kh + c16), 36 * dh + g);            // + 64 st
+  const int vlo = 16 * tile_slot(lds_row(8 * g + (c16 >> 2)), 0) + 8 * (c16 & 3) + 128 * wave;
+  const int vhi = 16 * tile_slot(lds_row(8 * g + 4 + (c16 >> 2)), 0) + 8 * (c16 & 3) + 128 * wave;
   const int ntiles = (nent + kMT - 1) / kMT;
-  // Q and the lookups are in registers from here on: the loop below then waits only for
-  // its own tiles' loads
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) settle(qf[ht][st]);
-  __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
+  // Tiles stream through a 3-slot LDS ring from registers: at the top of step t every
+  // wave writes its share of tile t+1 (loaded during step t-1) into the slot tile t-2
+  // held, then starts loading tile t+2 into the same registers.  Step t then runs P.V of
+  // tile t-1 together with the logits of tile t (both MFMA work), a barrier, the softmax
+  // of tile t, and a barrier.
+  TileRegs r;
   if (ntiles > 0) {
-    // always two tiles: rows past the list read row 0 of the pool (valid memory) into a
-    // slot nobody reads, and the load count stays fixed
-    int rid[kMaxLoadsPerWave];
-    tile_rowids(tl, rowid, 0, nent, rid);
-    issue_tile(tl, pool, rid, kv[0]);
-    tile_rowids(tl, rowid, kMT, nent, rid);
-    issue_tile(tl, pool, rid, kv[1]);
+    load_tile(r, pool, rowid, 0, nent);
+    store_tile(r, kv[0]);
   }
-  for (int tile = 0; tile < ntiles; ++tile)
-    mla_tile(kv[tile % kRing], kv[(tile + 2) % kRing], rowid, &spart[0][0][0], &pmat[0][0], s_alpha,
-             s_grow, pool, tl, tile, ntiles, nent, qf, ka, vb, scale_log2, o, m_run, l_run);
+  if (ntiles > 1) load_tile(r, pool, rowid, kMT, nent);
+  lds_barrier();
+  for (int t = 0; t <= ntiles; ++t) {
+    if (t + 1 < ntiles) store_tile(r, kv[(t + 1) % 3]);
+    if (t + 2 < ntiles) load_tile(r, pool, rowid, (t + 2) * kMT, nent);
+    const int er = t * kMT + (lane & 31);
+    const int vr = er < nent ? rowid[er] : -1;
+    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // entry r valid -> bit r
+    if (t >= 1) pv_phase(kv[(t - 1) % 3], vlo, vhi, &pmat[0][0], s_alpha, s_grow, o);
+    if (t < ntiles) logits_phase(kv[t % 3], ka, qf, &spart[0][0][0]);
+    lds_barrier();
+    if (t < ntiles)
+      softmax_phase(&spart[0][0][0], &pmat[0][0], s_alpha, s_grow, vmask, scale_log2, m_run, l_run);
+    lds_barrier();
+  }
 
   // ---- epilogue: per-head (m, l) from the softmax owners
   if ((lane & 7) == 0) {
