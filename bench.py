@@ -184,7 +184,9 @@ def run_bench(args):
     step_bytes = sum(step_parts.values())
     copies = args.copies or max(1, min(64, -(-2 * MALL_BYTES // step_bytes)))
 
-    inputs = [I.make_inputs(I.shrink(cfg, seed=cfg.seed + 1000 * c), dev) for c in range(copies)]
+    # copies: same lengths and page layout, new data
+    inputs = [I.make_inputs(I.shrink(cfg, seed=cfg.seed + 1000 * c, layout_seed=cfg.seed), dev)
+              for c in range(copies)]
     buf = P.run_inputs(inputs[0])
     torch.cuda.synchronize()
 
@@ -305,6 +307,33 @@ def _counter_per_dispatch(d, counter, pick):
     return per
 
 
+def summarize_counters(args):
+    """Per-kernel averages of every counter of a --pmc run (the path's kernels only).
+    SQ counters are summed over their instances, GRBM ones (one per XCD) take the
+    maximum; with both present, MfmaUtil is rocprofv3's own definition:
+    sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMDs) with 1024 SIMDs."""
+    c = _db(args.summarize_counters)
+    per = {}
+    for kname, disp, cname, val in c.execute(
+            "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+        k = _short(kname or "")
+        if not k.endswith("_kernel"):
+            continue
+        d = per.setdefault(k, {}).setdefault(cname, {})
+        d[disp] = max(d.get(disp, 0.0), val) if cname.startswith("GRBM_") else d.get(disp, 0.0) + val
+    print(f"# rocprofv3 counters: {args.title}")
+    print(f"# profiled with : {args.command}")
+    print(f"# summarised by : python bench.py --summarize-counters <output dir>")
+    for k in sorted(per):
+        print(k)
+        avg = {cname: sum(d.values()) / len(d) for cname, d in per[k].items()}
+        for cname, d in sorted(per[k].items()):
+            print(f"   {cname:28s} {avg[cname]:18.1f}  per dispatch ({len(d)} dispatches)")
+        if avg.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            util = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] * 1024)
+            print(f"   {'MfmaUtil':28s} {100 * util:18.1f}  % (1024 SIMDs)")
+
+
 def summarize_traffic(args):
     import dsa_inputs as I
     kernel, cfg = args.kernel, I.CONFIGS[args.workload]
@@ -352,6 +381,7 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-traffic", action="store_true")
+    ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     ap.add_argument("--kernel")
@@ -369,6 +399,8 @@ def main():
         return summarize_trace(args)
     if args.summarize_traffic:
         return summarize_traffic(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures "
               f"the path on one MI355X; how it would shard over several is described, not run.",

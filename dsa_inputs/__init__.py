@@ -41,6 +41,8 @@ class Config:
                      ending at position ctx-1 of a single request
     layers         : DSA layers sharing one indexer (IndexShare group); 1 = plain DSA
     identity_pages : physical block i holds logical block i (else a random permutation)
+    layout_seed    : seed of the context lengths and the page permutation when set (else
+                     `seed`): copies of a workload with new data but the same layout
     """
     name: str
     seed: int
@@ -61,6 +63,7 @@ class Config:
     prefill_tokens: int = 0
     layers: int = 1
     identity_pages: bool = False
+    layout_seed: Optional[int] = None
 
     @property
     def row_dim(self) -> int:
@@ -100,8 +103,12 @@ def shrink(cfg: Config, **over) -> Config:
 
 def _gen(cfg: Config, tensor_id: int, layer: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
-    # distinct, reproducible stream per (config seed, tensor, layer)
-    g.manual_seed((cfg.seed * 1_000_003 + tensor_id * 10_007 + layer * 101 + 17) & 0x7FFFFFFFFFFF)
+    # distinct, reproducible stream per (config seed, tensor, layer); the layout tensors
+    # (lengths, page permutation) follow layout_seed when it is set
+    seed = cfg.seed
+    if cfg.layout_seed is not None and tensor_id in (_T_LENS, _T_PERM):
+        seed = cfg.layout_seed
+    g.manual_seed((seed * 1_000_003 + tensor_id * 10_007 + layer * 101 + 17) & 0x7FFFFFFFFFFF)
     return g
 
 

@@ -115,21 +115,6 @@ __device__ __forceinline__ float group8_sum(float v) {
 // Minimum over the wave, in every lane (min a = ~max ~a keeps 0 the identity).
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
 
-// One global_load_lds_dwordx4: the 16 bytes at each lane's `gptr` land in LDS at
-// lds_base + 16 * lane (lds_base is wave-uniform and is passed in M0).
-// Issued from inline asm on purpose: for the builtin, the compiler treats every later LDS
-// access as possibly aliasing any load still in flight into LDS and drains all of them
-// first (s_waitcnt vmcnt(0)), which serialises a prefetch ring.  Every caller waits for
-// its own loads with an explicit s_waitcnt vmcnt(n) before the destination is read.  The
-// instruction writes no VGPR (its data goes to LDS) and reads its address VGPRs when it
-// issues, so no register the compiler reuses is left in flight; the s_nop covers the
-// M0-write-to-LDS-DMA wait state.
-__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)DSA_LDS(void, const_cast<void*>(lds_base)));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
-}
-
 // Makes `v` available in registers at this point: its loads complete here rather than
 // wherever the scheduler would sink them (e.g. into a loop whose waits it would then
 // count against loads issued outside its view).
@@ -138,15 +123,12 @@ __device__ __forceinline__ void settle(const T& v) {
   asm volatile("" ::"v"(v));
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
-#define DSA_VMCNT(n) (((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
+// s_waitcnt immediate waiting for LDS/scalar operations only (gfx9 encoding: vmcnt[3:0]
+// and [15:14] all ones, expcnt[6:4] all ones, lgkmcnt[11:8] zero)
 #define DSA_LGKMCNT0 0xc07f
 
-// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
-// outstanding global load (vmcnt(0)), which would drain loads that are deliberately left
-// in flight across the barrier (prefetched tiles).  This waits only for the wave's own
-// LDS operations; asynchronous global->LDS copies must be waited for explicitly (vmcnt)
-// by the wave that issued them before it reaches the barrier.
+// Workgroup barrier for LDS traffic only: waits for the wave's own LDS operations, not for
+// global loads still in flight into registers (prefetched tiles stay in flight across it).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
   asm volatile("" ::: "memory");

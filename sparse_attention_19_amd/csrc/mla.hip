@@ -290,6 +290,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   // held, then starts loading tile t+2 into the same registers.  Step t then runs P.V of
   // tile t-1 together with the logits of tile t (both MFMA work), a barrier, the softmax
   // of tile t, and a barrier.
+  // Q is in registers from here on (its loads complete here, not inside the loop, where
+  // the compiler would count them against the tile loads in flight)
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) settle(qf[ht][st]);
   TileRegs r;
   if (ntiles > 0) {
     load_tile(r, pool, rowid, 0, nent);
