@@ -12,8 +12,8 @@
 // bf16 instance (64 heads, 512 + 64): a workgroup of 8 waves handles one (token, split)
 // pair and walks its slice of the selected list in tiles of 32 rows:
 //   gather   : page-translate each position once into an LDS row-id list; each tile's
-//              1152-byte rows are fetched with coalesced 16-byte register loads one step
-//              ahead and written into a 3-slot LDS ring (rows padded to 73 chunks and
+//              1152-byte rows are fetched with coalesced 16-byte register loads three
+//              tiles ahead of their P.V and written into a 3-slot LDS ring (rows padded to 73 chunks and
 //              placed so that both operand reads below are free of bank conflicts), so
 //              every row is read from HBM exactly once
 //   logits   : S^T[key][head] = K[key][:] . Q^T on 16x16x32 MFMA, Q held in registers;
@@ -22,7 +22,9 @@
 //              scale, rescale of O only when the max grows by more than 2^8); P to LDS
 //   P.V      : O[head][dim] += P[head][key] . V[key][dim], each wave 64 output dims of all
 //              heads; the V operand comes from the same LDS tile through the transposing
-//              ds_read_b64_tr_b16; it runs in the same phase as the next tile's logits
+//              ds_read_b64_tr_b16
+// The softmax of tile t shares a phase with the logits MFMAs of tile t+1, so its VALU
+// work issues while the matrix cores run.
 // When there are few tokens, splits of the selected list run in parallel workgroups and a
 // combine kernel merges their partial (O, max, sum) with log-sum-exp weights.
 #include <math.h>
@@ -55,7 +57,8 @@ constexpr float kRescaleSlack = 8.f;            // log2 units a running max may 
 __device__ __forceinline__ int tile_slot(int row, int ch) { return row * kRowSlots + ch; }
 
 // Resolve the token's (request, n) and this split's slice [i0, i0 + nent) of the
-// selected list; fills rowid[] with global row ids (phys * 64 + slot) or -1.
+// selected list; fills rowid[] with global row ids (phys * 64 + slot) or -1, up to the
+// end of the slice's last 32-entry tile.
 __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const int* block_table,
                                              const int* seq_len, int max_blocks, int batch,
                                              int64_t num_blocks, const int* q_row, const int* q_pos,
@@ -84,6 +87,9 @@ __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const in
     }
     rowid[e] = rid;
   }
+  // entries up to the end of the last tile read as "no position"
+  const int padded = (nent + kMT - 1) / kMT * kMT;
+  for (int e = nent + threadIdx.x; e < padded; e += blockDim.x) rowid[e] = -1;
 }
 
 // LDS row of list entry k of a tile: within each group of 8 the entries go to rows
@@ -101,30 +107,35 @@ struct TileRegs {
   u32x4 v[kLoads];
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const uint8_t* pool, const int* rowid, int e0,
-                                          int nent) {
+// Straight-line: the row-id reads go out first, then the five loads (the fifth chunk
+// exists for waves 0-3 only: 2304 = 4.5 x 512 chunks -- a wave-uniform, scalar test).
+__device__ __forceinline__ void load_tile(TileRegs& r, const uint8_t* pool, const int* rowid, int e0) {
   const int tid = threadIdx.x;
+  const bool fifth = __builtin_amdgcn_readfirstlane(tid >> 6) < (kTileChunks - 4 * kThreads) / 64;
+  int rid[kLoads];
 #pragma unroll
   for (int m = 0; m < kLoads; ++m) {
-    const int q = tid + kThreads * m;
-    if (q < kTileChunks) {
-      const int key = q / kChunks, ch = q - key * kChunks;
-      const int e = e0 + key;
-      const int rid = e < nent ? rowid[e] : -1;
-      r.v[m] = *reinterpret_cast<const u32x4*>(pool + (int64_t)(rid >= 0 ? rid : 0) * kRowBytes + 16 * ch);
-    }
+    const int q = min(tid + kThreads * m, kTileChunks - 1);
+    rid[m] = rowid[e0 + q / kChunks];
+  }
+#pragma unroll
+  for (int m = 0; m < kLoads; ++m) {
+    const int q = min(tid + kThreads * m, kTileChunks - 1);
+    const int ch = q - (q / kChunks) * kChunks;
+    if (m < kLoads - 1 || fifth)
+      r.v[m] = *reinterpret_cast<const u32x4*>(pool + (int64_t)max(rid[m], 0) * kRowBytes + 16 * ch);
   }
 }
 
 __device__ __forceinline__ void store_tile(const TileRegs& r, uint8_t* dst) {
   const int tid = threadIdx.x;
+  const bool fifth = __builtin_amdgcn_readfirstlane(tid >> 6) < (kTileChunks - 4 * kThreads) / 64;
 #pragma unroll
   for (int m = 0; m < kLoads; ++m) {
-    const int q = tid + kThreads * m;
-    if (q < kTileChunks) {
-      const int key = q / kChunks, ch = q - key * kChunks;
+    const int q = min(tid + kThreads * m, kTileChunks - 1);
+    const int key = q / kChunks, ch = q - key * kChunks;
+    if (m < kLoads - 1 || fifth)
       *reinterpret_cast<u32x4*>(dst + 16 * tile_slot(lds_row(key), ch)) = r.v[m];
-    }
   }
 }
 
@@ -161,44 +172,83 @@ __device__ __forceinline__ void logits_phase(const uint8_t* kb, int ka, const bf
         sacc[ht];
 }
 
-// Online-softmax update of the owned head over one tile's 32 keys (8 lanes x 4 keys):
-// P (bf16) to pmat, the O rescale factor to s_alpha, and whether any head of this wave
-// rescales to s_grow.
-__device__ __forceinline__ void softmax_phase(const float* spart, uint16_t* pmat, float* s_alpha,
-                                              int* s_grow, uint32_t vmask, float scale_log2,
-                                              float& m_run, float& l_run) {
+// Online-softmax update of the owned head over one tile's 32 keys (8 lanes x 4 keys, from
+// the partials in sp_in): P (bf16) to pmat, the O rescale factor to s_alpha, and whether
+// any head of this wave rescales to s_grow.  Interleaved with it, the logits MFMAs of the
+// next tile (slot kb, partials to sp_out): each logits k-step issues two MFMAs, and one slice of
+// the softmax chain follows it, so the VALU work issues while the MFMAs execute.  The
+// sched_barrier fences keep the compiler from regrouping the two streams.
+__device__ __forceinline__ void softmax_with_logits(const float* sp_in, float* sp_out, const uint8_t* kb,
+                                                    int ka, const bf16x8 (&qf)[2][kSteps],
+                                                    uint16_t* pmat, float* s_alpha, int* s_grow,
+                                                    uint32_t vmask, float scale_log2, float& m_run,
+                                                    float& l_run) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hg = wave & 1, dh = (wave >> 1) & 1, kh = wave >> 2;
+  const int g = lane >> 4, c16 = lane & 15;
   const int sm_head = 8 * wave + (lane >> 3);
   const int sm_key = 4 * (lane & 7);
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(&spart[sm_head * kSRow + sm_key]);
-  const f32x4 a1 = *reinterpret_cast<const f32x4*>(&spart[(kH + sm_head) * kSRow + sm_key]);
+  f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + ka);
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sp_in[sm_head * kSRow + sm_key]);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + sm_head) * kSRow + sm_key]);
+  // one logits k-step: MFMAs on the fragment in hand, fetch the next one
+#define DSA_KSTEP(st)                                                        \
+  {                                                                          \
+    const bf16x8 cur = a;                                                    \
+    if ((st) + 1 < kSteps) a = *reinterpret_cast<const bf16x8*>(kb + ka + 64 * ((st) + 1)); \
+    sacc[0] = mfma16(cur, qf[0][st], sacc[0]);                               \
+    sacc[1] = mfma16(cur, qf[1][st], sacc[1]);                               \
+  }                                                                          \
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(0)
   float x[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     x[j] = (vmask >> (sm_key + j)) & 1u ? (a0[j] + a1[j]) * scale_log2 : -INFINITY;
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(1)
   const float tmax = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(2)
   // the running max only moves when a logit exceeds it by more than the slack, so
   // exp2(x - m) stays <= 2^8 and the O rescale is rare
   const bool grow = tmax > m_run + kRescaleSlack;
   const float m_new = grow ? tmax : m_run;
   const bool none = (m_new == -INFINITY);
   const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(3)
   float p[4], psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
     psum += p[j];
   }
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(4)
   psum = group8_sum(psum);
   l_run = l_run * alpha + psum;
   m_run = m_new;
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(5)
   const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
   const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
   *reinterpret_cast<uint2*>(&pmat[sm_head * kPRow + sm_key]) = make_uint2(lo, hi);
-  if ((lane & 7) == 0) s_alpha[sm_head] = alpha;
-  if (lane == 0) s_grow[wave] = __ballot(alpha != 1.f) != 0;
+  // branch-free: the 8 lanes of a head store the same alpha, all lanes the same flag
+  s_alpha[sm_head] = alpha;
+  s_grow[wave] = __ballot(alpha != 1.f) != 0;
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(6)
+  DSA_KSTEP(7)
+  DSA_KSTEP(8)
+#undef DSA_KSTEP
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+    *reinterpret_cast<f32x4*>(&sp_out[(dh * kH + 32 * hg + 16 * ht + c16) * kSRow + 16 * kh + 4 * g]) =
+        sacc[ht];
 }
 
 // O[64 heads][dims 64w + 16dt + c16] = alpha * O + P . V for one tile (slot `kb`).
@@ -242,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t kv[3][kTileBytes];
   __shared__ int rowid[kMaxList];
-  __shared__ __attribute__((aligned(16))) float spart[2][kH][kSRow];   // [dh][head][key]
+  __shared__ __attribute__((aligned(16))) float spart[2][2][kH][kSRow];   // [buf][dh][head][key]
   __shared__ __attribute__((aligned(16))) uint16_t pmat[kH][kPRow];    // P[head][key] bf16
   __shared__ __attribute__((aligned(16))) float s_alpha[kH];
   __shared__ float s_ml[kH][2];
@@ -285,11 +335,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   const int vlo = 16 * tile_slot(lds_row(8 * g + (c16 >> 2)), 0) + 8 * (c16 & 3) + 128 * wave;
   const int vhi = 16 * tile_slot(lds_row(8 * g + 4 + (c16 >> 2)), 0) + 8 * (c16 & 3) + 128 * wave;
   const int ntiles = (nent + kMT - 1) / kMT;
-  // Tiles stream through a 3-slot LDS ring from registers: at the top of step t every
-  // wave writes its share of tile t+1 (loaded during step t-1) into the slot tile t-2
-  // held, then starts loading tile t+2 into the same registers.  Step t then runs P.V of
-  // tile t-1 together with the logits of tile t (both MFMA work), a barrier, the softmax
-  // of tile t, and a barrier.
+  // Tiles stream through a 3-slot LDS ring from registers, and each step overlaps the
+  // softmax of tile t with the logits MFMAs of tile t+1 (partial logits double-buffered):
+  //   phase 1: logits(t+1) -> spart[(t+1)&1] and softmax(t) from spart[t&1] -> P, alpha,
+  //            interleaved so that about four softmax VALU instructions issue under
+  //            each MFMA
+  //   phase 2: P.V(t); tile t+2 (loaded into registers during step t-1) into the slot
+  //            tile t-1 held; load tile t+3 into the registers
+  // with a barrier after each phase.
   // Q is in registers from here on (its loads complete here, not inside the loop, where
   // the compiler would count them against the tile loads in flight)
 #pragma unroll
@@ -298,22 +351,28 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     for (int st = 0; st < kSteps; ++st) settle(qf[ht][st]);
   TileRegs r;
   if (ntiles > 0) {
-    load_tile(r, pool, rowid, 0, nent);
+    load_tile(r, pool, rowid, 0);
     store_tile(r, kv[0]);
   }
-  if (ntiles > 1) load_tile(r, pool, rowid, kMT, nent);
+  if (ntiles > 1) {
+    load_tile(r, pool, rowid, kMT);
+    store_tile(r, kv[1]);
+  }
+  if (ntiles > 2) load_tile(r, pool, rowid, 2 * kMT);
   lds_barrier();
-  for (int t = 0; t <= ntiles; ++t) {
-    if (t + 1 < ntiles) store_tile(r, kv[(t + 1) % 3]);
-    if (t + 2 < ntiles) load_tile(r, pool, rowid, (t + 2) * kMT, nent);
-    const int er = t * kMT + (lane & 31);
-    const int vr = er < nent ? rowid[er] : -1;
+  if (ntiles > 0) logits_phase(kv[0], ka, qf, &spart[0][0][0][0]);
+  lds_barrier();
+  for (int t = 0; t < ntiles; ++t) {
+    const int vr = rowid[t * kMT + (lane & 31)];
     const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // entry r valid -> bit r
-    if (t >= 1) pv_phase(kv[(t - 1) % 3], vlo, vhi, &pmat[0][0], s_alpha, s_grow, o);
-    if (t < ntiles) logits_phase(kv[t % 3], ka, qf, &spart[0][0][0]);
+    // The logits of tile t+1 run unconditionally (one straight-line block); on the last
+    // step they read a slot nobody needs and write partials nobody reads.
+    softmax_with_logits(&spart[t & 1][0][0][0], &spart[(t + 1) & 1][0][0][0], kv[(t + 1) % 3], ka,
+                        qf, &pmat[0][0], s_alpha, s_grow, vmask, scale_log2, m_run, l_run);
     lds_barrier();
-    if (t < ntiles)
-      softmax_phase(&spart[0][0][0], &pmat[0][0], s_alpha, s_grow, vmask, scale_log2, m_run, l_run);
+    pv_phase(kv[t % 3], vlo, vhi, &pmat[0][0], s_alpha, s_grow, o);
+    if (t + 2 < ntiles) store_tile(r, kv[(t + 2) % 3]);
+    if (t + 3 < ntiles) load_tile(r, pool, rowid, (t + 3) * kMT);
     lds_barrier();
   }
 
