@@ -9,11 +9,11 @@
 // the per-head logits never leave registers.
 //   decode  : HBM-bound streaming of the key cache, read exactly once.  Each workgroup is a
 //             single wave that owns a range of one request's keys and streams it in 32-key
-//             slices (8 KB) through a 3-slot LDS ring filled by global_load_lds_dwordx4
-//             (no staging registers; two slices in flight while the third is consumed).
+//             slices (8 KB, 1 KB per load, non-temporal so the stream does not displace
+//             cached data) through registers two slices ahead and a 2-slot LDS ring.
 //             Rows land XOR-swizzled (16-byte chunk c of row r at chunk c ^ (r % 16)) so
-//             the MFMA operand reads are bank-conflict-free; scores collect in LDS and
-//             leave in one coalesced burst.
+//             the MFMA operand reads are bank-conflict-free; the head weights stay in
+//             scalar registers; scores collect in LDS and leave in one burst.
 //   prefill : 8 query tokens per workgroup (one per wave of 8) share a double-buffered
 //             128-key LDS tile -> each key tile is fetched from L2/MALL once per 8 tokens
 //             (MFMA-bound).
@@ -199,7 +199,14 @@ constexpr int kSlice = 32;                       // keys per slice
 constexpr int kSliceBytes = kSlice * kRowBytes;  // 8 KB
 constexpr int kMaxRange = 1024;
 
-__device__ __forceinline__ float score32_swz(const QFrag& f, const uint8_t* slice) {
+// Q fragments of one token for the decode kernel (the head weights are uniform and are
+// read where they are applied, so they stay in scalar registers).
+struct DecodeQ { bf16x8 a[2][8]; };
+
+// Scores of one swizzled 32-key slice; valid in lanes 0..31 (lane = key).  C slot j of the
+// 32-head block i holds head 32i + 8(j/4) + 4(lane/32) + j%4: each lane half sums its own
+// heads with their weights, and the two halves are added.
+__device__ __forceinline__ float score32_swz(const DecodeQ& f, const float* w_tok, const uint8_t* slice) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, h = lane >> 5;
   const uint8_t* row = slice + n * kRowBytes;
@@ -211,12 +218,17 @@ __device__ __forceinline__ float score32_swz(const QFrag& f, const uint8_t* slic
     c0 = mfma32(f.a[0][s], b, c0);
     c1 = mfma32(f.a[1][s], b, c1);
   }
-  float p = 0.f;
+  float p0 = 0.f, p1 = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    p = fmaf(f.w[0][j], fmaxf(c0[j], 0.f), p);
-    p = fmaf(f.w[1][j], fmaxf(c1[j], 0.f), p);
+    const int r = 8 * (j >> 2) + (j & 3);
+    const float x0 = fmaxf(c0[j], 0.f), x1 = fmaxf(c1[j], 0.f);
+    p0 = fmaf(w_tok[r], x0, p0);
+    p0 = fmaf(w_tok[32 + r], x1, p0);
+    p1 = fmaf(w_tok[4 + r], x0, p1);
+    p1 = fmaf(w_tok[36 + r], x1, p1);
   }
+  float p = h ? p1 : p0;
   p += __shfl_xor(p, 32, kWave);
   return p + 0.0f;   // canonical +0.0
 }
@@ -233,6 +245,15 @@ __device__ __forceinline__ void load_slice(SliceRegs& r, const uint8_t* rows) {
   for (int i = 0; i < 8; ++i) r.v[i] = *reinterpret_cast<const u32x4*>(rows + 1024 * i + 16 * lane);
 }
 
+// The same for the key cache, with non-temporal loads: the keys are read once per step, so
+// they should not displace what the caches hold (the freshly written scores above all).
+__device__ __forceinline__ void stream_slice(SliceRegs& r, const uint8_t* rows) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows + 1024 * i + 16 * lane));
+}
+
 // Into an LDS slot with the XOR swizzle score32_swz reads: chunk c of row r at c ^ (r % 16).
 __device__ __forceinline__ void store_slice(const SliceRegs& r, uint8_t* dst) {
   const int lane = threadIdx.x & 63;
@@ -240,6 +261,22 @@ __device__ __forceinline__ void store_slice(const SliceRegs& r, uint8_t* dst) {
   for (int i = 0; i < 8; ++i) {
     const int row = 4 * i + (lane >> 4);
     *reinterpret_cast<u32x4*>(dst + row * kRowBytes + 16 * ((lane & 15) ^ (row & 15))) = r.v[i];
+  }
+}
+
+// Q of one token (64 rows of 256 B = 16 KB) reaches the A-operand layout of score32_swz
+// through LDS: coalesced 1 KB loads (as two slices), rows stored with the slice swizzle,
+// then each lane reads its row's 16-byte chunks (conflict-free).  Fetching the A layout
+// straight from global memory would touch 64 cache lines per load.
+__device__ __forceinline__ void read_decode_q(DecodeQ& f, const uint8_t* stage) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint8_t* row = stage + (32 * i + n) * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      f.a[i][s] = as_bf8(*reinterpret_cast<const uint4*>(row + 16 * ((8 * h + s) ^ (n & 15))));
   }
 }
 
@@ -268,8 +305,8 @@ __global__ __launch_bounds__(64) void indexer_decode_kernel(
   if (lane < nbk) my_phys = block_table[(int64_t)b * max_blocks + blk0 + lane];
   const bool my_ok = my_phys >= 0 && my_phys < num_blocks;
 
-  QFrag f;
-  load_qfrag(f, q_idx + (int64_t)t * kHi * kRowBytes, w + (int64_t)t * kHi);
+  DecodeQ f;
+  const float* w_tok = w + (int64_t)t * kHi;
 
   // rows of slice sl (an unusable page reads block 0 -- always valid memory -- and its
   // scores are zeroed)
@@ -280,46 +317,63 @@ __global__ __launch_bounds__(64) void indexer_decode_kernel(
     return pool + ((int64_t)(ok ? phys : 0) * kBlock + (key0 + sl * kSlice) % kBlock) * kRowBytes;
   };
   auto score_slice = [&](int sl) {
-    float p = score32_swz(f, ring[sl & 1]);
+    float p = score32_swz(f, w_tok, ring[sl & 1]);
     const int page = (sl * kSlice) / kBlock;
     if (__shfl((int)my_ok, page, kWave) == 0) p = 0.f;   // empty row: score 0
     if (lane < kSlice) sc[sl * kSlice + lane] = p;
   };
-  // Q and the page lookups are in registers from here on
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) settle(f.a[h][i]);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) settle(f.w[h][j]);
-  }
-  settle(my_phys);
   // Slices stream through registers two ahead and a 2-slot LDS ring: at step sl the
   // registers of slice sl+1 go to slot (sl+1)&1 (which held slice sl-1) and are reloaded
   // with slice sl+3, then slice sl is scored from slot sl&1.  The second slice of a
   // one-slice range lies in the same 64-key page, so it reads valid memory.
-  SliceRegs ra, rb;
-  load_slice(ra, slice_rows(0));
-  load_slice(rb, slice_rows(1));
+  // Q (two coalesced slices' worth) and the first two slices are loaded together; Q
+  // passes through the ring before the slices use it, and is in registers from then on
+  // (left to the compiler, its loads would sink into the loop and be counted against the
+  // slice loads in flight)
+  SliceRegs qa, qb, ra, rb;
+  load_slice(qa, q_idx + (int64_t)t * kHi * kRowBytes);
+  load_slice(qb, q_idx + (int64_t)t * kHi * kRowBytes + kSliceBytes);
+  stream_slice(ra, slice_rows(0));
+  stream_slice(rb, slice_rows(1));
+  store_slice(qa, ring[0]);
+  store_slice(qb, ring[1]);
+  read_decode_q(f, &ring[0][0]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) settle(f.a[h][i]);
   store_slice(ra, ring[0]);
-  if (ns > 2) load_slice(ra, slice_rows(2));
+  if (ns > 2) stream_slice(ra, slice_rows(2));
   for (int sl = 0; sl < ns; sl += 2) {
     if (sl + 1 < ns) {
       store_slice(rb, ring[1]);
-      if (sl + 3 < ns) load_slice(rb, slice_rows(sl + 3));
+      if (sl + 3 < ns) stream_slice(rb, slice_rows(sl + 3));
     }
     score_slice(sl);
     if (sl + 1 < ns) {
       if (sl + 2 < ns) {
         store_slice(ra, ring[0]);
-        if (sl + 4 < ns) load_slice(ra, slice_rows(sl + 4));
+        if (sl + 4 < ns) stream_slice(ra, slice_rows(sl + 4));
       }
       score_slice(sl + 1);
     }
   }
+  // the range's scores leave in one burst of non-temporal stores (16 bytes per lane when
+  // the row is 16-byte aligned)
   __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
   float* dst = scores + (int64_t)t * ld + key0;
-  for (int i = lane; i < key_end - key0; i += kWave) dst[i] = sc[i];
+  const int cnt = key_end - key0;
+  if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+    for (int i = 4 * lane; i < cnt; i += 4 * kWave) {
+      if (i + 4 <= cnt) {
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sc[i]), reinterpret_cast<f32x4*>(&dst[i]));
+      } else {
+        for (int j = i; j < cnt; ++j) __builtin_nontemporal_store(sc[j], &dst[j]);
+      }
+    }
+  } else {
+    for (int i = lane; i < cnt; i += kWave) __builtin_nontemporal_store(sc[i], &dst[i]);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
