@@ -9,20 +9,22 @@
 // Affects DRAM Memory TAM", §Sparse MLA: DSA uses MLA's MQA mode; §MLA changes: d = 512,
 // r = 64, the roofline algebra of that mode).
 //
-// bf16 instance (64 heads, 512 + 64): a workgroup of 8 waves handles one (token, split)
-// pair and walks its slice of the selected list in tiles of 32 rows:
-//   gather   : page-translate each position once into an LDS row-id list; each tile's
-//              1152-byte rows are fetched with coalesced 16-byte register loads three
-//              tiles ahead of their P.V and written into a 3-slot LDS ring (rows padded to 73 chunks and
-//              placed so that both operand reads below are free of bank conflicts), so
-//              every row is read from HBM exactly once
+// bf16 instance (64 heads, 512 + 64): a workgroup of 4 waves (one per SIMD) handles one
+// (token, split) pair and walks its slice of the selected list in tiles of 32 rows:
+//   gather   : page-translate each position once into an LDS row-id list; each wave loads
+//              its quarter of a tile's 1152-byte rows straight into the registers that feed
+//              the logits MFMAs, one tile ahead, so every row is read from HBM exactly once
+//              and the K operand never passes through LDS
 //   logits   : S^T[key][head] = K[key][:] . Q^T on 16x16x32 MFMA, Q held in registers;
-//              the 8 waves split heads, dims and keys and exchange partials through LDS
+//              the waves split dims and keys and add their partials through LDS
 //   softmax  : online (running max / sum per head, exp2 with log2(e) folded into the
-//              scale, rescale of O only when the max grows by more than 2^8); P to LDS
-//   P.V      : O[head][dim] += P[head][key] . V[key][dim], each wave 64 output dims of all
-//              heads; the V operand comes from the same LDS tile through the transposing
-//              ds_read_b64_tr_b16
+//              scale); the max is set by a head's first valid entries and only moves when
+//              a logit exceeds it by more than 32 (log2 units), so O is never rescaled
+//              inside the loop (a split where it does move runs again from the final max);
+//              P to LDS
+//   P.V      : O[head][dim] += P[head][key] . V[key][dim], each wave 128 output dims of all
+//              heads; V is the latent part of the same registers, stored once to LDS and
+//              read with the transposing ds_read_b64_tr_b16
 // The softmax of tile t shares a phase with the logits MFMAs of tile t+1, so its VALU
 // work issues while the matrix cores run.
 // When there are few tokens, splits of the selected list run in parallel workgroups and a
@@ -43,14 +45,16 @@ constexpr int kMT = 32;                         // rows per tile
 constexpr int kRowSlots = kChunks + 1;          // LDS row stride: 73 chunks (odd)
 constexpr int kTileSlots = kMT * kRowSlots;     // 2336
 constexpr int kTileBytes = kTileSlots * 16;     // 37376
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTileChunks = kMT * kChunks;      // 2304 16-byte chunks per tile
-constexpr int kLoads = (kTileChunks + kThreads - 1) / kThreads;   // 5 per thread (the last partial)
 constexpr int kMaxList = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.f;            // log2 units a running max may lag behind
+// The running max of a head only moves when a logit exceeds it by more than this (log2
+// units), so P = exp2(x - m) <= 2^32 in bf16 and fp32 and O never needs rescaling inside
+// the tile loop; a split whose max does move after O has started to accumulate is run a
+// second time with the final max fixed from the start (a rare, slow path).
+constexpr float kMaxSlack = 32.f;
 
 // LDS placement of 16-byte chunk `ch` of tile row `row`: rows 73 chunks apart, so the 16
 // rows of one MFMA operand fetch fall on 16 different 16-byte bank groups (9r mod 16).
@@ -99,183 +103,165 @@ __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const in
 // banks apart).
 __device__ __forceinline__ int lds_row(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
-// Register-staged gather of one tile (list entries e0 .. e0+31): thread t fetches chunks
-// q = t + 512 m (entry q / 72, chunk q % 72), so each wave reads one or two whole rows
-// per load -- contiguous 1152-byte runs.  Entries without a valid position read row 0 of
-// the pool (always valid memory, finite data); their logits are masked.
-struct TileRegs {
-  u32x4 v[kLoads];
-};
-
-// Straight-line: the row-id reads go out first, then the five loads (the fifth chunk
-// exists for waves 0-3 only: 2304 = 4.5 x 512 chunks -- a wave-uniform, scalar test).
-__device__ __forceinline__ void load_tile(TileRegs& r, const uint8_t* pool, const int* rowid, int e0) {
-  const int tid = threadIdx.x;
-  const bool fifth = __builtin_amdgcn_readfirstlane(tid >> 6) < (kTileChunks - 4 * kThreads) / 64;
-  int rid[kLoads];
-#pragma unroll
-  for (int m = 0; m < kLoads; ++m) {
-    const int q = min(tid + kThreads * m, kTileChunks - 1);
-    rid[m] = rowid[e0 + q / kChunks];
-  }
-#pragma unroll
-  for (int m = 0; m < kLoads; ++m) {
-    const int q = min(tid + kThreads * m, kTileChunks - 1);
-    const int ch = q - (q / kChunks) * kChunks;
-    if (m < kLoads - 1 || fifth)
-      r.v[m] = *reinterpret_cast<const u32x4*>(pool + (int64_t)max(rid[m], 0) * kRowBytes + 16 * ch);
-  }
-}
-
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint8_t* dst) {
-  const int tid = threadIdx.x;
-  const bool fifth = __builtin_amdgcn_readfirstlane(tid >> 6) < (kTileChunks - 4 * kThreads) / 64;
-#pragma unroll
-  for (int m = 0; m < kLoads; ++m) {
-    const int q = min(tid + kThreads * m, kTileChunks - 1);
-    const int key = q / kChunks, ch = q - key * kChunks;
-    if (m < kLoads - 1 || fifth)
-      *reinterpret_cast<u32x4*>(dst + 16 * tile_slot(lds_row(key), ch)) = r.v[m];
-  }
-}
-
-// Per 32-row tile, 8 waves split the work three ways so that every tile byte is read from
-// LDS as few times as the register budget allows (2 waves per SIMD):
-//   logits  : wave w = (hg = w & 1: heads 32hg..32hg+31, dh = (w >> 1) & 1: dims
-//             288dh..288dh+287, kh = w >> 2: keys 16kh..16kh+15) computes partial
-//             S^T[key][head]; each K fragment read from LDS feeds two MFMAs (two head
-//             tiles).  Partials go to LDS.
-//   softmax : wave w owns heads 8w..8w+7 over all 32 keys: sums the two partials, applies
-//             the online-softmax update, writes P (bf16) and the per-head O rescale.
-//   P.V     : wave w owns output dims 64w..64w+63 of all 64 heads; each V fragment (read
-//             once from LDS with the transposing ds_read_b64_tr_b16) feeds four MFMAs.
-constexpr int kSRow = 36;          // partial-logit row stride (floats): conflict-free 16-byte writes
-constexpr int kPRow = 40;          // P row stride (bf16): 80 bytes, conflict-free operand reads
+// Per 32-entry tile, the 4 waves (one per SIMD) split the work so that the K operand of the
+// logits never passes through LDS:
+//   gather  : wave w = (dh = w & 1: dims 288dh..288dh+287, kt = w >> 1: entries
+//             16kt..16kt+15) loads its share of the tile's rows straight into the
+//             A-operand layout of the logits MFMA (lane: entry 16kt + c16, 16 bytes at dim
+//             288dh + 32st + 8g, st = 0..8): each row byte is fetched exactly once, two
+//             tiles ahead of use.  The latent part (dims < 512) of those registers is also
+//             written to an LDS V slot for P.V.
+//   logits  : partial S^T[entry][head] over the wave's dim half for all 64 heads (4 head
+//             tiles x 9 k-steps); the two halves meet in LDS.
+//   softmax : wave w owns heads 16w..16w+15 over all 32 entries (lane: head 16w + c16,
+//             entries 8g..8g+7): sums the two partials, applies the online-softmax update,
+//             writes P (bf16) and the per-head O rescale.
+//   P.V     : wave w owns output dims 128w..128w+127 of all 64 heads; each V fragment (read
+//             with the transposing ds_read_b64_tr_b16) feeds four MFMAs.
+constexpr int kSRow = 36;          // partial-logit row stride (floats): conflict-free 16-byte access
+constexpr int kPRow = 40;          // P row stride (bf16): 80 bytes, conflict-free operand access
 constexpr int kSteps = kRow / 64;  // 9 k-steps of 32 dims per dim half
 
-// Partial logits of one tile (slot `kb`) into spart[dh][head][key].
-__device__ __forceinline__ void logits_phase(const uint8_t* kb, int ka, const bf16x8 (&qf)[2][kSteps],
-                                             float* spart) {
+// K fragments of one tile held by one wave: k.v[st] = 16 bytes of entry 16kt + c16 at dim
+// 288dh + 32st + 8g.  Entries without a valid position read row 0 of the pool (always valid
+// memory, finite data); their logits are masked.
+struct KRegs {
+  bf16x8 v[kSteps];
+};
+
+// Source of the wave's fragments of the tile at list entry e0.
+__device__ __forceinline__ const uint8_t* k_src(const uint8_t* pool, const int* rowid, int e0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hg = wave & 1, dh = (wave >> 1) & 1, kh = wave >> 2;
-  const int g = lane >> 4, c16 = lane & 15;
-  f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int st = 0; st < kSteps; ++st) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + ka + 64 * st);
-    sacc[0] = mfma16(a, qf[0][st], sacc[0]);
-    sacc[1] = mfma16(a, qf[1][st], sacc[1]);
-  }
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-    *reinterpret_cast<f32x4*>(&spart[(dh * kH + 32 * hg + 16 * ht + c16) * kSRow + 16 * kh + 4 * g]) =
-        sacc[ht];
+  const int dh = wave & 1, kt = wave >> 1, g = lane >> 4, c16 = lane & 15;
+  const int rid = rowid[e0 + 16 * kt + c16];
+  return pool + (int64_t)max(rid, 0) * kRowBytes + 576 * dh + 16 * g;
 }
 
-// Online-softmax update of the owned head over one tile's 32 keys (8 lanes x 4 keys, from
-// the partials in sp_in): P (bf16) to pmat, the O rescale factor to s_alpha, and whether
-// any head of this wave rescales to s_grow.  Interleaved with it, the logits MFMAs of the
-// next tile (slot kb, partials to sp_out): each logits k-step issues two MFMAs, and one slice of
-// the softmax chain follows it, so the VALU work issues while the MFMAs execute.  The
-// sched_barrier fences keep the compiler from regrouping the two streams.
-__device__ __forceinline__ void softmax_with_logits(const float* sp_in, float* sp_out, const uint8_t* kb,
-                                                    int ka, const bf16x8 (&qf)[2][kSteps],
-                                                    uint16_t* pmat, float* s_alpha, int* s_grow,
-                                                    uint32_t vmask, float scale_log2, float& m_run,
-                                                    float& l_run) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hg = wave & 1, dh = (wave >> 1) & 1, kh = wave >> 2;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int sm_head = 8 * wave + (lane >> 3);
-  const int sm_key = 4 * (lane & 7);
-  f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + ka);
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sp_in[sm_head * kSRow + sm_key]);
-  const f32x4 a1 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + sm_head) * kSRow + sm_key]);
-  // one logits k-step: MFMAs on the fragment in hand, fetch the next one
-#define DSA_KSTEP(st)                                                        \
-  {                                                                          \
-    const bf16x8 cur = a;                                                    \
-    if ((st) + 1 < kSteps) a = *reinterpret_cast<const bf16x8*>(kb + ka + 64 * ((st) + 1)); \
-    sacc[0] = mfma16(cur, qf[0][st], sacc[0]);                               \
-    sacc[1] = mfma16(cur, qf[1][st], sacc[1]);                               \
-  }                                                                          \
-  __builtin_amdgcn_sched_barrier(0);
-  DSA_KSTEP(0)
-  float x[4];
+__device__ __forceinline__ void load_k(KRegs& r, const uint8_t* src) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    x[j] = (vmask >> (sm_key + j)) & 1u ? (a0[j] + a1[j]) * scale_log2 : -INFINITY;
+  for (int st = 0; st < kSteps; ++st) r.v[st] = *reinterpret_cast<const bf16x8*>(src + 64 * st);
+}
+
+// Byte offset in a V slot of the wave's fragment chunk 36dh + g of entry 16kt + c16 (the
+// latent dims of the K fragments are stored there for P.V; the 16 entries of one store
+// land on 16 different bank groups).
+__device__ __forceinline__ int v_offset() {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int dh = wave & 1, kt = wave >> 1, g = lane >> 4, c16 = lane & 15;
+  return 16 * tile_slot(lds_row(16 * kt + c16), 36 * dh + g);
+}
+
+// Partial logits of the tile in `k` into sp[dh][head][entry] (lane: head 16ht + c16,
+// entries 16kt + 4g .. +3).
+__device__ __forceinline__ void store_partials(const f32x4 (&sacc)[4], float* sp) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int dh = wave & 1, kt = wave >> 1, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+    *reinterpret_cast<f32x4*>(&sp[(dh * kH + 16 * ht + c16) * kSRow + 16 * kt + 4 * g]) = sacc[ht];
+}
+
+// Logits k-step st of a tile: its four MFMAs, the store of its fragment to the V slot (the
+// rope dims of the upper half land in the row padding, which nothing reads) and, with
+// kPrefetch, the same fragment of the tile after next loaded into the freed registers.
+template <bool kPrefetch>
+__device__ __forceinline__ void logits_kstep(int st, KRegs& k, const bf16x8 (&qf)[4][kSteps],
+                                             f32x4 (&sacc)[4], uint8_t* vdst, const uint8_t* knext) {
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) sacc[ht] = mfma16(k.v[st], qf[ht][st], sacc[ht]);
+  *reinterpret_cast<bf16x8*>(vdst + 64 * st) = k.v[st];
+  if (kPrefetch) k.v[st] = *reinterpret_cast<const bf16x8*>(knext + 64 * st);
+}
+
+// Online-softmax update of the wave's 16 heads over one tile (partials in sp_in): P (bf16)
+// to pmat; ovf records a running max that moved after the head's first valid entries (O
+// would need rescaling: the split is re-run).  With kLogits, the logits MFMAs of the next tile (fragments in k, partials to
+// sp_out), the V store of that tile (to vnext) and, with kPrefetch, the loads of the tile
+// after next (from knext, into k) are interleaved with it, so that the
+// softmax VALU work issues while the matrix cores run; the sched_barrier fences keep the
+// compiler from regrouping the streams.
+template <bool kLogits, bool kPrefetch>
+__device__ __forceinline__ void softmax_step(const float* sp_in, float* sp_out, KRegs& k,
+                                             uint8_t* vnext, const uint8_t* knext,
+                                             const bf16x8 (&qf)[4][kSteps], uint16_t* pmat,
+                                             uint32_t vmask, float scale_log2, float& m_run,
+                                             float& l_run, bool& ovf) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int head = 16 * wave + c16;
+  f32x4 sacc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  uint8_t* vdst = kLogits ? vnext + v_offset() : nullptr;
+#define DSA_KSTEP(st)                                                              \
+  if (kLogits) logits_kstep<kPrefetch>(st, k, qf, sacc, vdst, knext);              \
+  __builtin_amdgcn_sched_barrier(0);
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sp_in[head * kSRow + 8 * g]);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(&sp_in[head * kSRow + 8 * g + 4]);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + head) * kSRow + 8 * g]);
+  const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + head) * kSRow + 8 * g + 4]);
+  DSA_KSTEP(0)
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = (vmask >> (8 * g + j)) & 1u ? (a0[j] + b0[j]) * scale_log2 : -INFINITY;
+    x[4 + j] = (vmask >> (8 * g + 4 + j)) & 1u ? (a1[j] + b1[j]) * scale_log2 : -INFINITY;
+  }
+  float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
   __builtin_amdgcn_sched_barrier(0);
   DSA_KSTEP(1)
-  const float tmax = group8_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
   __builtin_amdgcn_sched_barrier(0);
   DSA_KSTEP(2)
-  // the running max only moves when a logit exceeds it by more than the slack, so
-  // exp2(x - m) stays <= 2^8 and the O rescale is rare
-  const bool grow = tmax > m_run + kRescaleSlack;
+  // the running max is set by the head's first valid entries and only moves again when a
+  // logit exceeds it by more than the slack -- which sets ovf (O was accumulated against
+  // the old max); l stays consistent either way
+  const bool grow = tmax > m_run + kMaxSlack;
   const float m_new = grow ? tmax : m_run;
   const bool none = (m_new == -INFINITY);
   const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-  __builtin_amdgcn_sched_barrier(0);
-  DSA_KSTEP(3)
-  float p[4], psum = 0.f;
+  ovf |= alpha != 1.f;
+  float p[8], psum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 8; ++j) {
     p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
     psum += p[j];
   }
+  psum += shfl_xor_f(psum, 16);
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_KSTEP(3)
+  psum += shfl_xor_f(psum, 32);
   __builtin_amdgcn_sched_barrier(0);
   DSA_KSTEP(4)
-  psum = group8_sum(psum);
   l_run = l_run * alpha + psum;
   m_run = m_new;
+  uint32_t pk[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    pk[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j + 1]) << 16);
+  *reinterpret_cast<u32x4*>(&pmat[head * kPRow + 8 * g]) = u32x4{pk[0], pk[1], pk[2], pk[3]};
   __builtin_amdgcn_sched_barrier(0);
   DSA_KSTEP(5)
-  const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
-  const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
-  *reinterpret_cast<uint2*>(&pmat[sm_head * kPRow + sm_key]) = make_uint2(lo, hi);
-  // branch-free: the 8 lanes of a head store the same alpha, all lanes the same flag
-  s_alpha[sm_head] = alpha;
-  s_grow[wave] = __ballot(alpha != 1.f) != 0;
-  __builtin_amdgcn_sched_barrier(0);
   DSA_KSTEP(6)
   DSA_KSTEP(7)
   DSA_KSTEP(8)
 #undef DSA_KSTEP
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-    *reinterpret_cast<f32x4*>(&sp_out[(dh * kH + 32 * hg + 16 * ht + c16) * kSRow + 16 * kh + 4 * g]) =
-        sacc[ht];
+  if (kLogits) store_partials(sacc, sp_out);
 }
 
-// O[64 heads][dims 64w + 16dt + c16] = alpha * O + P . V for one tile (slot `kb`).
-__device__ __forceinline__ void pv_phase(const uint8_t* kb, int vlo, int vhi, const uint16_t* pmat,
-                                         const float* s_alpha, const int* s_grow, f32x4 (&o)[4][4]) {
+// O[64 heads][dims 128w + 16dt + c16] += P . V for one tile (V slot `vs`).
+__device__ __forceinline__ void pv_step(const uint8_t* vs, int vlo, int vhi, const uint16_t* pmat,
+                                        f32x4 (&o)[4][8]) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const int4 gr0 = *reinterpret_cast<const int4*>(&s_grow[0]);
-  const int4 gr1 = *reinterpret_cast<const int4*>(&s_grow[4]);
-  if (gr0.x | gr0.y | gr0.z | gr0.w | gr1.x | gr1.y | gr1.z | gr1.w) {
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const f32x4 al = *reinterpret_cast<const f32x4*>(&s_alpha[16 * ht + 4 * g]);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[ht][dt][j] *= al[j];
-    }
-  }
   bf16x8 pa[4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
     pa[ht] = *reinterpret_cast<const bf16x8*>(&pmat[(16 * ht + c16) * kPRow + 8 * g]);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const s16x4 lo = lds_read_tr16(kb + vlo + 32 * dt);
-    const s16x4 hi = lds_read_tr16(kb + vhi + 32 * dt);
+  for (int dt = 0; dt < 8; ++dt) {
+    const s16x4 lo = lds_read_tr16(vs + vlo + 32 * dt);
+    const s16x4 hi = lds_read_tr16(vs + vhi + 32 * dt);
     const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
                                                            hi[0], hi[1], hi[2], hi[3]};
     const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
@@ -284,102 +270,128 @@ __device__ __forceinline__ void pv_phase(const uint8_t* kb, int vlo, int vhi, co
   }
 }
 
+// grid (splits, T), 256 threads.  splits == 1: normalized bf16 output (+ lse); else the
+// split's unnormalized fp32 partial O and (max, sum) in log2 units go to the workspace.
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
     const int* __restrict__ block_table, const int* __restrict__ seq_len, int max_blocks, int batch,
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
     int64_t ld_idx, int k, float scale_log2, int splits, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv[3][kTileBytes];
+  // V slots (two tiles); before the loop the same bytes stage Q (64 rows of 73 chunks)
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][kTileBytes];
   __shared__ int rowid[kMaxList];
-  __shared__ __attribute__((aligned(16))) float spart[2][2][kH][kSRow];   // [buf][dh][head][key]
-  __shared__ __attribute__((aligned(16))) uint16_t pmat[kH][kPRow];    // P[head][key] bf16
-  __shared__ __attribute__((aligned(16))) float s_alpha[kH];
+  __shared__ __attribute__((aligned(16))) float spart[2][2][kH][kSRow];   // [buf][dh][head][entry]
+  __shared__ __attribute__((aligned(16))) uint16_t pmat[kH][kPRow];    // P[head][entry] bf16
   __shared__ float s_ml[kH][2];
-  __shared__ __attribute__((aligned(16))) int s_grow[kWaves];   // owner wave rescales a head
+  __shared__ int s_ovf[kWaves];
+  static_assert(2 * kTileBytes >= kH * kRowSlots * 16, "Q staging fits in the V slots");
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hg = wave & 1, dh = (wave >> 1) & 1, kh = wave >> 2;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int dh = wave & 1, g = lane >> 4, c16 = lane & 15;
   const int t = blockIdx.y, sp = blockIdx.x;
 
-  // Q^T fragments (B operand) of head tiles ht = 0, 1: head 32hg + 16ht + c16,
-  // dims 288dh + 32st + 8g .. +8; issued first so their latency overlaps the lookups
-  bf16x8 qf[2][kSteps];
+  // Q: coalesced 16-byte loads (thread tid takes chunks tid + 256i of the 64 x 72), issued
+  // first so that their latency overlaps the list lookups
+  constexpr int kQLoads = kH * kChunks / kThreads;   // 18
+  static_assert(kQLoads * kThreads == kH * kChunks, "Q chunks divide evenly");
+  u32x4 qs[kQLoads];
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const uint4* src = reinterpret_cast<const uint4*>(
-        q + ((int64_t)t * kH + 32 * hg + 16 * ht + c16) * kRowBytes + 576 * dh + 16 * g);
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) qf[ht][st] = as_bf8(src[4 * st]);
-  }
+  for (int i = 0; i < kQLoads; ++i)
+    qs[i] = *reinterpret_cast<const u32x4*>(q + (int64_t)t * kH * kRowBytes + 16 * (tid + kThreads * i));
   int nent;
   resolve_rows(t, sp, splits, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos,
                idx, ld_idx, k, rowid, nent);
   __syncthreads();
-
-  // softmax state of the owned head (lanes 8i..8i+7 hold head 8w + i)
-  const int sm_head = 8 * wave + (lane >> 3);
-  const int sm_key = 4 * (lane & 7);
-  float m_run = -INFINITY, l_run = 0.f;
-
-  f32x4 o[4][4];                              // [head tile][dim tile]
+  const int ntiles = (nent + kMT - 1) / kMT;
+  // the first tile's fragments go out before Q is unpacked
+  KRegs kr;
+  if (ntiles > 0) load_k(kr, k_src(pool, rowid, 0));
+  uint8_t* qst = &vbuf[0][0];
+#pragma unroll
+  for (int i = 0; i < kQLoads; ++i) {
+    const int c = tid + kThreads * i, row = c / kChunks, ch = c - row * kChunks;
+    *reinterpret_cast<u32x4*>(qst + 16 * (row * kRowSlots + ch)) = qs[i];
+  }
+  __syncthreads();
+  // Q^T fragments (B operand) of head tiles ht = 0..3: head 16ht + c16, dims 288dh + 32st +
+  // 8g .. +8; in registers from here on (left to the compiler, their reads would sink into
+  // the loop)
+  bf16x8 qf[4][kSteps];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < kSteps; ++st)
+      qf[ht][st] = *reinterpret_cast<const bf16x8*>(qst + 16 * ((16 * ht + c16) * kRowSlots + 36 * dh + 4 * st + g));
+  __syncthreads();   // the staging bytes become V slots
 
-  // operand addresses: K of entry 16kh + c16 at chunk 36dh + g (+ 4 per k-step); V of
-  // entries 8g + c16/4 (lo) and 8g + 4 + c16/4 (hi), bytes 8 (c16 % 4) of dims 64w..
-  const int ka = 16 * tile_slot(lds_row(16 * kh + c16), 36 * dh + g);            // + 64 st
-  const int vlo = 16 * tile_slot(lds_row(8 * g + (c16 >> 2)), 0) + 8 * (c16 & 3) + 128 * wave;
-  const int vhi = 16 * tile_slot(lds_row(8 * g + 4 + (c16 >> 2)), 0) + 8 * (c16 & 3) + 128 * wave;
-  const int ntiles = (nent + kMT - 1) / kMT;
-  // Tiles stream through a 3-slot LDS ring from registers, and each step overlaps the
-  // softmax of tile t with the logits MFMAs of tile t+1 (partial logits double-buffered):
-  //   phase 1: logits(t+1) -> spart[(t+1)&1] and softmax(t) from spart[t&1] -> P, alpha,
-  //            interleaved so that about four softmax VALU instructions issue under
-  //            each MFMA
-  //   phase 2: P.V(t); tile t+2 (loaded into registers during step t-1) into the slot
-  //            tile t-1 held; load tile t+3 into the registers
-  // with a barrier after each phase.
-  // Q is in registers from here on (its loads complete here, not inside the loop, where
-  // the compiler would count them against the tile loads in flight)
+  float m_run = -INFINITY, l_run = 0.f;   // of head 16w + c16 (same in the 4 lane groups)
+  f32x4 o[4][8];                          // [head tile][dim tile]
+  // V operand addresses: entries 8g + c16/4 (lo) and 8g + 4 + c16/4 (hi), bytes 8 (c16 % 4)
+  // of dims 128w..
+  const int vlo = 16 * tile_slot(lds_row(8 * g + (c16 >> 2)), 0) + 8 * (c16 & 3) + 256 * wave;
+  const int vhi = 16 * tile_slot(lds_row(8 * g + 4 + (c16 >> 2)), 0) + 8 * (c16 & 3) + 256 * wave;
+
+  // One register set holds the fragments of the next tile: each logits k-step reloads its
+  // registers with the tile after next.  Tile t's V and partial logits use slot t % 2.
+  // Step t:
+  //   phase A: softmax(t) from spart[t&1], interleaved with the logits of tile t+1 (to
+  //            spart[(t+1)&1]), its V store (to slot (t+1)&1) and the loads of tile t+2
+  //   phase B: P.V(t)
+  // with a barrier after each phase.  Before the loop: logits and V of tile 0.  A second
+  // pass (rare) starts from the first pass's final max with O and l cleared.
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
+    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) settle(qf[ht][st]);
-  TileRegs r;
-  if (ntiles > 0) {
-    load_tile(r, pool, rowid, 0);
-    store_tile(r, kv[0]);
-  }
-  if (ntiles > 1) {
-    load_tile(r, pool, rowid, kMT);
-    store_tile(r, kv[1]);
-  }
-  if (ntiles > 2) load_tile(r, pool, rowid, 2 * kMT);
-  lds_barrier();
-  if (ntiles > 0) logits_phase(kv[0], ka, qf, &spart[0][0][0][0]);
-  lds_barrier();
-  for (int t = 0; t < ntiles; ++t) {
-    const int vr = rowid[t * kMT + (lane & 31)];
-    const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // entry r valid -> bit r
-    // The logits of tile t+1 run unconditionally (one straight-line block); on the last
-    // step they read a slot nobody needs and write partials nobody reads.
-    softmax_with_logits(&spart[t & 1][0][0][0], &spart[(t + 1) & 1][0][0][0], kv[(t + 1) % 3], ka,
-                        qf, &pmat[0][0], s_alpha, s_grow, vmask, scale_log2, m_run, l_run);
+      for (int dt = 0; dt < 8; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    bool ovf = false;
+    if (ntiles > 0) {
+      f32x4 sacc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      uint8_t* vdst = vbuf[0] + v_offset();
+      if (ntiles > 1) {
+        const uint8_t* nx = k_src(pool, rowid, kMT);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) logits_kstep<true>(st, kr, qf, sacc, vdst, nx);
+      } else {
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) logits_kstep<false>(st, kr, qf, sacc, vdst, nullptr);
+      }
+      store_partials(sacc, &spart[0][0][0][0]);
+    }
     lds_barrier();
-    pv_phase(kv[t % 3], vlo, vhi, &pmat[0][0], s_alpha, s_grow, o);
-    if (t + 2 < ntiles) store_tile(r, kv[(t + 2) % 3]);
-    if (t + 3 < ntiles) load_tile(r, pool, rowid, (t + 3) * kMT);
-    lds_barrier();
+    for (int tt = 0; tt < ntiles; ++tt) {
+      const int vr = rowid[tt * kMT + (lane & 31)];
+      const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // entry r valid -> bit r
+      float* sp_in = &spart[tt & 1][0][0][0];
+      float* sp_out = &spart[(tt + 1) & 1][0][0][0];
+      if (tt + 2 < ntiles)
+        softmax_step<true, true>(sp_in, sp_out, kr, vbuf[(tt + 1) & 1], k_src(pool, rowid, (tt + 2) * kMT),
+                                 qf, &pmat[0][0], vmask, scale_log2, m_run, l_run, ovf);
+      else if (tt + 1 < ntiles)
+        softmax_step<true, false>(sp_in, sp_out, kr, vbuf[(tt + 1) & 1], nullptr, qf, &pmat[0][0],
+                                  vmask, scale_log2, m_run, l_run, ovf);
+      else
+        softmax_step<false, false>(sp_in, nullptr, kr, nullptr, nullptr, qf, &pmat[0][0], vmask,
+                                   scale_log2, m_run, l_run, ovf);
+      lds_barrier();
+      pv_step(vbuf[tt & 1], vlo, vhi, &pmat[0][0], o);
+      lds_barrier();
+    }
+    const bool wave_ovf = __ballot(ovf) != 0;   // all lanes take part in the vote
+    if (lane == 0) s_ovf[wave] = wave_ovf;
+    __syncthreads();
+    const int any = s_ovf[0] | s_ovf[1] | s_ovf[2] | s_ovf[3];
+    __syncthreads();   // s_ovf is rewritten by a second pass
+    if (!any) break;
+    if (ntiles > 0) load_k(kr, k_src(pool, rowid, 0));
   }
 
   // ---- epilogue: per-head (m, l) from the softmax owners
-  if ((lane & 7) == 0) {
-    s_ml[sm_head][0] = m_run;
-    s_ml[sm_head][1] = l_run;
+  if (g == 0) {
+    s_ml[16 * wave + c16][0] = m_run;
+    s_ml[16 * wave + c16][1] = l_run;
   }
   __syncthreads();
   if (splits == 1) {
@@ -390,9 +402,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
         const int head = 16 * ht + 4 * g + j;
         const float l = s_ml[head][1];
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* dst = out + ((int64_t)t * kH + head) * kDl + 64 * wave + c16;
+        uint16_t* dst = out + ((int64_t)t * kH + head) * kDl + 128 * wave + c16;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dst[16 * dt] = f2bf_bits(o[ht][dt][j] * inv);
+        for (int dt = 0; dt < 8; ++dt) dst[16 * dt] = f2bf_bits(o[ht][dt][j] * inv);
       }
     if (lse && tid < kH) {
       const float m = s_ml[tid][0], l = s_ml[tid][1];
@@ -404,9 +416,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float* dst = ws_o + (base + 16 * ht + 4 * g + j) * kDl + 64 * wave + c16;
+        float* dst = ws_o + (base + 16 * ht + 4 * g + j) * kDl + 128 * wave + c16;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dst[16 * dt] = o[ht][dt][j];
+        for (int dt = 0; dt < 8; ++dt) dst[16 * dt] = o[ht][dt][j];
       }
     if (tid < kH) {
       ws_ml[(base + tid) * 2 + 0] = s_ml[tid][0];

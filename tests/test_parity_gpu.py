@@ -156,6 +156,26 @@ def test_mla_alternative_scale():
         check_token(inp, buf, t)
 
 
+def test_mla_running_max_moves_late():
+    # rows in the second half of every context are scaled up, so the logits of a split that
+    # spans the boundary rise by far more than 32 (log2 units) after its first tiles: the
+    # running max moves after O has started to accumulate and the split runs a second pass
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=4, ctx_range=(3000, 9000))
+    inp = I.make_inputs(cfg, DEV)
+    lens = inp["seq_len"].tolist()
+    bt = inp["block_table"].cpu()
+    phys = sorted({int(bt[b, j]) for b, n in enumerate(lens) for j in range((n // 2) // 64 + 1, (n + 63) // 64)})
+    sel = torch.tensor(phys, dtype=torch.long, device=DEV)
+    for pool in inp["kv_pools"]:
+        pool[sel] = (pool[sel].float() * 8).to(pool.dtype)
+    inp["q"] = [(q.float() * 4).to(q.dtype) for q in inp["q"]]
+    log(f"[gpu] late-max lens {lens}, {len(phys)} scaled pages")
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in range(len(lens)):
+        check_token(inp, buf, t)
+
+
 # ------------------------------------------------------------------ top-k in isolation
 
 def _topk_case(scores: np.ndarray, n_valid, k):
