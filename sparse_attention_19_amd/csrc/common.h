@@ -93,23 +93,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Reductions over each group of 8 consecutive lanes, result in all 8: quad_perm swaps
-// (xor 1, xor 2) combine each quad, row_half_mirror (lane i <-> 7 - i within 8) the two
-// quads of the group.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
-                                                               0xf, 0xf, true));
+// Reductions over the four 16-lane rows of a wave, per column (lanes c, c+16, c+32, c+48),
+// with gfx950's row-swap instructions: permlane16_swap pairs rows (0,1) and (2,3),
+// permlane32_swap pairs the two halves; every lane ends with the column's result, and the
+// lanes of one column add in the same order.
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float group8_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));       // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));       // quad_perm [2,3,0,1]
-  return fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-}
-__device__ __forceinline__ float group8_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  return v + dpp_f<0x141>(v);
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Minimum over the wave, in every lane (min a = ~max ~a keeps 0 the identity).

@@ -110,17 +110,28 @@ __device__ __forceinline__ int lds_row(int k) { return (k & ~7) | ((k & 3) << 1)
 //             A-operand layout of the logits MFMA (lane: entry 16kt + c16, 16 bytes at dim
 //             288dh + 32st + 8g, st = 0..8): each row byte is fetched exactly once, two
 //             tiles ahead of use.  The latent part (dims < 512) of those registers is also
-//             written to an LDS V slot for P.V.
+//             written to an LDS V tile for P.V.
 //   logits  : partial S^T[entry][head] over the wave's dim half for all 64 heads (4 head
 //             tiles x 9 k-steps); the two halves meet in LDS.
 //   softmax : wave w owns heads 16w..16w+15 over all 32 entries (lane: head 16w + c16,
 //             entries 8g..8g+7): sums the two partials, applies the online-softmax update,
-//             writes P (bf16) and the per-head O rescale.
+//             writes P (bf16).
 //   P.V     : wave w owns output dims 128w..128w+127 of all 64 heads; each V fragment (read
 //             with the transposing ds_read_b64_tr_b16) feeds four MFMAs.
+// One phase per tile: step t runs the logits of tile t+1, the softmax of tile t and P.V of
+// tile t-1, interleaved (they only meet through LDS buffers written one step earlier), with
+// one barrier at its end.
 constexpr int kSRow = 36;          // partial-logit row stride (floats): conflict-free 16-byte access
 constexpr int kPRow = 40;          // P row stride (bf16): 80 bytes, conflict-free operand access
 constexpr int kSteps = kRow / 64;  // 9 k-steps of 32 dims per dim half
+constexpr int kVSteps1 = 7;        // k-steps of the upper dim half that are latent (V) dims
+constexpr int kVRowBytes = kDl * 2;            // V tile row: 512 dims, 1024 bytes
+constexpr int kVTileBytes = kMT * kVRowBytes;  // 32 KB
+
+// V tile layout: row r (entry r of the tile) holds 64 16-byte chunks, chunk c at position
+// c ^ vswz(r).  The 16 entries of one fragment store (rows 16kt..16kt+15, same chunk) and
+// the 4 rows x 2 chunks of one transposing read fall on distinct 16-byte bank groups.
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
 
 // K fragments of one tile held by one wave: k.v[st] = 16 bytes of entry 16kt + c16 at dim
 // 288dh + 32st + 8g.  Entries without a valid position read row 0 of the pool (always valid
@@ -142,17 +153,48 @@ __device__ __forceinline__ void load_k(KRegs& r, const uint8_t* src) {
   for (int st = 0; st < kSteps; ++st) r.v[st] = *reinterpret_cast<const bf16x8*>(src + 64 * st);
 }
 
-// Byte offset in a V slot of the wave's fragment chunk 36dh + g of entry 16kt + c16 (the
-// latent dims of the K fragments are stored there for P.V; the 16 entries of one store
-// land on 16 different bank groups).
-__device__ __forceinline__ int v_offset() {
+// Per-lane LDS addressing of the V tiles.
+struct VAddr {
+  int st_row, st_sw, st_c0;   // fragment store: row byte offset, swizzle, chunk of k-step 0
+  int tr_lo, tr_hi;           // transposing reads: row bytes + 256w + 8 (c16 & 1)
+  int z_lo, z_hi;             // chunk xor (within the wave's 16-chunk block)
+};
+
+__device__ __forceinline__ VAddr v_addr() {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int dh = wave & 1, kt = wave >> 1, g = lane >> 4, c16 = lane & 15;
-  return 16 * tile_slot(lds_row(16 * kt + c16), 36 * dh + g);
+  VAddr a;
+  const int r = 16 * kt + c16;
+  a.st_row = r * kVRowBytes;
+  a.st_sw = vswz(r);
+  a.st_c0 = 36 * dh + g;
+  // lane m = c16 of row group g reads entry 8g (+4) + m/4, dims 128w + 16dt + 4(m%4)..+3:
+  // chunk 16w + 2dt + (m%4)/2, byte 8 (m%2) of it
+  const int rlo = 8 * g + (c16 >> 2), rhi = rlo + 4, h = (c16 >> 1) & 1;
+  a.tr_lo = rlo * kVRowBytes + 256 * wave + 8 * (c16 & 1);
+  a.tr_hi = rhi * kVRowBytes + 256 * wave + 8 * (c16 & 1);
+  a.z_lo = h ^ vswz(rlo);
+  a.z_hi = h ^ vswz(rhi);
+  return a;
 }
 
-// Partial logits of the tile in `k` into sp[dh][head][entry] (lane: head 16ht + c16,
-// entries 16kt + 4g .. +3).
+// Logits k-step st of a tile: its four MFMAs, the store of its fragment's latent dims to the
+// V tile and, with kPrefetch, the same fragment of the tile two ahead loaded into the freed
+// registers.
+template <bool kPrefetch>
+__device__ __forceinline__ void logits_kstep(int st, KRegs& k, const bf16x8 (&qf)[4][kSteps],
+                                             f32x4 (&sacc)[4], uint8_t* vt, const VAddr& va,
+                                             const uint8_t* knext) {
+  const int dh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1;   // wave-uniform
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) sacc[ht] = mfma16(k.v[st], qf[ht][st], sacc[ht]);
+  if (dh == 0 || st < kVSteps1)
+    *reinterpret_cast<bf16x8*>(vt + va.st_row + 16 * ((va.st_c0 + 4 * st) ^ va.st_sw)) = k.v[st];
+  if (kPrefetch) k.v[st] = *reinterpret_cast<const bf16x8*>(knext + 64 * st);
+}
+
+// Partial logits of a tile into sp[dh][head][entry] (lane: head 16ht + c16, entries
+// 16kt + 4g .. +3).
 __device__ __forceinline__ void store_partials(const f32x4 (&sacc)[4], float* sp) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int dh = wave & 1, kt = wave >> 1, g = lane >> 4, c16 = lane & 15;
@@ -161,113 +203,109 @@ __device__ __forceinline__ void store_partials(const f32x4 (&sacc)[4], float* sp
     *reinterpret_cast<f32x4*>(&sp[(dh * kH + 16 * ht + c16) * kSRow + 16 * kt + 4 * g]) = sacc[ht];
 }
 
-// Logits k-step st of a tile: its four MFMAs, the store of its fragment to the V slot (the
-// rope dims of the upper half land in the row padding, which nothing reads) and, with
-// kPrefetch, the same fragment of the tile after next loaded into the freed registers.
-template <bool kPrefetch>
-__device__ __forceinline__ void logits_kstep(int st, KRegs& k, const bf16x8 (&qf)[4][kSteps],
-                                             f32x4 (&sacc)[4], uint8_t* vdst, const uint8_t* knext) {
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) sacc[ht] = mfma16(k.v[st], qf[ht][st], sacc[ht]);
-  *reinterpret_cast<bf16x8*>(vdst + 64 * st) = k.v[st];
-  if (kPrefetch) k.v[st] = *reinterpret_cast<const bf16x8*>(knext + 64 * st);
+__device__ __forceinline__ bf16x8 v_frag(const uint8_t* vt, const VAddr& va, int dt) {
+  const s16x4 lo = lds_read_tr16(vt + va.tr_lo + 16 * ((2 * dt) ^ va.z_lo));
+  const s16x4 hi = lds_read_tr16(vt + va.tr_hi + 16 * ((2 * dt) ^ va.z_hi));
+  const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
+                                                         hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v8);
 }
 
-// Online-softmax update of the wave's 16 heads over one tile (partials in sp_in): P (bf16)
-// to pmat; ovf records a running max that moved after the head's first valid entries (O
-// would need rescaling: the split is re-run).  With kLogits, the logits MFMAs of the next tile (fragments in k, partials to
-// sp_out), the V store of that tile (to vnext) and, with kPrefetch, the loads of the tile
-// after next (from knext, into k) are interleaved with it, so that the
-// softmax VALU work issues while the matrix cores run; the sched_barrier fences keep the
-// compiler from regrouping the streams.
-template <bool kLogits, bool kPrefetch>
-__device__ __forceinline__ void softmax_step(const float* sp_in, float* sp_out, KRegs& k,
-                                             uint8_t* vnext, const uint8_t* knext,
-                                             const bf16x8 (&qf)[4][kSteps], uint16_t* pmat,
-                                             uint32_t vmask, float scale_log2, float& m_run,
-                                             float& l_run, bool& ovf) {
+// One pipeline step (see above).  kSoft: softmax of the tile whose partials are in sp_in
+// (P to pm_out); kLogits: logits of the next tile (fragments in k, partials to sp_out, V to
+// vt_out); kPrefetch: reload k from knext; kPV: P.V of the previous tile (P in pm_in, V in
+// vt_in).  sched_barrier fences keep the three streams interleaved as written, so the
+// softmax chain's VALU work issues while the matrix cores run.
+template <bool kSoft, bool kLogits, bool kPrefetch, bool kPV>
+__device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint16_t* pm_out,
+                                         const uint16_t* pm_in, uint8_t* vt_out,
+                                         const uint8_t* vt_in, KRegs& k, const uint8_t* knext,
+                                         const bf16x8 (&qf)[4][kSteps], f32x4 (&o)[4][8],
+                                         const VAddr& va, uint32_t vmask, float scale_log2,
+                                         float& m_run, float& l_run, bool& ovf) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int head = 16 * wave + c16;
   f32x4 sacc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  uint8_t* vdst = kLogits ? vnext + v_offset() : nullptr;
-#define DSA_KSTEP(st)                                                              \
-  if (kLogits) logits_kstep<kPrefetch>(st, k, qf, sacc, vdst, knext);              \
-  __builtin_amdgcn_sched_barrier(0);
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sp_in[head * kSRow + 8 * g]);
-  const f32x4 a1 = *reinterpret_cast<const f32x4*>(&sp_in[head * kSRow + 8 * g + 4]);
-  const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + head) * kSRow + 8 * g]);
-  const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + head) * kSRow + 8 * g + 4]);
-  DSA_KSTEP(0)
-  float x[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    x[j] = (vmask >> (8 * g + j)) & 1u ? (a0[j] + b0[j]) * scale_log2 : -INFINITY;
-    x[4 + j] = (vmask >> (8 * g + 4 + j)) & 1u ? (a1[j] + b1[j]) * scale_log2 : -INFINITY;
+  // LDS reads first: partials of the softmax tile, P and the first V fragments
+  f32x4 a0, a1, b0, b1;
+  if (kSoft) {
+    a0 = *reinterpret_cast<const f32x4*>(&sp_in[head * kSRow + 8 * g]);
+    a1 = *reinterpret_cast<const f32x4*>(&sp_in[head * kSRow + 8 * g + 4]);
+    b0 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + head) * kSRow + 8 * g]);
+    b1 = *reinterpret_cast<const f32x4*>(&sp_in[(kH + head) * kSRow + 8 * g + 4]);
   }
-  float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-  __builtin_amdgcn_sched_barrier(0);
-  DSA_KSTEP(1)
-  tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-  __builtin_amdgcn_sched_barrier(0);
-  DSA_KSTEP(2)
-  // the running max is set by the head's first valid entries and only moves again when a
-  // logit exceeds it by more than the slack -- which sets ovf (O was accumulated against
-  // the old max); l stays consistent either way
-  const bool grow = tmax > m_run + kMaxSlack;
-  const float m_new = grow ? tmax : m_run;
-  const bool none = (m_new == -INFINITY);
-  const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-  ovf |= alpha != 1.f;
-  float p[8], psum = 0.f;
+  bf16x8 pa[4], vf0, vf1;
+  if (kPV) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
-    psum += p[j];
+    for (int ht = 0; ht < 4; ++ht)
+      pa[ht] = *reinterpret_cast<const bf16x8*>(&pm_in[(16 * ht + c16) * kPRow + 8 * g]);
+    vf0 = v_frag(vt_in, va, 0);
+    vf1 = v_frag(vt_in, va, 1);
   }
-  psum += shfl_xor_f(psum, 16);
   __builtin_amdgcn_sched_barrier(0);
-  DSA_KSTEP(3)
-  psum += shfl_xor_f(psum, 32);
-  __builtin_amdgcn_sched_barrier(0);
-  DSA_KSTEP(4)
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  uint32_t pk[4];
+  // slot s: logits k-step s, P.V dims tile s (fetching tile s + 2), one softmax slice
+#define DSA_SLOT(s)                                                                        \
+  if (kLogits) logits_kstep<kPrefetch>(s, k, qf, sacc, vt_out, va, knext);                 \
+  if (kPV && (s) < 8) {                                                                    \
+    const bf16x8 vcur = ((s) & 1) ? vf1 : vf0;                                             \
+    if ((s) + 2 < 8) {                                                                     \
+      if ((s) & 1) vf1 = v_frag(vt_in, va, (s) + 2); else vf0 = v_frag(vt_in, va, (s) + 2);\
+    }                                                                                      \
+    _Pragma("unroll") for (int ht = 0; ht < 4; ++ht) o[ht][(s) & 7] = mfma16(pa[ht], vcur, o[ht][(s) & 7]); \
+  }
+  float x[8], p[8];
+  float m_new = m_run, psum = 0.f;
+  DSA_SLOT(0)
+  if (kSoft) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    pk[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j]) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j + 1]) << 16);
-  *reinterpret_cast<u32x4*>(&pmat[head * kPRow + 8 * g]) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    for (int j = 0; j < 4; ++j) {
+      x[j] = (vmask >> (8 * g + j)) & 1u ? (a0[j] + b0[j]) * scale_log2 : -INFINITY;
+      x[4 + j] = (vmask >> (8 * g + 4 + j)) & 1u ? (a1[j] + b1[j]) * scale_log2 : -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    tmax = rows4_max(tmax);
+    const bool grow = tmax > m_run + kMaxSlack;
+    m_new = grow ? tmax : m_run;
+    ovf |= grow && m_run != -INFINITY;
+  }
   __builtin_amdgcn_sched_barrier(0);
-  DSA_KSTEP(5)
-  DSA_KSTEP(6)
-  DSA_KSTEP(7)
-  DSA_KSTEP(8)
-#undef DSA_KSTEP
+  DSA_SLOT(1)
+  if (kSoft) {
+    const bool none = (m_new == -INFINITY);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = none ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
+      psum += p[j];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_SLOT(2)
+  if (kSoft) {
+    // l restarts from the new max when it moves (the split then runs again anyway)
+    l_run = (m_new == m_run ? l_run : 0.f) + rows4_sum(psum);
+    m_run = m_new;
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pk[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j + 1]) << 16);
+    *reinterpret_cast<u32x4*>(&pm_out[head * kPRow + 8 * g]) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_SLOT(3)
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_SLOT(4)
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_SLOT(5)
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_SLOT(6)
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_SLOT(7)
+  __builtin_amdgcn_sched_barrier(0);
+  DSA_SLOT(8)
+#undef DSA_SLOT
   if (kLogits) store_partials(sacc, sp_out);
-}
-
-// O[64 heads][dims 128w + 16dt + c16] += P . V for one tile (V slot `vs`).
-__device__ __forceinline__ void pv_step(const uint8_t* vs, int vlo, int vhi, const uint16_t* pmat,
-                                        f32x4 (&o)[4][8]) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  bf16x8 pa[4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht)
-    pa[ht] = *reinterpret_cast<const bf16x8*>(&pmat[(16 * ht + c16) * kPRow + 8 * g]);
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const s16x4 lo = lds_read_tr16(vs + vlo + 32 * dt);
-    const s16x4 hi = lds_read_tr16(vs + vhi + 32 * dt);
-    const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
-                                                           hi[0], hi[1], hi[2], hi[3]};
-    const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) o[ht][dt] = mfma16(pa[ht], vf, o[ht][dt]);
-  }
 }
 
 // grid (splits, T), 256 threads.  splits == 1: normalized bf16 output (+ lse); else the
@@ -278,14 +316,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
     int64_t ld_idx, int k, float scale_log2, int splits, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  // V slots (two tiles); before the loop the same bytes stage Q (64 rows of 73 chunks)
-  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][kTileBytes];
+  // three V tiles; before the loop the same bytes stage Q (64 rows of 73 chunks)
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[3][kVTileBytes];
   __shared__ int rowid[kMaxList];
   __shared__ __attribute__((aligned(16))) float spart[2][2][kH][kSRow];   // [buf][dh][head][entry]
-  __shared__ __attribute__((aligned(16))) uint16_t pmat[kH][kPRow];    // P[head][entry] bf16
+  __shared__ __attribute__((aligned(16))) uint16_t pmat[2][kH][kPRow];  // [buf] P[head][entry]
   __shared__ float s_ml[kH][2];
   __shared__ int s_ovf[kWaves];
-  static_assert(2 * kTileBytes >= kH * kRowSlots * 16, "Q staging fits in the V slots");
+  static_assert(3 * kVTileBytes >= kH * kRowSlots * 16, "Q staging fits in the V tiles");
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int dh = wave & 1, g = lane >> 4, c16 = lane & 15;
@@ -315,71 +353,77 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   }
   __syncthreads();
   // Q^T fragments (B operand) of head tiles ht = 0..3: head 16ht + c16, dims 288dh + 32st +
-  // 8g .. +8; in registers from here on (left to the compiler, their reads would sink into
-  // the loop)
+  // 8g .. +8 (the staging rows are 73 chunks apart: conflict-free)
   bf16x8 qf[4][kSteps];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
     for (int st = 0; st < kSteps; ++st)
       qf[ht][st] = *reinterpret_cast<const bf16x8*>(qst + 16 * ((16 * ht + c16) * kRowSlots + 36 * dh + 4 * st + g));
-  __syncthreads();   // the staging bytes become V slots
+  __syncthreads();   // the staging bytes become V tiles
 
+  const VAddr va = v_addr();
   float m_run = -INFINITY, l_run = 0.f;   // of head 16w + c16 (same in the 4 lane groups)
   f32x4 o[4][8];                          // [head tile][dim tile]
-  // V operand addresses: entries 8g + c16/4 (lo) and 8g + 4 + c16/4 (hi), bytes 8 (c16 % 4)
-  // of dims 128w..
-  const int vlo = 16 * tile_slot(lds_row(8 * g + (c16 >> 2)), 0) + 8 * (c16 & 3) + 256 * wave;
-  const int vhi = 16 * tile_slot(lds_row(8 * g + 4 + (c16 >> 2)), 0) + 8 * (c16 & 3) + 256 * wave;
-
-  // One register set holds the fragments of the next tile: each logits k-step reloads its
-  // registers with the tile after next.  Tile t's V and partial logits use slot t % 2.
-  // Step t:
-  //   phase A: softmax(t) from spart[t&1], interleaved with the logits of tile t+1 (to
-  //            spart[(t+1)&1]), its V store (to slot (t+1)&1) and the loads of tile t+2
-  //   phase B: P.V(t)
-  // with a barrier after each phase.  Before the loop: logits and V of tile 0.  A second
-  // pass (rare) starts from the first pass's final max with O and l cleared.
+  // One register set holds the fragments of the next tile (each logits k-step reloads its
+  // registers with the tile after).  Tile t: partials in spart[t % 2], P in pmat[t % 2],
+  // V in vbuf[t % 3].  Step t (t = 0..ntiles) = logits(t+1) + softmax(t) + P.V(t-1);
+  // before the first step, the logits of tile 0.  A second pass (rare) starts from the first
+  // pass's final max with O and l cleared.
+  bool ovf_step = false;   // this lane's head moved its max after O started (this pass)
+  // step tt with the given stages (kSoft = tt < ntiles, kLogits = tt + 1 < ntiles,
+  // kPrefetch = tt + 2 < ntiles, kPV = tt >= 1)
+#define DSA_STEP(kSoft, kLogits, kPrefetch, kPV, tt)                                             \
+  {                                                                                            \
+    const int e_ = min((tt), ntiles - 1) * kMT + (lane & 31);                                  \
+    const uint32_t vmask_ = (uint32_t)__ballot(lane < 32 && rowid[e_] >= 0);                   \
+    mla_step<kSoft, kLogits, kPrefetch, kPV>(                                                   \
+        &spart[(tt) & 1][0][0][0], &spart[((tt) + 1) & 1][0][0][0], &pmat[(tt) & 1][0][0],     \
+        &pmat[((tt) + 1) & 1][0][0], vbuf[((tt) + 1) % 3], vbuf[((tt) + 2) % 3], kr,             \
+        kPrefetch ? k_src(pool, rowid, ((tt) + 2) * kMT) : nullptr, qf, o, va, vmask_,          \
+        scale_log2, m_run, l_run, ovf_step);                                                   \
+    lds_barrier();                                                                             \
+  }
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
-    bool ovf = false;
-    if (ntiles > 0) {
+    ovf_step = false;
+    if (ntiles > 0) {   // logits and V of tile 0; the set is reloaded with tile 1
       f32x4 sacc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      uint8_t* vdst = vbuf[0] + v_offset();
       if (ntiles > 1) {
         const uint8_t* nx = k_src(pool, rowid, kMT);
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) logits_kstep<true>(st, kr, qf, sacc, vdst, nx);
+        for (int st = 0; st < kSteps; ++st) logits_kstep<true>(st, kr, qf, sacc, vbuf[0], va, nx);
       } else {
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) logits_kstep<false>(st, kr, qf, sacc, vdst, nullptr);
+        for (int st = 0; st < kSteps; ++st) logits_kstep<false>(st, kr, qf, sacc, vbuf[0], va, nullptr);
       }
       store_partials(sacc, &spart[0][0][0][0]);
     }
     lds_barrier();
-    for (int tt = 0; tt < ntiles; ++tt) {
-      const int vr = rowid[tt * kMT + (lane & 31)];
-      const uint32_t vmask = (uint32_t)__ballot(lane < 32 && vr >= 0);   // entry r valid -> bit r
-      float* sp_in = &spart[tt & 1][0][0][0];
-      float* sp_out = &spart[(tt + 1) & 1][0][0][0];
-      if (tt + 2 < ntiles)
-        softmax_step<true, true>(sp_in, sp_out, kr, vbuf[(tt + 1) & 1], k_src(pool, rowid, (tt + 2) * kMT),
-                                 qf, &pmat[0][0], vmask, scale_log2, m_run, l_run, ovf);
-      else if (tt + 1 < ntiles)
-        softmax_step<true, false>(sp_in, sp_out, kr, vbuf[(tt + 1) & 1], nullptr, qf, &pmat[0][0],
-                                  vmask, scale_log2, m_run, l_run, ovf);
-      else
-        softmax_step<false, false>(sp_in, nullptr, kr, nullptr, nullptr, qf, &pmat[0][0], vmask,
-                                   scale_log2, m_run, l_run, ovf);
-      lds_barrier();
-      pv_step(vbuf[tt & 1], vlo, vhi, &pmat[0][0], o);
-      lds_barrier();
+    if (ntiles > 0) {
+      // step 0 (no P.V yet)
+      if (ntiles > 2) DSA_STEP(true, true, true, false, 0)
+      else if (ntiles > 1) DSA_STEP(true, true, false, false, 0)
+      else DSA_STEP(true, false, false, false, 0)
+      // steady state: every stage
+      int tt = 1;
+      for (; tt + 2 < ntiles; ++tt) DSA_STEP(true, true, true, true, tt)
+      // the last steps: no more loads, then no more logits, then P.V alone
+      if (tt + 1 < ntiles) {
+        DSA_STEP(true, true, false, true, tt)
+        ++tt;
+      }
+      if (tt < ntiles) {
+        DSA_STEP(true, false, false, true, tt)
+        ++tt;
+      }
+      DSA_STEP(false, false, false, true, tt)
     }
-    const bool wave_ovf = __ballot(ovf) != 0;   // all lanes take part in the vote
+    const bool wave_ovf = __ballot(ovf_step) != 0;   // all lanes take part in the vote
     if (lane == 0) s_ovf[wave] = wave_ovf;
     __syncthreads();
     const int any = s_ovf[0] | s_ovf[1] | s_ovf[2] | s_ovf[3];
