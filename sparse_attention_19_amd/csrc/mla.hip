@@ -129,9 +129,10 @@ constexpr int kVRowBytes = kDl * 2;            // V tile row: 512 dims, 1024 byt
 constexpr int kVTileBytes = kMT * kVRowBytes;  // 32 KB
 
 // V tile layout: row r (entry r of the tile) holds 64 16-byte chunks, chunk c at position
-// c ^ vswz(r).  The 16 entries of one fragment store (rows 16kt..16kt+15, same chunk) and
-// the 4 rows x 2 chunks of one transposing read fall on distinct 16-byte bank groups.
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+// c ^ vswz(r).  LDS serves 128 bytes (8 x 16) per cycle: the 8 consecutive entries of one
+// fragment store (same chunk) land on 8 distinct 16-byte slots, and the 4 rows x 32 bytes of
+// one transposing read on 4 distinct 32-byte slots.
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
 
 // K fragments of one tile held by one wave: k.v[st] = 16 bytes of entry 16kt + c16 at dim
 // 288dh + 32st + 8g.  Entries without a valid position read row 0 of the pool (always valid
