@@ -93,6 +93,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// max(x, 0) for finite x as a single v_med3_f32 (clamp to [0, FLT_MAX]).  fmaxf costs two
+// instructions in IEEE mode: the compiler first quiets a possible signalling NaN.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.4028235e38f); }
+
 // Reductions over the four 16-lane rows of a wave, per column (lanes c, c+16, c+32, c+48),
 // with gfx950's row-swap instructions: permlane16_swap pairs rows (0,1) and (2,3),
 // permlane32_swap pairs the two halves; every lane ends with the column's result, and the

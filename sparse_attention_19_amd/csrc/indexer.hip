@@ -102,8 +102,8 @@ __device__ __forceinline__ float score32(const QFrag& f, const uint8_t* lds, int
   float p = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    p = fmaf(f.w[0][j], fmaxf(c0[j], 0.f), p);
-    p = fmaf(f.w[1][j], fmaxf(c1[j], 0.f), p);
+    p = fmaf(f.w[0][j], relu(c0[j]), p);
+    p = fmaf(f.w[1][j], relu(c1[j]), p);
   }
   p += __shfl_xor(p, 32, kWave);
   return p + 0.0f;   // canonical +0.0
