@@ -43,7 +43,7 @@ METRIC = "DSA decode tokens/s at 32K–128K ctx + achieved HBM GB/s fraction"
 
 # kernel -> source file that defines it (its hash decides whether stored counters still apply)
 KERNEL_SRC = {
-    "indexer_decode_kernel": "indexer.hip", "indexer_bf16_kernel": "indexer.hip",
+    "indexer_decode_kernel": "indexer.hip", "indexer_prefill_kernel": "indexer.hip",
     "indexer_f32_kernel": "indexer.hip", "topk_chunk_kernel": "topk.hip", "topk_merge_kernel": "topk.hip",
     "mla_bf16_kernel": "mla.hip", "mla_combine_kernel": "mla.hip", "mla_f32_kernel": "mla.hip",
 }
@@ -101,7 +101,7 @@ def algorithmic(cfg, kernels_seen=()):
     mla_bound = "mfma" if (prefill and mfma_ok) else "hbm"
     out = {
         "indexer_decode_kernel": (ix_b, ix_f, "hbm"),
-        "indexer_bf16_kernel": (ix_b, ix_f, ix_bound),
+        "indexer_prefill_kernel": (ix_b, ix_f, ix_bound),
         "indexer_f32_kernel": (ix_b, ix_f, "hbm"),
         "topk_chunk_kernel": (tk_in + (0 if merge else tk_out), 0, "hbm"),
         "topk_merge_kernel": (tk_out, 0, "hbm"),

@@ -87,18 +87,17 @@ __device__ __forceinline__ void load_qfrag(QFrag& f, const uint8_t* q_tok, const
   }
 }
 
-// Scores of 32 keys (LDS rows r0..r0+31) for one token; result valid in lanes 0..31
-// (lane = key).
-__device__ __forceinline__ float score32(const QFrag& f, const uint8_t* lds, int r0) {
+// B fragments (32 keys x 128 dims) of LDS rows r0..r0+31: lane l holds row r0 + l%32,
+// bytes 128 (l/32) + 16 s, s = 0..7.
+__device__ __forceinline__ void load_b(bf16x8 (&b)[8], const uint8_t* lds, int r0) {
   const int lane = threadIdx.x & 63;
   const uint8_t* base = lds + (r0 + (lane & 31)) * kLdsRow + (lane >> 5) * 128;
-  f32x16 c0 = {}, c1 = {};
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const bf16x8 b = as_bf8(*reinterpret_cast<const uint4*>(base + 16 * s));
-    c0 = mfma32(f.a[0][s], b, c0);
-    c1 = mfma32(f.a[1][s], b, c1);
-  }
+  for (int s = 0; s < 8; ++s) b[s] = as_bf8(*reinterpret_cast<const uint4*>(base + 16 * s));
+}
+
+// Score of key r0 + lane (valid in lanes 0..31) from the accumulators of 32 keys x 64 heads.
+__device__ __forceinline__ float epilogue32(const QFrag& f, const f32x16& c0, const f32x16& c1) {
   float p = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -109,18 +108,18 @@ __device__ __forceinline__ float score32(const QFrag& f, const uint8_t* lds, int
   return p + 0.0f;   // canonical +0.0
 }
 
-// grid.x: key chunks of `tiles_per_wg` tiles; grid.y: token groups.
-//   decode : 4 waves, 1 token per workgroup, wave w scores keys 32w..32w+31 of each tile
-//   prefill: 8 waves, 8 tokens per workgroup (token t0 + w in wave w), every wave scores
-//            all 128 keys of each tile
-template <bool kDecode>
-__global__ __launch_bounds__(kDecode ? 256 : 512) void indexer_bf16_kernel(
+// Prefill: 8 waves, token t0 + w in wave w (8 tokens per workgroup); grid.x: key chunks of
+// `tiles_per_wg` 128-key tiles, grid.y: token groups.  Each key tile is fetched from
+// L2/MALL once per 8 tokens into a double-buffered LDS tile; every wave scores all 128 keys
+// of the tile in four 32-key parts, reading part p + 1's B fragments while part p's MFMAs
+// drain and its epilogue runs.
+__global__ __launch_bounds__(512) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ pool,
     int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
     int max_blocks, int batch, const int* __restrict__ q_row, const int* __restrict__ q_pos, int T,
     int tiles_per_wg, float* __restrict__ scores, int64_t ld) {
-  constexpr int kThreads = kDecode ? 256 : 512;
-  constexpr int kTPG = kDecode ? 1 : kThreads / kWave;   // tokens per workgroup
+  constexpr int kThreads = 512;
+  constexpr int kTPG = kThreads / kWave;   // tokens per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTileBytes];
   __shared__ int s_req[kTPG];
   __shared__ int s_n[kTPG];
@@ -158,12 +157,12 @@ __global__ __launch_bounds__(kDecode ? 256 : 512) void indexer_bf16_kernel(
     if (key_begin >= key_end) continue;
     const int* bt_row = block_table + (int64_t)b * max_blocks;
 
-    // this wave's token, if it belongs to request b
-    const int slot = kDecode ? 0 : wave;
-    const int tok = (s_req[slot] == b) ? t0 + slot : -1;
-    const int tn = (tok >= 0) ? s_n[slot] : 0;
+    // this wave's token, if it belongs to request b (wave-uniform)
+    const int tok = (s_req[wave] == b) ? t0 + wave : -1;
+    const int tn = (tok >= 0) ? s_n[wave] : 0;
     QFrag f;
     if (tok >= 0) load_qfrag(f, q_idx + (int64_t)tok * kHi * kRowBytes, w + (int64_t)tok * kHi);
+    float* out = scores + (int64_t)max(tok, 0) * ld;
 
     TileRegs<kThreads> regs;
     load_tile<kThreads>(regs, pool, num_blocks, bt_row, key_begin, nmax);
@@ -173,18 +172,21 @@ __global__ __launch_bounds__(kDecode ? 256 : 512) void indexer_bf16_kernel(
       __syncthreads();
       if (key0 + kTileKeys < key_end)
         load_tile<kThreads>(regs, pool, num_blocks, bt_row, key0 + kTileKeys, nmax);
-      if (tok >= 0) {
-        if (kDecode) {
-          const float p = score32(f, lds[buf], wave * 32);
-          const int s = key0 + wave * 32 + lane;
-          if (lane < 32 && s < tn) scores[(int64_t)tok * ld + s] = p;
-        } else {
-          for (int part = 0; part < kTileKeys / 32; ++part) {
-            if (key0 + part * 32 >= tn) break;
-            const float p = score32(f, lds[buf], part * 32);
-            const int s = key0 + part * 32 + lane;
-            if (lane < 32 && s < tn) scores[(int64_t)tok * ld + s] = p;
+      if (tok >= 0 && key0 < tn) {
+        bf16x8 bq[2][8];
+        load_b(bq[0], lds[buf], 0);
+#pragma unroll
+        for (int part = 0; part < kTileKeys / 32; ++part) {
+          f32x16 c0 = {}, c1 = {};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            c0 = mfma32(f.a[0][s], bq[part & 1][s], c0);
+            c1 = mfma32(f.a[1][s], bq[part & 1][s], c1);
           }
+          if (part + 1 < kTileKeys / 32) load_b(bq[(part + 1) & 1], lds[buf], 32 * (part + 1));
+          const float p = epilogue32(f, c0, c1);
+          const int s = key0 + part * 32 + lane;
+          if (lane < 32 && s < tn) out[s] = p;
         }
       }
       buf ^= 1;
@@ -428,8 +430,8 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
       const int per = 64;
       dim3 grid((tiles + per - 1) / per, (a.T + 7) / 8);
       {
-        const KernelEvents ev("indexer_bf16_kernel");
-        hipExtLaunchKernelGGL(indexer_bf16_kernel<false>, grid, dim3(512), 0, stream, ev.start,
+        const KernelEvents ev("indexer_prefill_kernel");
+        hipExtLaunchKernelGGL(indexer_prefill_kernel, grid, dim3(512), 0, stream, ev.start,
                               ev.stop, 0, (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool,
                               a.num_blocks, a.block_table, a.seq_len, a.max_blocks, a.batch,
                               a.q_row, a.q_pos, a.T, per, a.scores, a.ld);
