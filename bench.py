@@ -307,11 +307,16 @@ def _counter_per_dispatch(d, counter, pick):
     return per
 
 
+N_XCC = 8   # MI355X: 8 accelerator complex dies, each with its own GRBM
+
+
 def summarize_counters(args):
     """Per-kernel averages of every counter of a --pmc run (the path's kernels only).
-    SQ counters are summed over their instances, GRBM ones (one per XCD) take the
-    maximum; with both present, MfmaUtil is rocprofv3's own definition:
-    sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMDs) with 1024 SIMDs."""
+    The database stores one value per dispatch and counter, summed over the counter's
+    dimensions; a GRBM counter is kept per XCC, so the per-die value is that sum / N_XCC.
+    MfmaUtil, when collected, is rocprofv3's own derived counter
+    sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMDs); otherwise it is
+    computed the same way from the raw counters (1024 SIMDs)."""
     c = _db(args.summarize_counters)
     per = {}
     for kname, disp, cname, val in c.execute(
@@ -320,18 +325,19 @@ def summarize_counters(args):
         if not k.endswith("_kernel"):
             continue
         d = per.setdefault(k, {}).setdefault(cname, {})
-        d[disp] = max(d.get(disp, 0.0), val) if cname.startswith("GRBM_") else d.get(disp, 0.0) + val
+        d[disp] = d.get(disp, 0.0) + val
     print(f"# rocprofv3 counters: {args.title}")
     print(f"# profiled with : {args.command}")
     print(f"# summarised by : python bench.py --summarize-counters <output dir>")
+    print(f"# values per dispatch, summed over the counter's dimensions (GRBM_*: over {N_XCC} XCCs)")
     for k in sorted(per):
         print(k)
         avg = {cname: sum(d.values()) / len(d) for cname, d in per[k].items()}
         for cname, d in sorted(per[k].items()):
             print(f"   {cname:28s} {avg[cname]:18.1f}  per dispatch ({len(d)} dispatches)")
-        if avg.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
-            util = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] * 1024)
-            print(f"   {'MfmaUtil':28s} {100 * util:18.1f}  % (1024 SIMDs)")
+        if "MfmaUtil" not in avg and avg.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            util = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / N_XCC * 1024)
+            print(f"   {'MfmaUtil (computed)':28s} {100 * util:18.1f}  % (1024 SIMDs)")
 
 
 def summarize_traffic(args):
