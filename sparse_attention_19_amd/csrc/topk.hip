@@ -10,9 +10,10 @@
 // workgroup holds a chunk of up to 32768 keys in registers (32 consecutive keys per
 // thread, staged through a bank-conflict-free padded LDS copy) and selects in three steps:
 //   1. pruning : the key tau of a fixed rank among 1024 evenly spaced samples bounds the
-//                answer from below (one wave selects it on its own, 8-bit radix levels
-//                in a private 256-bin histogram); the keys >= tau (about 2k + 768 of
-//                them) are compacted, in position order, into an LDS candidate list.  If
+//                answer from below (one wave finds it on its own, two 8-bit radix levels
+//                in a private 256-bin histogram, stopping at the lower edge of the bin
+//                that holds it); the keys >= tau (about 2k + 768 of them) are
+//                compacted, in position order, into an LDS candidate list.  If
 //                that list would hold fewer than k or more than 8192 keys, all keys stay
 //                candidates.
 //   2. select  : the exact k-th largest key theta, by radix levels of 12 bits over the
@@ -101,9 +102,13 @@ __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, Smem& sm,
   *mx = b;
 }
 
-// rank-th largest (1-based, rank <= number of nonzero entries) of the 1024 entries of
-// `v` (LDS), zero entries ignored, computed by one wave alone: 8-bit radix levels over
-// [min, max] with a private histogram `hs` (LDS, kSampleBins words, 16-byte aligned).
+// A lower bound of the rank-th largest (1-based, rank <= number of nonzero entries) of the
+// 1024 entries of `v` (LDS), zero entries ignored, computed by one wave alone: 8-bit radix
+// levels over [min, max] with a private histogram `hs` (LDS, kSampleBins words, 16-byte
+// aligned).  After kMaxLevels levels it stops at the lower edge of the bin that holds the
+// rank-th entry (exact when the range is at most 8 * kMaxLevels bits wide): a slightly
+// lower bound only admits a few more candidates.
+template <int kMaxLevels>
 __device__ __forceinline__ uint32_t wave_select_rank(const uint32_t* v, uint32_t rank, uint32_t* hs) {
   const int lane = threadIdx.x & 63;
   uint32_t s[16];
@@ -125,7 +130,7 @@ __device__ __forceinline__ uint32_t wave_select_rank(const uint32_t* v, uint32_t
   const uint32_t hi = wave_max_u32(mx);
   int W = (hi <= L) ? 0 : 32 - __clz(hi - L);
   uint32_t remaining = rank;
-  while (W > 0) {
+  for (int level = 0; W > 0 && level < kMaxLevels; ++level) {
     const int shift = W > 8 ? W - 8 : 0;
     reinterpret_cast<uint4*>(hs)[lane] = make_uint4(0, 0, 0, 0);
     wave_lds_fence();
@@ -299,7 +304,7 @@ __device__ __forceinline__ void topk_of_list(const uint32_t (&key)[R], int count
     const uint32_t rank = (uint32_t)((want * (uint64_t)ns + (uint64_t)count - 1) / (uint64_t)count);
     if (rank >= 1 && rank < (uint32_t)ns) {
       if (tid < kWave) {
-        const uint32_t tau = wave_select_rank(samp, rank, hist_b);
+        const uint32_t tau = wave_select_rank<2>(samp, rank, hist_b);
         if (tid == 0) sm.tau = tau;
       }
       __syncthreads();
