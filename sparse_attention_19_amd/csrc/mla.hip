@@ -42,9 +42,7 @@ constexpr int kH = 64, kDl = 512, kRow = 576;
 constexpr int kRowBytes = kRow * 2;             // 1152
 constexpr int kChunks = kRowBytes / 16;         // 72 x 16 B per row
 constexpr int kMT = 32;                         // rows per tile
-constexpr int kRowSlots = kChunks + 1;          // LDS row stride: 73 chunks (odd)
-constexpr int kTileSlots = kMT * kRowSlots;     // 2336
-constexpr int kTileBytes = kTileSlots * 16;     // 37376
+constexpr int kRowSlots = kChunks + 1;          // Q staging row stride: 73 chunks (odd)
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxList = 2048;
@@ -56,9 +54,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // second time with the final max fixed from the start (a rare, slow path).
 constexpr float kMaxSlack = 32.f;
 
-// LDS placement of 16-byte chunk `ch` of tile row `row`: rows 73 chunks apart, so the 16
-// rows of one MFMA operand fetch fall on 16 different 16-byte bank groups (9r mod 16).
-__device__ __forceinline__ int tile_slot(int row, int ch) { return row * kRowSlots + ch; }
 
 // Resolve the token's (request, n) and this split's slice [i0, i0 + nent) of the
 // selected list; fills rowid[] with global row ids (phys * 64 + slot) or -1, up to the
@@ -96,11 +91,8 @@ __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const in
   for (int e = nent + threadIdx.x; e < padded; e += blockDim.x) rowid[e] = -1;
 }
 
-// LDS row of list entry k of a tile: within each group of 8 the entries go to rows
-// 0,2,4,6,1,3,5,7.  With the 73-chunk row stride this keeps both operand reads free of
-// bank conflicts: the logits read 16 consecutive entries at one chunk (rows 4 banks
-// apart), the transposing V read takes 4 consecutive entries per 16-lane group (now 8
-// banks apart).
+// LDS row of entry k of a tile: within each group of 8 the entries go to rows
+// 0,2,4,6,1,3,5,7 (see the V tile layout below).
 __device__ __forceinline__ int lds_row(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
 // Per 32-entry tile, the 4 waves (one per SIMD) split the work so that the K operand of the
@@ -125,14 +117,14 @@ constexpr int kSRow = 36;          // partial-logit row stride (floats): conflic
 constexpr int kPRow = 40;          // P row stride (bf16): 80 bytes, conflict-free operand access
 constexpr int kSteps = kRow / 64;  // 9 k-steps of 32 dims per dim half
 constexpr int kVSteps1 = 7;        // k-steps of the upper dim half that are latent (V) dims
-constexpr int kVRowBytes = kDl * 2;            // V tile row: 512 dims, 1024 bytes
-constexpr int kVTileBytes = kMT * kVRowBytes;  // 32 KB
-
-// V tile layout: row r (entry r of the tile) holds 64 16-byte chunks, chunk c at position
-// c ^ vswz(r).  LDS serves 128 bytes (8 x 16) per cycle: the 8 consecutive entries of one
-// fragment store (same chunk) land on 8 distinct 16-byte slots, and the 4 rows x 32 bytes of
-// one transposing read on 4 distinct 32-byte slots.
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// V tile layout: entry k of the tile sits in row lds_row(k), rows 1040 bytes (65 16-byte
+// chunks) apart, dims 8c..8c+7 in chunk c.  LDS serves 128 bytes (8 x 16) per cycle and the
+// row stride moves each row by one 16-byte slot: the 8 consecutive entries of one fragment
+// store (same chunk) land on 8 distinct slots, and the 4 rows x 32 bytes of one
+// transposing read (entries 4j..4j+3 -> rows 2 apart) on 8 distinct slots.  Every address
+// is a per-lane base plus a constant offset per k-step or dims tile.
+constexpr int kVRowBytes = 65 * 16;             // 1040
+constexpr int kVTileBytes = kMT * kVRowBytes;   // 33280
 
 // K fragments of one tile held by one wave: k.v[st] = 16 bytes of entry 16kt + c16 at dim
 // 288dh + 32st + 8g.  Entries without a valid position read row 0 of the pool (always valid
@@ -156,26 +148,21 @@ __device__ __forceinline__ void load_k(KRegs& r, const uint8_t* src) {
 
 // Per-lane LDS addressing of the V tiles.
 struct VAddr {
-  int st_row, st_sw, st_c0;   // fragment store: row byte offset, swizzle, chunk of k-step 0
-  int tr_lo, tr_hi;           // transposing reads: row bytes + 256w + 8 (c16 & 1)
-  int z_lo, z_hi;             // chunk xor (within the wave's 16-chunk block)
+  int st;       // fragment store of k-step 0 (k-step st at + 64 st)
+  int tr_lo;    // transposing read, entries 8g + c16/4, dims tile 0 (tile dt at + 32 dt)
+  int tr_hi;    // the same for entries 8g + 4 + c16/4
 };
 
 __device__ __forceinline__ VAddr v_addr() {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int dh = wave & 1, kt = wave >> 1, g = lane >> 4, c16 = lane & 15;
   VAddr a;
-  const int r = 16 * kt + c16;
-  a.st_row = r * kVRowBytes;
-  a.st_sw = vswz(r);
-  a.st_c0 = 36 * dh + g;
+  a.st = lds_row(16 * kt + c16) * kVRowBytes + 16 * (36 * dh + g);
   // lane m = c16 of row group g reads entry 8g (+4) + m/4, dims 128w + 16dt + 4(m%4)..+3:
-  // chunk 16w + 2dt + (m%4)/2, byte 8 (m%2) of it
-  const int rlo = 8 * g + (c16 >> 2), rhi = rlo + 4, h = (c16 >> 1) & 1;
-  a.tr_lo = rlo * kVRowBytes + 256 * wave + 8 * (c16 & 1);
-  a.tr_hi = rhi * kVRowBytes + 256 * wave + 8 * (c16 & 1);
-  a.z_lo = h ^ vswz(rlo);
-  a.z_hi = h ^ vswz(rhi);
+  // bytes 256w + 32dt + 8(m%4) of its row
+  const int off = 256 * wave + 8 * (c16 & 3);
+  a.tr_lo = lds_row(8 * g + (c16 >> 2)) * kVRowBytes + off;
+  a.tr_hi = lds_row(8 * g + 4 + (c16 >> 2)) * kVRowBytes + off;
   return a;
 }
 
@@ -184,13 +171,13 @@ __device__ __forceinline__ VAddr v_addr() {
 // registers.
 template <bool kPrefetch>
 __device__ __forceinline__ void logits_kstep(int st, KRegs& k, const bf16x8 (&qf)[4][kSteps],
-                                             f32x4 (&sacc)[4], uint8_t* vt, const VAddr& va,
+                                             f32x4 (&sacc)[4], uint8_t* vbase, int vst,
                                              const uint8_t* knext) {
   const int dh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1;   // wave-uniform
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) sacc[ht] = mfma16(k.v[st], qf[ht][st], sacc[ht]);
   if (dh == 0 || st < kVSteps1)
-    *reinterpret_cast<bf16x8*>(vt + va.st_row + 16 * ((va.st_c0 + 4 * st) ^ va.st_sw)) = k.v[st];
+    *reinterpret_cast<bf16x8*>(vbase + vst + 64 * st) = k.v[st];
   if (kPrefetch) k.v[st] = *reinterpret_cast<const bf16x8*>(knext + 64 * st);
 }
 
@@ -204,9 +191,9 @@ __device__ __forceinline__ void store_partials(const f32x4 (&sacc)[4], float* sp
     *reinterpret_cast<f32x4*>(&sp[(dh * kH + 16 * ht + c16) * kSRow + 16 * kt + 4 * g]) = sacc[ht];
 }
 
-__device__ __forceinline__ bf16x8 v_frag(const uint8_t* vt, const VAddr& va, int dt) {
-  const s16x4 lo = lds_read_tr16(vt + va.tr_lo + 16 * ((2 * dt) ^ va.z_lo));
-  const s16x4 hi = lds_read_tr16(vt + va.tr_hi + 16 * ((2 * dt) ^ va.z_hi));
+__device__ __forceinline__ bf16x8 v_frag(const uint8_t* vbase, int vlo, int vhi, int dt) {
+  const s16x4 lo = lds_read_tr16(vbase + vlo + 32 * dt);
+  const s16x4 hi = lds_read_tr16(vbase + vhi + 32 * dt);
   const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3],
                                                          hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v8);
@@ -214,13 +201,13 @@ __device__ __forceinline__ bf16x8 v_frag(const uint8_t* vt, const VAddr& va, int
 
 // One pipeline step (see above).  kSoft: softmax of the tile whose partials are in sp_in
 // (P to pm_out); kLogits: logits of the next tile (fragments in k, partials to sp_out, V to
-// vt_out); kPrefetch: reload k from knext; kPV: P.V of the previous tile (P in pm_in, V in
-// vt_in).  sched_barrier fences keep the three streams interleaved as written, so the
+// vbase + vo_out); kPrefetch: reload k from knext; kPV: P.V of the previous tile (P in pm_in,
+// V in vbase + vo_in).  sched_barrier fences keep the three streams interleaved as written, so the
 // softmax chain's VALU work issues while the matrix cores run.
 template <bool kSoft, bool kLogits, bool kPrefetch, bool kPV>
 __device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint16_t* pm_out,
-                                         const uint16_t* pm_in, uint8_t* vt_out,
-                                         const uint8_t* vt_in, KRegs& k, const uint8_t* knext,
+                                         const uint16_t* pm_in, uint8_t* vbase, int vo_out,
+                                         int vo_in, KRegs& k, const uint8_t* knext,
                                          const bf16x8 (&qf)[4][kSteps], f32x4 (&o)[4][8],
                                          const VAddr& va, uint32_t vmask, float scale_log2,
                                          float& m_run, float& l_run, bool& ovf) {
@@ -228,6 +215,11 @@ __device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint
   const int g = lane >> 4, c16 = lane & 15;
   const int head = 16 * wave + c16;
   f32x4 sacc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // this step's V addresses: one base per stream (the empty asm keeps the compiler from
+  // hoisting one address per k-step out of the tile loop); the per-k-step and per-dims-tile
+  // parts are instruction offsets
+  int vst = vo_out + va.st, vlo = vo_in + va.tr_lo, vhi = vo_in + va.tr_hi;
+  asm volatile("" : "+v"(vst), "+v"(vlo), "+v"(vhi));
   // LDS reads first: partials of the softmax tile, P and the first V fragments
   f32x4 a0, a1, b0, b1;
   if (kSoft) {
@@ -241,17 +233,17 @@ __device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
       pa[ht] = *reinterpret_cast<const bf16x8*>(&pm_in[(16 * ht + c16) * kPRow + 8 * g]);
-    vf0 = v_frag(vt_in, va, 0);
-    vf1 = v_frag(vt_in, va, 1);
+    vf0 = v_frag(vbase, vlo, vhi, 0);
+    vf1 = v_frag(vbase, vlo, vhi, 1);
   }
   __builtin_amdgcn_sched_barrier(0);
   // slot s: logits k-step s, P.V dims tile s (fetching tile s + 2), one softmax slice
 #define DSA_SLOT(s)                                                                        \
-  if (kLogits) logits_kstep<kPrefetch>(s, k, qf, sacc, vt_out, va, knext);                 \
+  if (kLogits) logits_kstep<kPrefetch>(s, k, qf, sacc, vbase, vst, knext);                 \
   if (kPV && (s) < 8) {                                                                    \
     const bf16x8 vcur = ((s) & 1) ? vf1 : vf0;                                             \
     if ((s) + 2 < 8) {                                                                     \
-      if ((s) & 1) vf1 = v_frag(vt_in, va, (s) + 2); else vf0 = v_frag(vt_in, va, (s) + 2);\
+      if ((s) & 1) vf1 = v_frag(vbase, vlo, vhi, (s) + 2); else vf0 = v_frag(vbase, vlo, vhi, (s) + 2);\
     }                                                                                      \
     _Pragma("unroll") for (int ht = 0; ht < 4; ++ht) o[ht][(s) & 7] = mfma16(pa[ht], vcur, o[ht][(s) & 7]); \
   }
@@ -261,8 +253,13 @@ __device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint
   if (kSoft) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[j] = (vmask >> (8 * g + j)) & 1u ? (a0[j] + b0[j]) * scale_log2 : -INFINITY;
-      x[4 + j] = (vmask >> (8 * g + 4 + j)) & 1u ? (a1[j] + b1[j]) * scale_log2 : -INFINITY;
+      x[j] = (a0[j] + b0[j]) * scale_log2;
+      x[4 + j] = (a1[j] + b1[j]) * scale_log2;
+    }
+    if (vmask != 0xFFFFFFFFu) {   // a tile with entries that have no position (rare)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (!((vmask >> (8 * g + j)) & 1u)) x[j] = -INFINITY;
     }
     float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     tmax = rows4_max(tmax);
@@ -380,7 +377,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const uint32_t vmask_ = (uint32_t)__ballot(lane < 32 && rowid[e_] >= 0);                   \
     mla_step<kSoft, kLogits, kPrefetch, kPV>(                                                   \
         &spart[(tt) & 1][0][0][0], &spart[((tt) + 1) & 1][0][0][0], &pmat[(tt) & 1][0][0],     \
-        &pmat[((tt) + 1) & 1][0][0], vbuf[((tt) + 1) % 3], vbuf[((tt) + 2) % 3], kr,             \
+        &pmat[((tt) + 1) & 1][0][0], &vbuf[0][0], ((tt) + 1) % 3 * kVTileBytes,                  \
+        ((tt) + 2) % 3 * kVTileBytes, kr,                                                        \
         kPrefetch ? k_src(pool, rowid, ((tt) + 2) * kMT) : nullptr, qf, o, va, vmask_,          \
         scale_log2, m_run, l_run, ovf_step);                                                   \
     lds_barrier();                                                                             \
@@ -397,10 +395,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       if (ntiles > 1) {
         const uint8_t* nx = k_src(pool, rowid, kMT);
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) logits_kstep<true>(st, kr, qf, sacc, vbuf[0], va, nx);
+        for (int st = 0; st < kSteps; ++st) logits_kstep<true>(st, kr, qf, sacc, &vbuf[0][0], va.st, nx);
       } else {
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) logits_kstep<false>(st, kr, qf, sacc, vbuf[0], va, nullptr);
+        for (int st = 0; st < kSteps; ++st) logits_kstep<false>(st, kr, qf, sacc, &vbuf[0][0], va.st, nullptr);
       }
       store_partials(sacc, &spart[0][0][0][0]);
     }
