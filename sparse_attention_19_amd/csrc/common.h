@@ -43,7 +43,6 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(DSA_LDS(s16x4, const_cast<void*>(lds_addr)));
 }
 
-__device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
 __device__ __forceinline__ bf16x8 as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
@@ -53,7 +52,6 @@ __device__ __forceinline__ uint16_t f2bf_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float bf_bits2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Compiler-level ordering point for LDS traffic exchanged between lanes of one wave
 // (LDS operations of a wave execute in order in hardware).
