@@ -176,6 +176,21 @@ def test_mla_running_max_moves_late():
         check_token(inp, buf, t)
 
 
+def test_mla_splits_repeat_bitwise():
+    # 40 tokens -> 6 splits per token and a combine: a second call on the same buffers and
+    # workspace reproduces the first bit for bit (no state carried between calls)
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=40, ctx_range=(2500, 9000))
+    inp = I.make_inputs(cfg, DEV)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    first, first_lse = buf.outs[0].clone(), buf.lses[0].clone()
+    P.run_inputs(inp, buf, step=1)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.outs[0], first) and torch.equal(buf.lses[0], first_lse)
+    for t in (0, 17, 39):
+        check_token(inp, buf, t)
+
+
 # ------------------------------------------------------------------ top-k in isolation
 
 def _topk_case(scores: np.ndarray, n_valid, k):
