@@ -44,7 +44,8 @@ METRIC = "DSA decode tokens/s at 32K–128K ctx + achieved HBM GB/s fraction"
 # kernel -> source file that defines it (its hash decides whether stored counters still apply)
 KERNEL_SRC = {
     "indexer_decode_kernel": "indexer.hip", "indexer_prefill_kernel": "indexer.hip",
-    "indexer_f32_kernel": "indexer.hip", "topk_chunk_kernel": "topk.hip", "topk_merge_kernel": "topk.hip",
+    "indexer_f32_kernel": "indexer.hip", "topk_prune_kernel": "topk.hip", "topk_select_kernel": "topk.hip",
+    "topk_onepass_kernel": "topk.hip",
     "mla_bf16_kernel": "mla.hip", "mla_combine_kernel": "mla.hip", "mla_f32_kernel": "mla.hip",
 }
 
@@ -78,8 +79,8 @@ def algorithmic(cfg, kernels_seen=()):
 
     indexer  keys 2*Di B per cached position (once), q_idx + w per token, fp32 score per
              visible (token, position) pair; 2*Hi*Di FLOP per pair
-    top-k    the fp32 scores read, k int32 indices written per token (split between the
-             chunk and merge kernels when both run)
+    top-k    the fp32 scores read (by the prune kernel when it runs), k int32 indices
+             written per token (by the select kernel); both by the one-pass kernel
     MLA      2*(Dl+Dr) B per selected row per token (one layer per launch), q, idx, and
              out + lse per token; 2*H*(2*Dl+Dr) FLOP per selected row
     """
@@ -95,7 +96,7 @@ def algorithmic(cfg, kernels_seen=()):
     mla_in = sel * cfg.row_dim * eb + T * cfg.H * cfg.row_dim * eb + T * cfg.k * 4
     mla_out = T * cfg.H * (cfg.Dl * eb + 4)
     mla_f = 2 * sel * cfg.H * (cfg.row_dim + cfg.Dl)
-    merge = "topk_merge_kernel" in kernels_seen
+    prune = "topk_prune_kernel" in kernels_seen
     combine = "mla_combine_kernel" in kernels_seen
     ix_bound = "mfma" if (prefill and mfma_ok) else "hbm"
     mla_bound = "mfma" if (prefill and mfma_ok) else "hbm"
@@ -103,8 +104,9 @@ def algorithmic(cfg, kernels_seen=()):
         "indexer_decode_kernel": (ix_b, ix_f, "hbm"),
         "indexer_prefill_kernel": (ix_b, ix_f, ix_bound),
         "indexer_f32_kernel": (ix_b, ix_f, "hbm"),
-        "topk_chunk_kernel": (tk_in + (0 if merge else tk_out), 0, "hbm"),
-        "topk_merge_kernel": (tk_out, 0, "hbm"),
+        "topk_prune_kernel": (tk_in, 0, "hbm"),
+        "topk_select_kernel": (tk_out + (0 if prune else tk_in), 0, "hbm"),
+        "topk_onepass_kernel": (tk_in + tk_out, 0, "hbm"),
         "mla_bf16_kernel": (mla_in + (0 if combine else mla_out), mla_f, mla_bound),
         "mla_combine_kernel": (mla_out, 0, "hbm"),
         "mla_f32_kernel": (mla_in + mla_out, mla_f, "hbm"),

@@ -6,29 +6,36 @@
 // §Lightning Indexer and §Sparse MLA: top-K with K = 2048, shared by every head; queries
 // attending to fewer than K tokens stay dense).
 //
-// Scores become order-preserving uint32 keys (-0.0 folded into +0.0).  A 1024-thread
-// workgroup holds a chunk of up to 32768 keys in registers (32 consecutive keys per
-// thread, staged through a bank-conflict-free padded LDS copy) and selects in three steps:
-//   1. pruning : the key tau of a fixed rank among 1024 evenly spaced samples bounds the
-//                answer from below (one wave finds it on its own, two 8-bit radix levels
-//                in a private 256-bin histogram, stopping at the lower edge of the bin
-//                that holds it); the keys >= tau (about 2k + 768 of them) are
-//                compacted, in position order, into an LDS candidate list.  If
-//                that list would hold fewer than k or more than 8192 keys, all keys stay
-//                candidates.
-//   2. select  : the exact k-th largest key theta, by radix levels of 12 bits over the
-//                range [lowest candidate, highest key] (at most 3 levels) with two
-//                alternating 4096-bin LDS histograms (one is cleared while the other
-//                fills, so a level costs three barriers); lanes of a wave that fall in
-//                one bin add once.
-//   3. compact : per-thread counts of (> theta, == theta), one packed block scan, and the
-//                first need_eq ties in position order give every selected position its
-//                output slot -- ascending and independent of scheduling.
-// Wave scans and reductions run on DPP lane moves; block scans take one barrier each.
-// Rows longer than 32768 run that procedure per 32768-key chunk (grid rows x chunks),
-// writing each chunk's top-k (key, position) list to the workspace; a merge kernel then
-// selects the row's top-k from those lists in batches of at most 8192 candidates.  This
-// is exact: an element of the row's top-k is also in the top-k of its own chunk.
+// Scores become order-preserving uint32 keys (-0.0 folded into +0.0); every valid key is
+// >= 1 (0 would be a NaN, and NaN scores are not supported).  Each row's selection:
+//   tau     : a lower bound for the key of rank about 2k + 768, from 2048 samples of the
+//             row (512 runs of 4 consecutive scores, evenly spaced): two 8-bit radix
+//             levels over the samples' range, stopping at the lower edge of the bin that
+//             holds rank (2k + 768) * 2048 / n among them.
+//   prune   : the positions with key >= tau are the candidates (about 2k + 768).
+//   select  : the exact k-th largest candidate key theta, by 8-bit radix levels over
+//             [tau, row max] with the candidates in registers (8 per thread of a
+//             1024-thread workgroup): the histogram fills through LDS atomics and every
+//             wave scans the 256 bins by itself, so a level costs one barrier.
+//   compact : one block scan of packed (> theta, == theta) counts gives every position
+//             with key > theta, and the first need_eq with key == theta, its output slot;
+//             the positions come out ascending.
+// Exact: once at least k positions have key >= tau, theta >= tau, so every position with
+// key >= theta is a candidate.  Rows of at most 8192 positions skip tau (all positions are
+// candidates); a row whose candidates number fewer than k or more than 8192 (heavy ties,
+// adversarial rows) runs select and compact streaming the whole row from memory instead.
+// Kernels:
+//   ld <= 32768 : topk_onepass_kernel, one workgroup per row; the row goes through
+//                 coalesced loads into a padded LDS copy, from which the samples and the
+//                 candidates' keys are read.
+//   ld >  32768 : topk_prune_kernel (grid rows x G, 256 threads: several workgroups per row
+//                 when rows are few) computes tau redundantly in each workgroup, streams its
+//                 share of the row's 4096-position blocks and writes one bit per position;
+//                 topk_select_kernel (one workgroup per row) lists the marked positions,
+//                 gathers their keys and selects.
+// The result does not depend on scheduling.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -36,35 +43,145 @@ namespace dsa {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kR = 32;                          // keys per thread
-constexpr int kChunk = kThreads * kR;           // 32768 keys per workgroup
-constexpr int kPadWords = kChunk + kChunk / 32; // padded LDS copy: item e at e + e/32
-constexpr int kCap = 8192;                      // candidate list capacity
-constexpr int kCR = kCap / kThreads;            // 8 candidates per thread
-constexpr int kBins = 4096;
-constexpr int kHistWords = kBins + kWave;       // + one dummy word per lane
-constexpr int kSampleBins = 256;                // wave-private histogram of the sample select
-constexpr int kSampleMargin = 768;              // candidates aimed for above 2k
-constexpr int kMaxK = 2048;
-static_assert(kThreads * 4 == kBins, "one uint4 of bins per thread");
-static_assert(kChunk / 32 + 2 * kHistWords <= kPadWords, "histogram fits in the free pad area");
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kCap = 8192;                       // candidates held in registers
+constexpr int kOnePass = 32768;                  // longest row pruned inside the select kernel
+constexpr int kCR = kCap / kSelThreads;          // 8 per thread
+constexpr int kPruneThreads = 256;
+constexpr int kPruneWaves = kPruneThreads / kWave;
+constexpr int kPBlock = 4096;                    // positions per prune block, 16 per thread
+constexpr int kRuns = 512;                       // sample runs of 4 consecutive scores
+constexpr int kSamples = 4 * kRuns;              // 2048
+constexpr int kSamplesPerThread = kSamples / kPruneThreads;   // 8: two runs
+constexpr int kSampleMargin = 768;               // candidates aimed for above 2k
+constexpr int kBins = 256;
+constexpr int kHistWords = kBins + kWave;        // + one dummy word per lane
+constexpr int kPruneTarget = 2048;               // prune workgroups aimed for per launch
+static_assert(kPBlock == 16 * kPruneThreads, "four float4 per thread per block");
+static_assert(kSamplesPerThread == 8, "two sample runs per thread");
+static_assert(kHistWords % 4 == 0 && kHistWords / 4 <= kPruneThreads, "histogram clears");
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-struct Smem {
-  uint32_t wsum[3][kWaves];   // block-scan partials (levels alternate 0/1; the lists use 2)
-  uint32_t wred[2][kWaves];   // block min / max partials
-  uint32_t sel[2][2];         // per radix level: (bin, count above it), alternating
-  uint32_t tau;
+__device__ __forceinline__ int row_len(const int* n_valid, int n_add, int64_t ld, int row) {
+  const int64_t n = (int64_t)n_valid[row] + n_add;
+  return (int)(n < 0 ? 0 : (n > ld ? ld : n));
+}
+
+__device__ __forceinline__ int range_bits(uint32_t lo, uint32_t hi) {
+  return hi <= lo ? 0 : 32 - __clz(hi - lo);
+}
+
+// OR over each group of 8 consecutive lanes, result in all 8: quad_perm swaps (xor 1,
+// xor 2) within each quad, then row_half_mirror (lane i <-> 7 - i) across the two quads.
+__device__ __forceinline__ uint32_t group8_or(uint32_t v) {
+  v |= DSA_DPP(v, 0xB1, 0xf, false);
+  v |= DSA_DPP(v, 0x4E, 0xf, false);
+  v |= DSA_DPP(v, 0x141, 0xf, false);
+  return v;
+}
+
+// One radix level's histogram: key goes to bin (key - L) >> shift when it lies in
+// [L, L + 2^W) (L >= 1, so empty entries -- key 0 -- never count); keys out of range go to
+// a per-lane dummy word past the bins.  rmask = 2^W - 1 (all ones for W = 32).
+__device__ __forceinline__ void hist_add(uint32_t key, uint32_t L, uint32_t rmask, int shift,
+                                         uint32_t* hist) {
+  const uint32_t d = key - L;
+  const bool in = key >= L && d <= rmask;
+  atomicAdd(&hist[in ? (d >> shift) : (uint32_t)(kBins + (threadIdx.x & 63))], 1u);
+}
+
+__device__ __forceinline__ uint32_t range_mask(int W) { return W >= 32 ? 0xFFFFFFFFu : (1u << W) - 1u; }
+
+// The bin holding the rank-th largest counted key (1-based, rank <= the number counted)
+// and the count above that bin, in every lane of the calling wave.  Lane l scans bins
+// 255-4l .. 252-4l (descending); each wave does this on its own.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rank, uint32_t* bin,
+                                         uint32_t* above) {
+  const int lane = threadIdx.x & 63;
+  const uint4 c4 = reinterpret_cast<const uint4*>(hist)[kBins / 4 - 1 - lane];
+  const uint32_t c[4] = {c4.w, c4.z, c4.y, c4.x};
+  const uint32_t local = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_incl_add(local);
+  const uint32_t excl = incl - local;
+  const uint64_t hit = __ballot(excl < rank && rank <= incl);
+  const int f = max(__ffsll((unsigned long long)hit) - 1, 0);
+  uint32_t b = 0, a = 0, run = excl;
+  bool found = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (!found && run + c[q] >= rank) {
+      b = (uint32_t)(kBins - 1 - 4 * lane - q);
+      a = run;
+      found = true;
+    }
+    if (!found) run += c[q];
+  }
+  *bin = (uint32_t)__builtin_amdgcn_readlane((int)b, f);
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)a, f);
+}
+
+// Radix selection state: the answer lies in [L, L + 2^W), with `remaining` of the wanted
+// rank still to go inside it.  Level `level` fills hist[level % 3] and clears
+// hist[(level + 1) % 3] for the next one (that buffer's last readers finished before the
+// previous level's barrier), so a level takes one barrier; hist[0] must be zero, and
+// cleared before a barrier, when the selection starts.
+struct Radix {
+  uint32_t L;
+  int W;
+  uint32_t remaining;
+  int level;
 };
 
-// Exclusive scan of one value per thread over the block; *total receives the sum.  One
-// barrier: `wsum` must not be written again before every thread has returned.
+__device__ __forceinline__ int radix_shift(const Radix& s) { return s.W > 8 ? s.W - 8 : 0; }
+
+__device__ __forceinline__ void radix_clear_next(const Radix& s, uint32_t (*hist)[kHistWords]) {
+  if (threadIdx.x < kHistWords / 4)
+    reinterpret_cast<uint4*>(hist[(s.level + 1) % 3])[threadIdx.x] = make_uint4(0, 0, 0, 0);
+}
+
+// After the level's histogram is complete (past a barrier): narrow to the bin found.
+__device__ __forceinline__ void radix_narrow(Radix& s, uint32_t (*hist)[kHistWords]) {
+  const int shift = radix_shift(s);
+  uint32_t bin, above;
+  find_bin(hist[s.level % 3], s.remaining, &bin, &above);
+  s.remaining -= above;
+  s.L += bin << shift;
+  s.W = shift;
+  ++s.level;
+}
+
+// Exact rank-th largest of the R keys per thread of the block (list entries R*t .. R*t+R-1
+// of thread t; the first `count` entries are valid keys in [lo, hi], lo >= 1, rank <=
+// count; the others are 0).  Waves holding no valid entry skip the histograms.  Returns
+// theta; s.remaining is then the number of keys equal to theta that belong to the top
+// `rank`.
+template <int R>
+__device__ __forceinline__ uint32_t select_regs(const uint32_t (&key)[R], uint32_t count, uint32_t lo,
+                                                uint32_t hi, uint32_t rank,
+                                                uint32_t (*hist)[kHistWords], Radix& s) {
+  const bool busy = (uint32_t)((threadIdx.x >> 6) * kWave * R) < count;   // wave-uniform
+  s = Radix{lo, range_bits(lo, hi), rank, 0};
+  while (s.W > 0) {
+    radix_clear_next(s, hist);
+    const int shift = radix_shift(s);
+    const uint32_t rmask = range_mask(s.W);
+    if (busy) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) hist_add(key[r], s.L, rmask, shift, hist[s.level % 3]);
+    }
+    __syncthreads();
+    radix_narrow(s, hist);
+  }
+  return s.L;
+}
+
+// Exclusive scan of one value per thread over the block (kSelThreads); *total gets the
+// sum.  One barrier: `wsum` must not be written again before every thread has returned.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_add(v);
@@ -72,7 +189,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < kSelWaves; ++w) {
     const uint32_t x = wsum[w];
     before += (w < wave) ? x : 0u;
     tot += x;
@@ -81,174 +198,16 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   return before + incl - v;
 }
 
-// Block-wide min and max (one barrier; Smem::wred is reused only after further barriers).
-__device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, Smem& sm, uint32_t* mn,
-                                             uint32_t* mx) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (lane == 0) {
-    sm.wred[0][wave] = lo;
-    sm.wred[1][wave] = hi;
-  }
-  __syncthreads();
-  uint32_t a = 0xFFFFFFFFu, b = 0u;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    a = min(a, sm.wred[0][w]);
-    b = max(b, sm.wred[1][w]);
-  }
-  *mn = a;
-  *mx = b;
-}
-
-// A lower bound of the rank-th largest (1-based, rank <= number of nonzero entries) of the
-// 1024 entries of `v` (LDS), zero entries ignored, computed by one wave alone: 8-bit radix
-// levels over [min, max] with a private histogram `hs` (LDS, kSampleBins words, 16-byte
-// aligned).  After kMaxLevels levels it stops at the lower edge of the bin that holds the
-// rank-th entry (exact when the range is at most 8 * kMaxLevels bits wide): a slightly
-// lower bound only admits a few more candidates.
-template <int kMaxLevels>
-__device__ __forceinline__ uint32_t wave_select_rank(const uint32_t* v, uint32_t rank, uint32_t* hs) {
-  const int lane = threadIdx.x & 63;
-  uint32_t s[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 x = reinterpret_cast<const uint4*>(v)[4 * lane + i];
-    s[4 * i] = x.x;
-    s[4 * i + 1] = x.y;
-    s[4 * i + 2] = x.z;
-    s[4 * i + 3] = x.w;
-  }
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    mn = min(mn, s[r] ? s[r] : 0xFFFFFFFFu);
-    mx = max(mx, s[r]);
-  }
-  uint32_t L = wave_min_u32(mn);
-  const uint32_t hi = wave_max_u32(mx);
-  int W = (hi <= L) ? 0 : 32 - __clz(hi - L);
-  uint32_t remaining = rank;
-  for (int level = 0; W > 0 && level < kMaxLevels; ++level) {
-    const int shift = W > 8 ? W - 8 : 0;
-    reinterpret_cast<uint4*>(hs)[lane] = make_uint4(0, 0, 0, 0);
-    wave_lds_fence();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t d = s[r] - L;
-      if (s[r] != 0u && s[r] >= L && (W >= 32 || d < (1u << W))) atomicAdd(&hs[d >> shift], 1u);
-    }
-    wave_lds_fence();
-    // lane l owns bins 255-4l .. 252-4l (descending)
-    const uint4 c4 = reinterpret_cast<const uint4*>(hs)[kSampleBins / 4 - 1 - lane];
-    const uint32_t c[4] = {c4.w, c4.z, c4.y, c4.x};
-    const uint32_t local = c[0] + c[1] + c[2] + c[3];
-    const uint32_t incl = wave_incl_add(local);
-    const uint32_t excl = incl - local;
-    const uint64_t hit = __ballot(excl < remaining && remaining <= incl);
-    const int f = __ffsll((unsigned long long)hit) - 1;
-    uint32_t bin = 0, above = 0;
-    if (lane == f) {
-      uint32_t run = excl;
-      bool found = false;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (!found && run + c[q] >= remaining) {
-          bin = (uint32_t)(kSampleBins - 1 - 4 * lane - q);
-          above = run;
-          found = true;
-        }
-        if (!found) run += c[q];
-      }
-    }
-    bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, f);
-    above = (uint32_t)__builtin_amdgcn_readlane((int)above, f);
-    remaining -= above;
-    L += bin << shift;
-    W = shift;
-    wave_lds_fence();
-  }
-  return L;
-}
-
-// Exact `rank`-th largest (1-based, rank <= number of valid keys) of the keys of all
-// threads, every valid key lying in [lo, hi] with lo >= 1 (key 0 marks an empty slot).
-// Returns theta and the number of keys equal to theta that belong to the top `rank`.
-// hist_a must be zero (cleared before a barrier that precedes the call); both histograms
-// (kHistWords words, 16-byte aligned) are left dirty.
-template <int R>
-__device__ __forceinline__ void select_rank(const uint32_t (&key)[R], uint32_t lo, uint32_t hi,
-                                            uint32_t rank, uint32_t* hist_a, uint32_t* hist_b,
-                                            Smem& sm, uint32_t* theta, uint32_t* need_eq) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t L = lo;
-  int W = (hi <= lo) ? 0 : 32 - __clz(hi - lo);
-  uint32_t remaining = rank;
-  uint32_t* cur = hist_a;
-  uint32_t* nxt = hist_b;
-  int level = 0;
-  while (W > 0) {
-    const int shift = W > 12 ? W - 12 : 0;
-    // the other buffer feeds the next level; its last reads were before the previous
-    // level's final barrier
-    reinterpret_cast<uint4*>(nxt)[tid] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      // branch-free: lanes outside the range add to a private dummy word; lanes sharing
-      // lane 0's bin are counted once, by lane 0
-      const uint32_t d = key[r] - L;
-      const bool a = key[r] >= L && (W >= 32 || d < (1u << W));
-      const uint32_t bin = a ? (d >> shift) : (uint32_t)(kBins + lane);
-      const uint32_t b0 = __builtin_amdgcn_readfirstlane(bin);
-      const uint64_t same = __ballot(bin == b0);
-      const bool in0 = bin == b0;
-      const uint32_t addr = in0 ? (lane == 0 ? b0 : (uint32_t)(kBins + lane)) : bin;
-      const uint32_t inc = in0 ? (lane == 0 ? (uint32_t)__popcll(same) : 0u) : 1u;
-      atomicAdd(&cur[addr], inc);
-    }
-    __syncthreads();
-    // thread t owns bins 4095-4t .. 4092-4t (descending)
-    const uint4 c4 = reinterpret_cast<const uint4*>(cur)[kBins / 4 - 1 - tid];
-    const uint32_t c[4] = {c4.w, c4.z, c4.y, c4.x};
-    const uint32_t local = c[0] + c[1] + c[2] + c[3];
-    uint32_t total;
-    const uint32_t excl = block_excl_scan(local, sm.wsum[level & 1], &total);
-    if (excl < remaining && remaining <= excl + local) {
-      uint32_t run = excl;
-      bool found = false;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (!found && run + c[q] >= remaining) {
-          sm.sel[level & 1][0] = (uint32_t)(kBins - 1 - 4 * tid - q);
-          sm.sel[level & 1][1] = run;
-          found = true;
-        }
-        if (!found) run += c[q];
-      }
-    }
-    __syncthreads();
-    remaining -= sm.sel[level & 1][1];
-    L += sm.sel[level & 1][0] << shift;
-    W = shift;
-    uint32_t* t = cur;
-    cur = nxt;
-    nxt = t;
-    ++level;
-    (void)wave;
-  }
-  *theta = L;
-  *need_eq = remaining;
-}
-
-// Ordered compaction: thread t's R entries follow those of threads < t in list order
-// (theta >= 1, so empty slots -- key 0 -- are never selected).
-// emit(r, slot) for every selected entry; slot = its rank in list order.
+// Ordered compaction of R consecutive list entries per thread (thread t: entries
+// R*t .. R*t + R - 1): the entries > theta and the first eq_left entries == theta, in list
+// order, get consecutive slots from slot0 on; emit(r, slot) for each.  theta >= 1, so empty
+// entries (key 0) are never taken.  Returns the block's packed counts (gt | eq << 16).
 template <int R, typename Emit>
-__device__ __forceinline__ void compact(const uint32_t (&key)[R], uint32_t theta,
-                                        uint32_t need_eq, uint32_t* wsum, Emit emit) {
+__device__ __forceinline__ uint32_t compact(const uint32_t (&key)[R], uint32_t theta,
+                                            uint32_t eq_left, uint32_t slot0, uint32_t* wsum,
+                                            Emit emit) {
   static_assert(R <= 32, "selection masks are 32-bit");
-  uint32_t gtm = 0, eqm = 0;      // per-entry flags as bit masks (bit r = entry r)
+  uint32_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     gtm |= (key[r] > theta ? 1u : 0u) << r;
@@ -257,289 +216,476 @@ __device__ __forceinline__ void compact(const uint32_t (&key)[R], uint32_t theta
   const uint32_t gt = __popc(gtm), eq = __popc(eqm);
   uint32_t total;
   const uint32_t before = block_excl_scan(gt | (eq << 16), wsum, &total);
-  // ties taken by earlier threads, then by this one (its first entries equal to theta).
-  // Clamping before subtracting keeps every difference non-negative (no guarded
-  // subtraction that an optimiser could hoist out of its guard).
-  const uint32_t taken_before = min(before >> 16, need_eq);
-  uint32_t keep = min(eq, need_eq - taken_before);
+  // ties taken by earlier threads, then by this one (its first entries equal to theta);
+  // clamping before subtracting keeps every difference non-negative
+  const uint32_t taken_before = min(before >> 16, eq_left);
+  uint32_t keep = min(eq, eq_left - taken_before);
   uint32_t rest = eqm;
   for (; keep > 0; --keep) rest &= rest - 1u;
   const uint32_t selm = gtm | (eqm ^ rest);
-  const uint32_t slot0 = (before & 0xFFFFu) + taken_before;
+  const uint32_t base = slot0 + (before & 0xFFFFu) + taken_before;
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (selm & (1u << r)) emit(r, slot0 + (uint32_t)__popc(selm & ((1u << r) - 1u)));
+    if (selm & (1u << r)) emit(r, base + (uint32_t)__popc(selm & ((1u << r) - 1u)));
+  return total;
 }
 
-// Top-k of a list held as R consecutive entries per thread (entry (t, r) = item R*t + r),
-// with count > k items in total; entries past the list hold key 0.  Valid keys are never 0
-// (0 is the key of a NaN, and NaN scores are not supported).
-// emit(item, key, slot) for each selected item.  Scratch (LDS): hist_a (zero on entry),
-// hist_b, and for R > kCR the samples (kThreads words), the candidate list (kCap keys and
-// kCap items) -- none of it overlapping the others.  Every thread must have finished any
-// earlier use of hist_b / the candidate area before it enters (the first barrier here
-// orders all later writes to them).
-template <int R, typename Emit>
-__device__ __forceinline__ void topk_of_list(const uint32_t (&key)[R], int count, uint32_t k,
-                                             Smem& sm, uint32_t* hist_a, uint32_t* hist_b,
-                                             uint32_t* samp, uint32_t* cand_key, uint32_t* cand_item,
-                                             Emit emit) {
-  const int tid = threadIdx.x;
+// ------------------------------------------------------------------ prune
+
+// Sample run i (of 512) of a row of n > kCap positions: positions
+// 4 * floor(i * floor(n / 4) / 512) .. + 3, evenly spaced and inside the row.
+__device__ __forceinline__ int sample_pos(int run, int n) {
+  return 4 * (int)(((int64_t)run * (n >> 2)) / kRuns);
+}
+
+__device__ __forceinline__ void load_run(const float* src, int p, bool vec, uint32_t* s) {
+  float4 v;
+  if (vec) {
+    v = *reinterpret_cast<const float4*>(src + p);
+  } else {
+    v = make_float4(src[p], src[p + 1], src[p + 2], src[p + 3]);
+  }
+  s[0] = order_key(v.x);
+  s[1] = order_key(v.y);
+  s[2] = order_key(v.z);
+  s[3] = order_key(v.w);
+}
+
+// Rank among the 2048 samples of the key expected to have about 2k + 768 keys of the row
+// (n > kCap) at or above it.
+__device__ __forceinline__ uint32_t sample_rank(int k, int n) {
+  const uint64_t want = 2ull * (uint64_t)k + kSampleMargin;
+  const uint64_t r = (want * kSamples + (uint64_t)n - 1) / (uint64_t)n;
+  return (uint32_t)(r < (uint64_t)kSamples ? r : (uint64_t)kSamples);
+}
+
+// tau of one row from its 2048 samples (S per thread, 0 = no sample): the lower edge of
+// the bin that holds the rank-th largest sample after two 8-bit radix levels over the
+// samples' [min, max].  Every workgroup of the row computes the same value.  `extra` is
+// maximised over the block alongside (*xmax).  Clears and uses hist[0] and hist[1]; three
+// barriers.  kWavesB: waves in the block (at most kSelWaves).
+template <int kWavesB, int S>
+__device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t rank, uint32_t extra,
+                                               uint32_t (*hist)[kHistWords], uint32_t (*red)[2 * kSelWaves],
+                                               uint32_t* xmax) {
+  static_assert(kWavesB <= kSelWaves, "reduction slots");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < S; ++r) {
+    mn = min(mn, s[r] ? s[r] : 0xFFFFFFFFu);
+    mx = max(mx, s[r]);
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  extra = wave_max_u32(extra);
+  if (tid < 2 * kHistWords / 4) reinterpret_cast<uint4*>(&hist[0][0])[tid] = make_uint4(0, 0, 0, 0);
+  if (lane == 0) {
+    red[0][wave] = mn;
+    red[1][wave] = mx;
+    red[1][kWavesB + wave] = extra;
+  }
+  __syncthreads();
+  uint32_t L = 0xFFFFFFFFu, hi = 0u, xm = 0u;
+#pragma unroll
+  for (int w = 0; w < kWavesB; ++w) {
+    L = min(L, red[0][w]);
+    hi = max(hi, red[1][w]);
+    xm = max(xm, red[1][kWavesB + w]);
+  }
+  *xmax = xm;
+  int W = range_bits(L, hi);
+  for (int level = 0; level < 2 && W > 0; ++level) {
+    const int shift = W > 8 ? W - 8 : 0;
+    const uint32_t rmask = range_mask(W);
+#pragma unroll
+    for (int r = 0; r < S; ++r) hist_add(s[r], L, rmask, shift, hist[level]);
+    __syncthreads();
+    uint32_t bin, above;
+    find_bin(hist[level], rank, &bin, &above);
+    rank -= above;
+    L += bin << shift;
+    W = shift;
+  }
+  return L;
+}
+
+// ------------------------------------------------------------------ prune
+
+struct PruneSmem {
+  uint32_t hist[2][kHistWords];
+  uint32_t red[2][2 * kSelWaves];   // [0]: per-wave minima; [1]: maxima, then the extra maxima
+};
+
+// Stage 1, grid (rows, G), when ld > kOnePass, for rows of more than kCap positions:
+// bit p of the row's mask = (key(p) >= tau) for p < n; tau_out[row]; wmax[row][slice][wave]
+// = the largest key the wave saw (0 if none).  Block b of the row (positions 4096b ..) belongs to slice b % G.
+__global__ __launch_bounds__(kPruneThreads) void topk_prune_kernel(
+    const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
+    uint32_t* __restrict__ mask, int64_t mw, uint32_t* __restrict__ tau_out,
+    uint32_t* __restrict__ wmax) {
+  __shared__ __attribute__((aligned(16))) PruneSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x, slice = blockIdx.y, G = gridDim.y;
+  const int n = row_len(n_valid, n_add, ld, row);
+  if (n <= kCap) return;
+  uint32_t* wm = wmax + ((int64_t)row * G + slice) * kPruneWaves;
+  if ((int64_t)slice * kPBlock >= n) {   // no block for this slice
+    if (lane == 0) wm[wave] = 0u;
+    return;
+  }
+  const float* src = scores + (int64_t)row * ld;
+  const bool vec = ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0) && (ld & 3) == 0;
+
+  uint32_t s[kSamplesPerThread];
+  load_run(src, sample_pos(tid, n), vec, s);
+  load_run(src, sample_pos(tid + kPruneThreads, n), vec, s + 4);
+  uint32_t unused;
+  const uint32_t tau = sample_tau<kPruneWaves, kSamplesPerThread>(s, sample_rank(k, n), 0u, sm.hist,
+                                                                  sm.red, &unused);
+  if (slice == 0 && tid == 0) tau_out[row] = tau;
+
+  uint32_t* mrow = mask + (int64_t)row * mw;
+  const int nwords = (n + 31) >> 5;
+  uint32_t kmax = 0u;
+  for (int64_t b = slice; b * kPBlock < n; b += G) {
+    const int p0 = (int)(b * kPBlock);
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + 4 * (tid + kPruneThreads * u);
+      if (vec && p + 3 < n) {
+        v[u] = *reinterpret_cast<const float4*>(src + p);
+      } else {
+        v[u].x = p < n ? src[p] : 0.f;
+        v[u].y = p + 1 < n ? src[p + 1] : 0.f;
+        v[u].z = p + 2 < n ? src[p + 2] : 0.f;
+        v[u].w = p + 3 < n ? src[p + 3] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + 4 * (tid + kPruneThreads * u);
+      const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t nib = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t key = p + j < n ? order_key(x[j]) : 0u;
+        kmax = max(kmax, key);
+        nib |= (key >= tau && key != 0u ? 1u : 0u) << j;
+      }
+      // the word of positions p0 + 1024u + 32 * (tid / 8) .. + 31 gathers the nibbles of
+      // 8 consecutive lanes
+      const uint32_t word = group8_or(nib << (4 * (tid & 7)));
+      const int wi = (p0 >> 5) + 32 * u + (tid >> 3);
+      if ((tid & 7) == 0 && wi < nwords) mrow[wi] = word;
+    }
+  }
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) wm[wave] = kmax;
+}
+
+// ------------------------------------------------------------------ select
+
+struct SelSmem {
+  uint32_t hist[3][kHistWords];
+  uint32_t wsum[2][kSelWaves];
+  uint32_t red[2][2 * kSelWaves];   // as in PruneSmem
+};
+
+// Exact top-k of a whole row streamed from memory (valid keys in [1, hi], k < n): radix
+// levels over the row, then an ordered compaction in blocks of 8192 positions (thread t:
+// 8t .. 8t+7 of each block).  hist[0] must be zero (cleared before a barrier) and wsum[1]
+// free on entry.
+__device__ __forceinline__ void select_streamed(const float* src, int n, uint32_t hi, int k,
+                                                SelSmem& sm, int* out) {
+  const int tid = threadIdx.x;
+  Radix st{1u, range_bits(1u, hi), (uint32_t)k, 0};
+  while (st.W > 0) {
+    radix_clear_next(st, sm.hist);
+    const int shift = radix_shift(st);
+    const uint32_t rmask = range_mask(st.W);
+    for (int p = tid; p < n; p += kSelThreads)
+      hist_add(order_key(src[p]), st.L, rmask, shift, sm.hist[st.level % 3]);
+    __syncthreads();
+    radix_narrow(st, sm.hist);
+  }
+  const uint32_t theta = st.L;
+  uint32_t eq_left = st.remaining, slot0 = 0;
+  // the scans alternate between the two partial buffers
+  for (int p0 = 0, it = 1; p0 < n; p0 += kCap, ++it) {
+    uint32_t key[kCR];
+#pragma unroll
+    for (int r = 0; r < kCR; ++r) {
+      const int p = p0 + kCR * tid + r;
+      key[r] = p < n ? order_key(src[p]) : 0u;
+    }
+    const uint32_t tot = compact<kCR>(key, theta, eq_left, slot0, sm.wsum[it & 1],
+                                      [&](int r, uint32_t slot) { out[slot] = p0 + kCR * tid + r; });
+    const uint32_t eq_taken = min(tot >> 16, eq_left);
+    slot0 += (tot & 0xFFFFu) + eq_taken;
+    eq_left -= eq_taken;
+  }
+}
+
+// Rows of k < n <= kCap positions: every position is a candidate, thread t holding
+// positions 8t .. 8t+7 in registers.  hist[0] need not be clear; wsum[1] must be free.
+__device__ __forceinline__ void select_direct(const float* src, int n, int k, SelSmem& sm, int* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
+  uint32_t key[kCR];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int r = 0; r < kCR; ++r) {
+    const int p = kCR * tid + r;
+    key[r] = p < n ? order_key(src[p]) : 0u;
     mn = min(mn, key[r] ? key[r] : 0xFFFFFFFFu);
     mx = max(mx, key[r]);
   }
-  const bool try_prune = R > kCR && count > kCap;
-  if (try_prune) samp[tid] = key[R / 2];              // sample = item R*t + R/2
-  uint32_t kmin, kmax;
-  block_minmax(mn, mx, sm, &kmin, &kmax);
-
-  bool pruned = false;
-  if (try_prune) {
-    // 1. lower bound tau: a fixed rank among the valid samples (threads holding > R/2 items)
-    const int ns = count > R / 2 ? min(kThreads, (count - R / 2 - 1) / R + 1) : 0;
-    const uint64_t want = 2ull * k + kSampleMargin;
-    const uint32_t rank = (uint32_t)((want * (uint64_t)ns + (uint64_t)count - 1) / (uint64_t)count);
-    if (rank >= 1 && rank < (uint32_t)ns) {
-      if (tid < kWave) {
-        const uint32_t tau = wave_select_rank<2>(samp, rank, hist_b);
-        if (tid == 0) sm.tau = tau;
-      }
-      __syncthreads();
-      const uint32_t tau = sm.tau;
-      uint32_t cm = 0;
-#pragma unroll
-      for (int r = 0; r < R; ++r) cm |= (key[r] >= tau ? 1u : 0u) << r;
-      uint32_t ctot;
-      const uint32_t off = block_excl_scan((uint32_t)__popc(cm), sm.wsum[2], &ctot);
-      if (ctot >= k && ctot <= (uint32_t)kCap) {
-        pruned = true;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (cm & (1u << r)) {
-            const uint32_t o = off + (uint32_t)__popc(cm & ((1u << r) - 1u));
-            cand_key[o] = key[r];
-            cand_item[o] = (uint32_t)(R * tid + r);
-          }
-        __syncthreads();
-        uint32_t ck[kCR];
-#pragma unroll
-        for (int r = 0; r < kCR; ++r) {
-          const uint32_t v = cand_key[kCR * tid + r];   // in bounds: kCR * 1024 == kCap
-          ck[r] = (uint32_t)(kCR * tid + r) < ctot ? v : 0u;
-        }
-        uint32_t theta, need_eq;
-        select_rank<kCR>(ck, tau, kmax, k, hist_a, hist_b, sm, &theta, &need_eq);   // 2.
-        compact<kCR>(ck, theta, need_eq, sm.wsum[2], [&](int r, uint32_t slot) {       // 3.
-          emit(cand_item[kCR * tid + r], ck[r], slot);
-        });
-      }
-    }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    sm.red[0][wave] = mn;
+    sm.red[1][wave] = mx;
   }
-  if (!pruned) {
-    uint32_t theta, need_eq;
-    select_rank<R>(key, kmin, kmax, k, hist_a, hist_b, sm, &theta, &need_eq);
-    compact<R>(key, theta, need_eq, sm.wsum[2],
-               [&](int r, uint32_t slot) { emit((uint32_t)(R * tid + r), key[r], slot); });
+  __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    lo = min(lo, sm.red[0][w]);
+    hi = max(hi, sm.red[1][w]);
   }
+  Radix st;
+  const uint32_t theta = select_regs<kCR>(key, (uint32_t)n, lo, hi, (uint32_t)k, sm.hist, st);
+  compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
+               [&](int r, uint32_t slot) { out[slot] = kCR * tid + r; });
 }
 
-__device__ __forceinline__ int row_len(const int* n_valid, int n_add, int64_t ld, int row) {
-  const int64_t n = (int64_t)n_valid[row] + n_add;
-  return (int)(n < 0 ? 0 : (n > ld ? ld : n));
-}
-
-// Stage 1, grid (rows, chunks): rows with n <= k get 0..n-1 and -1 padding; rows with
-// k < n <= 32768 get their final top-k; longer rows write each chunk's top-k as
-// (key, position) lists: ws_key / ws_pos [row][chunk][k], ws_cnt [row][chunk].
-// LDS: the padded chunk copy; once every thread holds its keys in registers it becomes
-// the candidate list (words 0 .. 2*kCap) and the second histogram (after that).
-__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
+// Stage 2 after the prune kernel (ld > kOnePass), one workgroup per row: rows of at most
+// kCap positions select from registers directly, longer ones from the candidates the prune
+// kernel marked.
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
-    int* __restrict__ idx, int64_t ld_idx, uint32_t* __restrict__ ws_key, int* __restrict__ ws_pos,
-    int* __restrict__ ws_cnt, int max_chunks) {
-  __shared__ __attribute__((aligned(16))) uint32_t pad[kPadWords];
-  __shared__ __attribute__((aligned(16))) uint32_t hist_a[kHistWords];
-  __shared__ __attribute__((aligned(16))) uint32_t samp[kThreads];
-  __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x, chunk = blockIdx.y;
+    int* __restrict__ idx, int64_t ld_idx, const uint32_t* __restrict__ mask, int64_t mw,
+    const uint32_t* __restrict__ tau_in, const uint32_t* __restrict__ wmax, int G) {
+  __shared__ __attribute__((aligned(16))) SelSmem sm;
+  __shared__ uint32_t cpos[kCap];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
   const int n = row_len(n_valid, n_add, ld, row);
   int* out = idx + (int64_t)row * ld_idx;
   if (n <= k) {
-    if (chunk == 0)
-      for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < k; i += kSelThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const int c0 = chunk * kChunk;
-  if (c0 >= n) return;
-  const int cnt = min(kChunk, n - c0);
-  const bool multi = n > kChunk;
+  const float* src = scores + (int64_t)row * ld;
+  if (n <= kCap) {
+    select_direct(src, n, k, sm, out);
+    return;
+  }
 
-  reinterpret_cast<uint4*>(hist_a)[tid] = make_uint4(0, 0, 0, 0);   // zero for select_rank
-  // coalesced 16-byte loads into the padded LDS copy
-  const float* src = scores + (int64_t)row * ld + c0;
-  if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-    const int n4 = cnt >> 2;
-    const float4* s4 = reinterpret_cast<const float4*>(src);
-    for (int base = 0; base < n4; base += kThreads * 8) {
-      float4 v[8];
+  // candidates from the prune bits: thread t owns the words [t * wpt, (t + 1) * wpt)
+  if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
+  const uint32_t* mrow = mask + (int64_t)row * mw;
+  const int nwords = (n + 31) >> 5;
+  const int wpt = (nwords + kSelThreads - 1) / kSelThreads;
+  const int w0 = tid * wpt, w1 = min(nwords, w0 + wpt);
+  constexpr int kKeep = 4;   // words kept in registers between the count and the listing
+  uint32_t wk[kKeep];
+  uint32_t cnt = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i4 = base + tid + u * kThreads;
-        v[u] = i4 < n4 ? s4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i4 = base + tid + u * kThreads;
-        if (i4 < n4) {
-          const int e = 4 * i4, a = e + (e >> 5);
-          pad[a] = order_key(v[u].x);
-          pad[a + 1] = order_key(v[u].y);
-          pad[a + 2] = order_key(v[u].z);
-          pad[a + 3] = order_key(v[u].w);
-        }
-      }
-    }
-    for (int e = 4 * n4 + tid; e < cnt; e += kThreads) pad[e + (e >> 5)] = order_key(src[e]);
-  } else {
-    for (int e = tid; e < cnt; e += kThreads) pad[e + (e >> 5)] = order_key(src[e]);
+  for (int j = 0; j < kKeep; ++j) {
+    wk[j] = w0 + j < w1 ? mrow[w0 + j] : 0u;
+    cnt += __popc(wk[j]);
   }
-  __syncthreads();
-  const int64_t lbase = ((int64_t)row * max_chunks + chunk) * k;
-  if (multi && cnt <= k) {                            // short last chunk: all of it
-    for (int i = tid; i < cnt; i += kThreads) {
-      ws_key[lbase + i] = pad[i + (i >> 5)];
-      ws_pos[lbase + i] = c0 + i;
+  for (int w = w0 + kKeep; w < w1; ++w) cnt += __popc(mrow[w]);
+  const int64_t nblocks = ((int64_t)n + kPBlock - 1) / kPBlock;
+  const int nslices = (int)(nblocks < G ? nblocks : G);
+  const uint32_t* wrow = wmax + (int64_t)row * G * kPruneWaves;
+  uint32_t mx = 0u;
+  for (int i = tid; i < nslices * kPruneWaves; i += kSelThreads) mx = max(mx, wrow[i]);
+  const uint32_t tau = tau_in[row];
+  mx = wave_max_u32(mx);
+  if (lane == 0) sm.red[1][wave] = mx;
+  uint32_t total;
+  uint32_t off = block_excl_scan(cnt, sm.wsum[0], &total);
+  uint32_t hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) hi = max(hi, sm.red[1][w]);
+
+  if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
+    // the candidates' positions in order, then their keys (8 per thread)
+#pragma unroll
+    for (int j = 0; j < kKeep; ++j) {
+      uint32_t m = wk[j];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        cpos[off++] = (uint32_t)(32 * (w0 + j) + b);
+      }
     }
-    if (tid == 0) ws_cnt[(int64_t)row * max_chunks + chunk] = cnt;
+    for (int w = w0 + kKeep; w < w1; ++w) {
+      uint32_t m = mrow[w];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        cpos[off++] = (uint32_t)(32 * w + b);
+      }
+    }
+    __syncthreads();
+    uint32_t key[kCR];
+#pragma unroll
+    for (int r = 0; r < kCR; ++r) {
+      const uint32_t i = (uint32_t)(kCR * tid + r);
+      key[r] = i < total ? order_key(src[cpos[i]]) : 0u;
+    }
+    Radix st;
+    const uint32_t theta = select_regs<kCR>(key, total, tau, hi, (uint32_t)k, sm.hist, st);
+    compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
+                 [&](int r, uint32_t slot) { out[slot] = (int)cpos[kCR * tid + r]; });
     return;
   }
-  uint32_t key[kR];
-  const int nv = cnt - kR * tid;                    // entries of this thread (may be <= 0)
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const uint32_t v = pad[33 * tid + r];          // in bounds: 33 * 1023 + 31 < kPadWords
-    key[r] = r < nv ? v : 0u;
-  }
-  // (topk_of_list's first barrier comes after every thread has read its keys, so pad is
-  // free from there on)
-  uint32_t* cand_key = pad;
-  uint32_t* cand_item = pad + kCap;
-  uint32_t* hist_b = pad + 2 * kCap;
-  topk_of_list<kR>(key, cnt, (uint32_t)k, sm, hist_a, hist_b, samp, cand_key, cand_item,
-                   [&](uint32_t item, uint32_t kv, uint32_t slot) {
-                     if (slot >= (uint32_t)k) return;
-                     if (!multi) {
-                       out[slot] = (int)item;
-                     } else {
-                       ws_key[lbase + slot] = kv;
-                       ws_pos[lbase + slot] = c0 + (int)item;
-                     }
-                   });
-  if (multi && tid == 0) ws_cnt[(int64_t)row * max_chunks + chunk] = k;
+  select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
 }
 
-// Stage 2, one workgroup per row longer than 32768: merge the chunk lists.  The running
-// selection (at most k entries) is followed by as many whole chunk lists as fit in 8192
-// entries; their top-k becomes the new running selection.  All lists are in position
-// order and chunks are consecutive, so the concatenation is in position order.
-__global__ __launch_bounds__(kThreads) void topk_merge_kernel(
-    int64_t ld, const int* __restrict__ n_valid, int n_add, int k, int* __restrict__ idx,
-    int64_t ld_idx, const uint32_t* __restrict__ ws_key, const int* __restrict__ ws_pos,
-    const int* __restrict__ ws_cnt, int max_chunks) {
-  __shared__ __attribute__((aligned(16))) uint32_t lkey[kCap];
-  __shared__ int lpos[kCap];
-  __shared__ uint32_t nkey[kMaxK];
-  __shared__ int npos[kMaxK];
-  __shared__ __attribute__((aligned(16))) uint32_t hist_a[kHistWords];
-  __shared__ __attribute__((aligned(16))) uint32_t hist_b[kHistWords];
-  __shared__ Smem sm;
+// The whole selection in one workgroup per row, launched when ld <= kOnePass.  Rows of
+// kCap < n <= kOnePass: the scores go through coalesced loads into a padded LDS copy (item
+// e at word e + e/32, so that thread t reads its 32 consecutive keys 32t .. 32t+31 without
+// bank conflicts); tau comes from the row's samples, read from that copy; the positions of
+// the keys >= tau are listed in order (16 bits each) and their keys read back from the copy.
+constexpr int kPadWords = kOnePass + kOnePass / 32;
+
+__global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
+    const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
+    int* __restrict__ idx, int64_t ld_idx) {
+  __shared__ __attribute__((aligned(16))) SelSmem sm;
+  __shared__ uint32_t pad[kPadWords];
+  __shared__ uint16_t cpos[kCap];
+  constexpr int kR1 = kOnePass / kSelThreads;
+  static_assert(kR1 == 32, "one 32-bit candidate mask per thread");
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int n = row_len(n_valid, n_add, ld, row);
-  if (n <= kChunk || n <= k) return;
-  const int nchunks = (n + kChunk - 1) / kChunk;
-  const int* cnts = ws_cnt + (int64_t)row * max_chunks;
-  int cur = 0, c = 0;
-  while (c < nchunks) {
-    int fill = cur;
-    while (c < nchunks && fill + cnts[c] <= kCap) {
-      const int m = cnts[c];
-      const int64_t lb = ((int64_t)row * max_chunks + c) * k;
-      for (int i = tid; i < m; i += kThreads) {
-        lkey[fill + i] = ws_key[lb + i];
-        lpos[fill + i] = ws_pos[lb + i];
-      }
-      fill += m;
-      ++c;
-    }
-    reinterpret_cast<uint4*>(hist_a)[tid] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
-    if (fill > k) {
-      uint32_t ck[kCR];
-#pragma unroll
-      for (int r = 0; r < kCR; ++r) {
-        const uint32_t v = lkey[kCR * tid + r];      // in bounds: kCR * 1024 == kCap
-        ck[r] = kCR * tid + r < fill ? v : 0u;
-      }
-      // 8 entries per thread: topk_of_list does no pruning, so it needs no sample or
-      // candidate scratch
-      topk_of_list<kCR>(ck, fill, (uint32_t)k, sm, hist_a, hist_b, nullptr, nullptr, nullptr,
-                        [&](uint32_t item, uint32_t kv, uint32_t slot) {
-                          if (slot < (uint32_t)k) {
-                            nkey[slot] = kv;
-                            npos[slot] = lpos[item];
-                          }
-                        });
-      __syncthreads();
-      for (int i = tid; i < k; i += kThreads) {
-        lkey[i] = nkey[i];
-        lpos[i] = npos[i];
-      }
-      cur = k;
-    } else {
-      cur = fill;
-    }
-    __syncthreads();
-  }
   int* out = idx + (int64_t)row * ld_idx;
-  for (int i = tid; i < k; i += kThreads) out[i] = i < cur ? lpos[i] : -1;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kSelThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* src = scores + (int64_t)row * ld;
+  if (n <= kCap) {
+    select_direct(src, n, k, sm, out);
+    return;
+  }
+  // coalesced 16-byte loads (float4 i4 = tid + 1024u) into the padded copy
+  const bool vec = ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0) && (ld & 3) == 0;
+  {
+    float4 v[kR1 / 4];
+#pragma unroll
+    for (int u = 0; u < kR1 / 4; ++u) {
+      const int p = 4 * (tid + kSelThreads * u);
+      if (vec && p + 3 < n) {
+        v[u] = *reinterpret_cast<const float4*>(src + p);
+      } else {
+        v[u].x = p < n ? src[p] : 0.f;
+        v[u].y = p + 1 < n ? src[p + 1] : 0.f;
+        v[u].z = p + 2 < n ? src[p + 2] : 0.f;
+        v[u].w = p + 3 < n ? src[p + 3] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kR1 / 4; ++u) {
+      const int p = 4 * (tid + kSelThreads * u), a = p + (p >> 5);
+      pad[a] = p < n ? order_key(v[u].x) : 0u;
+      pad[a + 1] = p + 1 < n ? order_key(v[u].y) : 0u;
+      pad[a + 2] = p + 2 < n ? order_key(v[u].z) : 0u;
+      pad[a + 3] = p + 3 < n ? order_key(v[u].w) : 0u;
+    }
+  }
+  __syncthreads();
+  uint32_t key[kR1];
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int r = 0; r < kR1; ++r) {
+    key[r] = pad[(kR1 + 1) * tid + r];   // item 32t + r
+    mx = max(mx, key[r]);
+  }
+  uint32_t smp[4] = {0u, 0u, 0u, 0u};
+  if (tid < kRuns) {
+    const int p = sample_pos(tid, n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) smp[j] = pad[p + j + ((p + j) >> 5)];
+  }
+  uint32_t hi;
+  const uint32_t tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), mx, sm.hist, sm.red, &hi);
+  uint32_t cm = 0;
+#pragma unroll
+  for (int r = 0; r < kR1; ++r) cm |= (key[r] >= tau ? 1u : 0u) << r;   // tau >= 1
+  // hist[0]'s last readers finished before the second sample level's barrier
+  if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
+  uint32_t total;
+  uint32_t off = block_excl_scan((uint32_t)__popc(cm), sm.wsum[0], &total);
+  if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
+    for (uint32_t m = cm; m; m &= m - 1u) cpos[off++] = (uint16_t)(kR1 * tid + __ffs(m) - 1);
+    __syncthreads();
+    uint32_t ck[kCR];
+#pragma unroll
+    for (int r = 0; r < kCR; ++r) {
+      const uint32_t i = (uint32_t)(kCR * tid + r);
+      const uint32_t q = i < total ? cpos[i] : 0u;
+      ck[r] = i < total ? pad[q + (q >> 5)] : 0u;
+    }
+    Radix st;
+    const uint32_t theta = select_regs<kCR>(ck, total, tau, hi, (uint32_t)k, sm.hist, st);
+    compact<kCR>(ck, theta, st.remaining, 0u, sm.wsum[1],
+                 [&](int r, uint32_t slot) { out[slot] = (int)cpos[kCR * tid + r]; });
+    return;
+  }
+  select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
 }
 
-int chunks_of(int64_t ld) { return (int)((ld + kChunk - 1) / kChunk); }
+// Prune workgroups per row: about kPruneTarget per launch, at most one per block.
+int prune_slices(int rows, int64_t ld) {
+  const int64_t blocks = (ld + kPBlock - 1) / kPBlock;
+  const int64_t want = (kPruneTarget + (int64_t)rows - 1) / std::max(rows, 1);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, blocks));
+}
+
+int64_t mask_words(int64_t ld) { return ((ld + 31) / 32 + 3) / 4 * 4; }
+
+size_t tau_words(int rows) { return ((size_t)rows + 3) / 4 * 4; }
 
 }  // namespace
 
+// mask [rows][mask_words] | tau [rows] (padded to 16 bytes) | wmax [rows][G][4]
 size_t topk_workspace_bytes(int rows, int64_t ld, int k) {
-  const int mc = chunks_of(ld);
-  if (mc <= 1 || rows <= 0) return 0;
-  return (size_t)rows * mc * ((size_t)k * 8 + 4);
+  (void)k;
+  if (ld <= kOnePass || rows <= 0) return 0;
+  const size_t G = (size_t)prune_slices(rows, ld);
+  return ((size_t)rows * mask_words(ld) + tau_words(rows) + (size_t)rows * G * kPruneWaves) * 4;
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
-  const int mc = chunks_of(a.ld);
-  uint32_t* ws_key = nullptr;
-  int* ws_pos = nullptr;
-  int* ws_cnt = nullptr;
-  if (mc > 1) {
-    ws_key = (uint32_t*)a.ws;
-    ws_pos = (int*)(ws_key + (size_t)a.rows * mc * a.k);
-    ws_cnt = ws_pos + (size_t)a.rows * mc * a.k;
+  if (a.ld <= kOnePass) {
+    const KernelEvents ev("topk_onepass_kernel");
+    hipExtLaunchKernelGGL(topk_onepass_kernel, dim3(a.rows), dim3(kSelThreads), 0, stream, ev.start,
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx);
+    return hipGetLastError();
+  }
+  const int G = prune_slices(a.rows, a.ld);
+  const int64_t mw = mask_words(a.ld);
+  uint32_t* mask = (uint32_t*)a.ws;
+  uint32_t* tau = mask + (size_t)a.rows * mw;
+  uint32_t* wmax = tau + tau_words(a.rows);
+  {
+    const KernelEvents ev("topk_prune_kernel");
+    hipExtLaunchKernelGGL(topk_prune_kernel, dim3(a.rows, G), dim3(kPruneThreads), 0, stream, ev.start,
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, mask, mw, tau, wmax);
   }
   {
-    const KernelEvents ev("topk_chunk_kernel");
-    hipExtLaunchKernelGGL(topk_chunk_kernel, dim3(a.rows, mc), dim3(kThreads), 0, stream, ev.start,
-                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx,
-                          ws_key, ws_pos, ws_cnt, mc);
-  }
-  if (mc > 1) {
-    const KernelEvents ev("topk_merge_kernel");
-    hipExtLaunchKernelGGL(topk_merge_kernel, dim3(a.rows), dim3(kThreads), 0, stream, ev.start,
-                          ev.stop, 0, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, ws_key,
-                          ws_pos, ws_cnt, mc);
+    const KernelEvents ev("topk_select_kernel");
+    hipExtLaunchKernelGGL(topk_select_kernel, dim3(a.rows), dim3(kSelThreads), 0, stream, ev.start,
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, mask,
+                          mw, tau, wmax, G);
   }
   return hipGetLastError();
 }

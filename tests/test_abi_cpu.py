@@ -104,7 +104,7 @@ def topk_call(**kw):
     (dict(rows=-1), L.DSA_ERR_INVALID),
     (dict(rows=0), L.DSA_OK),                             # empty: nothing enqueued
     (dict(rows=0, scores=None, idx=None), L.DSA_OK),      # ... and may pass NULL data
-    (dict(ld=40000), L.DSA_ERR_WORKSPACE),                # long rows need the merge workspace
+    (dict(ld=40000), L.DSA_ERR_WORKSPACE),                # long rows need the prune workspace
 ])
 def test_topk_rejects(kw, status):
     assert topk_call(**kw) == status
@@ -167,8 +167,12 @@ def test_workspace_sizes():
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 0, 0, 2048, 64, 512) == 0
     # rows of at most 32768 positions are selected in one workgroup: no workspace
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 64, 32768, 2048, 0, 0) == 0
-    # longer rows: per-chunk (key, position) lists and counts
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 40, 131072, 2048, 0, 0) == 40 * 4 * (2048 * 8 + 4)
+    # longer rows: one prune bit per position, tau per row (padded to 4 words), and the
+    # largest key of each prune wave (4 per workgroup, min(ceil(2048 / rows), blocks of
+    # 4096) workgroups per row)
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 1, 40000, 2048, 0, 0) == (1252 + 4 + 10 * 4) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 40, 131072, 2048, 0, 0) == \
+        (40 * 4096 + 40 + 40 * 32 * 4) * 4
 
 
 def test_index_cache_host_logic():

@@ -222,9 +222,24 @@ def test_topk_adversarial(k):
     rows.append(rng.integers(-3, 4, ld).astype(np.float64)); nv.append(0)         # empty
     rows.append(rng.integers(0, 50, ld).astype(np.float64)); nv.append(32768)    # cache edge
     rows.append(rng.integers(0, 50, ld).astype(np.float64)); nv.append(32769)
+    rows.append(rng.integers(0, 50, ld).astype(np.float64)); nv.append(8192)     # largest direct row
+    rows.append(rng.integers(0, 50, ld).astype(np.float64)); nv.append(8193)     # smallest pruned row
+    rows.append(rng.standard_normal(ld)); nv.append(ld)                          # pruned, distinct
     rows.append(-np.abs(rng.standard_normal(ld)) * 1e30); nv.append(ld)          # huge negatives
     rows.append(np.where(np.arange(ld) > ld - k - 3, 5.0, 1.0)); nv.append(ld)   # winners at the end
     _topk_case(np.stack(rows), nv, k)
+
+
+@pytest.mark.parametrize("rows", [300, 2500])
+def test_topk_many_rows(rows):
+    # relu-weighted sums like indexer scores, ragged lengths across the direct / pruned
+    # boundary; 300 rows prune with several workgroups per row, 2500 with one
+    rng = np.random.default_rng(rows)
+    ld = 20000
+    sc = np.maximum(rng.standard_normal((rows, ld)), 0.0) + 0.5 * np.maximum(rng.standard_normal((rows, ld)), 0.0)
+    nv = rng.integers(0, ld + 1, rows)
+    nv[:4] = [ld, 8192, 8193, 2048]
+    _topk_case(sc, nv.tolist(), 2048)
 
 
 def test_topk_long_rows_ties():
