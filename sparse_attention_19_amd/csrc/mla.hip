@@ -471,27 +471,43 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 }
 
 // Merge split partials: m = max m_s, L = sum l_s 2^(m_s - m), O = sum O_s 2^(m_s - m) / L.
-// grid (T, H, Z); one wave per (token, head) and 1/Z of the output dims, in passes of 64
-// dims (kPasses / Z of them).  Lane s first turns split s's (m_s, l_s) into its weight;
-// then lane 16a + c accumulates dims 4c..4c+3 of every pass over the splits a, a + 4, ...
-// with independent 16-byte loads (all in flight together), and the four split groups are
-// summed through LDS.  Requires splits <= 64 and Dl == 64 * kPasses.
+// grid (T, H, Z); one wave per (token, head) and 1/Z of the output dims, in kNP passes of
+// 64 dims (Z = kPasses / kNP).  Lane 16a + c handles dims 4c..4c+3 of each pass for the
+// splits a, a + 4, ...; lane s also reads split s's (m_s, l_s).  Every load of the wave is
+// issued before the first is used (one memory round trip): its slots (split, pass) are
+// registers, kCombSlots at a time.  The four split groups (the wave's four 16-lane rows)
+// are summed with row-swap lane moves, no LDS.  Requires splits <= 64 and
+// Dl == 64 * kPasses.
 constexpr int kPasses = kDl / 64;
+constexpr int kCombSlots = 8;
 
+template <int kNP>
 __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict__ ws_o,
                                                          const float* __restrict__ ws_ml, int splits,
                                                          int H, uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
-  __shared__ float wgt[64];
-  __shared__ float4 part[4][kPasses][16];
+  static_assert(kCombSlots % kNP == 0, "whole splits per slot batch");
+  constexpr int kSPB = kCombSlots / kNP;   // splits per slot batch
   const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int npass = kPasses / gridDim.z, pass0 = blockIdx.z * npass;
+  const int pass0 = blockIdx.z * kNP;
+  const int a = lane >> 4, c = lane & 15;
+  const int nsp = splits > a ? (splits - a + 3) >> 2 : 0;   // splits a, a + 4, ... of this lane
+  // slot (i, p): split a + 4i, pass p
+  const float* src = ws_o + (((int64_t)t * splits + a) * H + h) * kDl + 64 * pass0 + 4 * c;
+  const int64_t sstride = (int64_t)4 * H * kDl;
   float ms = -INFINITY, ls = 0.f;
   if (lane < splits) {
     const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (((int64_t)t * splits + lane) * H + h) * 2);
     ms = ml.x;
     ls = ml.y;
   }
+  float4 v[kSPB][kNP];
+#pragma unroll
+  for (int i = 0; i < kSPB; ++i)
+#pragma unroll
+    for (int p = 0; p < kNP; ++p)
+      v[i][p] = i < nsp ? *reinterpret_cast<const float4*>(src + i * sstride + 64 * p)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
   float m = ms;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, shfl_xor_f(m, off));
@@ -500,46 +516,41 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += shfl_xor_f(L, off);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  wgt[lane] = f * inv;
-  __syncthreads();
-  const int a = lane >> 4, c = lane & 15;
-  const float* src = ws_o + ((int64_t)t * splits * H + h) * kDl + 64 * pass0 + 4 * c;
-  float4 acc[kPasses];
+  const float wl = f * inv;   // weight of split `lane`
+  float4 acc[kNP];
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) acc[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = a; s < splits; s += 4) {
-    const float w = wgt[s];
-    const float* row = src + (int64_t)s * H * kDl;
+  for (int p = 0; p < kNP; ++p) acc[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0;;) {
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      if (p < npass) {
-        const float4 v = *reinterpret_cast<const float4*>(row + 64 * p);
-        acc[p].x = fmaf(w, v.x, acc[p].x);
-        acc[p].y = fmaf(w, v.y, acc[p].y);
-        acc[p].z = fmaf(w, v.z, acc[p].z);
-        acc[p].w = fmaf(w, v.w, acc[p].w);
+    for (int i = 0; i < kSPB; ++i) {
+      const float w = __shfl(wl, min(a + 4 * (i0 + i), 63), kWave);   // 0 past the last split
+#pragma unroll
+      for (int p = 0; p < kNP; ++p) {
+        acc[p].x = fmaf(w, v[i][p].x, acc[p].x);
+        acc[p].y = fmaf(w, v[i][p].y, acc[p].y);
+        acc[p].z = fmaf(w, v[i][p].z, acc[p].z);
+        acc[p].w = fmaf(w, v[i][p].w, acc[p].w);
       }
     }
+    i0 += kSPB;
+    if (i0 >= (splits + 3) / 4) break;   // more splits than registers: the next batch
+#pragma unroll
+    for (int i = 0; i < kSPB; ++i)
+#pragma unroll
+      for (int p = 0; p < kNP; ++p)
+        v[i][p] = i0 + i < nsp ? *reinterpret_cast<const float4*>(src + (i0 + i) * sstride + 64 * p)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  uint16_t* dst = out + ((int64_t)t * H + h) * kDl + 64 * pass0 + 4 * c;
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p)
-    if (p < npass) part[a][p][c] = acc[p];
-  __syncthreads();
-  for (int i = lane; i < 16 * npass; i += 64) {
-    const int p = i >> 4, cc = i & 15;
-    float4 r = part[0][p][cc];
-#pragma unroll
-    for (int g = 1; g < 4; ++g) {
-      const float4 q = part[g][p][cc];
-      r.x += q.x;
-      r.y += q.y;
-      r.z += q.z;
-      r.w += q.w;
+  for (int p = 0; p < kNP; ++p) {
+    const float rx = rows4_sum(acc[p].x), ry = rows4_sum(acc[p].y);
+    const float rz = rows4_sum(acc[p].z), rw = rows4_sum(acc[p].w);
+    if (a == (p & 3)) {
+      const uint32_t lo = (uint32_t)f2bf_bits(rx) | ((uint32_t)f2bf_bits(ry) << 16);
+      const uint32_t hi = (uint32_t)f2bf_bits(rz) | ((uint32_t)f2bf_bits(rw) << 16);
+      *reinterpret_cast<uint2*>(dst + 64 * p) = make_uint2(lo, hi);
     }
-    const uint32_t lo = (uint32_t)f2bf_bits(r.x) | ((uint32_t)f2bf_bits(r.y) << 16);
-    const uint32_t hi = (uint32_t)f2bf_bits(r.z) | ((uint32_t)f2bf_bits(r.w) << 16);
-    *reinterpret_cast<uint2*>(out + ((int64_t)t * H + h) * kDl + 64 * (pass0 + p) + 4 * cc) =
-        make_uint2(lo, hi);
   }
   if (lse && blockIdx.z == 0 && lane == 0)
     lse[(int64_t)t * H + h] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
@@ -641,11 +652,30 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
     }
     if (splits > 1) {
       // split the output dims over Z workgroups per (token, head) until ~2048 are in flight
+      // (and until a lane's (split, pass) slots fit in registers at once)
       int Z = 1;
-      while (Z < kPasses && (int64_t)a.T * kH * Z < 2048) Z *= 2;
+      while (Z < kPasses && ((int64_t)a.T * kH * Z < 2048 || (splits + 3) / 4 * (kPasses / Z) > kCombSlots))
+        Z *= 2;
       const KernelEvents ev("mla_combine_kernel");
-      hipExtLaunchKernelGGL(mla_combine_kernel, dim3(a.T, kH, Z), dim3(64), 0, stream, ev.start,
-                            ev.stop, 0, ws_o, ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+      const dim3 grid(a.T, kH, Z);
+      switch (kPasses / Z) {
+        case 8:
+          hipExtLaunchKernelGGL(mla_combine_kernel<8>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
+                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+          break;
+        case 4:
+          hipExtLaunchKernelGGL(mla_combine_kernel<4>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
+                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+          break;
+        case 2:
+          hipExtLaunchKernelGGL(mla_combine_kernel<2>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
+                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+          break;
+        default:
+          hipExtLaunchKernelGGL(mla_combine_kernel<1>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
+                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+          break;
+      }
     }
   } else {
     {

@@ -549,20 +549,27 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
 }
 
 // The whole selection in one workgroup per row, launched when ld <= kOnePass.  Rows of
-// kCap < n <= kOnePass: the scores go through coalesced loads into a padded LDS copy (item
-// e at word e + e/32, so that thread t reads its 32 consecutive keys 32t .. 32t+31 without
-// bank conflicts); tau comes from the row's samples, read from that copy; the positions of
-// the keys >= tau are listed in order (16 bits each) and their keys read back from the copy.
-constexpr int kPadWords = kOnePass + kOnePass / 32;
+// kCap < n <= kOnePass: the scores go through coalesced loads into a padded LDS copy, from
+// which every thread reads its 32 consecutive keys (32t .. 32t+31), the samples are read,
+// and, once the positions of the keys >= tau are listed in order (16 bits each), the
+// candidates' keys.  Copy layout: key e at word pad_word(e) = 36 * (e / 32) + e % 32, so a
+// group of 4 keys is one aligned 16-byte access and 8 lanes reading rows 36 words apart
+// hit 8 different 16-byte bank groups; the 4 spare words after each 32 hold 8 of the
+// 16-bit positions (list entry i at halfword 72 * (i / 8) + 64 + i % 8).
+constexpr int kPadWords = kOnePass / 32 * 36;
+
+__device__ __forceinline__ int pad_word(int e) { return 36 * (e >> 5) + (e & 31); }
+__device__ __forceinline__ int cpos_half(int i) { return 72 * (i >> 3) + 64 + (i & 7); }
 
 __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
     int* __restrict__ idx, int64_t ld_idx) {
   __shared__ __attribute__((aligned(16))) SelSmem sm;
-  __shared__ uint32_t pad[kPadWords];
-  __shared__ uint16_t cpos[kCap];
+  __shared__ __attribute__((aligned(16))) uint32_t pad[kPadWords];
+  uint16_t* cpos = reinterpret_cast<uint16_t*>(pad);
   constexpr int kR1 = kOnePass / kSelThreads;
   static_assert(kR1 == 32, "one 32-bit candidate mask per thread");
+  static_assert(kCap / 8 * 72 <= 2 * kPadWords, "positions fit in the spare words");
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int n = row_len(n_valid, n_add, ld, row);
@@ -594,26 +601,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kR1 / 4; ++u) {
-      const int p = 4 * (tid + kSelThreads * u), a = p + (p >> 5);
-      pad[a] = p < n ? order_key(v[u].x) : 0u;
-      pad[a + 1] = p + 1 < n ? order_key(v[u].y) : 0u;
-      pad[a + 2] = p + 2 < n ? order_key(v[u].z) : 0u;
-      pad[a + 3] = p + 3 < n ? order_key(v[u].w) : 0u;
+      const int p = 4 * (tid + kSelThreads * u);
+      *reinterpret_cast<uint4*>(&pad[pad_word(p)]) =
+          make_uint4(p < n ? order_key(v[u].x) : 0u, p + 1 < n ? order_key(v[u].y) : 0u,
+                     p + 2 < n ? order_key(v[u].z) : 0u, p + 3 < n ? order_key(v[u].w) : 0u);
     }
   }
   __syncthreads();
   uint32_t key[kR1];
   uint32_t mx = 0u;
 #pragma unroll
-  for (int r = 0; r < kR1; ++r) {
-    key[r] = pad[(kR1 + 1) * tid + r];   // item 32t + r
-    mx = max(mx, key[r]);
+  for (int u = 0; u < kR1 / 4; ++u) {
+    const uint4 q = *reinterpret_cast<const uint4*>(&pad[36 * tid + 4 * u]);   // keys 32t + 4u ..
+    key[4 * u] = q.x;
+    key[4 * u + 1] = q.y;
+    key[4 * u + 2] = q.z;
+    key[4 * u + 3] = q.w;
+    mx = max(max(mx, max(q.x, q.y)), max(q.z, q.w));
   }
   uint32_t smp[4] = {0u, 0u, 0u, 0u};
   if (tid < kRuns) {
-    const int p = sample_pos(tid, n);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) smp[j] = pad[p + j + ((p + j) >> 5)];
+    const uint4 q = *reinterpret_cast<const uint4*>(&pad[pad_word(sample_pos(tid, n))]);
+    smp[0] = q.x;
+    smp[1] = q.y;
+    smp[2] = q.z;
+    smp[3] = q.w;
   }
   uint32_t hi;
   const uint32_t tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), mx, sm.hist, sm.red, &hi);
@@ -625,19 +637,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
   uint32_t total;
   uint32_t off = block_excl_scan((uint32_t)__popc(cm), sm.wsum[0], &total);
   if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
-    for (uint32_t m = cm; m; m &= m - 1u) cpos[off++] = (uint16_t)(kR1 * tid + __ffs(m) - 1);
+    for (uint32_t m = cm; m; m &= m - 1u, ++off)
+      cpos[cpos_half((int)off)] = (uint16_t)(kR1 * tid + __ffs(m) - 1);
     __syncthreads();
     uint32_t ck[kCR];
 #pragma unroll
     for (int r = 0; r < kCR; ++r) {
-      const uint32_t i = (uint32_t)(kCR * tid + r);
-      const uint32_t q = i < total ? cpos[i] : 0u;
-      ck[r] = i < total ? pad[q + (q >> 5)] : 0u;
+      const int i = kCR * tid + r;
+      const int q = (uint32_t)i < total ? cpos[cpos_half(i)] : 0;
+      ck[r] = (uint32_t)i < total ? pad[pad_word(q)] : 0u;
     }
     Radix st;
     const uint32_t theta = select_regs<kCR>(ck, total, tau, hi, (uint32_t)k, sm.hist, st);
     compact<kCR>(ck, theta, st.remaining, 0u, sm.wsum[1],
-                 [&](int r, uint32_t slot) { out[slot] = (int)cpos[kCR * tid + r]; });
+                 [&](int r, uint32_t slot) { out[slot] = (int)cpos[cpos_half(kCR * tid + r)]; });
     return;
   }
   select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
