@@ -140,7 +140,7 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int
  * §MLA changes]: for request b with n = seq_len[b] and every head h
  *   S     = { idx[b][i] : i < k, 0 <= idx[b][i] < n }   if n > k
  *         = { 0, ..., n-1 }                              if n <= k (dense fallback,
- *                                                          idx row not read)
+ *                                                          entries of the idx row ignored)
  *   l_s   = sm_scale * q[b][h][0:Dl+Dr] . row_s[0:Dl+Dr]
  *   out[b][h][c] = sum_{s in S} softmax(l)_s * row_s[c]   for c < Dl
  *   lse[b][h]    = log sum_{s in S} exp(l_s)

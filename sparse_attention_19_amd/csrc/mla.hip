@@ -57,18 +57,31 @@ constexpr float kMaxSlack = 32.f;
 
 // Resolve the token's (request, n) and this split's slice [i0, i0 + nent) of the
 // selected list; fills rowid[] with global row ids (phys * 64 + slot) or -1, up to the
-// end of the slice's last 32-entry tile.
+// end of the slice's last 32-entry tile.  Two memory round trips whatever the slice
+// length: first the token's request and length together with the slice's list entries
+// (read as if n > k; the dense case ignores them), then every page-table entry at once.
 __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const int* block_table,
                                              const int* seq_len, int max_blocks, int batch,
                                              int64_t num_blocks, const int* q_row, const int* q_pos,
                                              const int* idx, int64_t ld_idx, int k, int* rowid,
                                              int& nent) {
+  constexpr int kPer = kMaxList / kThreads;   // list entries per thread, at most
+  const int tid = threadIdx.x;
   const int b = q_row ? q_row[t] : t;
+  int n = q_pos ? q_pos[t] + 1 : (t < batch ? seq_len[t] : 0);   // decode: request t
+  const int per_s = ((k + splits - 1) / splits + kMT - 1) / kMT * kMT;
+  const int i0_s = sp * per_s;
+  const int nent_s = max(0, min(k, i0_s + per_s) - i0_s);
+  int pos[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + kThreads * j;
+    pos[j] = e < nent_s ? idx[(int64_t)t * ld_idx + i0_s + e] : -1;
+  }
   if (b < 0 || b >= batch) {      // token of no request: empty set (out = 0, lse = -inf)
     nent = 0;
     return;
   }
-  int n = q_pos ? q_pos[t] + 1 : seq_len[b];
   n = max(0, min(n, max_blocks * kBlock));
   const bool dense = n <= k;
   const int cnt = dense ? n : k;
@@ -77,18 +90,23 @@ __device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const in
   const int i0 = sp * per;
   nent = max(0, min(cnt, i0 + per) - i0);
   const int* bt_row = block_table + (int64_t)b * max_blocks;
-  for (int e = threadIdx.x; e < nent; e += blockDim.x) {
-    const int p = dense ? i0 + e : idx[(int64_t)t * ld_idx + i0 + e];
-    int rid = -1;
-    if (p >= 0 && p < n) {
-      const int phys = bt_row[p >> 6];
-      if (phys >= 0 && phys < num_blocks) rid = phys * kBlock + (p & 63);
-    }
-    rowid[e] = rid;
+  int phys[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + kThreads * j;
+    if (dense) pos[j] = i0 + e;
+    const bool ok = e < nent && pos[j] >= 0 && pos[j] < n;
+    phys[j] = ok ? bt_row[pos[j] >> 6] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + kThreads * j;
+    if (e < nent)
+      rowid[e] = (phys[j] >= 0 && phys[j] < num_blocks) ? phys[j] * kBlock + (pos[j] & 63) : -1;
   }
   // entries up to the end of the last tile read as "no position"
   const int padded = (nent + kMT - 1) / kMT * kMT;
-  for (int e = nent + threadIdx.x; e < padded; e += blockDim.x) rowid[e] = -1;
+  for (int e = nent + tid; e < padded; e += kThreads) rowid[e] = -1;
 }
 
 // LDS row of entry k of a tile: within each group of 8 the entries go to rows
