@@ -315,15 +315,21 @@ __device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t 
 struct PruneSmem {
   uint32_t hist[2][kHistWords];
   uint32_t red[2][2 * kSelWaves];   // [0]: per-wave minima; [1]: maxima, then the extra maxima
+  uint32_t part[2][2 * kPruneWaves];   // list mode: per-wave packed counts (alternating blocks)
 };
 
 // Stage 1, grid (rows, G), when ld > kOnePass, for rows of more than kCap positions:
-// bit p of the row's mask = (key(p) >= tau) for p < n; tau_out[row]; wmax[row][slice][wave]
-// = the largest key the wave saw (0 if none).  Block b of the row (positions 4096b ..) belongs to slice b % G.
+// tau_out[row]; wmax[row][slice][wave] = the largest key the wave saw (0 if none).  Block
+// b of the row (positions 4096b ..) belongs to slice b % G.  Then either
+//   G > 1 (few rows): bit p of the row's mask = (key(p) >= tau) for p < n; or
+//   G == 1 (one workgroup per row): the candidates (key >= tau) in position order, as
+//          (key, position) pairs list[row][0 .. 8191] and their number lcnt[row] (pairs past
+//          8192 are counted, not stored).  Each block's candidates take their places
+//          from one block scan of packed per-thread counts.
 __global__ __launch_bounds__(kPruneThreads) void topk_prune_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
     uint32_t* __restrict__ mask, int64_t mw, uint32_t* __restrict__ tau_out,
-    uint32_t* __restrict__ wmax) {
+    uint32_t* __restrict__ wmax, uint32_t* __restrict__ lcnt, uint2* __restrict__ list) {
   __shared__ __attribute__((aligned(16))) PruneSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x, slice = blockIdx.y, G = gridDim.y;
@@ -345,10 +351,13 @@ __global__ __launch_bounds__(kPruneThreads) void topk_prune_kernel(
                                                                   sm.red, &unused);
   if (slice == 0 && tid == 0) tau_out[row] = tau;
 
+  const bool listed = G == 1;
   uint32_t* mrow = mask + (int64_t)row * mw;
+  uint2* lrow = list + (int64_t)row * kCap;
   const int nwords = (n + 31) >> 5;
-  uint32_t kmax = 0u;
-  for (int64_t b = slice; b * kPBlock < n; b += G) {
+  uint32_t kmax = 0u, listed_n = 0u;
+  int it = 0;
+  for (int64_t b = slice; b * kPBlock < n; b += G, ++it) {
     const int p0 = (int)(b * kPBlock);
     float4 v[4];
 #pragma unroll
@@ -363,24 +372,67 @@ __global__ __launch_bounds__(kPruneThreads) void topk_prune_kernel(
         v[u].w = p + 3 < n ? src[p + 3] : 0.f;
       }
     }
+    uint32_t key[4][4], nib[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = p0 + 4 * (tid + kPruneThreads * u);
       const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      uint32_t nib = 0;
+      nib[u] = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t key = p + j < n ? order_key(x[j]) : 0u;
-        kmax = max(kmax, key);
-        nib |= (key >= tau && key != 0u ? 1u : 0u) << j;
+        key[u][j] = p + j < n ? order_key(x[j]) : 0u;
+        kmax = max(kmax, key[u][j]);
+        nib[u] |= (key[u][j] >= tau && key[u][j] != 0u ? 1u : 0u) << j;
       }
-      // the word of positions p0 + 1024u + 32 * (tid / 8) .. + 31 gathers the nibbles of
-      // 8 consecutive lanes
-      const uint32_t word = group8_or(nib << (4 * (tid & 7)));
-      const int wi = (p0 >> 5) + 32 * u + (tid >> 3);
-      if ((tid & 7) == 0 && wi < nwords) mrow[wi] = word;
     }
+    if (!listed) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // the word of positions p0 + 1024u + 32 * (tid / 8) .. + 31 gathers the nibbles of
+        // 8 consecutive lanes
+        const uint32_t word = group8_or(nib[u] << (4 * (tid & 7)));
+        const int wi = (p0 >> 5) + 32 * u + (tid >> 3);
+        if ((tid & 7) == 0 && wi < nwords) mrow[wi] = word;
+      }
+      continue;
+    }
+    // position order in the block is (u, thread, j): candidate (u, t, j) goes after all
+    // those of u' < u and those of threads < t for the same u; the four per-u counts
+    // (at most 4 per thread, 1024 per block) travel as two packed 16-bit pairs
+    const uint32_t c01 = (uint32_t)__popc(nib[0]) | ((uint32_t)__popc(nib[1]) << 16);
+    const uint32_t c23 = (uint32_t)__popc(nib[2]) | ((uint32_t)__popc(nib[3]) << 16);
+    const uint32_t i01 = wave_incl_add(c01), i23 = wave_incl_add(c23);
+    uint32_t* pt = sm.part[it & 1];
+    if (lane == 63) {
+      pt[2 * wave] = i01;
+      pt[2 * wave + 1] = i23;
+    }
+    __syncthreads();
+    uint32_t b01 = 0, b23 = 0, t01 = 0, t23 = 0;
+#pragma unroll
+    for (int w = 0; w < kPruneWaves; ++w) {
+      const uint32_t x = pt[2 * w], y = pt[2 * w + 1];
+      b01 += w < wave ? x : 0u;
+      b23 += w < wave ? y : 0u;
+      t01 += x;
+      t23 += y;
+    }
+    const uint32_t e01 = b01 + i01 - c01, e23 = b23 + i23 - c23;
+    const uint32_t tot0 = t01 & 0xFFFFu, tot1 = t01 >> 16, tot2 = t23 & 0xFFFFu;
+    const uint32_t off[4] = {listed_n + (e01 & 0xFFFFu), listed_n + tot0 + (e01 >> 16),
+                             listed_n + tot0 + tot1 + (e23 & 0xFFFFu),
+                             listed_n + tot0 + tot1 + tot2 + (e23 >> 16)};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t slot = off[u] + (uint32_t)__popc(nib[u] & ((1u << j) - 1u));
+        if (((nib[u] >> j) & 1u) && slot < (uint32_t)kCap)
+          lrow[slot] = make_uint2(key[u][j], (uint32_t)(p0 + 4 * (tid + kPruneThreads * u) + j));
+      }
+    listed_n += (t01 & 0xFFFFu) + (t01 >> 16) + (t23 & 0xFFFFu) + (t23 >> 16);
   }
+  if (listed && tid == 0) lcnt[row] = listed_n;
   kmax = wave_max_u32(kmax);
   if (lane == 0) wm[wave] = kmax;
 }
@@ -463,11 +515,12 @@ __device__ __forceinline__ void select_direct(const float* src, int n, int k, Se
 
 // Stage 2 after the prune kernel (ld > kOnePass), one workgroup per row: rows of at most
 // kCap positions select from registers directly, longer ones from the candidates the prune
-// kernel marked.
+// kernel listed (G == 1) or marked (G > 1).
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
     int* __restrict__ idx, int64_t ld_idx, const uint32_t* __restrict__ mask, int64_t mw,
-    const uint32_t* __restrict__ tau_in, const uint32_t* __restrict__ wmax, int G) {
+    const uint32_t* __restrict__ tau_in, const uint32_t* __restrict__ wmax, int G,
+    const uint32_t* __restrict__ lcnt, const uint2* __restrict__ list) {
   __shared__ __attribute__((aligned(16))) SelSmem sm;
   __shared__ uint32_t cpos[kCap];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -484,8 +537,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     return;
   }
 
-  // candidates from the prune bits: thread t owns the words [t * wpt, (t + 1) * wpt)
   if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
+  if (G == 1) {   // the listed candidates: thread t takes entries 8t .. 8t+7
+    const uint32_t total = lcnt[row], tau = tau_in[row];
+    const uint32_t* w4 = wmax + (int64_t)row * kPruneWaves;
+    const uint32_t hi = max(max(w4[0], w4[1]), max(w4[2], w4[3]));
+    if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
+      uint32_t key[kCR], pos[kCR];
+#pragma unroll
+      for (int r = 0; r < kCR; ++r) {
+        const uint32_t i = (uint32_t)(kCR * tid + r);
+        const uint2 e = i < total ? list[(int64_t)row * kCap + i] : make_uint2(0u, 0u);
+        key[r] = e.x;
+        pos[r] = e.y;
+      }
+      Radix st;
+      const uint32_t theta = select_regs<kCR>(key, total, tau, hi, (uint32_t)k, sm.hist, st);
+      compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
+                   [&](int r, uint32_t slot) { out[slot] = (int)pos[r]; });
+      return;
+    }
+    select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
+    return;
+  }
+  // candidates from the prune bits: thread t owns the words [t * wpt, (t + 1) * wpt)
   const uint32_t* mrow = mask + (int64_t)row * mw;
   const int nwords = (n + 31) >> 5;
   const int wpt = (nwords + kSelThreads - 1) / kSelThreads;
@@ -665,16 +740,44 @@ int prune_slices(int rows, int64_t ld) {
 
 int64_t mask_words(int64_t ld) { return ((ld + 31) / 32 + 3) / 4 * 4; }
 
-size_t tau_words(int rows) { return ((size_t)rows + 3) / 4 * 4; }
+size_t pad4(size_t words) { return (words + 3) / 4 * 4; }
+
+// Workspace of the prune + select kernels (words): tau [rows] | wmax [rows][G][4] | then
+// G > 1: mask [rows][mask_words]; G == 1: lcnt [rows] | list [rows][kCap] (key, position).
+struct TopkWs {
+  uint32_t *tau, *wmax, *mask, *lcnt;
+  uint2* list;
+  size_t words;
+};
+
+TopkWs topk_ws(void* base, int rows, int64_t ld) {
+  const int G = prune_slices(rows, ld);
+  uint32_t* p = (uint32_t*)base;
+  TopkWs w{};
+  size_t o = 0;
+  w.tau = p ? p + o : nullptr;
+  o += pad4((size_t)rows);
+  w.wmax = p ? p + o : nullptr;
+  o += (size_t)rows * G * kPruneWaves;
+  if (G > 1) {
+    w.mask = p ? p + o : nullptr;
+    o += (size_t)rows * mask_words(ld);
+  } else {
+    w.lcnt = p ? p + o : nullptr;
+    o += pad4((size_t)rows);
+    w.list = p ? reinterpret_cast<uint2*>(p + o) : nullptr;
+    o += (size_t)rows * kCap * 2;
+  }
+  w.words = o;
+  return w;
+}
 
 }  // namespace
 
-// mask [rows][mask_words] | tau [rows] (padded to 16 bytes) | wmax [rows][G][4]
 size_t topk_workspace_bytes(int rows, int64_t ld, int k) {
   (void)k;
   if (ld <= kOnePass || rows <= 0) return 0;
-  const size_t G = (size_t)prune_slices(rows, ld);
-  return ((size_t)rows * mask_words(ld) + tau_words(rows) + (size_t)rows * G * kPruneWaves) * 4;
+  return topk_ws(nullptr, rows, ld).words * 4;
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
@@ -686,19 +789,18 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   }
   const int G = prune_slices(a.rows, a.ld);
   const int64_t mw = mask_words(a.ld);
-  uint32_t* mask = (uint32_t*)a.ws;
-  uint32_t* tau = mask + (size_t)a.rows * mw;
-  uint32_t* wmax = tau + tau_words(a.rows);
+  const TopkWs w = topk_ws(a.ws, a.rows, a.ld);
   {
     const KernelEvents ev("topk_prune_kernel");
     hipExtLaunchKernelGGL(topk_prune_kernel, dim3(a.rows, G), dim3(kPruneThreads), 0, stream, ev.start,
-                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, mask, mw, tau, wmax);
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, w.mask, mw, w.tau, w.wmax,
+                          w.lcnt, w.list);
   }
   {
     const KernelEvents ev("topk_select_kernel");
     hipExtLaunchKernelGGL(topk_select_kernel, dim3(a.rows), dim3(kSelThreads), 0, stream, ev.start,
-                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, mask,
-                          mw, tau, wmax, G);
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, w.mask,
+                          mw, w.tau, w.wmax, G, w.lcnt, w.list);
   }
   return hipGetLastError();
 }

@@ -230,15 +230,15 @@ def test_topk_adversarial(k):
     _topk_case(np.stack(rows), nv, k)
 
 
-@pytest.mark.parametrize("rows", [300, 2500])
-def test_topk_many_rows(rows):
+@pytest.mark.parametrize("rows,ld", [(300, 20000), (300, 40000), (2500, 40000)])
+def test_topk_many_rows(rows, ld):
     # relu-weighted sums like indexer scores, ragged lengths across the direct / pruned
-    # boundary; 300 rows prune with several workgroups per row, 2500 with one
-    rng = np.random.default_rng(rows)
-    ld = 20000
+    # boundaries; ld <= 32768 selects in one kernel, otherwise 300 rows prune with several
+    # workgroups per row (candidate bits) and 2500 with one (candidate lists)
+    rng = np.random.default_rng(rows + ld)
     sc = np.maximum(rng.standard_normal((rows, ld)), 0.0) + 0.5 * np.maximum(rng.standard_normal((rows, ld)), 0.0)
     nv = rng.integers(0, ld + 1, rows)
-    nv[:4] = [ld, 8192, 8193, 2048]
+    nv[:6] = [min(x, ld) for x in (ld, 8192, 8193, 2048, 32768, 32769)]
     _topk_case(sc, nv.tolist(), 2048)
 
 
