@@ -326,7 +326,7 @@ struct PruneSmem {
 //          (key, position) pairs list[row][0 .. 8191] and their number lcnt[row] (pairs past
 //          8192 are counted, not stored).  Each block's candidates take their places
 //          from one block scan of packed per-thread counts.
-__global__ __launch_bounds__(kPruneThreads) void topk_prune_kernel(
+__global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
     uint32_t* __restrict__ mask, int64_t mw, uint32_t* __restrict__ tau_out,
     uint32_t* __restrict__ wmax, uint32_t* __restrict__ lcnt, uint2* __restrict__ list) {
@@ -515,8 +515,9 @@ __device__ __forceinline__ void select_direct(const float* src, int n, int k, Se
 
 // Stage 2 after the prune kernel (ld > kOnePass), one workgroup per row: rows of at most
 // kCap positions select from registers directly, longer ones from the candidates the prune
-// kernel listed (G == 1) or marked (G > 1).
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+// kernel listed (kListed: G == 1; two workgroups fit a CU) or marked (G > 1).
+template <bool kListed>
+__global__ __launch_bounds__(kSelThreads, kListed ? 8 : 1) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
     int* __restrict__ idx, int64_t ld_idx, const uint32_t* __restrict__ mask, int64_t mw,
     const uint32_t* __restrict__ tau_in, const uint32_t* __restrict__ wmax, int G,
@@ -538,7 +539,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
 
   if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
-  if (G == 1) {   // the listed candidates: thread t takes entries 8t .. 8t+7
+  if (kListed) {   // the listed candidates: thread t takes entries 8t .. 8t+7
     const uint32_t total = lcnt[row], tau = tau_in[row];
     const uint32_t* w4 = wmax + (int64_t)row * kPruneWaves;
     const uint32_t hi = max(max(w4[0], w4[1]), max(w4[2], w4[3]));
@@ -551,12 +552,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         key[r] = e.x;
         pos[r] = e.y;
       }
+      __syncthreads();   // hist[0] is clear before the first level adds to it
       Radix st;
       const uint32_t theta = select_regs<kCR>(key, total, tau, hi, (uint32_t)k, sm.hist, st);
       compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
                    [&](int r, uint32_t slot) { out[slot] = (int)pos[r]; });
       return;
     }
+    __syncthreads();   // as above
     select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
     return;
   }
@@ -798,9 +801,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   }
   {
     const KernelEvents ev("topk_select_kernel");
-    hipExtLaunchKernelGGL(topk_select_kernel, dim3(a.rows), dim3(kSelThreads), 0, stream, ev.start,
-                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, w.mask,
-                          mw, w.tau, w.wmax, G, w.lcnt, w.list);
+    hipExtLaunchKernelGGL(G == 1 ? topk_select_kernel<true> : topk_select_kernel<false>, dim3(a.rows),
+                          dim3(kSelThreads), 0, stream, ev.start, ev.stop, 0, a.scores, a.ld, a.n_valid,
+                          a.n_add, a.k, a.idx, a.ld_idx, w.mask, mw, w.tau, w.wmax, G, w.lcnt, w.list);
   }
   return hipGetLastError();
 }
