@@ -282,6 +282,11 @@ __device__ __forceinline__ void read_decode_q(DecodeQ& f, const uint8_t* stage) 
   }
 }
 
+// kNtScores: the scores leave with non-temporal stores (many tokens: they would otherwise
+// displace cache lines that the key stream and the next kernels use; measured 8 us slower
+// at 40 x 128K).  With few tokens plain stores keep them cached for the top-k kernel that
+// reads them next (1 us faster at one token of 32K).
+template <bool kNtScores>
 __global__ __launch_bounds__(64) void indexer_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ pool,
     int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
@@ -360,21 +365,30 @@ __global__ __launch_bounds__(64) void indexer_decode_kernel(
       score_slice(sl + 1);
     }
   }
-  // the range's scores leave in one burst of non-temporal stores (16 bytes per lane when
-  // the row is 16-byte aligned)
+  // the range's scores leave in one burst (16 bytes per lane when the row is 16-byte
+  // aligned)
   __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
   float* dst = scores + (int64_t)t * ld + key0;
   const int cnt = key_end - key0;
+  auto put4 = [&](int i) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&sc[i]);
+    if (kNtScores) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(&dst[i]));
+    else *reinterpret_cast<f32x4*>(&dst[i]) = v;
+  };
+  auto put1 = [&](int i) {
+    if (kNtScores) __builtin_nontemporal_store(sc[i], &dst[i]);
+    else dst[i] = sc[i];
+  };
   if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
     for (int i = 4 * lane; i < cnt; i += 4 * kWave) {
       if (i + 4 <= cnt) {
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sc[i]), reinterpret_cast<f32x4*>(&dst[i]));
+        put4(i);
       } else {
-        for (int j = i; j < cnt; ++j) __builtin_nontemporal_store(sc[j], &dst[j]);
+        for (int j = i; j < cnt; ++j) put1(j);
       }
     }
   } else {
-    for (int i = lane; i < cnt; i += kWave) __builtin_nontemporal_store(sc[i], &dst[i]);
+    for (int i = lane; i < cnt; i += kWave) put1(i);
   }
 }
 
@@ -419,6 +433,9 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
   scores[(int64_t)t * ld + s] = acc + 0.0f;
 }
 
+// Decode scores of at most this many bytes per call stay in the caches (plain stores).
+constexpr int64_t kCachedScoresMax = 4 << 20;
+
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
@@ -443,9 +460,11 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
       int range = kMaxRange;
       while (range > 64 && (int64_t)a.T * ((max_keys + range - 1) / range) < 8192) range >>= 1;
       dim3 grid((max_keys + range - 1) / range, a.T);
+      const bool nt = (int64_t)a.T * max_keys * 4 > kCachedScoresMax;
       {
         const KernelEvents ev("indexer_decode_kernel");
-        hipExtLaunchKernelGGL(indexer_decode_kernel, grid, dim3(64), 0, stream, ev.start, ev.stop,
+        hipExtLaunchKernelGGL(nt ? indexer_decode_kernel<true> : indexer_decode_kernel<false>, grid,
+                              dim3(64), 0, stream, ev.start, ev.stop,
                               0, (const uint8_t*)a.q_idx, a.w, (const uint8_t*)a.pool, a.num_blocks,
                               a.block_table, a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos,
                               range, a.scores, a.ld);
