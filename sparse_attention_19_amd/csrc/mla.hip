@@ -501,10 +501,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 // grid (T, H, Z); one wave per (token, head) and 1/Z of the output dims, in kNP passes of
 // 64 dims (Z = kPasses / kNP).  Lane 16a + c handles dims 4c..4c+3 of each pass for the
 // splits a, a + 4, ...; lane s also reads split s's (m_s, l_s).  Every load of the wave is
-// issued before the first is used (one memory round trip): its slots (split, pass) are
-// registers, kCombSlots at a time.  The four split groups (the wave's four 16-lane rows)
-// are summed with row-swap lane moves, no LDS.  Requires splits <= 64 and
-// Dl == 64 * kPasses.
+// issued before the first is used (one memory round trip): its (split, pass) slots are
+// registers.  The four split groups (the wave's four 16-lane rows) are summed with
+// row-swap lane moves, no LDS.  Requires splits <= 64, ceil(splits / 4) * kNP <=
+// kCombSlots and Dl == 64 * kPasses.
 constexpr int kPasses = kDl / 64;
 constexpr int kCombSlots = 8;
 
@@ -513,8 +513,8 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
                                                          const float* __restrict__ ws_ml, int splits,
                                                          int H, uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
-  static_assert(kCombSlots % kNP == 0, "whole splits per slot batch");
-  constexpr int kSPB = kCombSlots / kNP;   // splits per slot batch
+  static_assert(kCombSlots % kNP == 0, "whole splits per lane");
+  constexpr int kSPL = kCombSlots / kNP;   // splits per lane, at most
   const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int pass0 = blockIdx.z * kNP;
   const int a = lane >> 4, c = lane & 15;
@@ -528,9 +528,9 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
     ms = ml.x;
     ls = ml.y;
   }
-  float4 v[kSPB][kNP];
+  float4 v[kSPL][kNP];
 #pragma unroll
-  for (int i = 0; i < kSPB; ++i)
+  for (int i = 0; i < kSPL; ++i)
 #pragma unroll
     for (int p = 0; p < kNP; ++p)
       v[i][p] = i < nsp ? *reinterpret_cast<const float4*>(src + i * sstride + 64 * p)
@@ -547,26 +547,16 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
   float4 acc[kNP];
 #pragma unroll
   for (int p = 0; p < kNP; ++p) acc[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0;;) {
 #pragma unroll
-    for (int i = 0; i < kSPB; ++i) {
-      const float w = __shfl(wl, min(a + 4 * (i0 + i), 63), kWave);   // 0 past the last split
+  for (int i = 0; i < kSPL; ++i) {
+    const float w = __shfl(wl, min(a + 4 * i, 63), kWave);   // 0 past the last split
 #pragma unroll
-      for (int p = 0; p < kNP; ++p) {
-        acc[p].x = fmaf(w, v[i][p].x, acc[p].x);
-        acc[p].y = fmaf(w, v[i][p].y, acc[p].y);
-        acc[p].z = fmaf(w, v[i][p].z, acc[p].z);
-        acc[p].w = fmaf(w, v[i][p].w, acc[p].w);
-      }
+    for (int p = 0; p < kNP; ++p) {
+      acc[p].x = fmaf(w, v[i][p].x, acc[p].x);
+      acc[p].y = fmaf(w, v[i][p].y, acc[p].y);
+      acc[p].z = fmaf(w, v[i][p].z, acc[p].z);
+      acc[p].w = fmaf(w, v[i][p].w, acc[p].w);
     }
-    i0 += kSPB;
-    if (i0 >= (splits + 3) / 4) break;   // more splits than registers: the next batch
-#pragma unroll
-    for (int i = 0; i < kSPB; ++i)
-#pragma unroll
-      for (int p = 0; p < kNP; ++p)
-        v[i][p] = i0 + i < nsp ? *reinterpret_cast<const float4*>(src + (i0 + i) * sstride + 64 * p)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   uint16_t* dst = out + ((int64_t)t * H + h) * kDl + 64 * pass0 + 4 * c;
 #pragma unroll
@@ -661,6 +651,17 @@ int mla_splits(int T, int k, bool bf16) {
   return s < tiles ? s : tiles;
 }
 
+// The combine splits the output dims over Z workgroups per (token, head) until ~2048 are
+// in flight, and until a lane's (split, pass) slots fit in registers (always by Z = 8 for
+// splits <= 32).
+int combine_slices(int T, int splits) {
+  int Z = 1;
+  while (Z < kPasses && ((int64_t)T * kH * Z < 2048 || (splits + 3) / 4 * (kPasses / Z) > kCombSlots))
+    Z *= 2;
+  return Z;
+}
+static_assert((32 + 3) / 4 * 1 <= kCombSlots, "32 splits fit at Z = kPasses");
+
 size_t mla_workspace_bytes(int T, int k, int H, int Dl, bool bf16) {
   const int s = mla_splits(T, k, bf16);
   if (s <= 1) return 0;
@@ -681,11 +682,7 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
                             a.sm_scale * kLog2e, splits, (uint16_t*)a.out, a.lse, ws_o, ws_ml);
     }
     if (splits > 1) {
-      // split the output dims over Z workgroups per (token, head) until ~2048 are in flight
-      // (and until a lane's (split, pass) slots fit in registers at once)
-      int Z = 1;
-      while (Z < kPasses && ((int64_t)a.T * kH * Z < 2048 || (splits + 3) / 4 * (kPasses / Z) > kCombSlots))
-        Z *= 2;
+      const int Z = combine_slices(a.T, splits);
       const KernelEvents ev("mla_combine_kernel");
       const dim3 grid(a.T, kH, Z);
       switch (kPasses / Z) {
