@@ -326,6 +326,7 @@ struct PruneSmem {
 //          (key, position) pairs list[row][0 .. 8191] and their number lcnt[row] (pairs past
 //          8192 are counted, not stored).  Each block's candidates take their places
 //          from one block scan of packed per-thread counts.
+template <bool kListed>
 __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
     uint32_t* __restrict__ mask, int64_t mw, uint32_t* __restrict__ tau_out,
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
                                                                   sm.red, &unused);
   if (slice == 0 && tid == 0) tau_out[row] = tau;
 
-  const bool listed = G == 1;
+  constexpr bool listed = kListed;   // G == 1: the scores are read once, non-temporally
   uint32_t* mrow = mask + (int64_t)row * mw;
   uint2* lrow = list + (int64_t)row * kCap;
   const int nwords = (n + 31) >> 5;
@@ -364,7 +365,12 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
     for (int u = 0; u < 4; ++u) {
       const int p = p0 + 4 * (tid + kPruneThreads * u);
       if (vec && p + 3 < n) {
-        v[u] = *reinterpret_cast<const float4*>(src + p);
+        if (listed) {
+          const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + p));
+          v[u] = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+          v[u] = *reinterpret_cast<const float4*>(src + p);
+        }
       } else {
         v[u].x = p < n ? src[p] : 0.f;
         v[u].y = p + 1 < n ? src[p + 1] : 0.f;
@@ -795,9 +801,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const TopkWs w = topk_ws(a.ws, a.rows, a.ld);
   {
     const KernelEvents ev("topk_prune_kernel");
-    hipExtLaunchKernelGGL(topk_prune_kernel, dim3(a.rows, G), dim3(kPruneThreads), 0, stream, ev.start,
-                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, w.mask, mw, w.tau, w.wmax,
-                          w.lcnt, w.list);
+    hipExtLaunchKernelGGL(G == 1 ? topk_prune_kernel<true> : topk_prune_kernel<false>, dim3(a.rows, G),
+                          dim3(kPruneThreads), 0, stream, ev.start, ev.stop, 0, a.scores, a.ld, a.n_valid,
+                          a.n_add, a.k, w.mask, mw, w.tau, w.wmax, w.lcnt, w.list);
   }
   {
     const KernelEvents ev("topk_select_kernel");
