@@ -242,6 +242,44 @@ def test_topk_many_rows(rows, ld):
     _topk_case(sc, nv.tolist(), 2048)
 
 
+def _adversarial_rows(rng, ld, k):
+    """Rows that defeat the sampled bound (ties, two values, winners at the end) next to
+    ordinary ones."""
+    return [
+        (np.full(ld, 3.0), ld),                                               # all equal
+        (rng.integers(0, 2, ld).astype(np.float64), ld),                     # two values
+        (np.where(np.arange(ld) > ld - k - 3, 5.0, 1.0), ld),                # winners at the end
+        (np.where(np.arange(ld) % 7 == 0, 2.0, 1.0), ld),                    # periodic ties
+        (rng.standard_normal(ld), ld),                                       # distinct values
+        (rng.integers(0, 50, ld).astype(np.float64), ld - 3),                # ragged length
+    ]
+
+
+@pytest.mark.parametrize("ld", [40000, 40001])
+def test_topk_listed_rows_adversarial(ld):
+    # 2048 rows: one prune workgroup per row, candidates listed; most rows short (dense or
+    # direct), a few adversarial ones of full length.  ld = 40001 leaves the rows unaligned
+    # (scalar loads)
+    rng = np.random.default_rng(ld)
+    rows = 2048
+    sc = rng.integers(0, 100, (rows, ld)).astype(np.float32)
+    nv = rng.integers(0, 9000, rows)
+    for i, (r, n) in enumerate(_adversarial_rows(rng, ld, 2048)):
+        sc[100 * i + 7] = r
+        nv[100 * i + 7] = n
+    _topk_case(sc, nv.tolist(), 2048)
+
+
+@pytest.mark.parametrize("ld", [30001, 40001])
+def test_topk_unaligned_rows(ld):
+    # rows not 16-byte aligned: the one-pass kernel (ld <= 32768) and the bit-marking prune
+    rng = np.random.default_rng(ld)
+    cases = _adversarial_rows(rng, ld, 64)
+    sc = np.stack([r for r, _ in cases] + [rng.integers(0, 1000, ld).astype(np.float64)])
+    nv = [n for _, n in cases] + [ld - 1]
+    _topk_case(sc, nv, 64)
+
+
 def test_topk_long_rows_ties():
     rng = np.random.default_rng(5)
     ld = 131072
