@@ -56,15 +56,17 @@ constexpr int kSamples = 4 * kRuns;              // 2048
 constexpr int kSamplesPerThread = kSamples / kPruneThreads;   // 8: two runs
 constexpr int kSampleMargin = 768;               // candidates aimed for above 2k
 constexpr int kBins = 256;
-constexpr int kHistWords = kBins + kWave;        // + one dummy word per lane
+constexpr int kHistWords = kBins;
 constexpr int kPruneTarget = 2048;               // prune workgroups aimed for per launch
 static_assert(kPBlock == 16 * kPruneThreads, "four float4 per thread per block");
 static_assert(kSamplesPerThread == 8, "two sample runs per thread");
 static_assert(kHistWords % 4 == 0 && kHistWords / 4 <= kPruneThreads, "histogram clears");
 
+// Negative values: all bits flipped; others: the sign bit set.  (x + 0.0f folds -0.0 into
+// +0.0.)
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ int row_len(const int* n_valid, int n_add, int64_t ld, int row) {
@@ -86,13 +88,13 @@ __device__ __forceinline__ uint32_t group8_or(uint32_t v) {
 }
 
 // One radix level's histogram: key goes to bin (key - L) >> shift when it lies in
-// [L, L + 2^W) (L >= 1, so empty entries -- key 0 -- never count); keys out of range go to
-// a per-lane dummy word past the bins.  rmask = 2^W - 1 (all ones for W = 32).
+// [L, L + 2^W) (L >= 1, so empty entries -- key 0 -- never count); keys out of range add
+// nothing (after the first level that is most of them, and their lanes sit out the atomic).
+// rmask = 2^W - 1 (all ones for W = 32).
 __device__ __forceinline__ void hist_add(uint32_t key, uint32_t L, uint32_t rmask, int shift,
                                          uint32_t* hist) {
   const uint32_t d = key - L;
-  const bool in = key >= L && d <= rmask;
-  atomicAdd(&hist[in ? (d >> shift) : (uint32_t)(kBins + (threadIdx.x & 63))], 1u);
+  if (key >= L && d <= rmask) atomicAdd(&hist[d >> shift], 1u);
 }
 
 __device__ __forceinline__ uint32_t range_mask(int W) { return W >= 32 ? 0xFFFFFFFFu : (1u << W) - 1u; }
@@ -187,14 +189,10 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   const uint32_t incl = wave_incl_add(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const uint32_t x = wsum[w];
-    before += (w < wave) ? x : 0u;
-    tot += x;
-  }
-  *total = tot;
+  // the wave totals, scanned once more across lanes 0..15 (wave-uniform results)
+  const uint32_t xi = wave_incl_add(lane < kSelWaves ? wsum[lane] : 0u);
+  const uint32_t before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)xi, wave - 1) : 0u;
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)xi, kSelWaves - 1);
   return before + incl - v;
 }
 
@@ -230,7 +228,7 @@ __device__ __forceinline__ uint32_t compact(const uint32_t (&key)[R], uint32_t t
   return total;
 }
 
-// ------------------------------------------------------------------ prune
+// ------------------------------------------------------------------ samples
 
 // Sample run i (of 512) of a row of n > kCap positions: positions
 // 4 * floor(i * floor(n / 4) / 512) .. + 3, evenly spaced and inside the row.
@@ -263,7 +261,7 @@ __device__ __forceinline__ uint32_t sample_rank(int k, int n) {
 // the bin that holds the rank-th largest sample after two 8-bit radix levels over the
 // samples' [min, max].  Every workgroup of the row computes the same value.  `extra` is
 // maximised over the block alongside (*xmax).  Clears and uses hist[0] and hist[1]; three
-// barriers.  kWavesB: waves in the block (at most kSelWaves).
+// barriers, for LDS only: global loads issued before the call stay in flight.  kWavesB: waves in the block (at most kSelWaves).
 template <int kWavesB, int S>
 __device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t rank, uint32_t extra,
                                                uint32_t (*hist)[kHistWords], uint32_t (*red)[2 * kSelWaves],
@@ -285,7 +283,7 @@ __device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t 
     red[1][wave] = mx;
     red[1][kWavesB + wave] = extra;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t L = 0xFFFFFFFFu, hi = 0u, xm = 0u;
 #pragma unroll
   for (int w = 0; w < kWavesB; ++w) {
@@ -300,7 +298,7 @@ __device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t 
     const uint32_t rmask = range_mask(W);
 #pragma unroll
     for (int r = 0; r < S; ++r) hist_add(s[r], L, rmask, shift, hist[level]);
-    __syncthreads();
+    lds_barrier();
     uint32_t bin, above;
     find_bin(hist[level], rank, &bin, &above);
     rank -= above;
@@ -667,29 +665,41 @@ __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
     select_direct(src, n, k, sm, out);
     return;
   }
-  // coalesced 16-byte loads (float4 i4 = tid + 1024u) into the padded copy
+  // The samples load first and tau comes from them while the row's 16-byte loads (float4
+  // i4 = tid + 1024u, coalesced) are still in flight: loads complete in order, and the
+  // sample levels' barriers wait for LDS only.
   const bool vec = ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0) && (ld & 3) == 0;
-  {
-    float4 v[kR1 / 4];
+  uint32_t smp[4] = {0u, 0u, 0u, 0u};
+  if (tid < kRuns) load_run(src, sample_pos(tid, n), vec, smp);
+  __builtin_amdgcn_sched_barrier(0);
+  float4 v[kR1 / 4];
 #pragma unroll
-    for (int u = 0; u < kR1 / 4; ++u) {
-      const int p = 4 * (tid + kSelThreads * u);
-      if (vec && p + 3 < n) {
-        v[u] = *reinterpret_cast<const float4*>(src + p);
-      } else {
-        v[u].x = p < n ? src[p] : 0.f;
-        v[u].y = p + 1 < n ? src[p + 1] : 0.f;
-        v[u].z = p + 2 < n ? src[p + 2] : 0.f;
-        v[u].w = p + 3 < n ? src[p + 3] : 0.f;
-      }
+  for (int u = 0; u < kR1 / 4; ++u) {
+    const int p = 4 * (tid + kSelThreads * u);
+    if (vec && p + 3 < n) {
+      v[u] = *reinterpret_cast<const float4*>(src + p);
+    } else {
+      v[u].x = p < n ? src[p] : 0.f;
+      v[u].y = p + 1 < n ? src[p + 1] : 0.f;
+      v[u].z = p + 2 < n ? src[p + 2] : 0.f;
+      v[u].w = p + 3 < n ? src[p + 3] : 0.f;
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t unused;
+  const uint32_t tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), 0u, sm.hist, sm.red, &unused);
+  // the keys into the padded copy
 #pragma unroll
-    for (int u = 0; u < kR1 / 4; ++u) {
-      const int p = 4 * (tid + kSelThreads * u);
-      *reinterpret_cast<uint4*>(&pad[pad_word(p)]) =
-          make_uint4(p < n ? order_key(v[u].x) : 0u, p + 1 < n ? order_key(v[u].y) : 0u,
-                     p + 2 < n ? order_key(v[u].z) : 0u, p + 3 < n ? order_key(v[u].w) : 0u);
+  for (int u = 0; u < kR1 / 4; ++u) {
+    const int p = 4 * (tid + kSelThreads * u);
+    uint4 q;
+    if (p + 3 < n) {
+      q = make_uint4(order_key(v[u].x), order_key(v[u].y), order_key(v[u].z), order_key(v[u].w));
+    } else {
+      q = make_uint4(p < n ? order_key(v[u].x) : 0u, p + 1 < n ? order_key(v[u].y) : 0u,
+                     p + 2 < n ? order_key(v[u].z) : 0u, 0u);
     }
+    *reinterpret_cast<uint4*>(&pad[pad_word(p)]) = q;
   }
   __syncthreads();
   uint32_t key[kR1];
@@ -703,23 +713,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
     key[4 * u + 3] = q.w;
     mx = max(max(mx, max(q.x, q.y)), max(q.z, q.w));
   }
-  uint32_t smp[4] = {0u, 0u, 0u, 0u};
-  if (tid < kRuns) {
-    const uint4 q = *reinterpret_cast<const uint4*>(&pad[pad_word(sample_pos(tid, n))]);
-    smp[0] = q.x;
-    smp[1] = q.y;
-    smp[2] = q.z;
-    smp[3] = q.w;
-  }
-  uint32_t hi;
-  const uint32_t tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), mx, sm.hist, sm.red, &hi);
-  uint32_t cm = 0;
+  uint32_t cm = 0;   // bit r: key r >= tau (tau >= 1)
 #pragma unroll
-  for (int r = 0; r < kR1; ++r) cm |= (key[r] >= tau ? 1u : 0u) << r;   // tau >= 1
-  // hist[0]'s last readers finished before the second sample level's barrier
+  for (int r = kR1 - 1; r >= 0; --r) cm = cm + cm + (uint32_t)(key[r] >= tau);
+  // hist[0]'s last readers finished before the second sample level's barrier; the row max
+  // travels with the candidate scan (red's readers finished before the same barrier)
   if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) sm.red[1][tid >> 6] = mx;
   uint32_t total;
   uint32_t off = block_excl_scan((uint32_t)__popc(cm), sm.wsum[0], &total);
+  uint32_t hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) hi = max(hi, sm.red[1][w]);
   if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
     for (uint32_t m = cm; m; m &= m - 1u, ++off)
       cpos[cpos_half((int)off)] = (uint16_t)(kR1 * tid + __ffs(m) - 1);
