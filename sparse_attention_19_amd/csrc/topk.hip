@@ -112,17 +112,12 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rank, ui
   const uint32_t excl = incl - local;
   const uint64_t hit = __ballot(excl < rank && rank <= incl);
   const int f = max(__ffsll((unsigned long long)hit) - 1, 0);
-  uint32_t b = 0, a = 0, run = excl;
-  bool found = false;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (!found && run + c[q] >= rank) {
-      b = (uint32_t)(kBins - 1 - 4 * lane - q);
-      a = run;
-      found = true;
-    }
-    if (!found) run += c[q];
-  }
+  // in the hit lane: the rank lies in the first of its bins q whose running count reaches
+  // it, q = the number of bins that stay below it
+  const uint32_t r1 = excl + c[0], r2 = r1 + c[1], r3 = r2 + c[2];
+  const uint32_t q = (r1 < rank ? 1u : 0u) + (r2 < rank ? 1u : 0u) + (r3 < rank ? 1u : 0u);
+  const uint32_t a = r3 < rank ? r3 : (r2 < rank ? r2 : (r1 < rank ? r1 : excl));
+  const uint32_t b = (uint32_t)(kBins - 1 - 4 * lane) - q;
   *bin = (uint32_t)__builtin_amdgcn_readlane((int)b, f);
   *above = (uint32_t)__builtin_amdgcn_readlane((int)a, f);
 }
@@ -259,13 +254,12 @@ __device__ __forceinline__ uint32_t sample_rank(int k, int n) {
 
 // tau of one row from its 2048 samples (S per thread, 0 = no sample): the lower edge of
 // the bin that holds the rank-th largest sample after two 8-bit radix levels over the
-// samples' [min, max].  Every workgroup of the row computes the same value.  `extra` is
-// maximised over the block alongside (*xmax).  Clears and uses hist[0] and hist[1]; three
-// barriers, for LDS only: global loads issued before the call stay in flight.  kWavesB: waves in the block (at most kSelWaves).
+// samples' [min, max].  Every workgroup of the row computes the same value.  Clears and
+// uses hist[0] and hist[1]; three barriers, for LDS only: global loads issued before the
+// call stay in flight.  kWavesB: waves in the block (at most kSelWaves).
 template <int kWavesB, int S>
-__device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t rank, uint32_t extra,
-                                               uint32_t (*hist)[kHistWords], uint32_t (*red)[2 * kSelWaves],
-                                               uint32_t* xmax) {
+__device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t rank,
+                                               uint32_t (*hist)[kHistWords], uint32_t (*red)[kSelWaves]) {
   static_assert(kWavesB <= kSelWaves, "reduction slots");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -276,22 +270,15 @@ __device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t 
   }
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
-  extra = wave_max_u32(extra);
   if (tid < 2 * kHistWords / 4) reinterpret_cast<uint4*>(&hist[0][0])[tid] = make_uint4(0, 0, 0, 0);
   if (lane == 0) {
     red[0][wave] = mn;
     red[1][wave] = mx;
-    red[1][kWavesB + wave] = extra;
   }
   lds_barrier();
-  uint32_t L = 0xFFFFFFFFu, hi = 0u, xm = 0u;
-#pragma unroll
-  for (int w = 0; w < kWavesB; ++w) {
-    L = min(L, red[0][w]);
-    hi = max(hi, red[1][w]);
-    xm = max(xm, red[1][kWavesB + w]);
-  }
-  *xmax = xm;
+  // lane w < kWavesB reads wave w's partials; one more wave reduction combines them
+  uint32_t L = wave_min_u32(lane < kWavesB ? red[0][lane] : 0xFFFFFFFFu);
+  const uint32_t hi = wave_max_u32(lane < kWavesB ? red[1][lane] : 0u);
   int W = range_bits(L, hi);
   for (int level = 0; level < 2 && W > 0; ++level) {
     const int shift = W > 8 ? W - 8 : 0;
@@ -312,7 +299,7 @@ __device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t 
 
 struct PruneSmem {
   uint32_t hist[2][kHistWords];
-  uint32_t red[2][2 * kSelWaves];   // [0]: per-wave minima; [1]: maxima, then the extra maxima
+  uint32_t red[2][kSelWaves];   // per-wave minima and maxima
   uint32_t part[2][2 * kPruneWaves];   // list mode: per-wave packed counts (alternating blocks)
 };
 
@@ -345,9 +332,7 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
   uint32_t s[kSamplesPerThread];
   load_run(src, sample_pos(tid, n), vec, s);
   load_run(src, sample_pos(tid + kPruneThreads, n), vec, s + 4);
-  uint32_t unused;
-  const uint32_t tau = sample_tau<kPruneWaves, kSamplesPerThread>(s, sample_rank(k, n), 0u, sm.hist,
-                                                                  sm.red, &unused);
+  const uint32_t tau = sample_tau<kPruneWaves, kSamplesPerThread>(s, sample_rank(k, n), sm.hist, sm.red);
   if (slice == 0 && tid == 0) tau_out[row] = tau;
 
   constexpr bool listed = kListed;   // G == 1: the scores are read once, non-temporally
@@ -446,7 +431,7 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
 struct SelSmem {
   uint32_t hist[3][kHistWords];
   uint32_t wsum[2][kSelWaves];
-  uint32_t red[2][2 * kSelWaves];   // as in PruneSmem
+  uint32_t red[2][kSelWaves];   // per-wave minima and maxima
 };
 
 // Exact top-k of a whole row streamed from memory (valid keys in [1, hi], k < n): radix
@@ -505,12 +490,8 @@ __device__ __forceinline__ void select_direct(const float* src, int n, int k, Se
     sm.red[1][wave] = mx;
   }
   __syncthreads();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    lo = min(lo, sm.red[0][w]);
-    hi = max(hi, sm.red[1][w]);
-  }
+  const uint32_t lo = wave_min_u32(lane < kSelWaves ? sm.red[0][lane] : 0xFFFFFFFFu);
+  const uint32_t hi = wave_max_u32(lane < kSelWaves ? sm.red[1][lane] : 0u);
   Radix st;
   const uint32_t theta = select_regs<kCR>(key, (uint32_t)n, lo, hi, (uint32_t)k, sm.hist, st);
   compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
@@ -591,9 +572,7 @@ __global__ __launch_bounds__(kSelThreads, kListed ? 8 : 1) void topk_select_kern
   if (lane == 0) sm.red[1][wave] = mx;
   uint32_t total;
   uint32_t off = block_excl_scan(cnt, sm.wsum[0], &total);
-  uint32_t hi = 0u;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) hi = max(hi, sm.red[1][w]);
+  const uint32_t hi = wave_max_u32(lane < kSelWaves ? sm.red[1][lane] : 0u);
 
   if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
     // the candidates' positions in order, then their keys (8 per thread)
@@ -686,8 +665,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t unused;
-  const uint32_t tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), 0u, sm.hist, sm.red, &unused);
+  const uint32_t tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), sm.hist, sm.red);
   // the keys into the padded copy
 #pragma unroll
   for (int u = 0; u < kR1 / 4; ++u) {
@@ -723,9 +701,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
   if ((tid & 63) == 0) sm.red[1][tid >> 6] = mx;
   uint32_t total;
   uint32_t off = block_excl_scan((uint32_t)__popc(cm), sm.wsum[0], &total);
-  uint32_t hi = 0u;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) hi = max(hi, sm.red[1][w]);
+  const uint32_t hi = wave_max_u32((tid & 63) < kSelWaves ? sm.red[1][tid & 63] : 0u);
   if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
     for (uint32_t m = cm; m; m &= m - 1u, ++off)
       cpos[cpos_half((int)off)] = (uint16_t)(kR1 * tid + __ffs(m) - 1);
