@@ -359,7 +359,11 @@ def summarize_traffic(args):
     f_kib = sum(fetch.values()) / len(fetch)
     w_kib = sum(write.values()) / len(write)
     traffic = (f_kib * f_fac + w_kib * w_fac) * 1024.0
-    alg, _ = algorithmic(cfg, kernels_seen={"mla_combine_kernel"} if args.combine else set())
+    seen = {"mla_combine_kernel"} if args.combine else set()
+    # rows longer than 32768 positions (ld = the longest context) go through the prune kernel
+    if -(-max(workload_sizes(cfg)[1]) // 64) * 64 > 32768:
+        seen.add("topk_prune_kernel")
+    alg, _ = algorithmic(cfg, kernels_seen=seen)
     rec = {"kernel": kernel, "workload": cfg.name, "source_sha": kernel_source_sha(kernel),
            "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
            "dispatches": len(fetch), "copy_fetch_factor": round(f_fac, 4), "copy_write_factor": round(w_fac, 4),
