@@ -30,9 +30,10 @@
 //                 candidates' keys are read.
 //   ld >  32768 : topk_prune_kernel (grid rows x G, 256 threads: several workgroups per row
 //                 when rows are few) computes tau redundantly in each workgroup, streams its
-//                 share of the row's 4096-position blocks and writes one bit per position;
-//                 topk_select_kernel (one workgroup per row) lists the marked positions,
-//                 gathers their keys and selects.
+//                 contiguous share of the row's 4096-position blocks and lists its
+//                 candidates as (key, position) pairs in position order;
+//                 topk_select_kernel (one workgroup per row) reads the G lists as one and
+//                 selects.
 // The result does not depend on scheduling.
 #include <algorithm>
 
@@ -58,6 +59,7 @@ constexpr int kSampleMargin = 768;               // candidates aimed for above 2
 constexpr int kBins = 256;
 constexpr int kHistWords = kBins;
 constexpr int kPruneTarget = 2048;               // prune workgroups aimed for per launch
+constexpr int kMaxSlices = 1024;                 // prune workgroups per row, at most
 static_assert(kPBlock == 16 * kPruneThreads, "four float4 per thread per block");
 static_assert(kSamplesPerThread == 8, "two sample runs per thread");
 static_assert(kHistWords % 4 == 0 && kHistWords / 4 <= kPruneThreads, "histogram clears");
@@ -76,15 +78,6 @@ __device__ __forceinline__ int row_len(const int* n_valid, int n_add, int64_t ld
 
 __device__ __forceinline__ int range_bits(uint32_t lo, uint32_t hi) {
   return hi <= lo ? 0 : 32 - __clz(hi - lo);
-}
-
-// OR over each group of 8 consecutive lanes, result in all 8: quad_perm swaps (xor 1,
-// xor 2) within each quad, then row_half_mirror (lane i <-> 7 - i) across the two quads.
-__device__ __forceinline__ uint32_t group8_or(uint32_t v) {
-  v |= DSA_DPP(v, 0xB1, 0xf, false);
-  v |= DSA_DPP(v, 0x4E, 0xf, false);
-  v |= DSA_DPP(v, 0x141, 0xf, false);
-  return v;
 }
 
 // One radix level's histogram: key goes to bin (key - L) >> shift when it lies in
@@ -299,31 +292,33 @@ __device__ __forceinline__ uint32_t sample_tau(const uint32_t (&s)[S], uint32_t 
 
 struct PruneSmem {
   uint32_t hist[2][kHistWords];
-  uint32_t red[2][kSelWaves];   // per-wave minima and maxima
-  uint32_t part[2][2 * kPruneWaves];   // list mode: per-wave packed counts (alternating blocks)
+  uint32_t red[2][kSelWaves];        // per-wave minima and maxima
+  uint32_t part[2][2 * kPruneWaves];  // per-wave packed counts (alternating blocks)
 };
 
-// Stage 1, grid (rows, G), when ld > kOnePass, for rows of more than kCap positions:
-// tau_out[row]; wmax[row][slice][wave] = the largest key the wave saw (0 if none).  Block
-// b of the row (positions 4096b ..) belongs to slice b % G.  Then either
-//   G > 1 (few rows): bit p of the row's mask = (key(p) >= tau) for p < n; or
-//   G == 1 (one workgroup per row): the candidates (key >= tau) in position order, as
-//          (key, position) pairs list[row][0 .. 8191] and their number lcnt[row] (pairs past
-//          8192 are counted, not stored).  Each block's candidates take their places
-//          from one block scan of packed per-thread counts.
-template <bool kListed>
+// Stage 1, grid (rows, G), when ld > kOnePass, for rows of more than kCap positions.  The
+// row's 4096-position blocks split into G contiguous ranges, one per workgroup (slice s:
+// blocks [s * nb / G, (s + 1) * nb / G)).  Every workgroup derives the row's tau from the
+// same samples, streams its blocks once (non-temporal loads) and lists its candidates
+// (key >= tau) in position order as (key, position) pairs list[row][s][0 .. 8191], their
+// number in lcnt[row][s] (pairs past 8192 are counted, not stored); each block's
+// candidates take their places from one block scan of packed per-thread counts.  Also
+// tau_out[row] and wmax[row][s][wave] = the largest key the wave saw (0 if none).
 __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
-    uint32_t* __restrict__ mask, int64_t mw, uint32_t* __restrict__ tau_out,
-    uint32_t* __restrict__ wmax, uint32_t* __restrict__ lcnt, uint2* __restrict__ list) {
+    uint32_t* __restrict__ tau_out, uint32_t* __restrict__ wmax, uint32_t* __restrict__ lcnt,
+    uint2* __restrict__ list) {
   __shared__ __attribute__((aligned(16))) PruneSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x, slice = blockIdx.y, G = gridDim.y;
   const int n = row_len(n_valid, n_add, ld, row);
   if (n <= kCap) return;
-  uint32_t* wm = wmax + ((int64_t)row * G + slice) * kPruneWaves;
-  if ((int64_t)slice * kPBlock >= n) {   // no block for this slice
-    if (lane == 0) wm[wave] = 0u;
+  const int64_t rs = (int64_t)row * G + slice;
+  const int64_t nb = ((int64_t)n + kPBlock - 1) / kPBlock;
+  const int64_t b0 = (int64_t)slice * nb / G, b1 = (int64_t)(slice + 1) * nb / G;
+  if (b0 >= b1) {   // no block for this slice
+    if (lane == 0) wmax[rs * kPruneWaves + wave] = 0u;
+    if (tid == 0) lcnt[rs] = 0u;
     return;
   }
   const float* src = scores + (int64_t)row * ld;
@@ -333,27 +328,20 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
   load_run(src, sample_pos(tid, n), vec, s);
   load_run(src, sample_pos(tid + kPruneThreads, n), vec, s + 4);
   const uint32_t tau = sample_tau<kPruneWaves, kSamplesPerThread>(s, sample_rank(k, n), sm.hist, sm.red);
-  if (slice == 0 && tid == 0) tau_out[row] = tau;
+  if (b0 == 0 && tid == 0) tau_out[row] = tau;   // the slice that owns block 0 (never empty)
 
-  constexpr bool listed = kListed;   // G == 1: the scores are read once, non-temporally
-  uint32_t* mrow = mask + (int64_t)row * mw;
-  uint2* lrow = list + (int64_t)row * kCap;
-  const int nwords = (n + 31) >> 5;
-  uint32_t kmax = 0u, listed_n = 0u;
+  uint2* lrow = list + rs * kCap;
+  uint32_t kmax = 0u, listed = 0u;
   int it = 0;
-  for (int64_t b = slice; b * kPBlock < n; b += G, ++it) {
+  for (int64_t b = b0; b < b1; ++b, ++it) {
     const int p0 = (int)(b * kPBlock);
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = p0 + 4 * (tid + kPruneThreads * u);
       if (vec && p + 3 < n) {
-        if (listed) {
-          const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + p));
-          v[u] = make_float4(x[0], x[1], x[2], x[3]);
-        } else {
-          v[u] = *reinterpret_cast<const float4*>(src + p);
-        }
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + p));
+        v[u] = make_float4(x[0], x[1], x[2], x[3]);
       } else {
         v[u].x = p < n ? src[p] : 0.f;
         v[u].y = p + 1 < n ? src[p + 1] : 0.f;
@@ -373,17 +361,6 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
         kmax = max(kmax, key[u][j]);
         nib[u] |= (key[u][j] >= tau && key[u][j] != 0u ? 1u : 0u) << j;
       }
-    }
-    if (!listed) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        // the word of positions p0 + 1024u + 32 * (tid / 8) .. + 31 gathers the nibbles of
-        // 8 consecutive lanes
-        const uint32_t word = group8_or(nib[u] << (4 * (tid & 7)));
-        const int wi = (p0 >> 5) + 32 * u + (tid >> 3);
-        if ((tid & 7) == 0 && wi < nwords) mrow[wi] = word;
-      }
-      continue;
     }
     // position order in the block is (u, thread, j): candidate (u, t, j) goes after all
     // those of u' < u and those of threads < t for the same u; the four per-u counts
@@ -408,9 +385,9 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
     }
     const uint32_t e01 = b01 + i01 - c01, e23 = b23 + i23 - c23;
     const uint32_t tot0 = t01 & 0xFFFFu, tot1 = t01 >> 16, tot2 = t23 & 0xFFFFu;
-    const uint32_t off[4] = {listed_n + (e01 & 0xFFFFu), listed_n + tot0 + (e01 >> 16),
-                             listed_n + tot0 + tot1 + (e23 & 0xFFFFu),
-                             listed_n + tot0 + tot1 + tot2 + (e23 >> 16)};
+    const uint32_t off[4] = {listed + (e01 & 0xFFFFu), listed + tot0 + (e01 >> 16),
+                             listed + tot0 + tot1 + (e23 & 0xFFFFu),
+                             listed + tot0 + tot1 + tot2 + (e23 >> 16)};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -419,11 +396,11 @@ __global__ __launch_bounds__(kPruneThreads, 8) void topk_prune_kernel(
         if (((nib[u] >> j) & 1u) && slot < (uint32_t)kCap)
           lrow[slot] = make_uint2(key[u][j], (uint32_t)(p0 + 4 * (tid + kPruneThreads * u) + j));
       }
-    listed_n += (t01 & 0xFFFFu) + (t01 >> 16) + (t23 & 0xFFFFu) + (t23 >> 16);
+    listed += (t01 & 0xFFFFu) + (t01 >> 16) + (t23 & 0xFFFFu) + (t23 >> 16);
   }
-  if (listed && tid == 0) lcnt[row] = listed_n;
+  if (tid == 0) lcnt[rs] = listed;
   kmax = wave_max_u32(kmax);
-  if (lane == 0) wm[wave] = kmax;
+  if (lane == 0) wmax[rs * kPruneWaves + wave] = kmax;
 }
 
 // ------------------------------------------------------------------ select
@@ -499,16 +476,16 @@ __device__ __forceinline__ void select_direct(const float* src, int n, int k, Se
 }
 
 // Stage 2 after the prune kernel (ld > kOnePass), one workgroup per row: rows of at most
-// kCap positions select from registers directly, longer ones from the candidates the prune
-// kernel listed (kListed: G == 1; two workgroups fit a CU) or marked (G > 1).
-template <bool kListed>
-__global__ __launch_bounds__(kSelThreads, kListed ? 8 : 1) void topk_select_kernel(
+// kCap positions select from registers directly, longer ones from the G slices' candidate
+// lists, which concatenate in position order (slice offsets from one block scan of their
+// counts; entry i of the row is found by a binary search over them).
+__global__ __launch_bounds__(kSelThreads, 8) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int* __restrict__ n_valid, int n_add, int k,
-    int* __restrict__ idx, int64_t ld_idx, const uint32_t* __restrict__ mask, int64_t mw,
-    const uint32_t* __restrict__ tau_in, const uint32_t* __restrict__ wmax, int G,
-    const uint32_t* __restrict__ lcnt, const uint2* __restrict__ list) {
+    int* __restrict__ idx, int64_t ld_idx, const uint32_t* __restrict__ tau_in,
+    const uint32_t* __restrict__ wmax, const uint32_t* __restrict__ lcnt,
+    const uint2* __restrict__ list, int G) {
   __shared__ __attribute__((aligned(16))) SelSmem sm;
-  __shared__ uint32_t cpos[kCap];
+  __shared__ uint32_t soff[kMaxSlices];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   const int n = row_len(n_valid, n_add, ld, row);
@@ -522,88 +499,51 @@ __global__ __launch_bounds__(kSelThreads, kListed ? 8 : 1) void topk_select_kern
     select_direct(src, n, k, sm, out);
     return;
   }
-
   if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
-  if (kListed) {   // the listed candidates: thread t takes entries 8t .. 8t+7
-    const uint32_t total = lcnt[row], tau = tau_in[row];
-    const uint32_t* w4 = wmax + (int64_t)row * kPruneWaves;
-    const uint32_t hi = max(max(w4[0], w4[1]), max(w4[2], w4[3]));
-    if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
-      uint32_t key[kCR], pos[kCR];
-#pragma unroll
-      for (int r = 0; r < kCR; ++r) {
-        const uint32_t i = (uint32_t)(kCR * tid + r);
-        const uint2 e = i < total ? list[(int64_t)row * kCap + i] : make_uint2(0u, 0u);
-        key[r] = e.x;
-        pos[r] = e.y;
-      }
-      __syncthreads();   // hist[0] is clear before the first level adds to it
-      Radix st;
-      const uint32_t theta = select_regs<kCR>(key, total, tau, hi, (uint32_t)k, sm.hist, st);
-      compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
-                   [&](int r, uint32_t slot) { out[slot] = (int)pos[r]; });
-      return;
-    }
-    __syncthreads();   // as above
-    select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
-    return;
-  }
-  // candidates from the prune bits: thread t owns the words [t * wpt, (t + 1) * wpt)
-  const uint32_t* mrow = mask + (int64_t)row * mw;
-  const int nwords = (n + 31) >> 5;
-  const int wpt = (nwords + kSelThreads - 1) / kSelThreads;
-  const int w0 = tid * wpt, w1 = min(nwords, w0 + wpt);
-  constexpr int kKeep = 4;   // words kept in registers between the count and the listing
-  uint32_t wk[kKeep];
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kKeep; ++j) {
-    wk[j] = w0 + j < w1 ? mrow[w0 + j] : 0u;
-    cnt += __popc(wk[j]);
-  }
-  for (int w = w0 + kKeep; w < w1; ++w) cnt += __popc(mrow[w]);
-  const int64_t nblocks = ((int64_t)n + kPBlock - 1) / kPBlock;
-  const int nslices = (int)(nblocks < G ? nblocks : G);
-  const uint32_t* wrow = wmax + (int64_t)row * G * kPruneWaves;
-  uint32_t mx = 0u;
-  for (int i = tid; i < nslices * kPruneWaves; i += kSelThreads) mx = max(mx, wrow[i]);
   const uint32_t tau = tau_in[row];
-  mx = wave_max_u32(mx);
-  if (lane == 0) sm.red[1][wave] = mx;
-  uint32_t total;
-  uint32_t off = block_excl_scan(cnt, sm.wsum[0], &total);
-  const uint32_t hi = wave_max_u32(lane < kSelWaves ? sm.red[1][lane] : 0u);
-
-  if (total >= (uint32_t)k && total <= (uint32_t)kCap) {
-    // the candidates' positions in order, then their keys (8 per thread)
-#pragma unroll
-    for (int j = 0; j < kKeep; ++j) {
-      uint32_t m = wk[j];
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1u;
-        cpos[off++] = (uint32_t)(32 * (w0 + j) + b);
-      }
-    }
-    for (int w = w0 + kKeep; w < w1; ++w) {
-      uint32_t m = mrow[w];
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1u;
-        cpos[off++] = (uint32_t)(32 * w + b);
-      }
-    }
+  uint32_t total, hi;
+  bool over;
+  if (G == 1) {   // one list: its count and the row max, read by every thread
+    total = lcnt[row];
+    over = total > (uint32_t)kCap;
+    const uint32_t* w4 = wmax + (int64_t)row * kPruneWaves;
+    hi = max(max(w4[0], w4[1]), max(w4[2], w4[3]));
+    if (tid == 0) soff[0] = 0u;
+    __syncthreads();   // hist[0] and soff are set before they are used
+  } else {   // slice counts (thread s < G) and the row's largest key, in one block scan
+    const uint32_t c = tid < G ? lcnt[(int64_t)row * G + tid] : 0u;
+    uint32_t mx = 0u;
+    for (int i = tid; i < G * kPruneWaves; i += kSelThreads) mx = max(mx, wmax[(int64_t)row * G * kPruneWaves + i]);
+    mx = wave_max_u32(mx);
+    if (lane == 0) sm.red[1][wave] = mx;
+    over = __syncthreads_or(c > (uint32_t)kCap) != 0;   // a slice overflowed
+    const uint32_t before = block_excl_scan(c, sm.wsum[0], &total);
+    hi = wave_max_u32(lane < kSelWaves ? sm.red[1][lane] : 0u);
+    if (tid < G) soff[tid] = before;
     __syncthreads();
-    uint32_t key[kCR];
+  }
+  if (!over && total >= (uint32_t)k && total <= (uint32_t)kCap) {
+    uint32_t key[kCR], pos[kCR];
 #pragma unroll
     for (int r = 0; r < kCR; ++r) {
       const uint32_t i = (uint32_t)(kCR * tid + r);
-      key[r] = i < total ? order_key(src[cpos[i]]) : 0u;
+      key[r] = 0u;
+      pos[r] = 0u;
+      if (i < total) {
+        int lo = 0, hi_s = G - 1;   // the last slice starting at or before i
+        while (lo < hi_s) {
+          const int mid = (lo + hi_s + 1) >> 1;
+          if (soff[mid] <= i) lo = mid; else hi_s = mid - 1;
+        }
+        const uint2 e = list[((int64_t)row * G + lo) * kCap + (i - soff[lo])];
+        key[r] = e.x;
+        pos[r] = e.y;
+      }
     }
     Radix st;
     const uint32_t theta = select_regs<kCR>(key, total, tau, hi, (uint32_t)k, sm.hist, st);
     compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
-                 [&](int r, uint32_t slot) { out[slot] = (int)cpos[kCR * tid + r]; });
+                 [&](int r, uint32_t slot) { out[slot] = (int)pos[r]; });
     return;
   }
   select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
@@ -726,23 +666,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_onepass_kernel(
 int prune_slices(int rows, int64_t ld) {
   const int64_t blocks = (ld + kPBlock - 1) / kPBlock;
   const int64_t want = (kPruneTarget + (int64_t)rows - 1) / std::max(rows, 1);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, blocks));
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, blocks, (int64_t)kMaxSlices}));
 }
-
-int64_t mask_words(int64_t ld) { return ((ld + 31) / 32 + 3) / 4 * 4; }
 
 size_t pad4(size_t words) { return (words + 3) / 4 * 4; }
 
-// Workspace of the prune + select kernels (words): tau [rows] | wmax [rows][G][4] | then
-// G > 1: mask [rows][mask_words]; G == 1: lcnt [rows] | list [rows][kCap] (key, position).
+// Workspace of the prune + select kernels (words): tau [rows] | wmax [rows][G][4] |
+// lcnt [rows][G] | list [rows][G][kCap] (key, position).
 struct TopkWs {
-  uint32_t *tau, *wmax, *mask, *lcnt;
+  uint32_t *tau, *wmax, *lcnt;
   uint2* list;
   size_t words;
 };
 
 TopkWs topk_ws(void* base, int rows, int64_t ld) {
-  const int G = prune_slices(rows, ld);
+  const size_t G = (size_t)prune_slices(rows, ld);
   uint32_t* p = (uint32_t*)base;
   TopkWs w{};
   size_t o = 0;
@@ -750,15 +688,10 @@ TopkWs topk_ws(void* base, int rows, int64_t ld) {
   o += pad4((size_t)rows);
   w.wmax = p ? p + o : nullptr;
   o += (size_t)rows * G * kPruneWaves;
-  if (G > 1) {
-    w.mask = p ? p + o : nullptr;
-    o += (size_t)rows * mask_words(ld);
-  } else {
-    w.lcnt = p ? p + o : nullptr;
-    o += pad4((size_t)rows);
-    w.list = p ? reinterpret_cast<uint2*>(p + o) : nullptr;
-    o += (size_t)rows * kCap * 2;
-  }
+  w.lcnt = p ? p + o : nullptr;
+  o += pad4((size_t)rows * G);
+  w.list = p ? reinterpret_cast<uint2*>(p + o) : nullptr;
+  o += (size_t)rows * G * kCap * 2;
   w.words = o;
   return w;
 }
@@ -779,19 +712,18 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int G = prune_slices(a.rows, a.ld);
-  const int64_t mw = mask_words(a.ld);
   const TopkWs w = topk_ws(a.ws, a.rows, a.ld);
   {
     const KernelEvents ev("topk_prune_kernel");
-    hipExtLaunchKernelGGL(G == 1 ? topk_prune_kernel<true> : topk_prune_kernel<false>, dim3(a.rows, G),
-                          dim3(kPruneThreads), 0, stream, ev.start, ev.stop, 0, a.scores, a.ld, a.n_valid,
-                          a.n_add, a.k, w.mask, mw, w.tau, w.wmax, w.lcnt, w.list);
+    hipExtLaunchKernelGGL(topk_prune_kernel, dim3(a.rows, G), dim3(kPruneThreads), 0, stream, ev.start,
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, w.tau, w.wmax, w.lcnt,
+                          w.list);
   }
   {
     const KernelEvents ev("topk_select_kernel");
-    hipExtLaunchKernelGGL(G == 1 ? topk_select_kernel<true> : topk_select_kernel<false>, dim3(a.rows),
-                          dim3(kSelThreads), 0, stream, ev.start, ev.stop, 0, a.scores, a.ld, a.n_valid,
-                          a.n_add, a.k, a.idx, a.ld_idx, w.mask, mw, w.tau, w.wmax, G, w.lcnt, w.list);
+    hipExtLaunchKernelGGL(topk_select_kernel, dim3(a.rows), dim3(kSelThreads), 0, stream, ev.start,
+                          ev.stop, 0, a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx, w.tau,
+                          w.wmax, w.lcnt, w.list, G);
   }
   return hipGetLastError();
 }

@@ -167,15 +167,16 @@ def test_workspace_sizes():
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 0, 0, 2048, 64, 512) == 0
     # rows of at most 32768 positions are selected in one workgroup: no workspace
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 64, 32768, 2048, 0, 0) == 0
-    # longer rows: tau per row (padded to 4 words) and the largest key of each prune wave
-    # (4 per workgroup, min(ceil(2048 / rows), blocks of 4096) workgroups per row); then
-    # one prune bit per position when there are several workgroups per row ...
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 1, 40000, 2048, 0, 0) == (4 + 10 * 4 + 1252) * 4
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 40, 131072, 2048, 0, 0) == \
-        (40 + 40 * 32 * 4 + 40 * 4096) * 4
-    # ... or, with one per row, a count and 8192 (key, position) pairs per row
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 4096, 131072, 2048, 0, 0) == \
-        (4096 + 4096 * 4 + 4096 + 2 * 4096 * 8192) * 4
+    # longer rows, G = min(ceil(2048 / rows), blocks of 4096, 1024) prune workgroups per
+    # row: tau per row (padded to 4 words), the largest key of each prune wave (4 per
+    # workgroup), a candidate count per workgroup (padded) and 8192 (key, position) pairs
+    # per workgroup
+    def words(rows, G):
+        pad4 = lambda x: -(-x // 4) * 4
+        return pad4(rows) + rows * G * 4 + pad4(rows * G) + rows * G * 8192 * 2
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 1, 40000, 2048, 0, 0) == words(1, 10) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 40, 131072, 2048, 0, 0) == words(40, 32) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 4096, 131072, 2048, 0, 0) == words(4096, 1) * 4
 
 
 def test_index_cache_host_logic():
