@@ -32,28 +32,31 @@ constexpr int kTileKeys = 128;                 // keys per LDS tile (2 pages)
 constexpr int kRowBytes = kDi * 2;             // 256 B per key row
 constexpr int kLdsRow = kRowBytes + 16;        // padded LDS row (conflict-free b128 reads)
 constexpr int kTileBytes = kTileKeys * kLdsRow;
+constexpr int kChunkTiles = 64;                // prefill: key tiles per workgroup
+static_assert(kChunkTiles * kTileKeys / kBlock <= 2 * kWave, "page table in two registers");
 
-// Loads one 128-key tile (2 pages) of a request starting at logical key `key0` (a
-// multiple of 128) into registers: thread t fetches 16-byte chunks t, t+kThreads, ...
-// (fully coalesced within each page).  Pages at or beyond n, and block-table entries
-// outside the pool, read as zeros.
+// Loads one 128-key tile (2 pages) starting at logical key `key0` (a multiple of 128)
+// into registers: thread t fetches 16-byte chunks t, t+kThreads, ... (fully coalesced
+// within each page).  `pg` holds the physical block of every page of the workgroup's key
+// chunk (lane j: page j, 64 + j), -1 for pages at or beyond the request's length or
+// outside the pool, which read as zeros; `lp0` is the tile's first page in the chunk.
 template <int kThreads>
 struct TileRegs { uint4 v[kTileKeys * 16 / kThreads]; };
 
 template <int kThreads>
 __device__ __forceinline__ void load_tile(TileRegs<kThreads>& r, const uint8_t* pool,
-                                          int64_t num_blocks, const int* bt_row, int key0, int n) {
+                                          const int (&pg)[2], int lp0) {
+  static_assert(kTileKeys * 16 / kThreads % 2 == 0, "whole pages per chunk group");
+  constexpr int kPerPage = kTileKeys * 16 / kThreads / 2;   // chunks per thread per page
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kTileKeys * 16 / kThreads; ++i) {
     const int id = tid + kThreads * i;           // 16-byte chunk id in the 32 KB tile
-    const int key = id >> 4;                     // 0..127
-    const int lblk = (key0 + key) >> 6;
-    int64_t phys = -1;
-    if (key0 + (key & ~63) < n) phys = bt_row[lblk];
-    if (phys >= 0 && phys < num_blocks) {
-      const int64_t off = ((phys * kBlock + ((key0 + key) & 63)) * kRowBytes) + (id & 15) * 16;
-      r.v[i] = *reinterpret_cast<const uint4*>(pool + off);
+    const int lp = lp0 + i / kPerPage;           // page of this chunk (workgroup-uniform)
+    const int phys = __builtin_amdgcn_readlane(lp < 64 ? pg[0] : pg[1], lp & 63);
+    if (phys >= 0) {
+      const uint8_t* page = pool + (int64_t)phys * (kBlock * kRowBytes);
+      r.v[i] = *reinterpret_cast<const uint4*>(page + (id & (kBlock * 16 - 1)) * 16);
     } else {
       r.v[i] = make_uint4(0, 0, 0, 0);
     }
@@ -104,15 +107,17 @@ __device__ __forceinline__ float epilogue32(const QFrag& f, const f32x16& c0, co
     p = fmaf(f.w[0][j], relu(c0[j]), p);
     p = fmaf(f.w[1][j], relu(c1[j]), p);
   }
-  p += __shfl_xor(p, 32, kWave);
-  return p + 0.0f;   // canonical +0.0
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return (__uint_as_float(r[0]) + __uint_as_float(r[1])) + 0.0f;   // canonical +0.0
 }
 
 // Prefill: 8 waves, token t0 + w in wave w (8 tokens per workgroup); grid.x: key chunks of
 // `tiles_per_wg` 128-key tiles, grid.y: token groups.  Each key tile is fetched from
-// L2/MALL once per 8 tokens into a double-buffered LDS tile; every wave scores all 128 keys
-// of the tile in four 32-key parts, reading part p + 1's B fragments while part p's MFMAs
-// drain and its epilogue runs.
+// L2/MALL once per 8 tokens into a double-buffered LDS tile; every wave scores the 128
+// keys of a tile in four 32-key parts.  The ReLU-weighted epilogue of each part runs
+// interleaved with the MFMAs of the next one (carried across tiles), and each B fragment
+// is re-read for the next part as soon as its MFMAs have issued, so a wave keeps its
+// matrix unit busy through its own vector work.
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ pool,
     int64_t num_blocks, const int* __restrict__ block_table, const int* __restrict__ seq_len,
@@ -120,6 +125,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     int tiles_per_wg, float* __restrict__ scores, int64_t ld) {
   constexpr int kThreads = 512;
   constexpr int kTPG = kThreads / kWave;   // tokens per workgroup
+  constexpr int kParts = kTileKeys / 32;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTileBytes];
   __shared__ int s_req[kTPG];
   __shared__ int s_n[kTPG];
@@ -157,6 +163,16 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     if (key_begin >= key_end) continue;
     const int* bt_row = block_table + (int64_t)b * max_blocks;
 
+    // physical blocks of the chunk's pages (at most 128), -1 where nothing is to be read
+    int pg[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lblk = (key_begin >> 6) + 64 * h + lane;
+      int phys = -1;
+      if (lblk * kBlock < key_end) phys = bt_row[lblk];
+      pg[h] = (phys >= 0 && phys < num_blocks) ? phys : -1;
+    }
+
     // this wave's token, if it belongs to request b (wave-uniform)
     const int tok = (s_req[wave] == b) ? t0 + wave : -1;
     const int tn = (tok >= 0) ? s_n[wave] : 0;
@@ -164,32 +180,65 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     if (tok >= 0) load_qfrag(f, q_idx + (int64_t)tok * kHi * kRowBytes, w + (int64_t)tok * kHi);
     float* out = scores + (int64_t)max(tok, 0) * ld;
 
+    // accumulators of the last part scored, whose epilogue is still to run (none yet:
+    // zeros, written nowhere)
+    f32x16 p0 = {}, p1 = {};
+    int pend = -1;
+    // scores of the last tile scored, written after the next barrier (so that their
+    // stores have a whole tile to complete before the wait for the next key tile):
+    // sc_lo holds keys sbase - 32 + lane, sc_hi keys sbase + 32 + lane
+    float sc_lo = 0.f, sc_hi = 0.f;
+    int sbase = -1;
+    const auto put = [&](int s, float v) {
+      if (s >= key_begin && s < tn) __builtin_nontemporal_store(v, &out[s]);
+    };
+
     TileRegs<kThreads> regs;
-    load_tile<kThreads>(regs, pool, num_blocks, bt_row, key_begin, nmax);
+    load_tile<kThreads>(regs, pool, pg, 0);
     int buf = 0;
     for (int key0 = key_begin; key0 < key_end; key0 += kTileKeys) {
       store_tile<kThreads>(regs, lds[buf]);
       __syncthreads();
+      if (sbase >= 0) {
+        put(sbase - 32 + lane, sc_lo);
+        put(sbase + 32 + lane, sc_hi);
+        sbase = -1;
+      }
       if (key0 + kTileKeys < key_end)
-        load_tile<kThreads>(regs, pool, num_blocks, bt_row, key0 + kTileKeys, nmax);
+        load_tile<kThreads>(regs, pool, pg, ((key0 - key_begin) >> 6) + 2);
       if (tok >= 0 && key0 < tn) {
-        bf16x8 bq[2][8];
-        load_b(bq[0], lds[buf], 0);
+        bf16x8 bq[8];
+        load_b(bq, lds[buf], 0);
 #pragma unroll
-        for (int part = 0; part < kTileKeys / 32; ++part) {
+        for (int part = 0; part < kParts; ++part) {
           f32x16 c0 = {}, c1 = {};
+          const uint8_t* next = lds[buf] + (32 * (part + 1) + (lane & 31)) * kLdsRow + (lane >> 5) * 128;
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            c0 = mfma32(f.a[0][s], bq[part & 1][s], c0);
-            c1 = mfma32(f.a[1][s], bq[part & 1][s], c1);
+            c0 = mfma32(f.a[0][s], bq[s], c0);
+            c1 = mfma32(f.a[1][s], bq[s], c1);
+            if (part + 1 < kParts) bq[s] = as_bf8(*reinterpret_cast<const uint4*>(next + 16 * s));
           }
-          if (part + 1 < kTileKeys / 32) load_b(bq[(part + 1) & 1], lds[buf], 32 * (part + 1));
-          const float p = epilogue32(f, c0, c1);
-          const int s = key0 + part * 32 + lane;
-          if (lane < 32 && s < tn) out[s] = p;
+          // the epilogue of the previous part (keys key0 + 32 * (part - 1) + lane % 32,
+          // the same in both halves of the wave): parts -1, 0 fill sc_lo, parts 1, 2 sc_hi
+          const float sc = epilogue32(f, p0, p1);
+          if (part < 2) sc_lo = (lane < 32) == (part == 0) ? sc : sc_lo;
+          else sc_hi = (lane < 32) == (part == 2) ? sc : sc_hi;
+          p0 = c0;
+          p1 = c1;
+          pend = key0 + 32 * part;
         }
+        sbase = key0;
       }
       buf ^= 1;
+    }
+    if (sbase >= 0) {
+      put(sbase - 32 + lane, sc_lo);
+      put(sbase + 32 + lane, sc_hi);
+    }
+    if (pend >= 0) {
+      const float sc = epilogue32(f, p0, p1);
+      if (lane < 32) put(pend + lane, sc);
     }
     __syncthreads();   // LDS reuse by the next request's tiles
   }
@@ -444,7 +493,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
     if (a.prefill) {
       // key chunks of 64 tiles (8192 keys) per workgroup, 8 tokens per workgroup
       const int tiles = (max_keys + kTileKeys - 1) / kTileKeys;
-      const int per = 64;
+      const int per = kChunkTiles;
       dim3 grid((tiles + per - 1) / per, (a.T + 7) / 8);
       {
         const KernelEvents ev("indexer_prefill_kernel");
