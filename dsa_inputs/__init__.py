@@ -87,6 +87,9 @@ def _cfgs() -> Dict[str, Config]:
         # prefill chunk: 4096 causal queries at positions 126976..131071 of a 131072 context
         "prefill_4096_at_128k": Config("prefill_4096_at_128k", seed=3, batch=1, ctx=131072,
                                        prefill_tokens=4096, identity_pages=True, **big),
+        # batched decode as decode_b64_paged with 128 MLA heads (DeepSeek-V3.2's count)
+        "decode_b64_paged_h128": Config("decode_b64_paged_h128", seed=5, batch=64, ctx=65536,
+                                        ctx_range=(4096, 65536), **dict(big, H=128)),
         # IndexShare decode: 4 layers, 32 requests at 131072 + 8 dense requests at 1500
         "indexshare_decode_4layer": Config("indexshare_decode_4layer", seed=4, batch=32,
                                            ctx=131072, extra_dense=(1500,) * 8, layers=4, **big),

@@ -32,6 +32,8 @@
  *     block_table[b * max_blocks + s / 64].
  *   - Supported instances:
  *       BF16 : indexer (Hi, Di) = (64, 128); MLA (H, Dl, Dr) = (64, 512, 64)  -- MFMA kernels
+ *              and MLA H = 128 (DeepSeek-V3.2's head count, the comparison point of
+ *              §MLA changes), run as two groups of 64 heads over the same rows
  *       F32  : indexer Hi <= 64, Di <= 128, Di % 4 == 0;
  *              MLA H <= 64, Dl + Dr <= 1024, Dl % 4 == 0, Dr % 4 == 0      -- VALU kernels
  *     k (top-k width) is 1..2048.  Anything else returns DSA_ERR_UNSUPPORTED.

@@ -88,8 +88,8 @@ dsa_status check_mla(const void* q, const dsa_pool* kv, const dsa_page_table* pt
   if (ld_idx < k) return fail(DSA_ERR_INVALID, "ld_idx %lld < k %d", (long long)ld_idx, k);
   if (!isfinite(sm_scale)) return fail(DSA_ERR_INVALID, "sm_scale is not finite");
   if (kv->dtype == DSA_BF16) {
-    if (H != 64 || Dl != 512 || Dr != 64)
-      return fail(DSA_ERR_UNSUPPORTED, "bf16 MLA supports (H, Dl, Dr) = (64, 512, 64) only, got (%d, %d, %d)",
+    if ((H != 64 && H != 128) || Dl != 512 || Dr != 64)
+      return fail(DSA_ERR_UNSUPPORTED, "bf16 MLA supports (H, Dl, Dr) = (64 or 128, 512, 64) only, got (%d, %d, %d)",
                   H, Dl, Dr);
     if (!aligned16(q) || !aligned16(out)) return fail(DSA_ERR_INVALID, "q/out not 16-byte aligned");
   } else {

@@ -69,7 +69,7 @@ struct MlaArgs {
   float* lse;
   void* ws;
 };
-int mla_splits(int T, int k, bool bf16);
+int mla_splits(int T, int k, int H, bool bf16);
 size_t mla_workspace_bytes(int T, int k, int H, int Dl, bool bf16);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
 

@@ -324,7 +324,10 @@ __device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint
   if (kLogits) store_partials(sacc, sp_out);
 }
 
-// grid (splits, T), 256 threads.  splits == 1: normalized bf16 output (+ lse); else the
+// grid (splits, T, H / 64), 256 threads: one workgroup per (split, token, group of 64 heads);
+// the token's H heads are consecutive in q, out, lse and the partials (groups of one token
+// read the same rows: H = 128 gathers each row twice, the second time mostly from the
+// caches).  splits == 1: normalized bf16 output (+ lse); else the
 // split's unnormalized fp32 partial O and (max, sum) in log2 units go to the workspace,
 // with non-temporal stores when kNtPartials (few tokens: the kernel then ends sooner,
 // measured 1.2 us at one token; with many tokens the combine reads the 30+ MB of partials
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
     const int* __restrict__ block_table, const int* __restrict__ seq_len, int max_blocks, int batch,
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
-    int64_t ld_idx, int k, float scale_log2, int splits, uint16_t* __restrict__ out,
+    int64_t ld_idx, int k, float scale_log2, int splits, int H, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   // three V tiles; before the loop the same bytes stage Q (64 rows of 73 chunks)
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[3][kVTileBytes];
@@ -348,6 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int dh = wave & 1, g = lane >> 4, c16 = lane & 15;
   const int t = blockIdx.y, sp = blockIdx.x;
+  const int64_t h0 = (int64_t)t * H + kH * blockIdx.z;   // the group's first head of the token
 
   // Q: coalesced 16-byte loads (thread tid takes chunks tid + 256i of the 64 x 72), issued
   // first so that their latency overlaps the list lookups
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   u32x4 qs[kQLoads];
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i)
-    qs[i] = *reinterpret_cast<const u32x4*>(q + (int64_t)t * kH * kRowBytes + 16 * (tid + kThreads * i));
+    qs[i] = *reinterpret_cast<const u32x4*>(q + h0 * kRowBytes + 16 * (tid + kThreads * i));
   int nent;
   resolve_rows(t, sp, splits, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos,
                idx, ld_idx, k, rowid, nent);
@@ -467,16 +471,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
         const int head = 16 * ht + 4 * g + j;
         const float l = s_ml[head][1];
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* dst = out + ((int64_t)t * kH + head) * kDl + 128 * wave + c16;
+        uint16_t* dst = out + (h0 + head) * kDl + 128 * wave + c16;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) dst[16 * dt] = f2bf_bits(o[ht][dt][j] * inv);
       }
     if (lse && tid < kH) {
       const float m = s_ml[tid][0], l = s_ml[tid][1];
-      lse[(int64_t)t * kH + tid] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+      lse[h0 + tid] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
   } else {
-    const int64_t base = ((int64_t)t * splits + sp) * kH;
+    const int64_t base = ((int64_t)t * splits + sp) * H + kH * blockIdx.z;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
@@ -640,13 +644,14 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(
 // Partials of at most this many (token, split) workgroups (8 MB) are stored non-temporally.
 constexpr int kNtPartialsMax = 64;
 
-// Splits of the selected list per token: as many (token, split) workgroups as fit in one
-// round on the 256 CUs (one workgroup per CU), at most 32 and never more than the list has
-// tiles.
-int mla_splits(int T, int k, bool bf16) {
+// Splits of the selected list per token: as many (token, split, head group) workgroups as
+// fit in one round on the 256 CUs (one workgroup per CU), at most 32 and never more than
+// the list has tiles.
+int mla_splits(int T, int k, int H, bool bf16) {
   if (!bf16 || T <= 0) return 1;
   const int tiles = (k + kMT - 1) / kMT;
-  int s = 256 / T;
+  const int units = T * (H > kH ? H / kH : 1);
+  int s = 256 / units;
   s = s < 1 ? 1 : (s > 32 ? 32 : s);
   return s < tiles ? s : tiles;
 }
@@ -654,53 +659,55 @@ int mla_splits(int T, int k, bool bf16) {
 // The combine splits the output dims over Z workgroups per (token, head) until ~2048 are
 // in flight, and until a lane's (split, pass) slots fit in registers (always by Z = 8 for
 // splits <= 32).
-int combine_slices(int T, int splits) {
+int combine_slices(int T, int H, int splits) {
   int Z = 1;
-  while (Z < kPasses && ((int64_t)T * kH * Z < 2048 || (splits + 3) / 4 * (kPasses / Z) > kCombSlots))
+  while (Z < kPasses && ((int64_t)T * H * Z < 2048 || (splits + 3) / 4 * (kPasses / Z) > kCombSlots))
     Z *= 2;
   return Z;
 }
 static_assert((32 + 3) / 4 * 1 <= kCombSlots, "32 splits fit at Z = kPasses");
 
 size_t mla_workspace_bytes(int T, int k, int H, int Dl, bool bf16) {
-  const int s = mla_splits(T, k, bf16);
+  const int s = mla_splits(T, k, H, bf16);
   if (s <= 1) return 0;
   return (size_t)T * s * H * (Dl + 2) * sizeof(float);
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
   if (a.bf16) {
-    const int splits = mla_splits(a.T, a.k, true);
+    const int splits = mla_splits(a.T, a.k, a.H, true);
+    const int groups = a.H / kH;
     float* ws_o = (float*)a.ws;
-    float* ws_ml = ws_o ? ws_o + (size_t)a.T * splits * kH * kDl : nullptr;
+    float* ws_ml = ws_o ? ws_o + (size_t)a.T * splits * a.H * kDl : nullptr;
     {
       const KernelEvents ev("mla_bf16_kernel");
-      auto kernel = (int64_t)a.T * splits <= kNtPartialsMax ? mla_bf16_kernel<true> : mla_bf16_kernel<false>;
-      hipExtLaunchKernelGGL(kernel, dim3(splits, a.T), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
+      auto kernel = (int64_t)a.T * splits * groups <= kNtPartialsMax ? mla_bf16_kernel<true>
+                                                                     : mla_bf16_kernel<false>;
+      hipExtLaunchKernelGGL(kernel, dim3(splits, a.T, groups), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
                             (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks, a.block_table,
                             a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k,
-                            a.sm_scale * kLog2e, splits, (uint16_t*)a.out, a.lse, ws_o, ws_ml);
+                            a.sm_scale * kLog2e, splits, a.H, (uint16_t*)a.out, a.lse, ws_o, ws_ml);
     }
     if (splits > 1) {
-      const int Z = combine_slices(a.T, splits);
+      const int Z = combine_slices(a.T, a.H, splits);
       const KernelEvents ev("mla_combine_kernel");
-      const dim3 grid(a.T, kH, Z);
+      const dim3 grid(a.T, a.H, Z);
       switch (kPasses / Z) {
         case 8:
           hipExtLaunchKernelGGL(mla_combine_kernel<8>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
-                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+                                ws_ml, splits, a.H, (uint16_t*)a.out, a.lse);
           break;
         case 4:
           hipExtLaunchKernelGGL(mla_combine_kernel<4>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
-                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+                                ws_ml, splits, a.H, (uint16_t*)a.out, a.lse);
           break;
         case 2:
           hipExtLaunchKernelGGL(mla_combine_kernel<2>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
-                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+                                ws_ml, splits, a.H, (uint16_t*)a.out, a.lse);
           break;
         default:
           hipExtLaunchKernelGGL(mla_combine_kernel<1>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, ws_o,
-                                ws_ml, splits, kH, (uint16_t*)a.out, a.lse);
+                                ws_ml, splits, a.H, (uint16_t*)a.out, a.lse);
           break;
       }
     }

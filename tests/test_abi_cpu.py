@@ -133,6 +133,9 @@ def mla_call(prefill=False, **kw):
     (dict(pt=None), L.DSA_ERR_INVALID),
     (dict(pool=pool(row=512)), L.DSA_ERR_INVALID),
     (dict(H=32), L.DSA_ERR_UNSUPPORTED),
+    (dict(H=96), L.DSA_ERR_UNSUPPORTED),                  # bf16: 64 or 128 heads
+    (dict(H=192), L.DSA_ERR_UNSUPPORTED),
+    (dict(H=128, Dl=256, Dr=320), L.DSA_ERR_UNSUPPORTED),
     (dict(Dl=256, Dr=320), L.DSA_ERR_UNSUPPORTED),
     (dict(k=4096, ld_idx=4096), L.DSA_ERR_UNSUPPORTED),
     (dict(ld_idx=100), L.DSA_ERR_INVALID),
@@ -165,6 +168,12 @@ def test_workspace_sizes():
     assert one == 32 * 64 * (512 + 2) * 4
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 4096, 0, 2048, 64, 512) == 0
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 0, 0, 2048, 64, 512) == 0
+    # 128 heads run as two 64-head workgroups per (token, split): one token still splits 32
+    # ways (64 workgroups), 64 tokens split 2 ways, 128 tokens do not split
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 1, 0, 2048, 128, 512) == 32 * 128 * (512 + 2) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 128, 512) == 64 * 2 * 128 * (512 + 2) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 64, 512) == 64 * 4 * 64 * (512 + 2) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 128, 0, 2048, 128, 512) == 0
     # rows of at most 32768 positions are selected in one workgroup: no workspace
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 64, 32768, 2048, 0, 0) == 0
     # longer rows, G = min(ceil(2048 / rows), blocks of 4096, 1024) prune workgroups per

@@ -6,7 +6,11 @@ import dsa_inputs as I
 
 def test_configs_present():
     assert set(I.CONFIGS) == {"tiny_fp32", "decode_b1_32k", "decode_b64_paged",
-                              "prefill_4096_at_128k", "indexshare_decode_4layer"}
+                              "prefill_4096_at_128k", "indexshare_decode_4layer",
+                              "decode_b64_paged_h128"}
+    h = I.CONFIGS["decode_b64_paged_h128"]
+    assert (h.H, h.Dl, h.Dr, h.Hi, h.Di, h.k) == (128, 512, 64, 64, 128, 2048)
+    assert I.context_lengths(h)[0] >= 4096 and len(I.context_lengths(h)) == 64
     c = I.CONFIGS["decode_b64_paged"]
     lens = I.context_lengths(c)
     assert len(lens) == 64 and min(lens) >= 4096 and max(lens) <= 65536

@@ -105,6 +105,40 @@ def test_bf16_decode_ragged_batch():
         check_token(inp, buf, t)
 
 
+def test_bf16_decode_h128_split():
+    # 128 MLA heads (two 64-head workgroups per token and split); few tokens: split partials
+    # and the combine; lengths straddle k (dense and sparse rows)
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=8, ctx_range=(1, 6000))
+    inp = I.make_inputs(cfg, DEV)
+    lens = inp["seq_len"].tolist()
+    log(f"[gpu] h128 split lens {lens}")
+    assert inp["q"][0].shape[1] == 128 and min(lens) <= 2048 < max(lens)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in range(len(lens)):
+        check_token(inp, buf, t)
+
+
+def test_bf16_decode_h128_unsplit():
+    # 130 tokens x 2 head groups fill the GPU without splitting: normalized output path
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=130, ctx_range=(1500, 5000))
+    inp = I.make_inputs(cfg, DEV)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in (0, 1, 64, 65, 128, 129):
+        check_token(inp, buf, t)
+
+
+def test_bf16_prefill_h128():
+    cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], ctx=2100, prefill_tokens=40, H=128)
+    inp = I.make_inputs(cfg, DEV)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    kc = {}
+    for t in (0, 13, 26, 39):
+        check_token(inp, buf, t, key_cache=kc)
+
+
 def test_bf16_decode_edge_lengths():
     # n = 1, n = k, n = k + 1, n a multiple of 64, n = 64k + 1
     lens = [1, 2048, 2049, 4096, 4097, 63, 65, 2047]
