@@ -421,6 +421,16 @@ def test_full_decode_b64_paged_sampled():
         check_token(inp, buf, t)
 
 
+def test_full_decode_b64_paged_h128_sampled():
+    # 128 MLA heads at full size: 64 tokens x 2 head groups, split in two
+    inp, buf = run_cfg(I.CONFIGS["decode_b64_paged_h128"])
+    lens = inp["seq_len"].tolist()
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 31})
+    for t in pick:
+        log(f"[gpu] decode_b64_h128 token {t} n={lens[t]}")
+        check_token(inp, buf, t)
+
+
 def test_full_indexshare_sampled():
     inp, buf = run_cfg(I.CONFIGS["indexshare_decode_4layer"])
     for t in (0, 19, 31, 32, 39):
