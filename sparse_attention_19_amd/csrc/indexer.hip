@@ -211,6 +211,9 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         load_b(bq, lds[buf], 0);
 #pragma unroll
         for (int part = 0; part < kParts; ++part) {
+          // raised wave priority over the part: the SIMD's other wave issues in this one's
+          // gaps instead of competing for each slot (measured 1.5 % faster)
+          __builtin_amdgcn_s_setprio(3);
           f32x16 c0 = {}, c1 = {};
           const uint8_t* next = lds[buf] + (32 * (part + 1) + (lane & 31)) * kLdsRow + (lane >> 5) * 128;
 #pragma unroll
@@ -227,6 +230,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
           p0 = c0;
           p1 = c1;
           pend = key0 + 32 * part;
+          __builtin_amdgcn_s_setprio(0);
         }
         sbase = key0;
       }
