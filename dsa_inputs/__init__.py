@@ -90,6 +90,10 @@ def _cfgs() -> Dict[str, Config]:
         # batched decode as decode_b64_paged with 128 MLA heads (DeepSeek-V3.2's count)
         "decode_b64_paged_h128": Config("decode_b64_paged_h128", seed=5, batch=64, ctx=65536,
                                         ctx_range=(4096, 65536), **dict(big, H=128)),
+        # the prefill chunk with 128 MLA heads
+        "prefill_4096_at_128k_h128": Config("prefill_4096_at_128k_h128", seed=6, batch=1,
+                                            ctx=131072, prefill_tokens=4096, identity_pages=True,
+                                            **dict(big, H=128)),
         # IndexShare decode: 4 layers, 32 requests at 131072 + 8 dense requests at 1500
         "indexshare_decode_4layer": Config("indexshare_decode_4layer", seed=4, batch=32,
                                            ctx=131072, extra_dense=(1500,) * 8, layers=4, **big),

@@ -7,7 +7,7 @@ import dsa_inputs as I
 def test_configs_present():
     assert set(I.CONFIGS) == {"tiny_fp32", "decode_b1_32k", "decode_b64_paged",
                               "prefill_4096_at_128k", "indexshare_decode_4layer",
-                              "decode_b64_paged_h128"}
+                              "decode_b64_paged_h128", "prefill_4096_at_128k_h128"}
     h = I.CONFIGS["decode_b64_paged_h128"]
     assert (h.H, h.Dl, h.Dr, h.Hi, h.Di, h.k) == (128, 512, 64, 64, 128, 2048)
     assert I.context_lengths(h)[0] >= 4096 and len(I.context_lengths(h)) == 64

@@ -438,6 +438,14 @@ def test_full_indexshare_sampled():
         check_token(inp, buf, t)
 
 
+def test_full_prefill_h128_sampled():
+    inp, buf = run_cfg(I.CONFIGS["prefill_4096_at_128k_h128"])
+    kc = {}
+    for t in (0, 2048, 4095):
+        log(f"[gpu] prefill h128 token {t}")
+        check_token(inp, buf, t, key_cache=kc)
+
+
 def test_full_prefill_sampled():
     inp, buf = run_cfg(I.CONFIGS["prefill_4096_at_128k"])
     kc = {}
