@@ -18,8 +18,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
     the first Dl (latent) dims
   * -0.0 scores are canonicalised to +0.0
 
-Pinning status (see tests/test_oracle_pins.py): every function below is pinned against
-brute force, closed forms and invariants; none is "parity unpinned".
+Pinning status (tests/test_oracle_pins.py, tests/test_oracle_mutants.py): every function
+below, and the composition in oracle/run.py that the GPU tests compare against, is pinned
+against brute force, closed forms, invariants or an independent library decode; none is
+"parity unpinned".
 """
 from __future__ import annotations
 
@@ -117,30 +119,40 @@ def mla_absorbed(q: np.ndarray, rows: np.ndarray, Dl: int, sm_scale: float):
 
 # --------------------------------------------------------------------------- composite steps
 
+def visible_count(q_pos: int) -> int:
+    """Positions a query token at position q_pos sees.
+
+    The pages do not say whether a query sees its own key; the reading taken here is
+    that the current token's key is cached before the indexer runs, so a decode token of
+    a context of L positions (q_pos = L - 1) sees all L, and a prefill query at position
+    p sees 0..p (causal).  [§Lightning Indexer] scores "every token" of the context."""
+    return int(q_pos) + 1
+
+
+def group_token(q_idx, w, key_rows, n, k, layers, Dl, sm_scale):
+    """One query token through an IndexShare group of DSA layers.
+
+    [§IndexShare] one indexer serves a group of DSA layers: the full (first) layer runs
+    the indexer and top-k and caches the top-K indices; each following shared layer
+    reuses that selection with its own queries and its own latent cache.  A group of one
+    layer is plain DSA.
+
+    key_rows : logical indexer-key rows 0..n-1 of the token's request (at least n rows)
+    layers   : per layer (q [H][Dl+Dr], rows_of) where rows_of(positions) returns that
+               layer's latent rows [S][Dl+Dr] for the given logical positions
+    Returns (scores f32 [n], idx int32 [k], [(out [H][Dl], lse [H]) per layer])."""
+    scores = indexer_scores(q_idx, w, key_rows[:n])
+    idx = topk_positions(scores, n, k)
+    sel = idx[idx >= 0]
+    results = [mla_absorbed(q, rows_of(sel), Dl, sm_scale) for q, rows_of in layers]
+    return scores, idx, results
+
+
 def decode_token(q_idx, w, key_rows, q, kv_rows, n, k, Dl, sm_scale):
     """One decode token of one DSA layer: indexer -> top-k -> sparse (or dense) MLA.
 
     key_rows / kv_rows hold the logical rows 0..n-1 of the request.
     Returns (scores f32 [n], idx int32 [k], out f64 [H][Dl], lse f64 [H])."""
-    scores = indexer_scores(q_idx, w, key_rows[:n])
-    idx = topk_positions(scores, n, k)
-    sel = idx[idx >= 0]
-    out, lse = mla_absorbed(q, kv_rows[sel], Dl, sm_scale)
+    scores, idx, [(out, lse)] = group_token(q_idx, w, key_rows, n, k, [(q, lambda pos: kv_rows[pos])],
+                                            Dl, sm_scale)
     return scores, idx, out, lse
-
-
-def indexshare_group(q_idx, w, key_rows, qs, kv_rows_per_layer, n, k, Dl, sm_scale):
-    """One decode token through an IndexShare group of layers.
-
-    [§IndexShare] one indexer serves every 4 DSA layers: the full layer caches its top-K
-    indices and the following shared layers reuse that selection with their own queries
-    and latent caches.  Returns (idx, [(out, lse) per layer])."""
-    scores = indexer_scores(q_idx, w, key_rows[:n])
-    idx = topk_positions(scores, n, k)
-    sel = idx[idx >= 0]
-    return idx, [mla_absorbed(q, kv[sel], Dl, sm_scale) for q, kv in zip(qs, kv_rows_per_layer)]
-
-
-def prefill_token(q_idx, w, key_rows, q, kv_rows, pos, k, Dl, sm_scale):
-    """One query token of a causal prefill chunk at position `pos`: it sees 0..pos."""
-    return decode_token(q_idx, w, key_rows, q, kv_rows, pos + 1, k, Dl, sm_scale)

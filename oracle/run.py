@@ -43,12 +43,15 @@ def selected_rows(pool: torch.Tensor, block_table_row: np.ndarray, positions: np
 def expected_token(inp: dict, t: int, layers=None, key_cache: dict = None) -> dict:
     """Oracle results for query token t of an input set (decode or prefill).
 
+    The token belongs to request q_row[t] and sees O.visible_count(q_pos[t]) positions;
+    O.group_token runs the indexer and top-k once and every listed layer attends over
+    that selection with its own q and latent pool (layer 0 alone is plain DSA).
     key_cache (optional) keeps each request's logical key rows between calls.
     Returns dict(scores f32 [n], idx int32 [k], out list of f64 [H][Dl], lse list [H], n)."""
     cfg = inp["cfg"]
     layers = range(cfg.layers) if layers is None else layers
     b = int(inp["q_row"][t])
-    n = int(inp["q_pos"][t]) + 1
+    n = O.visible_count(int(inp["q_pos"][t]))
     bt = inp["block_table"][b].cpu().numpy()
     if key_cache is not None and b in key_cache and key_cache[b].shape[0] >= n:
         keys = key_cache[b]
@@ -56,16 +59,12 @@ def expected_token(inp: dict, t: int, layers=None, key_cache: dict = None) -> di
         keys = request_rows(inp["k_pool"], bt, n)
         if key_cache is not None:
             key_cache[b] = keys
-    scores = O.indexer_scores(to_f64(inp["q_idx"][t]), to_f64(inp["w"][t]), keys[:n])
-    idx = O.topk_positions(scores, n, cfg.k)
-    sel = idx[idx >= 0]
-    outs, lses = [], []
-    for l in layers:
-        rows = selected_rows(inp["kv_pools"][l], bt, sel)
-        o, s = O.mla_absorbed(to_f64(inp["q"][l][t]), rows, cfg.Dl, cfg.sm_scale)
-        outs.append(o)
-        lses.append(s)
-    return dict(scores=scores, idx=idx, out=outs, lse=lses, n=n)
+    per_layer = [(to_f64(inp["q"][l][t]),
+                  (lambda pos, pool=inp["kv_pools"][l]: selected_rows(pool, bt, pos)))
+                 for l in layers]
+    scores, idx, res = O.group_token(to_f64(inp["q_idx"][t]), to_f64(inp["w"][t]), keys, n, cfg.k,
+                                     per_layer, cfg.Dl, cfg.sm_scale)
+    return dict(scores=scores, idx=idx, out=[o for o, _ in res], lse=[s for _, s in res], n=n)
 
 
 def expected_topk(scores: np.ndarray, n_valid: np.ndarray, k: int) -> np.ndarray:

@@ -20,7 +20,8 @@ from oracle import dsa_oracle as O
 def real_impl():
     return types.SimpleNamespace(indexer_scores=O.indexer_scores, topk_positions=O.topk_positions,
                                  mla_absorbed=O.mla_absorbed, logical_rows=O.logical_rows,
-                                 decode_token=O.decode_token)
+                                 decode_token=O.decode_token, bf16_bits_to_f64=O.bf16_bits_to_f64,
+                                 visible_count=O.visible_count, group_token=O.group_token)
 
 
 # ------------------------------------------------------------------ indexer
@@ -220,3 +221,104 @@ def check_sparse_equals_dense(impl, seed=4):
 
 
 ALL_CHECKS = [check_indexer, check_topk, check_attention, check_paging, check_sparse_equals_dense]
+
+
+# ------------------------------------------------------------------ bf16 decode
+
+def check_bf16_decode(impl):
+    """Every one of the 65 536 bfloat16 bit patterns decodes to the value torch's own CPU
+    bfloat16 -> float32 conversion gives (NaN patterns: NaN)."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):          # signalling-NaN patterns widen to NaN
+        got = impl.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().double().numpy()
+    nan = np.isnan(ref)
+    assert got.shape == (65536,) and got.dtype == np.float64
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # sign of zero survives: pattern 0x8000 is -0.0
+    assert np.signbit(got[0x8000]) and got[0x8000] == 0.0 and not np.signbit(got[0])
+
+
+# ------------------------------------------------------------------ composition used by the GPU tests
+
+def _brute_token(inp, t, layers):
+    """Token t of an input set, from scratch in Python: integer scores over positions
+    0..q_pos (Python ints), the stable order (score desc, position asc), and pure-Python
+    attention of each layer (its own q and pool) over the first layer's selection.
+    Values are read with torch's own dtype conversion, rows through the block table."""
+    cfg = inp["cfg"]
+    b = int(inp["q_row"][t])
+    n = int(inp["q_pos"][t]) + 1
+    bt = inp["block_table"][b].tolist()
+    qi = [[int(round(x)) for x in row] for row in inp["q_idx"][t].float().tolist()]
+    w = [int(round(x)) for x in inp["w"][t].float().tolist()]
+    kp = inp["k_pool"].float()
+    scores = []
+    for s in range(n):
+        key = [int(round(x)) for x in kp[bt[s // 64], s % 64].tolist()]
+        scores.append(sum(wj * max(0, sum(a * c for a, c in zip(qj, key))) for qj, wj in zip(qi, w)))
+    if n <= cfg.k:
+        sel = list(range(n))
+    else:
+        sel = sorted(sorted(range(n), key=lambda s: (-scores[s], s))[:cfg.k])
+    res = []
+    for l in layers:
+        pool = inp["kv_pools"][l].float()
+        rows = [pool[bt[s // 64], s % 64].double().tolist() for s in sel]
+        q = inp["q"][l][t].float().double().tolist()
+        res.append(_brute_attention(q, rows, cfg.Dl, cfg.sm_scale))
+    return scores, sel + [-1] * (cfg.k - len(sel)), res
+
+
+def composition_inputs():
+    """Tiny CPU input sets: a 2-layer fp32 group with dense and sparse rows, a 2-layer
+    bf16 group, and a prefill chunk whose tokens belong to two requests."""
+    import torch
+    import dsa_inputs as I
+    tiny = I.CONFIGS["tiny_fp32"]
+    sets = []
+    g1 = I.shrink(tiny, batch=3, ctx_range=(70, 300), extra_dense=(50,), identity_pages=False, layers=2)
+    sets.append(I.make_inputs(g1))
+    g2 = I.shrink(tiny, dtype=torch.bfloat16, batch=2, ctx_range=(100, 260), extra_dense=(33,),
+                  identity_pages=False, layers=2)
+    sets.append(I.make_inputs(g2))
+    base = I.shrink(tiny, batch=2, ctx=300, identity_pages=False)
+    pre = I.make_inputs(base)
+    T = 6
+    gen = torch.Generator().manual_seed(11)
+    pre["q_row"] = torch.tensor([0, 1, 0, 1, 1, 0], dtype=torch.int32)
+    pre["q_pos"] = torch.tensor([299, 10, 63, 64, 200, 150], dtype=torch.int32)
+    pre["q_idx"] = torch.randint(-3, 4, (T, 4, 32), generator=gen).float()
+    pre["w"] = torch.randint(0, 3, (T, 4), generator=gen).float()
+    pre["q"] = [torch.randn(T, 8, 80, generator=gen)]
+    pre["cfg"] = I.shrink(base, prefill_tokens=T)
+    sets.append(pre)
+    return sets
+
+
+def check_composition(impl, inputs=None):
+    """oracle/run.py's expected_token, run with impl's visibility rule and group
+    composition, against _brute_token on every token of the tiny input sets."""
+    from oracle import run as R
+    saved = (O.visible_count, O.group_token)
+    O.visible_count, O.group_token = impl.visible_count, impl.group_token
+    try:
+        for inp in (inputs or composition_inputs()):
+            cfg = inp["cfg"]
+            layers = list(range(cfg.layers))
+            for t in range(inp["q_idx"].shape[0]):
+                got = R.expected_token(inp, t)
+                scores, idx, res = _brute_token(inp, t, layers)
+                assert got["n"] == len(scores)
+                assert [int(v) for v in got["scores"].tolist()] == scores, (cfg.name, t)
+                assert got["idx"].tolist() == idx, (cfg.name, t)
+                for (o, l), (bo, bl) in zip(zip(got["out"], got["lse"]), res):
+                    assert np.allclose(o, bo, rtol=1e-12, atol=1e-12), (cfg.name, t)
+                    assert np.allclose(l, bl, rtol=1e-12, atol=1e-12), (cfg.name, t)
+    finally:
+        O.visible_count, O.group_token = saved
+
+
+ALL_CHECKS += [check_bf16_decode, check_composition]

@@ -106,6 +106,43 @@ def _ignores_table(pool, bt, n):
     return pool[s // 64, s % 64]
 
 
+def _bf16_shift15(bits):
+    u = bits.astype(np.uint16).astype(np.uint32) << np.uint32(15)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _bf16_unsigned(bits):
+    u = (bits.astype(np.uint16).astype(np.uint32) & np.uint32(0x7FFF)) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+_GROUP = O.group_token     # the real composition (the mutants below wrap it)
+
+
+def _sees_before_own(q_pos):
+    return int(q_pos)                 # off by one: the query does not see its own key
+
+
+def _layers_select_own(q_idx, w, key_rows, n, k, layers, Dl, sm_scale):
+    """Each shared layer picks its own top-k from its own (head-summed) attention logits."""
+    scores, idx, res = _GROUP(q_idx, w, key_rows, n, k, layers[:1], Dl, sm_scale)
+    for q, rows_of in layers[1:]:
+        own = (rows_of(np.arange(n)) @ q.T).sum(1).astype(np.float32)
+        sel = O.topk_positions(own, n, k)
+        res.append(O.mla_absorbed(q, rows_of(sel[sel >= 0]), Dl, sm_scale))
+    return scores, idx, res
+
+
+def _layers_use_q0(q_idx, w, key_rows, n, k, layers, Dl, sm_scale):
+    q0 = layers[0][0]
+    return _GROUP(q_idx, w, key_rows, n, k, [(q0, r) for _, r in layers], Dl, sm_scale)
+
+
+def _layers_use_pool0(q_idx, w, key_rows, n, k, layers, Dl, sm_scale):
+    r0 = layers[0][1]
+    return _GROUP(q_idx, w, key_rows, n, k, [(q, r0) for q, _ in layers], Dl, sm_scale)
+
+
 MUTANTS = {
     "indexer_no_relu": ("indexer_scores", _no_relu, P.check_indexer),
     "indexer_relu_after_weight": ("indexer_scores", _relu_after_weight, P.check_indexer),
@@ -122,6 +159,12 @@ MUTANTS = {
     "attn_lse": ("mla_absorbed", _lse_missing_max, P.check_attention),
     "paging_transposed": ("logical_rows", _transposed_block, P.check_paging),
     "paging_no_table": ("logical_rows", _ignores_table, P.check_paging),
+    "bf16_shift15": ("bf16_bits_to_f64", _bf16_shift15, P.check_bf16_decode),
+    "bf16_unsigned": ("bf16_bits_to_f64", _bf16_unsigned, P.check_bf16_decode),
+    "visibility_off_by_one": ("visible_count", _sees_before_own, P.check_composition),
+    "indexshare_layers_select_own": ("group_token", _layers_select_own, P.check_composition),
+    "indexshare_layers_use_q0": ("group_token", _layers_use_q0, P.check_composition),
+    "indexshare_layers_use_pool0": ("group_token", _layers_use_pool0, P.check_composition),
 }
 
 
