@@ -43,6 +43,9 @@ class Config:
     identity_pages : physical block i holds logical block i (else a random permutation)
     layout_seed    : seed of the context lengths and the page permutation when set (else
                      `seed`): copies of a workload with new data but the same layout
+    index_share    : with several layers, the first layer's selection serves the group
+                     (IndexShare); False runs the indexer and top-k in every layer, the plain
+                     DSA that IndexShare is compared with (same indexer inputs per layer)
     """
     name: str
     seed: int
@@ -64,6 +67,7 @@ class Config:
     layers: int = 1
     identity_pages: bool = False
     layout_seed: Optional[int] = None
+    index_share: bool = True
 
     @property
     def row_dim(self) -> int:
@@ -179,6 +183,7 @@ def make_inputs(cfg: Config, device="cpu") -> dict:
 
     Returns a dict with
       seq_len      int32 [B]            context length per request (query token included)
+      seq_len_host, q_row_host, q_pos_host   CPU int32 copies of seq_len, q_row, q_pos
       block_table  int32 [B][max_blocks]
       k_pool       [nblk][64][Di]       single-head indexer keys (cfg.dtype)
       q_idx        [T][Hi][Di]          indexer queries (cfg.dtype)
@@ -204,6 +209,9 @@ def make_inputs(cfg: Config, device="cpu") -> dict:
     inp = {
         "cfg": cfg,
         "seq_len": torch.tensor(lens, dtype=torch.int32, device=device),
+        "seq_len_host": torch.tensor(lens, dtype=torch.int32),
+        "q_row_host": q_row.clone(),
+        "q_pos_host": q_pos.clone(),
         "block_table": bt.to(device),
         "q_row": q_row.to(device),
         "q_pos": q_pos.to(device),

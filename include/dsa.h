@@ -23,9 +23,12 @@
  *   - Every argument is validated on the host BEFORE any HIP call.  A rejected call
  *     returns an error status, enqueues nothing, and leaves a message for
  *     dsa_last_error() (thread-local).  Nothing is thrown across the ABI.
- *   - Device contents (block tables, lengths, indices) are trusted only as far as the
- *     kernels' own bounds checks go: a position outside [0, n) in an index list is
- *     skipped; a block-table entry outside [0, num_blocks) reads as an empty row.
+ *   - Lengths and query positions come with host copies (seq_len_host, n_valid_host,
+ *     the chunk's *_host arrays) that must hold the same values as the device arrays;
+ *     the host copies are what the validation checks.  Other device contents (block
+ *     tables, indices) are trusted only as far as the kernels' own bounds checks go: a
+ *     position outside [0, n) in an index list is skipped; a block-table entry outside
+ *     [0, num_blocks) reads as an empty row; every length is clamped to max_blocks * 64.
  *   - Paged pools hold rows of `row_dim` elements in blocks of DSA_BLOCK positions:
  *     element (blk, slot, c) of a pool is at data[(blk * DSA_BLOCK + slot) * row_dim + c].
  *     Logical position s of request b is slot s % 64 of physical block
@@ -78,9 +81,22 @@ typedef struct {
 typedef struct {
   const int32_t* block_table;  /* device [batch][max_blocks] physical block ids */
   const int32_t* seq_len;      /* device [batch] context length incl. the current token */
+  const int32_t* seq_len_host; /* host [batch], the same values: every length is checked
+                                  against max_blocks * DSA_BLOCK before any launch */
   int32_t batch;
   int32_t max_blocks;          /* positions of a request are < max_blocks * DSA_BLOCK */
 } dsa_page_table;
+
+/* Query tokens of a causal prefill chunk: token t belongs to request q_row[t] and sits at
+ * position q_pos[t] of it, so it sees positions 0 .. q_pos[t] (the chunk's keys and
+ * latents are already in the caches).  The host copies hold the same values and are
+ * checked before any launch: 0 <= q_row[t] < batch and 0 <= q_pos[t] < seq_len[q_row[t]]. */
+typedef struct {
+  const int32_t* q_row;        /* device [T] */
+  const int32_t* q_pos;        /* device [T] */
+  const int32_t* q_row_host;   /* host [T] */
+  const int32_t* q_pos_host;   /* host [T] */
+} dsa_chunk;
 
 /* IndexShare top-k cache (host struct describing a caller-owned device buffer). */
 typedef struct {
@@ -103,18 +119,18 @@ typedef struct {
  *   w      device [T][Hi] fp32 head weights
  *   k_pool paged keys, row_dim = Di
  *   pt     page table
- *   q_row, q_pos  device [T] or both NULL.
- *          NULL (decode): token t belongs to request t (T == pt->batch) and sees
- *          n_t = seq_len[t] positions.  Otherwise (prefill chunk): token t belongs to
- *          request q_row[t] and sees n_t = q_pos[t] + 1 positions (causal).
+ *   chunk  NULL (decode): token t belongs to request t (T == pt->batch) and sees
+ *          n_t = seq_len[t] positions.  Otherwise (prefill chunk of T tokens): token t
+ *          belongs to request q_row[t] and sees n_t = q_pos[t] + 1 positions (causal).
  *   scores device [T][ld] fp32; entries s >= n_t are left untouched.  ld >= max_blocks*64.
+ * Errors: DSA_ERR_INVALID for a length outside [0, max_blocks*64], a chunk token outside
+ * its request, or a NULL pointer; DSA_ERR_UNSUPPORTED for dims without an instance.
  * Summation order is free: with integer-valued inputs whose partial sums stay below
  * 2^24 every score is exact.
  */
 dsa_status dsa_indexer_scores(const void* q_idx, const float* w, const dsa_pool* k_pool,
-                              const dsa_page_table* pt, const int32_t* q_row,
-                              const int32_t* q_pos, int32_t T, int32_t Hi, int32_t Di,
-                              float* scores, int64_t ld, void* stream);
+                              const dsa_page_table* pt, const dsa_chunk* chunk, int32_t T,
+                              int32_t Hi, int32_t Di, float* scores, int64_t ld, void* stream);
 
 /*
  * Top-k selection  [§Lightning Indexer: queries seeing fewer than K tokens stay dense,
@@ -126,6 +142,8 @@ dsa_status dsa_indexer_scores(const void* q_idx, const float* w, const dsa_pool*
  *              position, the lower position first; written in ascending order.
  * Scores compare as fp32 values (-0.0 == +0.0); NaN scores are not supported.
  *   scores  device [rows][ld] fp32      n_valid device [rows] int32
+ *   n_valid_host  host [rows], the same values; DSA_ERR_INVALID unless every
+ *                 0 <= n_valid[r] + n_add <= ld (checked before any launch)
  *   idx     device [rows][ld_idx] int32 (ld_idx >= k)
  *   ws/ws_bytes  workspace of dsa_workspace_bytes(DSA_OP_TOPK, rows, ld, k, 0, 0) bytes
  *                (for ld > 32768: per-row bounds and the (key, position) lists of the
@@ -133,9 +151,9 @@ dsa_status dsa_indexer_scores(const void* q_idx, const float* w, const dsa_pool*
  *                 entry do not matter; may be NULL when the size is 0)
  * The result is deterministic (independent of scheduling).
  */
-dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int32_t n_add,
-                    int32_t rows, int32_t k, int32_t* idx, int64_t ld_idx, void* ws,
-                    size_t ws_bytes, void* stream);
+dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid,
+                    const int32_t* n_valid_host, int32_t n_add, int32_t rows, int32_t k,
+                    int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Sparse MLA, absorbed (MQA) mode, one decode token per request  [§Sparse MLA,
@@ -150,8 +168,11 @@ dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int
  *   idx  device [B][ld_idx] int32 positions (e.g. from dsa_topk or an IndexShare cache)
  *   out  device [B][H][Dl] (kv->dtype)      lse device [B][H] fp32 or NULL
  *   ws   workspace of dsa_workspace_bytes(DSA_OP_MLA, B, 0, k, H, Dl) bytes
- * fp32 accumulation throughout; an empty S (only possible with a hand-made idx row)
- * gives out = 0 and lse = -inf.
+ * fp32 accumulation throughout; an empty S (n = 0, or a hand-made idx row) gives out = 0
+ * and lse = -inf.  Positions outside S never contribute, whatever their pool rows hold.
+ * Errors: DSA_ERR_INVALID for a length outside [0, max_blocks*64] or a NULL pointer,
+ * DSA_ERR_WORKSPACE for a missing or short workspace, DSA_ERR_UNSUPPORTED for dims
+ * without an instance.
  */
 dsa_status dsa_sparse_mla_decode(const void* q, const dsa_pool* kv, const dsa_page_table* pt,
                                  const int32_t* idx, int64_t ld_idx, int32_t k, int32_t H,
@@ -160,14 +181,15 @@ dsa_status dsa_sparse_mla_decode(const void* q, const dsa_pool* kv, const dsa_pa
 
 /*
  * Sparse MLA for a causal prefill chunk: as dsa_sparse_mla_decode for T query tokens,
- * token t belonging to request q_row[t] and seeing n = q_pos[t] + 1 positions.
+ * token t belonging to request chunk->q_row[t] and seeing n = q_pos[t] + 1 positions.
  *   q [T][H][Dl+Dr], idx [T][ld_idx], out [T][H][Dl], lse [T][H] or NULL (all device).
+ *   chunk  token positions (required when T > 0; checked as for dsa_indexer_scores)
  *   ws of dsa_workspace_bytes(DSA_OP_MLA, T, 0, k, H, Dl) bytes.
  */
 dsa_status dsa_sparse_mla_prefill(const void* q, const dsa_pool* kv, const dsa_page_table* pt,
-                                  const int32_t* q_row, const int32_t* q_pos, const int32_t* idx,
-                                  int64_t ld_idx, int32_t T, int32_t k, int32_t H, int32_t Dl,
-                                  int32_t Dr, float sm_scale, void* out, float* lse, void* ws,
+                                  const dsa_chunk* chunk, const int32_t* idx, int64_t ld_idx,
+                                  int32_t T, int32_t k, int32_t H, int32_t Dl, int32_t Dr,
+                                  float sm_scale, void* out, float* lse, void* ws,
                                   size_t ws_bytes, void* stream);
 
 /*
@@ -190,7 +212,9 @@ dsa_status dsa_index_cache_get(const dsa_index_cache* c, uint64_t step, int32_t 
                                const int32_t** idx);
 
 /* Workspace bytes an operation needs for `rows` query tokens (0 = none).  max_len is the
- * score row stride `ld` for DSA_OP_TOPK and is ignored for DSA_OP_MLA. */
+ * score row stride `ld` for DSA_OP_TOPK and is ignored for DSA_OP_MLA.  For DSA_OP_MLA
+ * the size is that of the bf16 instance (split partials); the fp32 instance needs none,
+ * so the figure is an upper bound for it. */
 size_t dsa_workspace_bytes(int32_t op, int32_t rows, int64_t max_len, int32_t k, int32_t H, int32_t Dl);
 
 /* Static name of a status; thread-local text of the last rejected call. */

@@ -14,11 +14,12 @@ from typing import Optional
 import torch
 
 from ._lib import (DSA_BF16, DSA_BLOCK, DSA_ERR_INVALID, DSA_F32, DSA_MAX_K, DSA_OP_MLA, DSA_OP_TOPK, LIB,
-                   LIB_PATH, DsaError, DsaIndexCache, DsaPageTable, DsaPool, check)
+                   LIB_PATH, DsaChunk, DsaError, DsaIndexCache, DsaPageTable, DsaPool, check)
 
 __all__ = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
-    "IndexCache", "dsa_workspace_bytes", "workspace", "DsaError", "LIB_PATH", "DSA_OP_TOPK", "DSA_OP_MLA",
+    "IndexCache", "PageTable", "Chunk", "dsa_workspace_bytes", "workspace", "DsaError", "LIB_PATH",
+    "DSA_OP_TOPK", "DSA_OP_MLA",
     "dsa_timing_start", "dsa_timing_collect",
 ]
 
@@ -55,11 +56,55 @@ def _pool(pool: torch.Tensor, name: str) -> DsaPool:
     return DsaPool(_dev(pool, name), pool.shape[0], DSA_BLOCK, pool.shape[2], _DT[pool.dtype])
 
 
-def _pt(block_table: torch.Tensor, seq_len: torch.Tensor) -> DsaPageTable:
-    if block_table.dim() != 2 or seq_len.dim() != 1 or seq_len.shape[0] != block_table.shape[0]:
-        raise ValueError("block_table must be [B][max_blocks] and seq_len [B]")
-    return DsaPageTable(_dev(block_table, "block_table", torch.int32), _dev(seq_len, "seq_len", torch.int32),
-                        block_table.shape[0], block_table.shape[1])
+def _host(t: torch.Tensor, name: str) -> int:
+    """Host pointer of a CPU int32 tensor (the host copy of a device length array)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 host (CPU) tensor")
+    return t.data_ptr()
+
+
+class PageTable:
+    """dsa_page_table: block_table [B][max_blocks] and seq_len [B] on the device, and the
+    host copy seq_len_host [B] (CPU int32, the same values) that the library checks."""
+
+    def __init__(self, block_table: torch.Tensor, seq_len: torch.Tensor, seq_len_host: torch.Tensor):
+        if block_table.dim() != 2 or seq_len.dim() != 1 or seq_len.shape[0] != block_table.shape[0]:
+            raise ValueError("block_table must be [B][max_blocks] and seq_len [B]")
+        if seq_len_host.shape != seq_len.shape:
+            raise ValueError("seq_len_host must have the shape of seq_len")
+        self.tensors = (block_table, seq_len, seq_len_host)   # kept alive with the struct
+        self.c = DsaPageTable(_dev(block_table, "block_table", torch.int32), _dev(seq_len, "seq_len", torch.int32),
+                              _host(seq_len_host, "seq_len_host"), block_table.shape[0], block_table.shape[1])
+
+    @property
+    def batch(self) -> int:
+        return self.c.batch
+
+    @property
+    def seq_len(self) -> torch.Tensor:
+        return self.tensors[1]
+
+    @property
+    def seq_len_host(self) -> torch.Tensor:
+        return self.tensors[2]
+
+
+class Chunk:
+    """dsa_chunk: the request q_row [T] and position q_pos [T] of each query token of a
+    prefill chunk on the device, and their host copies (CPU int32, the same values)."""
+
+    def __init__(self, q_row: torch.Tensor, q_pos: torch.Tensor, q_row_host: torch.Tensor,
+                 q_pos_host: torch.Tensor):
+        T = q_row.shape[0]
+        if any(x.dim() != 1 or x.shape[0] != T for x in (q_pos, q_row_host, q_pos_host)):
+            raise ValueError("q_row, q_pos and their host copies must all be [T]")
+        self.tensors = (q_row, q_pos, q_row_host, q_pos_host)
+        self.T = T
+        self.q_pos, self.q_pos_host = q_pos, q_pos_host
+        self.c = DsaChunk(_dev(q_row, "q_row", torch.int32), _dev(q_pos, "q_pos", torch.int32),
+                          _host(q_row_host, "q_row_host"), _host(q_pos_host, "q_pos_host"))
 
 
 def dsa_workspace_bytes(op: int, rows: int, max_len: int, k: int, H: int, Dl: int) -> int:
@@ -72,53 +117,56 @@ def workspace(op: int, rows: int, max_len: int, k: int, H: int, Dl: int, device)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def dsa_indexer_scores(q_idx, w, k_pool, block_table, seq_len, scores, q_row=None, q_pos=None, stream=None):
+def _ws(ws):
+    return (_opt(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size())
+
+
+def dsa_indexer_scores(q_idx, w, k_pool, pt: PageTable, scores, chunk: Optional[Chunk] = None, stream=None):
     """scores[t][s] for s < n_t (see dsa_indexer_scores in include/dsa.h).
-    q_idx [T][Hi][Di], w [T][Hi] fp32, k_pool [nblk][64][Di], scores [T][ld] fp32."""
+    q_idx [T][Hi][Di], w [T][Hi] fp32, k_pool [nblk][64][Di], scores [T][ld] fp32;
+    chunk None = decode (one token per request)."""
     T, Hi, Di = q_idx.shape
-    pool, pt = _pool(k_pool, "k_pool"), _pt(block_table, seq_len)
+    pool = _pool(k_pool, "k_pool")
     check(LIB.dsa_indexer_scores(_dev(q_idx, "q_idx", k_pool.dtype), _dev(w, "w", torch.float32),
-                                 ctypes.byref(pool), ctypes.byref(pt), _opt(q_row, "q_row", torch.int32),
-                                 _opt(q_pos, "q_pos", torch.int32), T, Hi, Di,
+                                 ctypes.byref(pool), ctypes.byref(pt.c),
+                                 None if chunk is None else ctypes.byref(chunk.c), T, Hi, Di,
                                  _dev(scores, "scores", torch.float32), scores.shape[1],
                                  _stream(stream, scores)))
 
 
-def dsa_topk(scores, n_valid, k, idx, n_add=0, ws=None, stream=None):
-    """idx[r] = top-k positions of scores[r][:n_valid[r] + n_add] (ascending, -1 padded)."""
+def dsa_topk(scores, n_valid, n_valid_host, k, idx, n_add=0, ws=None, stream=None):
+    """idx[r] = top-k positions of scores[r][:n_valid[r] + n_add] (ascending, -1 padded);
+    n_valid_host is the CPU int32 copy of n_valid."""
     rows, ld = scores.shape
+    if n_valid_host.shape != n_valid.shape:
+        raise ValueError("n_valid_host must have the shape of n_valid")
     check(LIB.dsa_topk(_dev(scores, "scores", torch.float32), ld, _dev(n_valid, "n_valid", torch.int32),
-                       n_add, rows, k, _dev(idx, "idx", torch.int32), idx.shape[1],
-                       _opt(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
-                       _stream(stream, scores)))
+                       _host(n_valid_host, "n_valid_host"), n_add, rows, k, _dev(idx, "idx", torch.int32),
+                       idx.shape[1], *_ws(ws), _stream(stream, scores)))
 
 
-def dsa_sparse_mla_decode(q, kv_pool, block_table, seq_len, idx, k, sm_scale, out, lse=None, ws=None,
-                          stream=None):
+def dsa_sparse_mla_decode(q, kv_pool, pt: PageTable, idx, k, sm_scale, out, lse=None, ws=None, stream=None):
     """Absorbed-mode sparse MLA for one decode token per request.
     q [B][H][Dl+Dr], kv_pool [nblk][64][Dl+Dr], idx [B][>=k] int32, out [B][H][Dl]."""
     B, H, D = q.shape
     Dl = out.shape[2]
-    pool, pt = _pool(kv_pool, "kv_pool"), _pt(block_table, seq_len)
-    check(LIB.dsa_sparse_mla_decode(_dev(q, "q", kv_pool.dtype), ctypes.byref(pool), ctypes.byref(pt),
+    pool = _pool(kv_pool, "kv_pool")
+    check(LIB.dsa_sparse_mla_decode(_dev(q, "q", kv_pool.dtype), ctypes.byref(pool), ctypes.byref(pt.c),
                                     _dev(idx, "idx", torch.int32), idx.shape[1], k, H, Dl, D - Dl,
                                     float(sm_scale), _dev(out, "out", kv_pool.dtype),
-                                    _opt(lse, "lse", torch.float32), _opt(ws, "ws"),
-                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream, q)))
+                                    _opt(lse, "lse", torch.float32), *_ws(ws), _stream(stream, q)))
 
 
-def dsa_sparse_mla_prefill(q, kv_pool, block_table, seq_len, q_row, q_pos, idx, k, sm_scale, out, lse=None,
-                           ws=None, stream=None):
+def dsa_sparse_mla_prefill(q, kv_pool, pt: PageTable, chunk: Chunk, idx, k, sm_scale, out, lse=None, ws=None,
+                           stream=None):
     """Absorbed-mode sparse MLA for a causal prefill chunk of T tokens."""
     T, H, D = q.shape
     Dl = out.shape[2]
-    pool, pt = _pool(kv_pool, "kv_pool"), _pt(block_table, seq_len)
-    check(LIB.dsa_sparse_mla_prefill(_dev(q, "q", kv_pool.dtype), ctypes.byref(pool), ctypes.byref(pt),
-                                     _dev(q_row, "q_row", torch.int32), _dev(q_pos, "q_pos", torch.int32),
-                                     _dev(idx, "idx", torch.int32), idx.shape[1], T, k, H, Dl, D - Dl,
-                                     float(sm_scale), _dev(out, "out", kv_pool.dtype),
-                                     _opt(lse, "lse", torch.float32), _opt(ws, "ws"),
-                                     0 if ws is None else ws.numel() * ws.element_size(), _stream(stream, q)))
+    pool = _pool(kv_pool, "kv_pool")
+    check(LIB.dsa_sparse_mla_prefill(_dev(q, "q", kv_pool.dtype), ctypes.byref(pool), ctypes.byref(pt.c),
+                                     ctypes.byref(chunk.c), _dev(idx, "idx", torch.int32), idx.shape[1], T, k,
+                                     H, Dl, D - Dl, float(sm_scale), _dev(out, "out", kv_pool.dtype),
+                                     _opt(lse, "lse", torch.float32), *_ws(ws), _stream(stream, q)))
 
 
 class IndexCache:

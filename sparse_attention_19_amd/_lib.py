@@ -18,6 +18,7 @@ DSA_F32, DSA_BF16 = 0, 1
 DSA_OP_TOPK, DSA_OP_MLA = 0, 1
 DSA_BLOCK = 64
 DSA_MAX_K = 2048
+ABI_VERSION = b"dsa-gfx950 0.2.0"   # argument layout this binding marshals for
 
 EXPORTS = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
@@ -34,7 +35,12 @@ class DsaPool(ctypes.Structure):
 
 class DsaPageTable(ctypes.Structure):
     _fields_ = [("block_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
-                ("batch", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+                ("seq_len_host", ctypes.c_void_p), ("batch", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+
+
+class DsaChunk(ctypes.Structure):
+    _fields_ = [("q_row", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+                ("q_row_host", ctypes.c_void_p), ("q_pos_host", ctypes.c_void_p)]
 
 
 class DsaIndexCache(ctypes.Structure):
@@ -49,11 +55,13 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     pool_p, pt_p, cache_p = ctypes.POINTER(DsaPool), ctypes.POINTER(DsaPageTable), ctypes.POINTER(DsaIndexCache)
+    chunk_p = ctypes.POINTER(DsaChunk)
     sig = {
-        "dsa_indexer_scores": [P, P, pool_p, pt_p, P, P, I32, I32, I32, P, I64, P],
-        "dsa_topk": [P, I64, P, I32, I32, I32, P, I64, P, SZ, P],
+        "dsa_indexer_scores": [P, P, pool_p, pt_p, chunk_p, I32, I32, I32, P, I64, P],
+        "dsa_topk": [P, I64, P, P, I32, I32, I32, P, I64, P, SZ, P],
         "dsa_sparse_mla_decode": [P, pool_p, pt_p, P, I64, I32, I32, I32, I32, F, P, P, P, SZ, P],
-        "dsa_sparse_mla_prefill": [P, pool_p, pt_p, P, P, P, I64, I32, I32, I32, I32, I32, F, P, P, P, SZ, P],
+        "dsa_sparse_mla_prefill": [P, pool_p, pt_p, chunk_p, P, I64, I32, I32, I32, I32, I32, F, P, P, P, SZ,
+                                   P],
         "dsa_index_cache_init": [cache_p, P, I64, I32, I32, I32],
         "dsa_index_cache_publish": [cache_p, ctypes.c_uint64],
         "dsa_index_cache_get": [cache_p, ctypes.c_uint64, I32, ctypes.POINTER(ctypes.c_void_p)],
@@ -76,6 +84,9 @@ def _load() -> ctypes.CDLL:
     lib.dsa_status_string.restype = ctypes.c_char_p
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_version.restype = ctypes.c_char_p
+    if lib.dsa_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} is stale ({lib.dsa_version().decode()}, this binding expects "
+                          f"{ABI_VERSION.decode()}): rebuild it with `python sparse_attention_19_amd/build.py`")
     return lib
 
 

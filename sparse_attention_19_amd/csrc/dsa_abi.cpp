@@ -51,26 +51,46 @@ dsa_status check_pool(const dsa_pool* p, const char* name, int32_t row_dim) {
   return DSA_OK;
 }
 
+// The page table, including every request length (from the host copy) against the
+// table's capacity max_blocks * 64.
 dsa_status check_pt(const dsa_page_table* pt) {
   if (!pt) return fail(DSA_ERR_INVALID, "page table is NULL");
   if (!pt->block_table || !pt->seq_len)
     return fail(DSA_ERR_INVALID, "page table: block_table/seq_len is NULL");
+  if (!pt->seq_len_host) return fail(DSA_ERR_INVALID, "page table: seq_len_host is NULL");
   if (pt->batch <= 0) return fail(DSA_ERR_INVALID, "page table: batch %d <= 0", pt->batch);
   if (pt->max_blocks <= 0 || pt->max_blocks > (INT32_MAX / DSA_BLOCK))
     return fail(DSA_ERR_INVALID, "page table: max_blocks %d out of range", pt->max_blocks);
+  const int64_t cap = (int64_t)pt->max_blocks * DSA_BLOCK;
+  for (int32_t b = 0; b < pt->batch; ++b) {
+    const int32_t n = pt->seq_len_host[b];
+    if (n < 0 || n > cap)
+      return fail(DSA_ERR_INVALID, "page table: seq_len[%d] = %d outside [0, max_blocks * 64 = %lld]", b, n,
+                  (long long)cap);
+  }
   return DSA_OK;
 }
 
-dsa_status check_tokens(const int32_t* q_row, const int32_t* q_pos, int32_t T,
-                        const dsa_page_table* pt, bool prefill) {
+// Query tokens: decode (chunk NULL) has one token per request; a prefill chunk's tokens
+// must each sit inside their request (host copies checked against seq_len_host).
+dsa_status check_tokens(const dsa_chunk* chunk, int32_t T, const dsa_page_table* pt, bool prefill) {
   if (T < 0) return fail(DSA_ERR_INVALID, "T = %d < 0", T);
-  if (prefill) {
-    if (T != 0 && (!q_row || !q_pos)) return fail(DSA_ERR_INVALID, "prefill needs q_row and q_pos");
-  } else {
-    if ((q_row == nullptr) != (q_pos == nullptr))
-      return fail(DSA_ERR_INVALID, "q_row and q_pos must be both NULL (decode) or both set");
-    if (!q_row && T != pt->batch)
+  if (!chunk) {
+    if (prefill && T != 0) return fail(DSA_ERR_INVALID, "prefill needs the chunk's token positions");
+    if (!prefill && T != pt->batch)
       return fail(DSA_ERR_INVALID, "decode: T = %d but page table batch = %d", T, pt->batch);
+    return DSA_OK;
+  }
+  if (T == 0) return DSA_OK;
+  if (!chunk->q_row || !chunk->q_pos || !chunk->q_row_host || !chunk->q_pos_host)
+    return fail(DSA_ERR_INVALID, "chunk: q_row/q_pos/q_row_host/q_pos_host is NULL");
+  for (int32_t t = 0; t < T; ++t) {
+    const int32_t b = chunk->q_row_host[t], p = chunk->q_pos_host[t];
+    if (b < 0 || b >= pt->batch)
+      return fail(DSA_ERR_INVALID, "chunk: q_row[%d] = %d outside [0, batch = %d)", t, b, pt->batch);
+    if (p < 0 || p >= pt->seq_len_host[b])
+      return fail(DSA_ERR_INVALID, "chunk: q_pos[%d] = %d outside [0, seq_len[%d] = %d)", t, p, b,
+                  pt->seq_len_host[b]);
   }
   return DSA_OK;
 }
@@ -150,15 +170,14 @@ KernelEvents::KernelEvents(const char* name) {
 extern "C" {
 
 dsa_status dsa_indexer_scores(const void* q_idx, const float* w, const dsa_pool* k_pool,
-                              const dsa_page_table* pt, const int32_t* q_row, const int32_t* q_pos,
-                              int32_t T, int32_t Hi, int32_t Di, float* scores, int64_t ld,
-                              void* stream) {
+                              const dsa_page_table* pt, const dsa_chunk* chunk, int32_t T, int32_t Hi,
+                              int32_t Di, float* scores, int64_t ld, void* stream) {
   if (T != 0 && (!q_idx || !w || !scores)) return fail(DSA_ERR_INVALID, "q_idx/w/scores is NULL");
   if (Hi <= 0 || Di <= 0) return fail(DSA_ERR_INVALID, "Hi/Di must be positive");
   dsa_status s = check_pool(k_pool, "k_pool", Di);
   if (s) return s;
   if ((s = check_pt(pt))) return s;
-  if ((s = check_tokens(q_row, q_pos, T, pt, false))) return s;
+  if ((s = check_tokens(chunk, T, pt, false))) return s;
   if (ld < (int64_t)pt->max_blocks * DSA_BLOCK)
     return fail(DSA_ERR_INVALID, "ld %lld < max_blocks * 64 = %lld", (long long)ld,
                 (long long)pt->max_blocks * DSA_BLOCK);
@@ -172,22 +191,30 @@ dsa_status dsa_indexer_scores(const void* q_idx, const float* w, const dsa_pool*
       return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer needs Hi <= 64, Di <= 128, Di %% 4 == 0");
   }
   if (T == 0) return ok();
+  const int32_t* q_row = chunk ? chunk->q_row : nullptr;
+  const int32_t* q_pos = chunk ? chunk->q_pos : nullptr;
   dsa::IndexerArgs a{q_idx, w, k_pool->data, k_pool->num_blocks, pt->block_table, pt->seq_len,
                      pt->max_blocks, pt->batch, q_row, q_pos, T, Hi, Di, bf16, q_row != nullptr,
                      scores, ld};
   return launched(dsa::launch_indexer(a, (hipStream_t)stream), "indexer launch");
 }
 
-dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int32_t n_add,
-                    int32_t rows, int32_t k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes,
-                    void* stream) {
-  if (rows != 0 && (!scores || !n_valid || !idx))
-    return fail(DSA_ERR_INVALID, "scores/n_valid/idx is NULL");
+dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, const int32_t* n_valid_host,
+                    int32_t n_add, int32_t rows, int32_t k, int32_t* idx, int64_t ld_idx, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (rows != 0 && (!scores || !n_valid || !n_valid_host || !idx))
+    return fail(DSA_ERR_INVALID, "scores/n_valid/n_valid_host/idx is NULL");
   if (rows < 0) return fail(DSA_ERR_INVALID, "rows = %d < 0", rows);
   if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_UNSUPPORTED, "k = %d outside [1, %d]", k, DSA_MAX_K);
   if (ld < 1 || ld > INT32_MAX) return fail(DSA_ERR_INVALID, "ld %lld out of range", (long long)ld);
   if (ld_idx < k) return fail(DSA_ERR_INVALID, "ld_idx %lld < k %d", (long long)ld_idx, k);
   if (n_add < 0 || n_add > 1) return fail(DSA_ERR_INVALID, "n_add must be 0 or 1");
+  for (int32_t r = 0; r < rows; ++r) {
+    const int64_t n = (int64_t)n_valid_host[r] + n_add;
+    if (n < 0 || n > ld)
+      return fail(DSA_ERR_INVALID, "row %d sees %lld positions, outside [0, ld = %lld]", r, (long long)n,
+                  (long long)ld);
+  }
   const size_t need = dsa::topk_workspace_bytes(rows, ld, k);
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws ? ws_bytes : 0);
@@ -211,16 +238,16 @@ dsa_status dsa_sparse_mla_decode(const void* q, const dsa_pool* kv, const dsa_pa
 }
 
 dsa_status dsa_sparse_mla_prefill(const void* q, const dsa_pool* kv, const dsa_page_table* pt,
-                                  const int32_t* q_row, const int32_t* q_pos, const int32_t* idx,
-                                  int64_t ld_idx, int32_t T, int32_t k, int32_t H, int32_t Dl,
-                                  int32_t Dr, float sm_scale, void* out, float* lse, void* ws,
-                                  size_t ws_bytes, void* stream) {
+                                  const dsa_chunk* chunk, const int32_t* idx, int64_t ld_idx, int32_t T,
+                                  int32_t k, int32_t H, int32_t Dl, int32_t Dr, float sm_scale, void* out,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
   dsa_status s = check_mla(q, kv, pt, idx, ld_idx, k, H, Dl, Dr, sm_scale, out, ws, ws_bytes, T);
   if (s) return s;
-  if ((s = check_tokens(q_row, q_pos, T, pt, true))) return s;
+  if ((s = check_tokens(chunk, T, pt, true))) return s;
   if (T == 0) return ok();
   dsa::MlaArgs a{q, kv->data, kv->num_blocks, pt->block_table, pt->seq_len, pt->max_blocks, pt->batch,
-                 q_row, q_pos, idx, ld_idx, T, k, H, Dl, Dr, sm_scale, kv->dtype == DSA_BF16, out, lse, ws};
+                 chunk->q_row, chunk->q_pos, idx, ld_idx, T, k, H, Dl, Dr, sm_scale, kv->dtype == DSA_BF16,
+                 out, lse, ws};
   return launched(dsa::launch_mla(a, (hipStream_t)stream), "sparse MLA prefill launch");
 }
 
@@ -280,7 +307,7 @@ const char* dsa_status_string(dsa_status s) {
 
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
-const char* dsa_version(void) { return "dsa-gfx950 0.1.0"; }
+const char* dsa_version(void) { return "dsa-gfx950 0.2.0"; }
 
 dsa_status dsa_timing_start(int32_t capacity) {
   if (capacity < 1 || capacity > (1 << 20))

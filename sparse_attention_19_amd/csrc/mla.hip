@@ -145,23 +145,33 @@ constexpr int kVRowBytes = 65 * 16;             // 1040
 constexpr int kVTileBytes = kMT * kVRowBytes;   // 33280
 
 // K fragments of one tile held by one wave: k.v[st] = 16 bytes of entry 16kt + c16 at dim
-// 288dh + 32st + 8g.  Entries without a valid position read row 0 of the pool (always valid
-// memory, finite data); their logits are masked.
+// 288dh + 32st + 8g.  Entries without a valid position read kZeroRow instead of a pool row:
+// their logits are masked, and their V rows must be zeros, not whatever a pool row holds
+// (P = 0 times a NaN or Inf left in an unused block would still be NaN in P.V).
 struct KRegs {
   bf16x8 v[kSteps];
 };
 
+__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kRowBytes] = {};
+
+// Row bytes in the global address space: with a generic pointer (the zero row's address
+// and the pool's met in a select) the compiler issues flat loads, which also count on
+// the LDS wait counter, so every LDS barrier would wait for the rows in flight.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+typedef const __attribute__((address_space(1))) bf16x8* gbf16x8;
+
 // Source of the wave's fragments of the tile at list entry e0.
-__device__ __forceinline__ const uint8_t* k_src(const uint8_t* pool, const int* rowid, int e0) {
+__device__ __forceinline__ gbytes k_src(const uint8_t* pool, const int* rowid, int e0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int dh = wave & 1, kt = wave >> 1, g = lane >> 4, c16 = lane & 15;
   const int rid = rowid[e0 + 16 * kt + c16];
-  return pool + (int64_t)max(rid, 0) * kRowBytes + 576 * dh + 16 * g;
+  const gbytes row = rid >= 0 ? (gbytes)pool + (int64_t)rid * kRowBytes : (gbytes)kZeroRow;
+  return row + 576 * dh + 16 * g;
 }
 
-__device__ __forceinline__ void load_k(KRegs& r, const uint8_t* src) {
+__device__ __forceinline__ void load_k(KRegs& r, gbytes src) {
 #pragma unroll
-  for (int st = 0; st < kSteps; ++st) r.v[st] = *reinterpret_cast<const bf16x8*>(src + 64 * st);
+  for (int st = 0; st < kSteps; ++st) r.v[st] = *(gbf16x8)(src + 64 * st);
 }
 
 // Per-lane LDS addressing of the V tiles.
@@ -190,13 +200,13 @@ __device__ __forceinline__ VAddr v_addr() {
 template <bool kPrefetch>
 __device__ __forceinline__ void logits_kstep(int st, KRegs& k, const bf16x8 (&qf)[4][kSteps],
                                              f32x4 (&sacc)[4], uint8_t* vbase, int vst,
-                                             const uint8_t* knext) {
+                                             gbytes knext) {
   const int dh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1;   // wave-uniform
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) sacc[ht] = mfma16(k.v[st], qf[ht][st], sacc[ht]);
   if (dh == 0 || st < kVSteps1)
     *reinterpret_cast<bf16x8*>(vbase + vst + 64 * st) = k.v[st];
-  if (kPrefetch) k.v[st] = *reinterpret_cast<const bf16x8*>(knext + 64 * st);
+  if (kPrefetch) k.v[st] = *(gbf16x8)(knext + 64 * st);
 }
 
 // Partial logits of a tile into sp[dh][head][entry] (lane: head 16ht + c16, entries
@@ -225,7 +235,7 @@ __device__ __forceinline__ bf16x8 v_frag(const uint8_t* vbase, int vlo, int vhi,
 template <bool kSoft, bool kLogits, bool kPrefetch, bool kPV>
 __device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint16_t* pm_out,
                                          const uint16_t* pm_in, uint8_t* vbase, int vo_out,
-                                         int vo_in, KRegs& k, const uint8_t* knext,
+                                         int vo_in, KRegs& k, gbytes knext,
                                          const bf16x8 (&qf)[4][kSteps], f32x4 (&o)[4][8],
                                          const VAddr& va, uint32_t vmask, float scale_log2,
                                          float& m_run, float& l_run, bool& ovf) {
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     if (ntiles > 0) {   // logits and V of tile 0; the set is reloaded with tile 1
       f32x4 sacc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       if (ntiles > 1) {
-        const uint8_t* nx = k_src(pool, rowid, kMT);
+        const gbytes nx = k_src(pool, rowid, kMT);
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) logits_kstep<true>(st, kr, qf, sacc, &vbuf[0][0], va.st, nx);
       } else {

@@ -14,8 +14,8 @@ from typing import List, Optional
 
 import torch
 
-from . import (DSA_OP_MLA, DSA_OP_TOPK, IndexCache, dsa_indexer_scores, dsa_sparse_mla_decode,
-               dsa_sparse_mla_prefill, dsa_topk, workspace)
+from . import (DSA_OP_MLA, DSA_OP_TOPK, Chunk, IndexCache, PageTable, dsa_indexer_scores,
+               dsa_sparse_mla_decode, dsa_sparse_mla_prefill, dsa_topk, workspace)
 
 
 @dataclasses.dataclass
@@ -27,11 +27,10 @@ class StepBuffers:
     ws_topk: Optional[torch.Tensor]
     ws_mla: Optional[torch.Tensor]
     cache: Optional[IndexCache]
-    n_valid: Optional[torch.Tensor] = None   # prefill: q_pos (n = q_pos + 1)
 
 
 def alloc_buffers(T: int, ld: int, k: int, H: int, Dl: int, layers: int, dtype, device,
-                  group: int = 4) -> StepBuffers:
+                  group: int = 4, share: bool = True) -> StepBuffers:
     idx = torch.empty((T, k), dtype=torch.int32, device=device)
     return StepBuffers(
         scores=torch.empty((T, ld), dtype=torch.float32, device=device),
@@ -40,47 +39,68 @@ def alloc_buffers(T: int, ld: int, k: int, H: int, Dl: int, layers: int, dtype, 
         lses=[torch.empty((T, H), dtype=torch.float32, device=device) for _ in range(layers)],
         ws_topk=workspace(DSA_OP_TOPK, T, ld, k, H, Dl, device),
         ws_mla=workspace(DSA_OP_MLA, T, 0, k, H, Dl, device),
-        cache=IndexCache(idx, k, group=max(group, 2)) if layers > 1 else None,
+        cache=IndexCache(idx, k, group=max(group, 2)) if layers > 1 and share else None,
     )
 
 
-def decode_step(q_idx, w, k_pool, kv_pools, qs, block_table, seq_len, k, sm_scale, buf: StepBuffers,
-                step: int = 0) -> None:
-    """One decode token per request through len(kv_pools) DSA layers sharing one indexer."""
-    dsa_indexer_scores(q_idx, w, k_pool, block_table, seq_len, buf.scores)
-    dsa_topk(buf.scores, seq_len, k, buf.idx, n_add=0, ws=buf.ws_topk)
+def decode_step(q_idx, w, k_pool, kv_pools, qs, pt: PageTable, k, sm_scale, buf: StepBuffers,
+                step: int = 0, share: bool = True) -> None:
+    """One decode token per request through len(kv_pools) DSA layers sharing one indexer
+    (share=False: every layer runs the indexer and top-k itself, as DSA without IndexShare)."""
+    if not share:
+        for kv, q, out, lse in zip(kv_pools, qs, buf.outs, buf.lses):
+            dsa_indexer_scores(q_idx, w, k_pool, pt, buf.scores)
+            dsa_topk(buf.scores, pt.seq_len, pt.seq_len_host, k, buf.idx, n_add=0, ws=buf.ws_topk)
+            dsa_sparse_mla_decode(q, kv, pt, buf.idx, k, sm_scale, out, lse, ws=buf.ws_mla)
+        return
+    dsa_indexer_scores(q_idx, w, k_pool, pt, buf.scores)
+    dsa_topk(buf.scores, pt.seq_len, pt.seq_len_host, k, buf.idx, n_add=0, ws=buf.ws_topk)
     if buf.cache is not None:
         buf.cache.publish(step)
     for layer, (kv, q) in enumerate(zip(kv_pools, qs)):
         idx = buf.idx if layer == 0 else buf.cache.get(step, layer)
-        dsa_sparse_mla_decode(q, kv, block_table, seq_len, idx, k, sm_scale, buf.outs[layer],
-                              buf.lses[layer], ws=buf.ws_mla)
+        dsa_sparse_mla_decode(q, kv, pt, idx, k, sm_scale, buf.outs[layer], buf.lses[layer], ws=buf.ws_mla)
 
 
-def prefill_step(q_idx, w, k_pool, kv_pools, qs, block_table, seq_len, q_row, q_pos, k, sm_scale,
+def prefill_step(q_idx, w, k_pool, kv_pools, qs, pt: PageTable, chunk: Chunk, k, sm_scale,
                  buf: StepBuffers, step: int = 0) -> None:
     """A causal prefill chunk: token t of request q_row[t] at position q_pos[t]."""
-    dsa_indexer_scores(q_idx, w, k_pool, block_table, seq_len, buf.scores, q_row=q_row, q_pos=q_pos)
-    dsa_topk(buf.scores, q_pos, k, buf.idx, n_add=1, ws=buf.ws_topk)
+    dsa_indexer_scores(q_idx, w, k_pool, pt, buf.scores, chunk=chunk)
+    dsa_topk(buf.scores, chunk.q_pos, chunk.q_pos_host, k, buf.idx, n_add=1, ws=buf.ws_topk)
     if buf.cache is not None:
         buf.cache.publish(step)
     for layer, (kv, q) in enumerate(zip(kv_pools, qs)):
         idx = buf.idx if layer == 0 else buf.cache.get(step, layer)
-        dsa_sparse_mla_prefill(q, kv, block_table, seq_len, q_row, q_pos, idx, k, sm_scale,
-                               buf.outs[layer], buf.lses[layer], ws=buf.ws_mla)
+        dsa_sparse_mla_prefill(q, kv, pt, chunk, idx, k, sm_scale, buf.outs[layer], buf.lses[layer],
+                               ws=buf.ws_mla)
 
 
-def run_inputs(inp: dict, buf: Optional[StepBuffers] = None, step: int = 0) -> StepBuffers:
-    """Run one step on an input set from dsa_inputs.make_inputs (tensors on the GPU)."""
+def page_table(inp: dict) -> PageTable:
+    """The page table of an input set from dsa_inputs.make_inputs."""
+    return PageTable(inp["block_table"], inp["seq_len"], inp["seq_len_host"])
+
+
+def chunk(inp: dict) -> Chunk:
+    """The query-token positions of a prefill input set."""
+    return Chunk(inp["q_row"], inp["q_pos"], inp["q_row_host"], inp["q_pos_host"])
+
+
+def run_inputs(inp: dict, buf: Optional[StepBuffers] = None, step: int = 0, pt: Optional[PageTable] = None,
+               ch: Optional[Chunk] = None) -> StepBuffers:
+    """Run one step on an input set from dsa_inputs.make_inputs (tensors on the GPU).
+    pt / ch: the input set's PageTable and Chunk when the caller keeps them (else built
+    here from the set)."""
     cfg = inp["cfg"]
     T = inp["q_idx"].shape[0]
     ld = inp["block_table"].shape[1] * 64
     if buf is None:
-        buf = alloc_buffers(T, ld, cfg.k, cfg.H, cfg.Dl, cfg.layers, cfg.dtype, inp["q_idx"].device)
+        buf = alloc_buffers(T, ld, cfg.k, cfg.H, cfg.Dl, cfg.layers, cfg.dtype, inp["q_idx"].device,
+                            share=cfg.index_share)
+    pt = pt or page_table(inp)
     if cfg.prefill_tokens:
-        prefill_step(inp["q_idx"], inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], inp["block_table"],
-                     inp["seq_len"], inp["q_row"], inp["q_pos"], cfg.k, cfg.sm_scale, buf, step)
+        prefill_step(inp["q_idx"], inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], pt, ch or chunk(inp),
+                     cfg.k, cfg.sm_scale, buf, step)
     else:
-        decode_step(inp["q_idx"], inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], inp["block_table"],
-                    inp["seq_len"], cfg.k, cfg.sm_scale, buf, step)
+        decode_step(inp["q_idx"], inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], pt, cfg.k, cfg.sm_scale,
+                    buf, step, share=cfg.index_share)
     return buf

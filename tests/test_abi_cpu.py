@@ -11,6 +11,7 @@ from sparse_attention_19_amd import _lib as L
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x10000          # 16-byte aligned, never dereferenced: every call below is rejected
 FAKE2 = 0x20000
+ACCEPTED = "accepted"   # lengths that pass every check (see test_topk_rejects)
 
 
 def declared_functions():
@@ -39,16 +40,30 @@ def pool(dtype=L.DSA_BF16, row=128, nblk=10, data=FAKE, bs=64):
     return L.DsaPool(data, nblk, bs, row, dtype)
 
 
-def pt(batch=2, max_blocks=4):
-    return L.DsaPageTable(FAKE, FAKE2, batch, max_blocks)
+_KEEP = []   # host arrays referenced by structs built below
+
+
+def host_i32(values):
+    arr = (ctypes.c_int32 * max(1, len(values)))(*values)
+    _KEEP.append(arr)
+    return ctypes.cast(arr, ctypes.c_void_p).value
+
+
+def pt(batch=2, max_blocks=4, lens=None, seq_len_host=True):
+    lens = [max_blocks * 64 - 1] * batch if lens is None else lens
+    return L.DsaPageTable(FAKE, FAKE2, host_i32(lens) if seq_len_host else None, batch, max_blocks)
+
+
+def chunk(rows, poss, host=True):
+    return L.DsaChunk(FAKE, FAKE2, host_i32(rows) if host else None, host_i32(poss) if host else None)
 
 
 def idx_call(**kw):
-    a = dict(q_idx=FAKE, w=FAKE, pool=pool(), pt=pt(), q_row=None, q_pos=None, T=2, Hi=64, Di=128,
-             scores=FAKE, ld=256)
+    a = dict(q_idx=FAKE, w=FAKE, pool=pool(), pt=pt(), chunk=None, T=2, Hi=64, Di=128, scores=FAKE, ld=256)
     a.update(kw)
     return L.LIB.dsa_indexer_scores(a["q_idx"], a["w"], ctypes.byref(a["pool"]) if a["pool"] else None,
-                                    ctypes.byref(a["pt"]) if a["pt"] else None, a["q_row"], a["q_pos"],
+                                    ctypes.byref(a["pt"]) if a["pt"] else None,
+                                    ctypes.byref(a["chunk"]) if a["chunk"] else None,
                                     a["T"], a["Hi"], a["Di"], a["scores"], a["ld"], None)
 
 
@@ -65,8 +80,16 @@ def idx_call(**kw):
     (dict(pool=pool(dtype=7)), L.DSA_ERR_UNSUPPORTED),
     (dict(pool=pool(data=FAKE + 4)), L.DSA_ERR_INVALID),
     (dict(T=3), L.DSA_ERR_INVALID),                       # decode: T must equal batch
-    (dict(q_row=FAKE), L.DSA_ERR_INVALID),                # q_row without q_pos
     (dict(ld=255), L.DSA_ERR_INVALID),                    # ld < max_blocks * 64
+    (dict(pt=pt(seq_len_host=False)), L.DSA_ERR_INVALID),            # no host lengths
+    (dict(pt=pt(lens=[256, 257])), L.DSA_ERR_INVALID),               # seq_len > max_blocks * 64
+    (dict(pt=pt(lens=[-1, 5])), L.DSA_ERR_INVALID),                  # negative length
+    (dict(pt=pt(lens=[256, 0])), L.DSA_OK),                          # both ends of the range
+    (dict(chunk=chunk([0, 1], [5, 5], host=False)), L.DSA_ERR_INVALID),   # chunk without host copies
+    (dict(chunk=chunk([0, 2], [5, 5])), L.DSA_ERR_INVALID),          # q_row outside the batch
+    (dict(chunk=chunk([0, -1], [5, 5])), L.DSA_ERR_INVALID),
+    (dict(chunk=chunk([0, 1], [5, 255])), L.DSA_ERR_INVALID),        # q_pos >= seq_len (255)
+    (dict(chunk=chunk([0, 1], [-1, 5])), L.DSA_ERR_INVALID),         # negative position
     (dict(Hi=32), L.DSA_ERR_UNSUPPORTED),                 # bf16 instance is 64 x 128
     (dict(Hi=8, Di=32, pool=pool(L.DSA_F32, row=32)), L.DSA_OK),   # fp32 small dims are fine ...
     (dict(Hi=8, Di=30, pool=pool(L.DSA_F32, row=30)), L.DSA_ERR_UNSUPPORTED),
@@ -78,7 +101,7 @@ def idx_call(**kw):
 def test_indexer_rejects(kw, status):
     if status == L.DSA_OK:
         # valid shape: only check it is not rejected for shape reasons -- with T = 0 no launch
-        kw = dict(kw, T=0, q_row=FAKE, q_pos=FAKE)
+        kw = dict(kw, T=0, chunk=chunk([], []))
     got = idx_call(**kw)
     assert got == status, L.LIB.dsa_last_error()
     if status != L.DSA_OK:
@@ -86,9 +109,11 @@ def test_indexer_rejects(kw, status):
 
 
 def topk_call(**kw):
-    a = dict(scores=FAKE, ld=1000, n_valid=FAKE2, n_add=0, rows=3, k=64, idx=FAKE, ld_idx=64, ws=None, wsb=0)
+    a = dict(scores=FAKE, ld=1000, n_valid=FAKE2, nvh=[1000, 10, 0], n_add=0, rows=3, k=64, idx=FAKE,
+             ld_idx=64, ws=None, wsb=0)
     a.update(kw)
-    return L.LIB.dsa_topk(a["scores"], a["ld"], a["n_valid"], a["n_add"], a["rows"], a["k"], a["idx"],
+    nvh = host_i32(a["nvh"]) if a["nvh"] is not None else None
+    return L.LIB.dsa_topk(a["scores"], a["ld"], a["n_valid"], nvh, a["n_add"], a["rows"], a["k"], a["idx"],
                           a["ld_idx"], a["ws"], a["wsb"], None)
 
 
@@ -103,21 +128,32 @@ def topk_call(**kw):
     (dict(n_add=2), L.DSA_ERR_INVALID),
     (dict(rows=-1), L.DSA_ERR_INVALID),
     (dict(rows=0), L.DSA_OK),                             # empty: nothing enqueued
-    (dict(rows=0, scores=None, idx=None), L.DSA_OK),      # ... and may pass NULL data
+    (dict(rows=0, scores=None, idx=None, nvh=None), L.DSA_OK),   # ... and may pass NULL data
     (dict(ld=40000), L.DSA_ERR_WORKSPACE),                # long rows need the prune workspace
+    (dict(nvh=None), L.DSA_ERR_INVALID),                  # no host copy of the lengths
+    (dict(nvh=[1001, 10, 0]), L.DSA_ERR_INVALID),         # a row longer than ld
+    (dict(nvh=[1000, 10, 0], n_add=1), L.DSA_ERR_INVALID),   # n_valid + n_add > ld
+    (dict(nvh=[999, 10, -1], n_add=1), ACCEPTED),    # -1 + 1 = 0 positions: valid
+    (dict(nvh=[5, -1, 0]), L.DSA_ERR_INVALID),            # negative length
 ])
 def test_topk_rejects(kw, status):
+    if status == ACCEPTED:
+        # valid lengths: accepted by every check; rows=0 afterwards keeps the call launch-free
+        # (the same host array is re-validated with rows=3 up to the workspace check)
+        assert topk_call(**dict(kw, ld=40000)) == L.DSA_ERR_WORKSPACE
+        return
     assert topk_call(**kw) == status
 
 
 def mla_call(prefill=False, **kw):
     a = dict(q=FAKE, pool=pool(row=576), pt=pt(), idx=FAKE, ld_idx=2048, k=2048, H=64, Dl=512, Dr=64,
-             scale=0.04, out=FAKE, lse=None, ws=FAKE2, wsb=1 << 40, q_row=FAKE, q_pos=FAKE, T=2)
+             scale=0.04, out=FAKE, lse=None, ws=FAKE2, wsb=1 << 40, chunk=chunk([0, 1], [3, 4]), T=2)
     a.update(kw)
     pp = ctypes.byref(a["pool"]) if a["pool"] else None
     tp = ctypes.byref(a["pt"]) if a["pt"] else None
     if prefill:
-        return L.LIB.dsa_sparse_mla_prefill(a["q"], pp, tp, a["q_row"], a["q_pos"], a["idx"], a["ld_idx"],
+        cp = ctypes.byref(a["chunk"]) if a["chunk"] else None
+        return L.LIB.dsa_sparse_mla_prefill(a["q"], pp, tp, cp, a["idx"], a["ld_idx"],
                                             a["T"], a["k"], a["H"], a["Dl"], a["Dr"], a["scale"], a["out"],
                                             a["lse"], a["ws"], a["wsb"], None)
     return L.LIB.dsa_sparse_mla_decode(a["q"], pp, tp, a["idx"], a["ld_idx"], a["k"], a["H"], a["Dl"],
@@ -145,20 +181,31 @@ def mla_call(prefill=False, **kw):
     (dict(out=FAKE + 2), L.DSA_ERR_INVALID),
     (dict(pool=pool(L.DSA_F32, row=80), H=65, Dl=64, Dr=16), L.DSA_ERR_UNSUPPORTED),
     (dict(pool=pool(L.DSA_F32, row=1028), H=8, Dl=1024, Dr=4), L.DSA_ERR_UNSUPPORTED),
+    (dict(pt=pt(seq_len_host=False)), L.DSA_ERR_INVALID),            # no host lengths
+    (dict(pt=pt(lens=[100, 257])), L.DSA_ERR_INVALID),               # seq_len > max_blocks * 64
 ])
 def test_mla_rejects(prefill, kw, status):
     assert mla_call(prefill, **kw) == status
 
 
+@pytest.mark.parametrize("ch", [
+    chunk([0, 1], [3, 4], host=False),      # no host copies of the positions
+    chunk([0, 2], [3, 4]),                  # q_row outside the batch
+    chunk([0, 1], [3, 255]),                # q_pos >= seq_len
+    chunk([0, 1], [-1, 4]),                 # negative position
+])
+def test_mla_prefill_rejects_positions(ch):
+    assert mla_call(True, chunk=ch) == L.DSA_ERR_INVALID
+
+
 def test_mla_f32_small_dims_accepted_without_workspace():
     # an empty prefill chunk passes every check and enqueues nothing
     assert mla_call(True, T=0, pool=pool(L.DSA_F32, row=80), H=8, Dl=64, Dr=16, k=64, ld_idx=64,
-                    ws=None, wsb=0) == L.DSA_OK
+                    ws=None, wsb=0, chunk=None) == L.DSA_OK
 
 
 def test_prefill_requires_positions():
-    assert mla_call(True, q_row=None) == L.DSA_ERR_INVALID
-    assert mla_call(True, q_pos=None) == L.DSA_ERR_INVALID
+    assert mla_call(True, chunk=None) == L.DSA_ERR_INVALID
     assert mla_call(True, T=-1) == L.DSA_ERR_INVALID
 
 

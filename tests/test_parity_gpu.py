@@ -3,18 +3,16 @@
 Bars: indexer scores and top-k index sets bit-exact; attention outputs within the
 normwise relative error 1e-5 (fp32) / 2e-2 (bf16) per (token, head) row:
 max_c |out - ref| / max_c |ref|; lse within 1e-5 relative (fp32) / 2e-3 absolute (bf16).
-Small cases check every token; the full-size workloads (the launch configuration the
-benchmark times) check sampled tokens, each computed one by one by the oracle.
+Small cases and the full-size decode workloads (the launch configuration the benchmark
+times) check every token; the full-size prefill chunks check 64 tokens spread over the
+chunk (its first and last, both sides of its midpoint, and evenly spaced ones), each
+computed one by one by the oracle.
 """
-import math
-import random
-
 import numpy as np
 import pytest
 import torch
 
 import dsa_inputs as I
-from oracle import dsa_oracle as O
 from oracle import run as R
 
 pytestmark = pytest.mark.gpu
@@ -61,6 +59,15 @@ def check_token(inp, buf, t, layers=None, key_cache=None, check_scores=True):
         else:
             assert np.abs(lse - exp["lse"][li]).max() <= 2e-3, np.abs(lse - exp["lse"][li]).max()
     return exp
+
+
+def set_lengths(inp, seq_len=None, q_row=None, q_pos=None):
+    """Replace an input set's lengths / token positions (device tensors and host copies)."""
+    for name, v in (("seq_len", seq_len), ("q_row", q_row), ("q_pos", q_pos)):
+        if v is not None:
+            host = torch.as_tensor(v, dtype=torch.int32).cpu().contiguous()
+            inp[name + "_host"] = host
+            inp[name] = host.to(DEV)
 
 
 def run_cfg(cfg, **over):
@@ -145,8 +152,7 @@ def test_bf16_decode_edge_lengths():
     cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=len(lens), ctx_range=None)
     inp = I.make_inputs(cfg, DEV)
     # override lengths: block tables are sized for cfg.ctx so any length <= ctx is valid
-    inp["seq_len"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    inp["q_pos"] = inp["seq_len"] - 1
+    set_lengths(inp, seq_len=lens, q_pos=[n - 1 for n in lens])
     buf = P.run_inputs(inp)
     torch.cuda.synchronize()
     for t in range(len(lens)):
@@ -166,9 +172,8 @@ def test_bf16_prefill_small_multi_request():
     cfg2 = I.shrink(I.CONFIGS["decode_b64_paged"], batch=2, ctx_range=None, ctx=3000)
     inp2 = I.make_inputs(cfg2, DEV)
     T = 24
-    q_row = torch.tensor([i % 2 for i in range(T)], dtype=torch.int32)
-    q_pos = torch.tensor([2990 - 100 * i if i % 3 else 2000 + i for i in range(T)], dtype=torch.int32)
-    inp2["q_row"], inp2["q_pos"] = q_row.to(DEV), q_pos.to(DEV)
+    set_lengths(inp2, q_row=[i % 2 for i in range(T)],
+                q_pos=[2990 - 100 * i if i % 3 else 2000 + i for i in range(T)])
     inp2["q_idx"] = inp2["q_idx"][:1].repeat(T, 1, 1).contiguous()
     inp2["q_idx"] = (inp2["q_idx"] + torch.arange(T, device=DEV).view(T, 1, 1).remainder(3)
                      .to(inp2["q_idx"].dtype) - 1).contiguous()
@@ -232,7 +237,7 @@ def _topk_case(scores: np.ndarray, n_valid, k):
     s = torch.from_numpy(scores.astype(np.float32)).to(DEV)
     nv = torch.tensor(n_valid, dtype=torch.int32, device=DEV)
     idx = torch.empty((rows, k), dtype=torch.int32, device=DEV)
-    D.dsa_topk(s, nv, k, idx, ws=D.workspace(D.DSA_OP_TOPK, rows, ld, k, 0, 0, DEV))
+    D.dsa_topk(s, nv, nv.cpu(), k, idx, ws=D.workspace(D.DSA_OP_TOPK, rows, ld, k, 0, 0, DEV))
     torch.cuda.synchronize()
     exp = R.expected_topk(scores.astype(np.float32), np.array(n_valid), k)
     got = idx.cpu().numpy()
@@ -329,7 +334,8 @@ def test_topk_prefill_offset():
     q_pos = [0, 99, 2047, 2048, 4999]
     s = torch.from_numpy(sc).to(DEV)
     idx = torch.empty((5, 2048), dtype=torch.int32, device=DEV)
-    D.dsa_topk(s, torch.tensor(q_pos, dtype=torch.int32, device=DEV), 2048, idx, n_add=1)
+    qp = torch.tensor(q_pos, dtype=torch.int32)
+    D.dsa_topk(s, qp.to(DEV), qp, 2048, idx, n_add=1)
     exp = R.expected_topk(sc, np.array(q_pos) + 1, 2048)
     assert np.array_equal(idx.cpu().numpy(), exp)
 
@@ -387,8 +393,8 @@ def test_indexshare_reuses_first_layer_selection():
     out = torch.empty_like(buf.outs[2])
     lse = torch.empty_like(buf.lses[2])
     ws = D.workspace(D.DSA_OP_MLA, 5, 0, cfg.k, cfg.H, cfg.Dl, DEV)
-    D.dsa_sparse_mla_decode(inp["q"][2], inp["kv_pools"][2], inp["block_table"], inp["seq_len"], idx,
-                            cfg.k, cfg.sm_scale, out, lse, ws=ws)
+    D.dsa_sparse_mla_decode(inp["q"][2], inp["kv_pools"][2], P.page_table(inp), idx, cfg.k, cfg.sm_scale,
+                            out, lse, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, buf.outs[2]) and torch.equal(lse, buf.lses[2])
 
@@ -396,13 +402,62 @@ def test_indexshare_reuses_first_layer_selection():
 def test_empty_prefill_chunk_is_a_noop():
     cfg = I.CONFIGS["decode_b1_32k"]
     z = torch.zeros((0,), dtype=torch.int32, device=DEV)
+    zh = torch.zeros((0,), dtype=torch.int32)
     kv = torch.zeros((1, 64, 576), dtype=torch.bfloat16, device=DEV)
     bt = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
     sl = torch.ones((1,), dtype=torch.int32, device=DEV)
     q = torch.zeros((0, 64, 576), dtype=torch.bfloat16, device=DEV)
     out = torch.zeros((0, 64, 512), dtype=torch.bfloat16, device=DEV)
     idx = torch.zeros((0, 2048), dtype=torch.int32, device=DEV)
-    D.dsa_sparse_mla_prefill(q, kv, bt, sl, z, z, idx, 2048, cfg.sm_scale, out)
+    D.dsa_sparse_mla_prefill(q, kv, D.PageTable(bt, sl, sl.cpu()), D.Chunk(z, z, zh, zh), idx, 2048,
+                             cfg.sm_scale, out)
+
+
+def test_lengths_rejected_before_launch():
+    # a length beyond the page table's capacity, a prefill position beyond its request and a
+    # top-k row longer than its stride are refused on the host; nothing is enqueued
+    inp = I.make_inputs(I.shrink(I.CONFIGS["decode_b64_paged"], batch=2, ctx_range=None, ctx=3000), DEV)
+    cap = inp["block_table"].shape[1] * 64
+    bad = torch.tensor([3000, cap + 1], dtype=torch.int32)
+    pt = D.PageTable(inp["block_table"], bad.to(DEV), bad)
+    scores = torch.empty((2, cap), dtype=torch.float32, device=DEV)
+    with pytest.raises(D.DsaError, match="seq_len"):
+        D.dsa_indexer_scores(inp["q_idx"], inp["w"], inp["k_pool"], pt, scores)
+    ch = D.Chunk(torch.zeros(2, dtype=torch.int32, device=DEV), torch.tensor([5, 3000], dtype=torch.int32,
+                 device=DEV), torch.zeros(2, dtype=torch.int32), torch.tensor([5, 3000], dtype=torch.int32))
+    with pytest.raises(D.DsaError, match="q_pos"):
+        D.dsa_indexer_scores(inp["q_idx"], inp["w"], inp["k_pool"], P.page_table(inp), scores, chunk=ch)
+    nv = torch.tensor([cap, cap + 1], dtype=torch.int32)
+    idx = torch.empty((2, 2048), dtype=torch.int32, device=DEV)
+    with pytest.raises(D.DsaError, match="positions"):
+        D.dsa_topk(scores, nv.to(DEV), nv, 2048, idx)
+    torch.cuda.synchronize()
+
+
+def test_mla_ignores_non_finite_rows_outside_the_selection():
+    # An unused block (physical 0, referenced by no request) full of NaN and Inf.  Rows whose
+    # list ends mid-tile (dense rows of ragged length, split tails) must not pick it up: the
+    # masked entries of a tile contribute nothing, not 0 * NaN.
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=6, ctx_range=(5, 3000))
+    inp = I.make_inputs(cfg, DEV)
+    for name in ("k_pool",):
+        pool = inp[name]
+        inp[name] = torch.cat([torch.zeros_like(pool[:1]), pool]).contiguous()
+    pools = []
+    for pool in inp["kv_pools"]:
+        junk = torch.full_like(pool[:1], float("nan"))
+        junk[0, ::2] = float("inf")
+        pools.append(torch.cat([junk, pool]).contiguous())
+    inp["kv_pools"] = pools
+    bt = inp["block_table"]
+    inp["block_table"] = torch.where(bt >= 0, bt + 1, bt).contiguous()
+    lens = inp["seq_len"].tolist()
+    log(f"[gpu] non-finite unused block, lens {lens}")
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(buf.outs[0].float()).all()
+    for t in range(len(lens)):
+        check_token(inp, buf, t)
 
 
 # ------------------------------------------------------------------ full-size workloads
@@ -412,44 +467,50 @@ def test_full_decode_b1_32k():
     check_token(inp, buf, 0)
 
 
-def test_full_decode_b64_paged_sampled():
+def test_full_decode_b64_paged_every_token():
     inp, buf = run_cfg(I.CONFIGS["decode_b64_paged"])
     lens = inp["seq_len"].tolist()
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 17, 40})
-    for t in pick:
+    for t in range(len(lens)):
         log(f"[gpu] decode_b64 token {t} n={lens[t]}")
         check_token(inp, buf, t)
 
 
-def test_full_decode_b64_paged_h128_sampled():
+def test_full_decode_b64_paged_h128_every_token():
     # 128 MLA heads at full size: 64 tokens x 2 head groups, split in two
     inp, buf = run_cfg(I.CONFIGS["decode_b64_paged_h128"])
     lens = inp["seq_len"].tolist()
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 31})
-    for t in pick:
+    for t in range(len(lens)):
         log(f"[gpu] decode_b64_h128 token {t} n={lens[t]}")
         check_token(inp, buf, t)
 
 
-def test_full_indexshare_sampled():
+def test_full_indexshare_every_token():
     inp, buf = run_cfg(I.CONFIGS["indexshare_decode_4layer"])
-    for t in (0, 19, 31, 32, 39):
-        log(f"[gpu] indexshare token {t}")
+    for t in range(inp["q_idx"].shape[0]):
+        log(f"[gpu] indexshare token {t} n={int(inp['seq_len_host'][t])}")
         check_token(inp, buf, t)
 
 
-def test_full_prefill_h128_sampled():
+def prefill_tokens_checked(T):
+    """64 tokens of a T-token chunk: the first two, the last two, both sides of the
+    midpoint and evenly spaced others."""
+    fixed = {0, 1, T // 2 - 1, T // 2, T - 2, T - 1}
+    spread = set(np.linspace(0, T - 1, 64 - len(fixed) + 2).round().astype(int).tolist())
+    pick = sorted(fixed | spread)
+    return pick[:64] if len(pick) >= 64 else pick
+
+
+def test_full_prefill_h128_spread():
     inp, buf = run_cfg(I.CONFIGS["prefill_4096_at_128k_h128"])
     kc = {}
-    for t in (0, 2048, 4095):
+    for t in prefill_tokens_checked(inp["q_idx"].shape[0]):
         log(f"[gpu] prefill h128 token {t}")
         check_token(inp, buf, t, key_cache=kc)
 
 
-def test_full_prefill_sampled():
+def test_full_prefill_spread():
     inp, buf = run_cfg(I.CONFIGS["prefill_4096_at_128k"])
     kc = {}
-    random.seed(3)
-    for t in sorted({0, 1, 2047, 4094, 4095, *random.sample(range(4096), 3)}):
+    for t in prefill_tokens_checked(inp["q_idx"].shape[0]):
         log(f"[gpu] prefill token {t}")
         check_token(inp, buf, t, key_cache=kc)
