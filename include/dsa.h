@@ -180,6 +180,23 @@ dsa_status dsa_sparse_mla_decode(const void* q, const dsa_pool* kv, const dsa_pa
                                  float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_sparse_mla_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as dsa_sparse_mla_decode, bit for
+ * bit; the split partials go to a device array the library holds on each GPU it runs on
+ * (dsa_workspace_bytes(DSA_OP_MLA, B, 0, k, H, Dl) bytes of it; every supported shape
+ * fits its 33,685,504 bytes, a larger need returns DSA_ERR_WORKSPACE).  It calls no
+ * allocating routine.  The first call on a device looks the array's address up with that
+ * device current, so `stream` must belong to the current device.  All calls on one GPU
+ * share its array: calls whose work overlaps on that GPU (different streams, or threads
+ * without ordering) race and give undefined results.
+ */
+dsa_status dsa_sparse_mla_decode_noalloc(const void* q, const dsa_pool* kv, const dsa_page_table* pt,
+                                         const int32_t* idx, int64_t ld_idx, int32_t k, int32_t H,
+                                         int32_t Dl, int32_t Dr, float sm_scale, void* out, float* lse,
+                                         void* stream);
+
+/*
  * Sparse MLA for a causal prefill chunk: as dsa_sparse_mla_decode for T query tokens,
  * token t belonging to request chunk->q_row[t] and seeing n = q_pos[t] + 1 positions.
  *   q [T][H][Dl+Dr], idx [T][ld_idx], out [T][H][Dl], lse [T][H] or NULL (all device).

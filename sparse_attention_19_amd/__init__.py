@@ -17,7 +17,8 @@ from ._lib import (DSA_BF16, DSA_BLOCK, DSA_ERR_INVALID, DSA_F32, DSA_MAX_K, DSA
                    LIB_PATH, DsaChunk, DsaError, DsaIndexCache, DsaPageTable, DsaPool, check)
 
 __all__ = [
-    "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+    "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc",
+    "dsa_sparse_mla_prefill",
     "IndexCache", "PageTable", "Chunk", "dsa_workspace_bytes", "workspace", "DsaError", "LIB_PATH",
     "DSA_OP_TOPK", "DSA_OP_MLA",
     "dsa_timing_start", "dsa_timing_collect",
@@ -155,6 +156,18 @@ def dsa_sparse_mla_decode(q, kv_pool, pt: PageTable, idx, k, sm_scale, out, lse=
                                     _dev(idx, "idx", torch.int32), idx.shape[1], k, H, Dl, D - Dl,
                                     float(sm_scale), _dev(out, "out", kv_pool.dtype),
                                     _opt(lse, "lse", torch.float32), *_ws(ws), _stream(stream, q)))
+
+
+def dsa_sparse_mla_decode_noalloc(q, kv_pool, pt: PageTable, idx, k, sm_scale, out, lse=None, stream=None):
+    """dsa_sparse_mla_decode with the split partials in the library's own device array:
+    no workspace argument, no allocation (calls that overlap on one GPU race)."""
+    B, H, D = q.shape
+    Dl = out.shape[2]
+    pool = _pool(kv_pool, "kv_pool")
+    check(LIB.dsa_sparse_mla_decode_noalloc(_dev(q, "q", kv_pool.dtype), ctypes.byref(pool), ctypes.byref(pt.c),
+                                            _dev(idx, "idx", torch.int32), idx.shape[1], k, H, Dl, D - Dl,
+                                            float(sm_scale), _dev(out, "out", kv_pool.dtype),
+                                            _opt(lse, "lse", torch.float32), _stream(stream, q)))
 
 
 def dsa_sparse_mla_prefill(q, kv_pool, pt: PageTable, chunk: Chunk, idx, k, sm_scale, out, lse=None, ws=None,

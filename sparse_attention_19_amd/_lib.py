@@ -21,8 +21,8 @@ DSA_MAX_K = 2048
 ABI_VERSION = b"dsa-gfx950 0.2.0"   # argument layout this binding marshals for
 
 EXPORTS = [
-    "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
-    "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
+    "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc",
+    "dsa_sparse_mla_prefill", "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
     "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
     "dsa_timing_start", "dsa_timing_collect",
 ]
@@ -60,6 +60,7 @@ def _load() -> ctypes.CDLL:
         "dsa_indexer_scores": [P, P, pool_p, pt_p, chunk_p, I32, I32, I32, P, I64, P],
         "dsa_topk": [P, I64, P, P, I32, I32, I32, P, I64, P, SZ, P],
         "dsa_sparse_mla_decode": [P, pool_p, pt_p, P, I64, I32, I32, I32, I32, F, P, P, P, SZ, P],
+        "dsa_sparse_mla_decode_noalloc": [P, pool_p, pt_p, P, I64, I32, I32, I32, I32, F, P, P, P],
         "dsa_sparse_mla_prefill": [P, pool_p, pt_p, chunk_p, P, I64, I32, I32, I32, I32, I32, F, P, P, P, SZ,
                                    P],
         "dsa_index_cache_init": [cache_p, P, I64, I32, I32, I32],

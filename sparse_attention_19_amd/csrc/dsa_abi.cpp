@@ -95,9 +95,10 @@ dsa_status check_tokens(const dsa_chunk* chunk, int32_t T, const dsa_page_table*
   return DSA_OK;
 }
 
+// scratch: the partials go to the library's own device array (no caller workspace)
 dsa_status check_mla(const void* q, const dsa_pool* kv, const dsa_page_table* pt, const int32_t* idx,
                      int64_t ld_idx, int32_t k, int32_t H, int32_t Dl, int32_t Dr, float sm_scale,
-                     const void* out, void* ws, size_t ws_bytes, int32_t T) {
+                     const void* out, void* ws, size_t ws_bytes, int32_t T, bool scratch = false) {
   // an empty chunk (T == 0) reads and writes nothing, so its data pointers may be NULL
   if (T != 0 && (!q || !out || !idx)) return fail(DSA_ERR_INVALID, "q/out/idx is NULL");
   if (H <= 0 || Dl <= 0 || Dr < 0) return fail(DSA_ERR_INVALID, "H/Dl/Dr must be positive");
@@ -117,6 +118,12 @@ dsa_status check_mla(const void* q, const dsa_pool* kv, const dsa_page_table* pt
       return fail(DSA_ERR_UNSUPPORTED, "fp32 MLA needs H <= 64, Dl + Dr <= 1024, Dl %% 4 == Dr %% 4 == 0");
   }
   const size_t need = dsa::mla_workspace_bytes(T, k, H, Dl, kv->dtype == DSA_BF16);
+  if (scratch) {
+    if (need > dsa::mla_scratch_bytes())
+      return fail(DSA_ERR_WORKSPACE, "%zu bytes of split partials needed, the library holds %zu", need,
+                  dsa::mla_scratch_bytes());
+    return DSA_OK;
+  }
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws ? ws_bytes : 0);
   if (need && !aligned16(ws)) return fail(DSA_ERR_INVALID, "workspace not 16-byte aligned");
@@ -235,6 +242,23 @@ dsa_status dsa_sparse_mla_decode(const void* q, const dsa_pool* kv, const dsa_pa
   dsa::MlaArgs a{q, kv->data, kv->num_blocks, pt->block_table, pt->seq_len, pt->max_blocks, pt->batch,
                  nullptr, nullptr, idx, ld_idx, T, k, H, Dl, Dr, sm_scale, kv->dtype == DSA_BF16, out, lse, ws};
   return launched(dsa::launch_mla(a, (hipStream_t)stream), "sparse MLA decode launch");
+}
+
+dsa_status dsa_sparse_mla_decode_noalloc(const void* q, const dsa_pool* kv, const dsa_page_table* pt,
+                                         const int32_t* idx, int64_t ld_idx, int32_t k, int32_t H, int32_t Dl,
+                                         int32_t Dr, float sm_scale, void* out, float* lse, void* stream) {
+  if (!pt) return fail(DSA_ERR_INVALID, "page table is NULL");
+  const int32_t T = pt->batch;
+  dsa_status s = check_mla(q, kv, pt, idx, ld_idx, k, H, Dl, Dr, sm_scale, out, nullptr, 0, T, true);
+  if (s) return s;
+  void* ws = nullptr;
+  if (dsa::mla_workspace_bytes(T, k, H, Dl, kv->dtype == DSA_BF16) > 0) {
+    const hipError_t e = dsa::mla_scratch(&ws);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+  }
+  dsa::MlaArgs a{q, kv->data, kv->num_blocks, pt->block_table, pt->seq_len, pt->max_blocks, pt->batch,
+                 nullptr, nullptr, idx, ld_idx, T, k, H, Dl, Dr, sm_scale, kv->dtype == DSA_BF16, out, lse, ws};
+  return launched(dsa::launch_mla(a, (hipStream_t)stream), "sparse MLA decode (no-alloc) launch");
 }
 
 dsa_status dsa_sparse_mla_prefill(const void* q, const dsa_pool* kv, const dsa_page_table* pt,

@@ -72,5 +72,9 @@ struct MlaArgs {
 int mla_splits(int T, int k, int H, bool bf16);
 size_t mla_workspace_bytes(int T, int k, int H, int Dl, bool bf16);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
+// The library's own device array for split partials: its size, and its address on the
+// current device (looked up once per device).
+size_t mla_scratch_bytes();
+hipError_t mla_scratch(void** ptr);
 
 }  // namespace dsa

@@ -31,6 +31,8 @@
 // combine kernel merges their partial (O, max, sum) with log-sum-exp weights.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -681,6 +683,37 @@ size_t mla_workspace_bytes(int T, int k, int H, int Dl, bool bf16) {
   const int s = mla_splits(T, k, H, bf16);
   if (s <= 1) return 0;
   return (size_t)T * s * H * (Dl + 2) * sizeof(float);
+}
+
+// ---- split partials without a caller workspace (dsa_sparse_mla_decode_noalloc)
+// At most 256 (token, split, head group) work items carry partials (mla_splits keeps
+// T * splits * groups <= 256 whenever splits > 1), each 64 heads x (512 + 2) fp32: the
+// largest workspace any call needs.  Every GPU the library runs on holds one copy of this
+// array until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress gives for the current device.
+constexpr size_t kScratchBytes = (size_t)256 * kH * (kDl + 2) * sizeof(float);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device, set on the first call there
+
+size_t mla_scratch_bytes() { return kScratchBytes; }
+
+hipError_t mla_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {

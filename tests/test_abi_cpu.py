@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -262,3 +262,36 @@ def test_timing_rejects_before_any_hip_call():
     # never started: collect reports -1 and says why
     assert L.LIB.dsa_timing_collect(None, None, 0) == -1
     assert b"off" in L.LIB.dsa_last_error()
+
+
+def noalloc_call(**kw):
+    a = dict(q=FAKE, pool=pool(row=576), pt=pt(), idx=FAKE, ld_idx=2048, k=2048, H=64, Dl=512, Dr=64,
+             scale=0.04, out=FAKE, lse=None)
+    a.update(kw)
+    pp = ctypes.byref(a["pool"]) if a["pool"] else None
+    tp = ctypes.byref(a["pt"]) if a["pt"] else None
+    return L.LIB.dsa_sparse_mla_decode_noalloc(a["q"], pp, tp, a["idx"], a["ld_idx"], a["k"], a["H"], a["Dl"],
+                                               a["Dr"], a["scale"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), L.DSA_ERR_INVALID),
+    (dict(pt=None), L.DSA_ERR_INVALID),
+    (dict(pt=pt(seq_len_host=False)), L.DSA_ERR_INVALID),
+    (dict(pt=pt(lens=[100, 257])), L.DSA_ERR_INVALID),
+    (dict(H=96), L.DSA_ERR_UNSUPPORTED),
+    (dict(k=4096, ld_idx=4096), L.DSA_ERR_UNSUPPORTED),
+    (dict(out=FAKE + 2), L.DSA_ERR_INVALID),
+])
+def test_noalloc_decode_rejects(kw, status):
+    assert noalloc_call(**kw) == status
+
+
+def test_noalloc_scratch_holds_every_workspace():
+    # the library's scratch array (33,685,504 bytes) covers the split partials of every
+    # batch size, head count and list width the bf16 decode accepts
+    scratch = 256 * 64 * (512 + 2) * 4
+    for H in (64, 128):
+        for k in (1, 31, 32, 33, 500, 2047, 2048):
+            for T in list(range(1, 300)) + [511, 512, 1000, 4096, 100000]:
+                assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, T, 0, k, H, 512) <= scratch, (H, k, T)
