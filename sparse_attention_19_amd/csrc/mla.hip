@@ -57,58 +57,105 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxSlack = 32.f;
 
 
-// Resolve the token's (request, n) and this split's slice [i0, i0 + nent) of the
-// selected list; fills rowid[] with global row ids (phys * 64 + slot) or -1, up to the
-// end of the slice's last 32-entry tile.  Two memory round trips whatever the slice
-// length: first the token's request and length together with the slice's list entries
-// (read as if n > k; the dense case ignores them), then every page-table entry at once.
-__device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const int* block_table,
-                                             const int* seq_len, int max_blocks, int batch,
-                                             int64_t num_blocks, const int* q_row, const int* q_pos,
-                                             const int* idx, int64_t ld_idx, int k, int* rowid,
-                                             int& nent) {
-  constexpr int kPer = kMaxList / kThreads;   // list entries per thread, at most
+// A split's slice of the selected list, loaded ahead of its page translation.
+constexpr int kPer = kMaxList / kThreads;   // list entries per thread, at most
+struct ListSlice {
+  int b, n;        // the token's request and visible positions
+  int pos[kPer];   // list entries tid + 256 j of the slice (read as if n > k)
+};
+
+// First memory round trip of a split: the token's request and length, and the slice's list
+// entries, all issued together (the dense case ignores the entries).
+__device__ __forceinline__ void load_list(int t, int sp, int splits, const int* seq_len, int batch,
+                                          const int* q_row, const int* q_pos, const int* idx, int64_t ld_idx,
+                                          int k, ListSlice& L) {
   const int tid = threadIdx.x;
-  const int b = q_row ? q_row[t] : t;
-  int n = q_pos ? q_pos[t] + 1 : (t < batch ? seq_len[t] : 0);   // decode: request t
+  L.b = q_row ? q_row[t] : t;
+  L.n = q_pos ? q_pos[t] + 1 : (t < batch ? seq_len[t] : 0);   // decode: request t
   const int per_s = ((k + splits - 1) / splits + kMT - 1) / kMT * kMT;
   const int i0_s = sp * per_s;
   const int nent_s = max(0, min(k, i0_s + per_s) - i0_s);
-  int pos[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = tid + kThreads * j;
-    pos[j] = e < nent_s ? idx[(int64_t)t * ld_idx + i0_s + e] : -1;
+    L.pos[j] = e < nent_s ? idx[(int64_t)t * ld_idx + i0_s + e] : -1;
   }
-  if (b < 0 || b >= batch) {      // token of no request: empty set (out = 0, lse = -inf)
-    nent = 0;
-    return;
-  }
-  n = max(0, min(n, max_blocks * kBlock));
+}
+
+// Second round trip: every page-table entry of the slice at once.  Sets nent (the slice
+// length) and phys[] (the physical block of each of the thread's entries, -1 for none).
+__device__ __forceinline__ void load_pages(ListSlice& L, int sp, int splits, const int* block_table,
+                                           int max_blocks, int batch, int k, int (&phys)[kPer], int& nent) {
+  const int tid = threadIdx.x;
+  const bool known = L.b >= 0 && L.b < batch;   // else a token of no request: empty set
+  const int n = known ? max(0, min(L.n, max_blocks * kBlock)) : 0;
   const bool dense = n <= k;
   const int cnt = dense ? n : k;
   int per = (cnt + splits - 1) / splits;
   per = (per + kMT - 1) / kMT * kMT;
   const int i0 = sp * per;
   nent = max(0, min(cnt, i0 + per) - i0);
-  const int* bt_row = block_table + (int64_t)b * max_blocks;
-  int phys[kPer];
+  const int* bt_row = block_table + (int64_t)(known ? L.b : 0) * max_blocks;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = tid + kThreads * j;
-    if (dense) pos[j] = i0 + e;
-    const bool ok = e < nent && pos[j] >= 0 && pos[j] < n;
-    phys[j] = ok ? bt_row[pos[j] >> 6] : -1;
+    if (dense) L.pos[j] = i0 + e;
+    const bool ok = e < nent && L.pos[j] >= 0 && L.pos[j] < n;
+    phys[j] = ok ? bt_row[L.pos[j] >> 6] : -1;
   }
+}
+
+// Row ids of the slice into rowid[] (phys * 64 + slot, or -1 for no position), padded with
+// -1 to the end of its last 32-entry tile and to at least one whole tile, so the first
+// tile's rows can be fetched whatever the slice length.
+__device__ __forceinline__ void write_rows(const ListSlice& L, const int (&phys)[kPer], int nent,
+                                           int64_t num_blocks, int* rowid) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = tid + kThreads * j;
     if (e < nent)
-      rowid[e] = (phys[j] >= 0 && phys[j] < num_blocks) ? phys[j] * kBlock + (pos[j] & 63) : -1;
+      rowid[e] = (phys[j] >= 0 && phys[j] < num_blocks) ? phys[j] * kBlock + (L.pos[j] & 63) : -1;
   }
-  // entries up to the end of the last tile read as "no position"
-  const int padded = (nent + kMT - 1) / kMT * kMT;
+  const int padded = max(kMT, (nent + kMT - 1) / kMT * kMT);
   for (int e = nent + tid; e < padded; e += kThreads) rowid[e] = -1;
+}
+
+// Both round trips: the token's (request, n) and this split's slice [i0, i0 + nent) of the
+// selected list (all n positions when n <= k) as row ids in rowid[].
+__device__ __forceinline__ void resolve_rows(int t, int sp, int splits, const int* block_table,
+                                             const int* seq_len, int max_blocks, int batch,
+                                             int64_t num_blocks, const int* q_row, const int* q_pos,
+                                             const int* idx, int64_t ld_idx, int k, int* rowid,
+                                             int& nent) {
+  ListSlice L;
+  int phys[kPer];
+  load_list(t, sp, splits, seq_len, batch, q_row, q_pos, idx, ld_idx, k, L);
+  load_pages(L, sp, splits, block_table, max_blocks, batch, k, phys, nent);
+  write_rows(L, phys, nent, num_blocks, rowid);
+}
+
+// Work item of workgroup L of a 1-D grid: (token t, split sp, group z of 64 heads).  In the
+// XCD order (T >= 8) all items of one token are adjacent in the XCD they run on: the
+// dispatcher hands consecutive workgroups to the 8 XCDs in turn, so workgroup L runs on XCD
+// L % 8, which takes tokens t = L % 8 (mod 8), each with its splits x groups items in a
+// row -- the token's query (73.7 KB per head group) then comes from that XCD's L2 after
+// its first fetch, and its head groups read the same rows there.  Workgroups past the last
+// token (t >= T) have nothing to do.  Otherwise: split fastest, then token, then group.
+__device__ __forceinline__ void work_item(int L, int splits, int groups, int T, bool xcd, int& t, int& sp,
+                                          int& z) {
+  if (xcd) {
+    const int x = L & 7, j = L >> 3, per = splits * groups;
+    const int tt = j / per, r = j - tt * per;
+    t = 8 * tt + x;
+    sp = r % splits;
+    z = r / splits;
+  } else {
+    sp = L % splits;
+    const int r = L / splits;
+    t = r % T;
+    z = r / T;
+  }
 }
 
 // LDS row of entry k of a tile: within each group of 8 the entries go to rows
@@ -336,21 +383,21 @@ __device__ __forceinline__ void mla_step(const float* sp_in, float* sp_out, uint
   if (kLogits) store_partials(sacc, sp_out);
 }
 
-// grid (splits, T, H / 64), 256 threads: one workgroup per (split, token, group of 64 heads);
+// 1-D grid of 256-thread workgroups, one per (split, token, group of 64 heads) (work_item);
 // the token's H heads are consecutive in q, out, lse and the partials (groups of one token
 // read the same rows: H = 128 gathers each row twice, the second time mostly from the
-// caches).  splits == 1: normalized bf16 output (+ lse); else the
-// split's unnormalized fp32 partial O and (max, sum) in log2 units go to the workspace,
-// with non-temporal stores when kNtPartials (few tokens: the kernel then ends sooner,
-// measured 1.2 us at one token; with many tokens the combine reads the 30+ MB of partials
-// faster when they stay cached).
+// caches).  splits == 1: normalized bf16 output (+ lse); else the split's normalized partial
+// O (bf16) and (max, sum) in log2 units (fp32) go to the workspace, with non-temporal
+// stores when kNtPartials (few tokens: the kernel then ends sooner, measured 1.2 us at one
+// token; with many tokens the combine reads the partials faster when they stay cached).
 template <bool kNtPartials>
 __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
     const int* __restrict__ block_table, const int* __restrict__ seq_len, int max_blocks, int batch,
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
-    int64_t ld_idx, int k, float scale_log2, int splits, int H, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    int64_t ld_idx, int k, float scale_log2, int splits, int groups, int T, int xcd, int H,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ ws_o,
+    float* __restrict__ ws_ml) {
   // three V tiles; before the loop the same bytes stage Q (64 rows of 73 chunks)
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[3][kVTileBytes];
   __shared__ int rowid[kMaxList];
@@ -362,25 +409,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int dh = wave & 1, g = lane >> 4, c16 = lane & 15;
-  const int t = blockIdx.y, sp = blockIdx.x;
-  const int64_t h0 = (int64_t)t * H + kH * blockIdx.z;   // the group's first head of the token
+  int t, sp, z;
+  work_item(blockIdx.x, splits, groups, T, xcd != 0, t, sp, z);
+  if (t >= T) return;   // past the last token (whole workgroup)
+  const int64_t h0 = (int64_t)t * H + kH * z;   // the group's first head of the token
 
-  // Q: coalesced 16-byte loads (thread tid takes chunks tid + 256i of the 64 x 72), issued
-  // first so that their latency overlaps the list lookups
+  // Loads go out in the order they are needed -- the slice's list entries, its page-table
+  // entries, then Q (coalesced 16-byte loads: thread tid takes chunks tid + 256i of the
+  // 64 x 72) -- so neither translation round trip waits behind the 73.7 KB of Q (loads
+  // complete in order); Q arrives during the page-table and first-tile round trips.
+  ListSlice ls;
+  int phys[kPer], nent;
+  load_list(t, sp, splits, seq_len, batch, q_row, q_pos, idx, ld_idx, k, ls);
+  load_pages(ls, sp, splits, block_table, max_blocks, batch, k, phys, nent);
   constexpr int kQLoads = kH * kChunks / kThreads;   // 18
   static_assert(kQLoads * kThreads == kH * kChunks, "Q chunks divide evenly");
   u32x4 qs[kQLoads];
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i)
     qs[i] = *reinterpret_cast<const u32x4*>(q + h0 * kRowBytes + 16 * (tid + kThreads * i));
-  int nent;
-  resolve_rows(t, sp, splits, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos,
-               idx, ld_idx, k, rowid, nent);
+  write_rows(ls, phys, nent, num_blocks, rowid);
   __syncthreads();
   const int ntiles = (nent + kMT - 1) / kMT;
-  // the first tile's fragments go out before Q is unpacked
+  // the first tile's fragments go out before Q is unpacked (an empty slice reads the zero
+  // row: no branch, so the wait for Q below does not also wait for these)
   KRegs kr;
-  if (ntiles > 0) load_k(kr, k_src(pool, rowid, 0));
+  load_k(kr, k_src(pool, rowid, 0));
   uint8_t* qst = &vbuf[0][0];
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i) {
@@ -405,7 +459,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   // registers with the tile after).  Tile t: partials in spart[t % 2], P in pmat[t % 2],
   // V in vbuf[t % 3].  Step t (t = 0..ntiles) = logits(t+1) + softmax(t) + P.V(t-1);
   // before the first step, the logits of tile 0.  A second pass (rare) starts from the first
-  // pass's final max with O and l cleared.
+  // pass's final max with O and l cleared.  (A second register set, two tiles in flight,
+  // measured slower: 2.02 against 1.82 us per tile on the 4-layer decode workload.)
   bool ovf_step = false;   // this lane's head moved its max after O started (this pass)
   // step tt with the given stages (kSoft = tt < ntiles, kLogits = tt + 1 < ntiles,
   // kPrefetch = tt + 2 < ntiles, kPV = tt >= 1)
@@ -460,6 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       }
       DSA_STEP(false, false, false, true, tt)
     }
+#undef DSA_STEP
     const bool wave_ovf = __ballot(ovf_step) != 0;   // all lanes take part in the vote
     if (lane == 0) s_ovf[wave] = wave_ovf;
     __syncthreads();
@@ -475,6 +531,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
     s_ml[16 * wave + c16][1] = l_run;
   }
   __syncthreads();
+  // O / l as bf16, straight from the accumulators: splits == 1 to the output (+ lse), else
+  // the split's partial O to the workspace with its (max, sum).  (Staging O through LDS for
+  // 16-byte coalesced stores measured slower, 3.2 against 2.6 us: with every workgroup
+  // finishing together the stores are bound by write bandwidth, not by their count.)
   if (splits == 1) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
@@ -492,18 +552,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
       lse[h0 + tid] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
   } else {
-    const int64_t base = ((int64_t)t * splits + sp) * H + kH * blockIdx.z;
+    const int64_t base = ((int64_t)t * splits + sp) * H + kH * z;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float* dst = ws_o + (base + 16 * ht + 4 * g + j) * kDl + 128 * wave + c16;
+        const int head = 16 * ht + 4 * g + j;
+        const float l = s_ml[head][1];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* dst = ws_o + (base + head) * kDl + 128 * wave + c16;
         if (kNtPartials) {
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) __builtin_nontemporal_store(o[ht][dt][j], &dst[16 * dt]);
+          for (int dt = 0; dt < 8; ++dt) __builtin_nontemporal_store(f2bf_bits(o[ht][dt][j] * inv), &dst[16 * dt]);
         } else {
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) dst[16 * dt] = o[ht][dt][j];
+          for (int dt = 0; dt < 8; ++dt) dst[16 * dt] = f2bf_bits(o[ht][dt][j] * inv);
         }
       }
     if (tid < kH) {
@@ -513,7 +576,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   }
 }
 
-// Merge split partials: m = max m_s, L = sum l_s 2^(m_s - m), O = sum O_s 2^(m_s - m) / L.
+// Merge split partials (O_s normalized by its own l_s): m = max m_s, L = sum l_s 2^(m_s - m),
+// O = sum (l_s 2^(m_s - m) / L) O_s.
 // grid (T, H, Z); one wave per (token, head) and 1/Z of the output dims, in kNP passes of
 // 64 dims (Z = kPasses / kNP).  Lane 16a + c handles dims 4c..4c+3 of each pass for the
 // splits a, a + 4, ...; lane s also reads split s's (m_s, l_s).  Every load of the wave is
@@ -525,7 +589,7 @@ constexpr int kPasses = kDl / 64;
 constexpr int kCombSlots = 8;
 
 template <int kNP>
-__global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict__ ws_o,
+__global__ __launch_bounds__(64) void mla_combine_kernel(const uint16_t* __restrict__ ws_o,
                                                          const float* __restrict__ ws_ml, int splits,
                                                          int H, uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
@@ -536,7 +600,7 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
   const int a = lane >> 4, c = lane & 15;
   const int nsp = splits > a ? (splits - a + 3) >> 2 : 0;   // splits a, a + 4, ... of this lane
   // slot (i, p): split a + 4i, pass p
-  const float* src = ws_o + (((int64_t)t * splits + a) * H + h) * kDl + 64 * pass0 + 4 * c;
+  const uint16_t* src = ws_o + (((int64_t)t * splits + a) * H + h) * kDl + 64 * pass0 + 4 * c;
   const int64_t sstride = (int64_t)4 * H * kDl;
   float ms = -INFINITY, ls = 0.f;
   if (lane < splits) {
@@ -544,13 +608,12 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
     ms = ml.x;
     ls = ml.y;
   }
-  float4 v[kSPL][kNP];
+  uint2 v[kSPL][kNP];   // 4 bf16 dims
 #pragma unroll
   for (int i = 0; i < kSPL; ++i)
 #pragma unroll
     for (int p = 0; p < kNP; ++p)
-      v[i][p] = i < nsp ? *reinterpret_cast<const float4*>(src + i * sstride + 64 * p)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[i][p] = i < nsp ? *reinterpret_cast<const uint2*>(src + i * sstride + 64 * p) : make_uint2(0u, 0u);
   float m = ms;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, shfl_xor_f(m, off));
@@ -559,7 +622,7 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += shfl_xor_f(L, off);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  const float wl = f * inv;   // weight of split `lane`
+  const float wl = ls * f * inv;   // weight of split `lane`
   float4 acc[kNP];
 #pragma unroll
   for (int p = 0; p < kNP; ++p) acc[p] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -568,10 +631,10 @@ __global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict
     const float w = __shfl(wl, min(a + 4 * i, 63), kWave);   // 0 past the last split
 #pragma unroll
     for (int p = 0; p < kNP; ++p) {
-      acc[p].x = fmaf(w, v[i][p].x, acc[p].x);
-      acc[p].y = fmaf(w, v[i][p].y, acc[p].y);
-      acc[p].z = fmaf(w, v[i][p].z, acc[p].z);
-      acc[p].w = fmaf(w, v[i][p].w, acc[p].w);
+      acc[p].x = fmaf(w, __uint_as_float(v[i][p].x << 16), acc[p].x);
+      acc[p].y = fmaf(w, __uint_as_float(v[i][p].x & 0xFFFF0000u), acc[p].y);
+      acc[p].z = fmaf(w, __uint_as_float(v[i][p].y << 16), acc[p].z);
+      acc[p].w = fmaf(w, __uint_as_float(v[i][p].y & 0xFFFF0000u), acc[p].w);
     }
   }
   uint16_t* dst = out + ((int64_t)t * H + h) * kDl + 64 * pass0 + 4 * c;
@@ -679,19 +742,20 @@ int combine_slices(int T, int H, int splits) {
 }
 static_assert((32 + 3) / 4 * 1 <= kCombSlots, "32 splits fit at Z = kPasses");
 
+// Split partials: O [T][splits][H][Dl] bf16, then (max, sum) [T][splits][H][2] fp32.
 size_t mla_workspace_bytes(int T, int k, int H, int Dl, bool bf16) {
   const int s = mla_splits(T, k, H, bf16);
   if (s <= 1) return 0;
-  return (size_t)T * s * H * (Dl + 2) * sizeof(float);
+  return (size_t)T * s * H * (2 * (size_t)Dl + 2 * sizeof(float));
 }
 
 // ---- split partials without a caller workspace (dsa_sparse_mla_decode_noalloc)
 // At most 256 (token, split, head group) work items carry partials (mla_splits keeps
-// T * splits * groups <= 256 whenever splits > 1), each 64 heads x (512 + 2) fp32: the
-// largest workspace any call needs.  Every GPU the library runs on holds one copy of this
+// T * splits * groups <= 256 whenever splits > 1), each 64 heads x (512 bf16 + 2 fp32):
+// the largest workspace any call needs.  Every GPU the library runs on holds one copy of this
 // array until the process ends; host code reaches it only through the address
 // hipGetSymbolAddress gives for the current device.
-constexpr size_t kScratchBytes = (size_t)256 * kH * (kDl + 2) * sizeof(float);
+constexpr size_t kScratchBytes = (size_t)256 * kH * (2 * kDl + 2 * sizeof(float));
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -720,16 +784,19 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
   if (a.bf16) {
     const int splits = mla_splits(a.T, a.k, a.H, true);
     const int groups = a.H / kH;
-    float* ws_o = (float*)a.ws;
-    float* ws_ml = ws_o ? ws_o + (size_t)a.T * splits * a.H * kDl : nullptr;
+    uint16_t* ws_o = (uint16_t*)a.ws;
+    float* ws_ml = ws_o ? (float*)(ws_o + (size_t)a.T * splits * a.H * kDl) : nullptr;
+    const bool xcd = a.T >= 8;
+    const int64_t items = (int64_t)(xcd ? (a.T + 7) / 8 * 8 : a.T) * splits * groups;
     {
       const KernelEvents ev("mla_bf16_kernel");
       auto kernel = (int64_t)a.T * splits * groups <= kNtPartialsMax ? mla_bf16_kernel<true>
                                                                      : mla_bf16_kernel<false>;
-      hipExtLaunchKernelGGL(kernel, dim3(splits, a.T, groups), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
+      hipExtLaunchKernelGGL(kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
                             (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks, a.block_table,
                             a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k,
-                            a.sm_scale * kLog2e, splits, a.H, (uint16_t*)a.out, a.lse, ws_o, ws_ml);
+                            a.sm_scale * kLog2e, splits, groups, a.T, (int)xcd, a.H, (uint16_t*)a.out, a.lse,
+                            ws_o, ws_ml);
     }
     if (splits > 1) {
       const int Z = combine_slices(a.T, a.H, splits);

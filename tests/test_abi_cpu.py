@@ -210,16 +210,18 @@ def test_prefill_requires_positions():
 
 
 def test_workspace_sizes():
-    # decode of 1 token splits the 2048-entry list 32 ways; a 4096-token prefill does not split
+    # decode of 1 token splits the 2048-entry list 32 ways; a 4096-token prefill does not split.
+    # Per (token, split, head): 512 bf16 of normalized partial O and fp32 (max, sum)
+    per = 512 * 2 + 2 * 4
     one = L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 1, 0, 2048, 64, 512)
-    assert one == 32 * 64 * (512 + 2) * 4
+    assert one == 32 * 64 * per
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 4096, 0, 2048, 64, 512) == 0
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 0, 0, 2048, 64, 512) == 0
     # 128 heads run as two 64-head workgroups per (token, split): one token still splits 32
     # ways (64 workgroups), 64 tokens split 2 ways, 128 tokens do not split
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 1, 0, 2048, 128, 512) == 32 * 128 * (512 + 2) * 4
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 128, 512) == 64 * 2 * 128 * (512 + 2) * 4
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 64, 512) == 64 * 4 * 64 * (512 + 2) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 1, 0, 2048, 128, 512) == 32 * 128 * per
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 128, 512) == 64 * 2 * 128 * per
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 64, 512) == 64 * 4 * 64 * per
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 128, 0, 2048, 128, 512) == 0
     # rows of at most 32768 positions are selected in one workgroup: no workspace
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 64, 32768, 2048, 0, 0) == 0
@@ -288,9 +290,9 @@ def test_noalloc_decode_rejects(kw, status):
 
 
 def test_noalloc_scratch_holds_every_workspace():
-    # the library's scratch array (33,685,504 bytes) covers the split partials of every
+    # the library's scratch array (16,908,288 bytes) covers the split partials of every
     # batch size, head count and list width the bf16 decode accepts
-    scratch = 256 * 64 * (512 + 2) * 4
+    scratch = 256 * 64 * (512 * 2 + 2 * 4)
     for H in (64, 128):
         for k in (1, 31, 32, 33, 500, 2047, 2048):
             for T in list(range(1, 300)) + [511, 512, 1000, 4096, 100000]:
