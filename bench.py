@@ -17,6 +17,8 @@ dsa_timing_start/collect) and the CPU oracle timed on a bounded sample of the sa
 workload's tokens.
 
 Two helper modes turn rocprofv3 output into the text summaries kept under profiles/:
+    --gather-ceiling            random 1152-byte row gathers with the sparse MLA's loads
+                                from pools in L2, Infinity Cache and HBM (--steps launches)
     --copy-calibration MIB      only copies MIB MiB device-to-device (--steps times),
                                 the reference for scaling FETCH_SIZE / WRITE_SIZE
     --summarize-trace DIR       per-kernel table of a --kernel-trace --stats run
@@ -349,6 +351,53 @@ def run_bench(args):
     print(json.dumps(res), flush=True)
 
 
+# pools of the gather-ceiling probe: (rows of 1152 bytes, what they stand for)
+GATHER_POOLS = [
+    (3_000, "3.5 MB: fits each XCD's 4 MB L2"),
+    (16_384, "19 MB: past the L2, inside the Infinity Cache"),
+    (131_072, "151 MB: the prefill chunk's 131072-position latent pool, inside the 256 MB Infinity Cache"),
+    (4_206_592, "4.85 GB: one layer's latent pool of the 4-layer decode workload, HBM"),
+]
+
+
+def run_gather_ceiling(args):
+    """Random 1152-byte row gathers (dsa_probe_row_gather) from pools of increasing size,
+    with the sparse MLA's loads (half a cache line per row per instruction) and with whole
+    128-byte lines: the bandwidth each level of the memory system gives these access
+    patterns.  The list is 4096 x 2048 uniform random rows (9.66 GB, the prefill chunk's
+    gather volume)."""
+    import torch
+    import sparse_attention_19_amd as D
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(7)
+    nlist = 4096 * 2048
+    res = {"metric": "random 1152-byte row gather bandwidth (sparse MLA access pattern)", "unit": "GB/s",
+           "list_rows": nlist, "bytes_per_launch": nlist * 1152, "pools": []}
+    for nrows, what in GATHER_POOLS:
+        pool = torch.empty((nrows, 576), dtype=torch.bfloat16, device=dev)
+        pool.view(torch.int16).random_(-2000, 2000, generator=g)
+        rows = torch.randint(0, nrows, (nlist,), dtype=torch.int32, device=dev, generator=g)
+        entry = {"rows": nrows, "pool_bytes": nrows * 1152, "what": what}
+        sink = D.dsa_probe_row_gather(pool, rows)
+        for lines in (False, True):
+            for _ in range(3):
+                D.dsa_probe_row_gather(pool, rows, sink, lines=lines)
+            torch.cuda.synchronize()
+            D.dsa_timing_start(args.steps)
+            for _ in range(args.steps):
+                D.dsa_probe_row_gather(pool, rows, sink, lines=lines)
+            ms = sorted(t for _, t in D.dsa_timing_collect())
+            med = ms[len(ms) // 2]
+            key = "whole_lines" if lines else "mla_loads"
+            entry[key] = {"median_ms": round(med, 4), "gbs": round(nlist * 1152 / (med * 1e-3) / 1e9, 1)}
+        res["pools"].append(entry)
+        print(f"[gather] {what}: MLA loads {entry['mla_loads']['gbs']} GB/s, whole lines "
+              f"{entry['whole_lines']['gbs']} GB/s", flush=True)
+        del pool, rows, sink
+        torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
 # workloads of the report: (config name, overrides, what it is)
 REPORT_WORKLOADS = [
     ("tiny_fp32", {}, "1 token, L = 256, fp32 (parity case)"),
@@ -619,6 +668,8 @@ def main():
     ap.add_argument("--no-index-share", action="store_true",
                     help="every layer runs its own indexer and top-k (the plain-DSA comparison)")
     ap.add_argument("--report", action="store_true", help="every workload; writes REPORT.md")
+    ap.add_argument("--gather-ceiling", action="store_true",
+                    help="random-row gather bandwidth per pool size (L2, Infinity Cache, HBM)")
     ap.add_argument("--report-cpu-budget", type=float, default=8.0, help="oracle seconds per workload")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -654,6 +705,8 @@ def main():
         return run_copy_calibration(args)
     if args.report:
         return run_report(args)
+    if args.gather_ceiling:
+        return run_gather_ceiling(args)
     run_bench(args)
 
 

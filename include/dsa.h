@@ -258,6 +258,22 @@ const char* dsa_version(void);
 dsa_status dsa_timing_start(int32_t capacity);
 int32_t dsa_timing_collect(const char** names, float* ms, int32_t cap);
 
+/*
+ * Memory-system probe, for benchmarks (not part of the method): reads the 1152-byte rows
+ * rows[0 .. nlist-1] of a pool of nrows rows (device [nrows][1152] bytes) in 32-row tiles,
+ * 2048 list entries per 256-thread workgroup, the next tile in flight, and writes one
+ * checksum word per thread to sink (device, dsa_probe_row_gather_sink_words(nlist)
+ * words).  lines = 0: the sparse MLA's own loads (16 bytes per lane of 16 rows per load
+ * instruction, half a cache line per row); lines = 1: whole 128-byte lines (8 rows per
+ * instruction).  Row ids outside [0, nrows) read row 0.  Timed like the path's kernels
+ * (dsa_timing_*), it gives the gather bandwidth the pool's size allows: L2-, Infinity-
+ * Cache- or HBM-resident.  DSA_ERR_INVALID for NULL pointers, non-positive sizes or lines
+ * other than 0 or 1.
+ */
+dsa_status dsa_probe_row_gather(const void* pool, int64_t nrows, const int32_t* rows, int64_t nlist,
+                                int32_t lines, uint32_t* sink, void* stream);
+size_t dsa_probe_row_gather_sink_words(int64_t nlist);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ __all__ = [
     "dsa_sparse_mla_prefill",
     "IndexCache", "PageTable", "Chunk", "dsa_workspace_bytes", "workspace", "DsaError", "LIB_PATH",
     "DSA_OP_TOPK", "DSA_OP_MLA",
-    "dsa_timing_start", "dsa_timing_collect",
+    "dsa_timing_start", "dsa_timing_collect", "dsa_probe_row_gather",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
@@ -199,6 +199,22 @@ class IndexCache:
         check(LIB.dsa_index_cache_get(ctypes.byref(self.c), step, layer_in_group, ctypes.byref(p)))
         assert p.value == self.idx.data_ptr()
         return self.idx
+
+
+def dsa_probe_row_gather(pool: torch.Tensor, rows: torch.Tensor, sink: Optional[torch.Tensor] = None,
+                         lines: bool = False, stream=None) -> torch.Tensor:
+    """Measurement aid: gather pool rows (1152-byte rows, [nrows][576] bf16) listed in rows
+    with the sparse MLA's loads (or whole cache lines); returns the checksum sink
+    (allocated here if not given)."""
+    if pool.element_size() * pool.shape[-1] != 1152:
+        raise ValueError("pool rows must be 1152 bytes")
+    nrows = pool.numel() * pool.element_size() // 1152
+    words = int(LIB.dsa_probe_row_gather_sink_words(rows.numel()))
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=pool.device)
+    check(LIB.dsa_probe_row_gather(_dev(pool, "pool"), nrows, _dev(rows, "rows", torch.int32), rows.numel(),
+                                   int(lines), _dev(sink, "sink", torch.int32), _stream(stream, pool)))
+    return sink
 
 
 def dsa_timing_start(capacity: int) -> None:

@@ -24,7 +24,7 @@ EXPORTS = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc",
     "dsa_sparse_mla_prefill", "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
     "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
-    "dsa_timing_start", "dsa_timing_collect",
+    "dsa_timing_start", "dsa_timing_collect", "dsa_probe_row_gather", "dsa_probe_row_gather_sink_words",
 ]
 
 
@@ -72,6 +72,8 @@ def _load() -> ctypes.CDLL:
         "dsa_version": [],
         "dsa_timing_start": [I32],
         "dsa_timing_collect": [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(F), I32],
+        "dsa_probe_row_gather": [P, I64, P, I64, I32, P, P],
+        "dsa_probe_row_gather_sink_words": [I64],
     }
     missing = [n for n in sig if not hasattr(lib, n)]
     if missing:
@@ -82,6 +84,7 @@ def _load() -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_int
     lib.dsa_workspace_bytes.restype = ctypes.c_size_t
+    lib.dsa_probe_row_gather_sink_words.restype = ctypes.c_size_t
     lib.dsa_status_string.restype = ctypes.c_char_p
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_version.restype = ctypes.c_char_p

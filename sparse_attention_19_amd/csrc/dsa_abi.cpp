@@ -333,6 +333,23 @@ const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
 const char* dsa_version(void) { return "dsa-gfx950 0.2.0"; }
 
+dsa_status dsa_probe_row_gather(const void* pool, int64_t nrows, const int32_t* rows, int64_t nlist,
+                                int32_t lines, uint32_t* sink, void* stream) {
+  if (!pool || !rows || !sink) return fail(DSA_ERR_INVALID, "pool/rows/sink is NULL");
+  if (nrows <= 0 || nlist <= 0) return fail(DSA_ERR_INVALID, "nrows %lld / nlist %lld must be positive",
+                                            (long long)nrows, (long long)nlist);
+  if (!aligned16(pool)) return fail(DSA_ERR_INVALID, "pool not 16-byte aligned");
+  if (dsa::probe_gather_workgroups(nlist) > INT32_MAX)
+    return fail(DSA_ERR_INVALID, "nlist %lld too long", (long long)nlist);
+  if (lines != 0 && lines != 1) return fail(DSA_ERR_INVALID, "lines must be 0 or 1");
+  return launched(dsa::launch_probe_row_gather(pool, nrows, rows, nlist, lines != 0, sink, (hipStream_t)stream),
+                  "row gather probe launch");
+}
+
+size_t dsa_probe_row_gather_sink_words(int64_t nlist) {
+  return nlist > 0 ? (size_t)dsa::probe_gather_workgroups(nlist) * 256 : 0;
+}
+
 dsa_status dsa_timing_start(int32_t capacity) {
   if (capacity < 1 || capacity > (1 << 20))
     return fail(DSA_ERR_INVALID, "timing capacity %d outside [1, %d]", capacity, 1 << 20);

@@ -77,4 +77,9 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
 size_t mla_scratch_bytes();
 hipError_t mla_scratch(void** ptr);
 
+// Measurement aid: random 1152-byte row gathers with the sparse MLA's access pattern.
+int64_t probe_gather_workgroups(int64_t nlist);
+hipError_t launch_probe_row_gather(const void* pool, int64_t nrows, const int* rows, int64_t nlist, bool lines,
+                                   uint32_t* sink, hipStream_t stream);
+
 }  // namespace dsa

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -297,3 +297,12 @@ def test_noalloc_scratch_holds_every_workspace():
         for k in (1, 31, 32, 33, 500, 2047, 2048):
             for T in list(range(1, 300)) + [511, 512, 1000, 4096, 100000]:
                 assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, T, 0, k, H, 512) <= scratch, (H, k, T)
+
+
+def test_probe_rejects():
+    assert L.LIB.dsa_probe_row_gather(None, 10, FAKE, 100, 0, FAKE2, None) == L.DSA_ERR_INVALID
+    assert L.LIB.dsa_probe_row_gather(FAKE, 0, FAKE, 100, 0, FAKE2, None) == L.DSA_ERR_INVALID
+    assert L.LIB.dsa_probe_row_gather(FAKE, 10, FAKE, 0, 0, FAKE2, None) == L.DSA_ERR_INVALID
+    assert L.LIB.dsa_probe_row_gather(FAKE + 8, 10, FAKE, 100, 0, FAKE2, None) == L.DSA_ERR_INVALID
+    assert L.LIB.dsa_probe_row_gather(FAKE, 10, FAKE, 100, 2, FAKE2, None) == L.DSA_ERR_INVALID
+    assert L.LIB.dsa_probe_row_gather_sink_words(4097) == 3 * 256
