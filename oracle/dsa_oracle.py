@@ -117,6 +117,38 @@ def mla_absorbed(q: np.ndarray, rows: np.ndarray, Dl: int, sm_scale: float):
     return out, lse
 
 
+# --------------------------------------------------------------------------- MHA mode
+
+def mla_mha(q_nope: np.ndarray, q_rope: np.ndarray, latent: np.ndarray, rope: np.ndarray,
+            w_uk: np.ndarray, w_uv: np.ndarray, sm_scale: float):
+    """MHA mode of MLA for one query token over a set of cached rows.
+
+    [§Sparse MLA] MLA runs either in MHA mode or in MQA mode; MHA mode gives every head its
+    own keys and values, up-projected from the cached latent, and spends fewer FLOPs per
+    (query, key) pair at a much larger memory footprint.  [§MLA changes] GLM-5's query-key
+    head: a 192-dim NoPE part and the 64-dim rope part (SDPA head dim 256).  Per head h:
+      K_h = [latent @ w_uk[h], rope],  V_h = latent @ w_uv[h]
+      out[h] = softmax_s(sm_scale * K_h[s] . [q_nope[h], q_rope[h]]) @ V_h
+    q_nope [H][dn], q_rope [H][dr], latent [S][dl], rope [S][dr], w_uk [H][dl][dn],
+    w_uv [H][dl][dv]  ->  out float64 [H][dv], lse float64 [H]
+    """
+    latent = latent.astype(np.float64)
+    rope = rope.astype(np.float64)
+    H = q_nope.shape[0]
+    out = np.empty((H, w_uv.shape[2]))
+    lse = np.empty(H)
+    for h in range(H):
+        k_nope = latent @ w_uk[h].astype(np.float64)                      # [S][dn]
+        v = latent @ w_uv[h].astype(np.float64)                           # [S][dv]
+        logits = sm_scale * (k_nope @ q_nope[h].astype(np.float64) + rope @ q_rope[h].astype(np.float64))
+        m = logits.max()
+        p = np.exp(logits - m)
+        z = p.sum()
+        out[h] = (p @ v) / z
+        lse[h] = m + np.log(z)
+    return out, lse
+
+
 # --------------------------------------------------------------------------- composite steps
 
 def visible_count(q_pos: int) -> int:

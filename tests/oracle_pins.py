@@ -21,7 +21,8 @@ def real_impl():
     return types.SimpleNamespace(indexer_scores=O.indexer_scores, topk_positions=O.topk_positions,
                                  mla_absorbed=O.mla_absorbed, logical_rows=O.logical_rows,
                                  decode_token=O.decode_token, bf16_bits_to_f64=O.bf16_bits_to_f64,
-                                 visible_count=O.visible_count, group_token=O.group_token)
+                                 visible_count=O.visible_count, group_token=O.group_token,
+                                 mla_mha=O.mla_mha)
 
 
 # ------------------------------------------------------------------ indexer
@@ -322,3 +323,52 @@ def check_composition(impl, inputs=None):
 
 
 ALL_CHECKS += [check_bf16_decode, check_composition]
+
+
+# ------------------------------------------------------------------ MHA mode
+
+def check_mha(impl, seed=5):
+    """MHA mode against a pure-Python brute force, and against MQA mode through the
+    absorption identity: with q' = [w_uk[h] @ q_nope[h], q_rope[h]] the absorbed attention
+    over [latent, rope] rows gives the latent-space output o, and o @ w_uv[h] is MHA mode's
+    output (the logits and the softmax are the same numbers), exactly in float64."""
+    rng = np.random.default_rng(seed)
+    for (H, dl, dn, dr, dv, S) in [(2, 6, 3, 2, 4, 5), (3, 16, 8, 4, 8, 33), (2, 8, 4, 4, 2, 1)]:
+        qn = rng.standard_normal((H, dn))
+        qr = rng.standard_normal((H, dr))
+        lat = rng.standard_normal((S, dl))
+        rp = rng.standard_normal((S, dr))
+        wuk = rng.standard_normal((H, dl, dn)) / np.sqrt(dl)
+        wuv = rng.standard_normal((H, dl, dv)) / np.sqrt(dl)
+        sc = 1.0 / np.sqrt(dn + dr)
+        out, lse = impl.mla_mha(qn, qr, lat, rp, wuk, wuv, sc)
+        assert out.shape == (H, dv) and lse.shape == (H,)
+        # brute force, per head, in Python floats
+        for h in range(H):
+            k = [[sum(lat[s][c] * wuk[h][c][j] for c in range(dl)) for j in range(dn)] + list(rp[s]) for s in range(S)]
+            v = [[sum(lat[s][c] * wuv[h][c][j] for c in range(dl)) for j in range(dv)] for s in range(S)]
+            q = list(qn[h]) + list(qr[h])
+            lg = [sc * sum(a * b for a, b in zip(q, k[s])) for s in range(S)]
+            m = max(lg)
+            e = [math.exp(x - m) for x in lg]
+            z = sum(e)
+            want = [sum(e[s] * v[s][j] for s in range(S)) / z for j in range(dv)]
+            assert np.allclose(out[h], want, rtol=1e-11, atol=1e-11)
+            assert abs(lse[h] - (m + math.log(z))) < 1e-11
+        # absorption identity: MQA mode over the latent rows, then the value up-projection
+        rows = np.concatenate([lat, rp], axis=1)
+        qabs = np.stack([np.concatenate([wuk[h] @ qn[h], qr[h]]) for h in range(H)])
+        o_lat, lse_abs = O.mla_absorbed(qabs, rows, dl, sc)
+        mqa = np.stack([o_lat[h] @ wuv[h] for h in range(H)])
+        assert np.allclose(out, mqa, rtol=1e-11, atol=1e-11)
+        assert np.allclose(lse, lse_abs, rtol=1e-11, atol=1e-11)
+    # closed form: no NoPE weights and a zero rope query -> uniform weights, the mean of V
+    lat = rng.standard_normal((7, 6))
+    wuv = rng.standard_normal((2, 6, 3))
+    out, lse = impl.mla_mha(rng.standard_normal((2, 3)), np.zeros((2, 2)), lat, rng.standard_normal((7, 2)),
+                            np.zeros((2, 6, 3)), wuv, 0.7)
+    assert np.allclose(out, np.stack([lat.mean(0) @ wuv[h] for h in range(2)]), atol=1e-12)
+    assert np.allclose(lse, math.log(7), atol=1e-12)
+
+
+ALL_CHECKS += [check_mha]

@@ -119,6 +119,22 @@ def _bf16_unsigned(bits):
 _GROUP = O.group_token     # the real composition (the mutants below wrap it)
 
 
+def _mha_no_rope(qn, qr, lat, rp, wuk, wuv, sc):
+    return O.mla_mha(qn, qr * 0, lat, rp, wuk, wuv, sc)
+
+
+def _mha_keys_without_rope(qn, qr, lat, rp, wuk, wuv, sc):
+    return O.mla_mha(qn, qr, lat, rp * 0, wuk, wuv, sc)
+
+
+def _mha_value_dims_reversed(qn, qr, lat, rp, wuk, wuv, sc):
+    return O.mla_mha(qn, qr, lat, rp, wuk, wuv[:, :, ::-1], sc)
+
+
+def _mha_no_scale(qn, qr, lat, rp, wuk, wuv, sc):
+    return O.mla_mha(qn, qr, lat, rp, wuk, wuv, 1.0)
+
+
 def _sees_before_own(q_pos):
     return int(q_pos)                 # off by one: the query does not see its own key
 
@@ -165,6 +181,10 @@ MUTANTS = {
     "indexshare_layers_select_own": ("group_token", _layers_select_own, P.check_composition),
     "indexshare_layers_use_q0": ("group_token", _layers_use_q0, P.check_composition),
     "indexshare_layers_use_pool0": ("group_token", _layers_use_pool0, P.check_composition),
+    "mha_no_rope": ("mla_mha", _mha_no_rope, P.check_mha),
+    "mha_keys_without_rope": ("mla_mha", _mha_keys_without_rope, P.check_mha),
+    "mha_value_dims_reversed": ("mla_mha", _mha_value_dims_reversed, P.check_mha),
+    "mha_no_scale": ("mla_mha", _mha_no_scale, P.check_mha),
 }
 
 
