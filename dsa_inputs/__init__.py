@@ -27,7 +27,11 @@ import torch
 BLOCK = 64  # tokens per page of every paged cache
 
 # tensor ids used to derive independent generator seeds
-_T_QIDX, _T_W, _T_KPOOL, _T_Q, _T_KV, _T_PERM, _T_LENS = range(7)
+_T_QIDX, _T_W, _T_KPOOL, _T_Q, _T_KV, _T_PERM, _T_LENS, _T_WUK, _T_WUV, _T_QMHA = range(10)
+
+# MLA's per-head dims for the MHA-mode inputs (GLM-5: 192 NoPE + 64 rope query-key dims; a
+# 128-dim value head)
+MHA_DN, MHA_DR, MHA_DV = 192, 64, 128
 
 
 @dataclasses.dataclass(frozen=True)
@@ -43,6 +47,8 @@ class Config:
     identity_pages : physical block i holds logical block i (else a random permutation)
     layout_seed    : seed of the context lengths and the page permutation when set (else
                      `seed`): copies of a workload with new data but the same layout
+    mha            : also draw MLA's MHA-mode inputs: up-projection weights and per-head
+                     queries of 192 NoPE + 64 rope dims (values 128 dims)
     index_share    : with several layers, the first layer's selection serves the group
                      (IndexShare); False runs the indexer and top-k in every layer, the plain
                      DSA that IndexShare is compared with (same indexer inputs per layer)
@@ -68,6 +74,7 @@ class Config:
     identity_pages: bool = False
     layout_seed: Optional[int] = None
     index_share: bool = True
+    mha: bool = False
 
     @property
     def row_dim(self) -> int:
@@ -191,6 +198,12 @@ def make_inputs(cfg: Config, device="cpu") -> dict:
       kv_pools     list over layers of [nblk][64][Dl+Dr] latent rows (cfg.dtype)
       q            list over layers of [T][H][Dl+Dr] absorbed queries (cfg.dtype)
       q_row, q_pos int32 [T]            request and position of each query token
+    With cfg.mha (MHA mode of MLA, layer 0's latent pool):
+      w_uk         [H][Dl][192]         latent -> NoPE key per head, N(0, 1/Dl)
+      w_uv         [H][Dl][128]         latent -> value per head, N(0, 1/Dl)
+      w_kv         [H][320][Dl]         per head w_uk transposed, then w_uv transposed (the
+                                        layout the projection kernels read)
+      q_mha        [T][H][256]          per-head query: 192 NoPE dims then 64 rope dims
     Decode: T = B, query t belongs to request t at position seq_len[t]-1.
     Prefill: T = prefill_tokens, all of request 0, positions ctx-T .. ctx-1.
     """
@@ -223,4 +236,16 @@ def make_inputs(cfg: Config, device="cpu") -> dict:
         "q": [_normal(cfg, _T_Q, l, (T, cfg.H, cfg.row_dim), cfg.dtype, device)
               for l in range(cfg.layers)],
     }
+    if cfg.mha:
+        # N(0, 1) scaled by 1/sqrt(Dl) in fp32 before rounding, so projected keys and values
+        # are about N(0, 1) like the latent rows
+        wuk = _chunked((cfg.H, cfg.Dl, MHA_DN), lambda sh: torch.randn(sh, generator=_gen(cfg, _T_WUK, 0, device),
+                                                                      device=device) / math.sqrt(cfg.Dl),
+                       cfg.dtype, device, rows_per_chunk=cfg.H)
+        wuv = _chunked((cfg.H, cfg.Dl, MHA_DV), lambda sh: torch.randn(sh, generator=_gen(cfg, _T_WUV, 0, device),
+                                                                      device=device) / math.sqrt(cfg.Dl),
+                       cfg.dtype, device, rows_per_chunk=cfg.H)
+        inp["w_uk"], inp["w_uv"] = wuk, wuv
+        inp["w_kv"] = torch.cat([wuk.transpose(1, 2), wuv.transpose(1, 2)], dim=1).contiguous()
+        inp["q_mha"] = _normal(cfg, _T_QMHA, 0, (T, cfg.H, MHA_DN + MHA_DR), cfg.dtype, device)
     return inp

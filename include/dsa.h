@@ -66,7 +66,7 @@ typedef enum {
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
 
 /* Operations that may need a workspace (argument of dsa_workspace_bytes). */
-typedef enum { DSA_OP_TOPK = 0, DSA_OP_MLA = 1 } dsa_op;
+typedef enum { DSA_OP_TOPK = 0, DSA_OP_MLA = 1, DSA_OP_MLA_MHA = 2, DSA_OP_MLA_HEADS = 3 } dsa_op;
 
 /* A paged cache pool in device memory: [num_blocks][DSA_BLOCK][row_dim] of dtype. */
 typedef struct {
@@ -210,6 +210,60 @@ dsa_status dsa_sparse_mla_prefill(const void* q, const dsa_pool* kv, const dsa_p
                                   size_t ws_bytes, void* stream);
 
 /*
+ * MLA's two modes for a causal prefill chunk, and the switch between them by context length
+ * [§Sparse MLA: MLA runs in MHA mode (every head with its own keys and values, fewer FLOPs
+ * per query-key pair, far more memory) or in MQA mode (the latent row shared by all heads,
+ * the absorbed form every other call here computes); DSA uses MQA mode, but below a
+ * sequence-length threshold MHA mode is faster; §MLA changes: GLM-5's query-key head is 192
+ * NoPE + 64 rope dims].  Per head h the dims are fixed: latent 512, rope 64, NoPE 192, value
+ * 128; H is 1..128 (MQA mode: 64 or 128); bf16 throughout, fp32 accumulation.  Weights:
+ *   w_uk  device [H][512][192]  W_UK_h: latent -> NoPE key (K_nope = latent . W_UK_h)
+ *   w_kv  device [H][320][512]  per head, W_UK_h transposed (192 rows) then W_UV_h transposed
+ *                               (128 rows), W_UV_h: latent -> value (V = latent . W_UV_h)
+ * The query of a token is q_mha [T][H][256]: 192 NoPE dims then 64 rope dims.
+ *
+ * dsa_mla_up_project   kv_mha[r][h] = [latent_r . W_UK_h, latent_r . W_UV_h] for every row r
+ *                      of the pool (kv device [num_blocks][64][576] bf16; kv_mha device
+ *                      [num_blocks * 64][H][320] bf16): MHA mode's per-head key and value cache
+ *                      (the rope part of the keys stays in the latent rows).
+ * dsa_mla_absorb_q     q_abs[t][h] = [W_UK_h . q_nope, q_rope] ([T][H][576]): the query of MQA
+ *                      mode, whose dot product with a latent row equals MHA mode's q . K_h.
+ * dsa_mla_unabsorb_o   o[t][h] = o_lat[t][h] . W_UV_h ([T][H][512] -> [T][H][128]): MQA mode's
+ *                      latent output to the head's value space.
+ * dsa_sparse_mla_prefill_mha
+ *                      out[t][h] = softmax over S_t of (sm_scale * q_mha[t][h] . K_h[s]) applied
+ *                      to V_h, K_h[s] = [kv_mha[s][h][0:192], latent_s[512:576]], V_h[s] =
+ *                      kv_mha[s][h][192:320]; S_t as for dsa_sparse_mla_prefill (its top-k list,
+ *                      or all positions 0..q_pos when it sees at most k).  Computed as masked
+ *                      dense attention over every position a token sees, 128 tokens of one
+ *                      request per workgroup: consecutive 128-token tiles of the chunk must each
+ *                      belong to one request and no token may see more than 65536 positions,
+ *                      else DSA_ERR_UNSUPPORTED.  out [T][H][128] bf16, lse [T][H] fp32 or NULL;
+ *                      ws of dsa_workspace_bytes(DSA_OP_MLA_MHA, T, max q_pos + 1, k, H, 512).
+ * dsa_mla_prefill_heads
+ *                      the same out and lse by the faster mode for the chunk's length: MHA mode
+ *                      (dsa_sparse_mla_prefill_mha over kv_mha, which the caller keeps up to
+ *                      date with dsa_mla_up_project) when kv_mha is given and no token sees
+ *                      more than mha_max_len positions, else MQA mode (dsa_mla_absorb_q,
+ *                      dsa_sparse_mla_prefill, dsa_mla_unabsorb_o); *mode (if not NULL) gets 1
+ *                      for MHA mode, 0 for MQA mode.  ws of dsa_workspace_bytes(
+ *                      DSA_OP_MLA_HEADS, T, max q_pos + 1, k, H, 512) bytes.
+ * All enqueue on `stream` and validate on the host first, as the other calls.
+ */
+dsa_status dsa_mla_up_project(const dsa_pool* kv, const void* w_kv, int32_t H, void* kv_mha, void* stream);
+dsa_status dsa_mla_absorb_q(const void* q_mha, const void* w_uk, int32_t T, int32_t H, void* q_abs, void* stream);
+dsa_status dsa_mla_unabsorb_o(const void* o_lat, const void* w_kv, int32_t T, int32_t H, void* o, void* stream);
+dsa_status dsa_sparse_mla_prefill_mha(const void* q_mha, const dsa_pool* kv, const void* kv_mha,
+                                      const dsa_page_table* pt, const dsa_chunk* chunk, const int32_t* idx,
+                                      int64_t ld_idx, int32_t T, int32_t k, int32_t H, float sm_scale,
+                                      void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+dsa_status dsa_mla_prefill_heads(const void* q_mha, const void* w_uk, const void* w_kv, const dsa_pool* kv,
+                                 const void* kv_mha, const dsa_page_table* pt, const dsa_chunk* chunk,
+                                 const int32_t* idx, int64_t ld_idx, int32_t T, int32_t k, int32_t H,
+                                 float sm_scale, int64_t mha_max_len, void* out, float* lse, int32_t* mode,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
  * IndexShare top-k cache  [§IndexShare: the full layer caches its top-K indices so the
  * following shared layers reuse the selection; one indexer per 4 DSA layers].
  * Host-side bookkeeping only; no HIP call.
@@ -229,7 +283,8 @@ dsa_status dsa_index_cache_get(const dsa_index_cache* c, uint64_t step, int32_t 
                                const int32_t** idx);
 
 /* Workspace bytes an operation needs for `rows` query tokens (0 = none).  max_len is the
- * score row stride `ld` for DSA_OP_TOPK and is ignored for DSA_OP_MLA.  For DSA_OP_MLA
+ * score row stride `ld` for DSA_OP_TOPK, the most positions a token sees (max q_pos + 1)
+ * for DSA_OP_MLA_MHA and DSA_OP_MLA_HEADS, and is ignored for DSA_OP_MLA.  For DSA_OP_MLA
  * the size is that of the bf16 instance (split partials); the fp32 instance needs none,
  * so the figure is an upper bound for it. */
 size_t dsa_workspace_bytes(int32_t op, int32_t rows, int64_t max_len, int32_t k, int32_t H, int32_t Dl);

@@ -70,3 +70,25 @@ def expected_token(inp: dict, t: int, layers=None, key_cache: dict = None) -> di
 def expected_topk(scores: np.ndarray, n_valid: np.ndarray, k: int) -> np.ndarray:
     """Top-k of every row of a score matrix [rows][ld] (fp32)."""
     return np.stack([O.topk_positions(scores[r], int(n_valid[r]), k) for r in range(scores.shape[0])])
+
+
+def expected_token_mha(inp: dict, t: int, heads=None) -> dict:
+    """Oracle MHA-mode output of query token t of an input set drawn with cfg.mha: the
+    token's selection (indexer scores, stable-sort top-k, dense below k) and dsa_oracle.mla_mha
+    over those rows of layer 0's latent pool with the input set's up-projection weights,
+    for the listed heads (all by default).
+    Returns dict(out f64 [heads][128], lse [heads], idx, n)."""
+    cfg = inp["cfg"]
+    b = int(inp["q_row"][t])
+    n = O.visible_count(int(inp["q_pos"][t]))
+    bt = inp["block_table"][b].cpu().numpy()
+    keys = request_rows(inp["k_pool"], bt, n)
+    scores = O.indexer_scores(to_f64(inp["q_idx"][t]), to_f64(inp["w"][t]), keys)
+    idx = O.topk_positions(scores, n, cfg.k)
+    rows = selected_rows(inp["kv_pools"][0], bt, idx[idx >= 0])
+    heads = list(range(cfg.H)) if heads is None else list(heads)
+    q = to_f64(inp["q_mha"][t])[heads]
+    dn = inp["w_uk"].shape[2]
+    out, lse = O.mla_mha(q[:, :dn], q[:, dn:], rows[:, :cfg.Dl], rows[:, cfg.Dl:], to_f64(inp["w_uk"][heads]),
+                         to_f64(inp["w_uv"][heads]), cfg.sm_scale)
+    return dict(out=out, lse=lse, idx=idx, n=n)

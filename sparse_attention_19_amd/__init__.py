@@ -13,12 +13,14 @@ from typing import Optional
 
 import torch
 
-from ._lib import (DSA_BF16, DSA_BLOCK, DSA_ERR_INVALID, DSA_F32, DSA_MAX_K, DSA_OP_MLA, DSA_OP_TOPK, LIB,
+from ._lib import (DSA_BF16, DSA_BLOCK, DSA_ERR_INVALID, DSA_F32, DSA_MAX_K, DSA_OP_MLA, DSA_OP_MLA_HEADS,
+                   DSA_OP_MLA_MHA, DSA_OP_TOPK, LIB,
                    LIB_PATH, DsaChunk, DsaError, DsaIndexCache, DsaPageTable, DsaPool, check)
 
 __all__ = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc",
-    "dsa_sparse_mla_prefill",
+    "dsa_sparse_mla_prefill", "dsa_mla_up_project", "dsa_mla_absorb_q", "dsa_mla_unabsorb_o",
+    "dsa_sparse_mla_prefill_mha", "dsa_mla_prefill_heads", "DSA_OP_MLA_MHA", "DSA_OP_MLA_HEADS",
     "IndexCache", "PageTable", "Chunk", "dsa_workspace_bytes", "workspace", "DsaError", "LIB_PATH",
     "DSA_OP_TOPK", "DSA_OP_MLA",
     "dsa_timing_start", "dsa_timing_collect", "dsa_probe_row_gather",
@@ -180,6 +182,59 @@ def dsa_sparse_mla_prefill(q, kv_pool, pt: PageTable, chunk: Chunk, idx, k, sm_s
                                      ctypes.byref(chunk.c), _dev(idx, "idx", torch.int32), idx.shape[1], T, k,
                                      H, Dl, D - Dl, float(sm_scale), _dev(out, "out", kv_pool.dtype),
                                      _opt(lse, "lse", torch.float32), *_ws(ws), _stream(stream, q)))
+
+
+def dsa_mla_up_project(kv_pool, w_kv, kv_mha, stream=None):
+    """kv_mha [num_blocks * 64][H][320] = per-head NoPE keys and values of every latent row."""
+    H = w_kv.shape[0]
+    pool = _pool(kv_pool, "kv_pool")
+    if kv_mha.numel() != kv_pool.shape[0] * kv_pool.shape[1] * H * 320:
+        raise ValueError("kv_mha must hold num_blocks * 64 x H x 320 elements")
+    check(LIB.dsa_mla_up_project(ctypes.byref(pool), _dev(w_kv, "w_kv", torch.bfloat16), H,
+                                 _dev(kv_mha, "kv_mha", torch.bfloat16), _stream(stream, kv_mha)))
+
+
+def dsa_mla_absorb_q(q_mha, w_uk, q_abs, stream=None):
+    """q_abs [T][H][576] = [W_UK_h . q_nope, q_rope] (MQA mode's query)."""
+    T, H, _ = q_mha.shape
+    check(LIB.dsa_mla_absorb_q(_dev(q_mha, "q_mha", torch.bfloat16), _dev(w_uk, "w_uk", torch.bfloat16), T, H,
+                               _dev(q_abs, "q_abs", torch.bfloat16), _stream(stream, q_abs)))
+
+
+def dsa_mla_unabsorb_o(o_lat, w_kv, o, stream=None):
+    """o [T][H][128] = o_lat [T][H][512] . W_UV_h (MQA mode's output to the value space)."""
+    T, H, _ = o_lat.shape
+    check(LIB.dsa_mla_unabsorb_o(_dev(o_lat, "o_lat", torch.bfloat16), _dev(w_kv, "w_kv", torch.bfloat16), T, H,
+                                 _dev(o, "o", torch.bfloat16), _stream(stream, o)))
+
+
+def dsa_sparse_mla_prefill_mha(q_mha, kv_pool, kv_mha, pt: PageTable, chunk: Chunk, idx, k, sm_scale, out, lse=None,
+                               ws=None, stream=None):
+    """MHA-mode attention of a prefill chunk: q_mha [T][H][256] -> out [T][H][128]."""
+    T, H, _ = q_mha.shape
+    pool = _pool(kv_pool, "kv_pool")
+    check(LIB.dsa_sparse_mla_prefill_mha(_dev(q_mha, "q_mha", torch.bfloat16), ctypes.byref(pool),
+                                         _dev(kv_mha, "kv_mha", torch.bfloat16), ctypes.byref(pt.c),
+                                         ctypes.byref(chunk.c), _dev(idx, "idx", torch.int32), idx.shape[1], T, k, H,
+                                         float(sm_scale), _dev(out, "out", torch.bfloat16),
+                                         _opt(lse, "lse", torch.float32), *_ws(ws), _stream(stream, out)))
+
+
+def dsa_mla_prefill_heads(q_mha, w_uk, w_kv, kv_pool, kv_mha, pt: PageTable, chunk: Chunk, idx, k, sm_scale,
+                          mha_max_len, out, lse=None, ws=None, stream=None) -> int:
+    """out [T][H][128] by MHA mode (no token sees more than mha_max_len positions and kv_mha
+    is given) or MQA mode; returns 1 for MHA mode, 0 for MQA mode."""
+    T, H, _ = q_mha.shape
+    pool = _pool(kv_pool, "kv_pool")
+    mode = ctypes.c_int32(-1)
+    check(LIB.dsa_mla_prefill_heads(_dev(q_mha, "q_mha", torch.bfloat16), _dev(w_uk, "w_uk", torch.bfloat16),
+                                    _dev(w_kv, "w_kv", torch.bfloat16), ctypes.byref(pool),
+                                    _opt(kv_mha, "kv_mha", torch.bfloat16), ctypes.byref(pt.c), ctypes.byref(chunk.c),
+                                    _dev(idx, "idx", torch.int32), idx.shape[1], T, k, H, float(sm_scale),
+                                    int(mha_max_len), _dev(out, "out", torch.bfloat16),
+                                    _opt(lse, "lse", torch.float32), ctypes.byref(mode), *_ws(ws),
+                                    _stream(stream, out)))
+    return mode.value
 
 
 class IndexCache:

@@ -15,14 +15,15 @@ LIB_PATH = os.path.join(HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_STALE_INDEX, DSA_ERR_HIP = range(6)
 DSA_F32, DSA_BF16 = 0, 1
-DSA_OP_TOPK, DSA_OP_MLA = 0, 1
+DSA_OP_TOPK, DSA_OP_MLA, DSA_OP_MLA_MHA, DSA_OP_MLA_HEADS = 0, 1, 2, 3
 DSA_BLOCK = 64
 DSA_MAX_K = 2048
 ABI_VERSION = b"dsa-gfx950 0.2.0"   # argument layout this binding marshals for
 
 EXPORTS = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc",
-    "dsa_sparse_mla_prefill", "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
+    "dsa_sparse_mla_prefill", "dsa_mla_up_project", "dsa_mla_absorb_q", "dsa_mla_unabsorb_o",
+    "dsa_sparse_mla_prefill_mha", "dsa_mla_prefill_heads", "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
     "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
     "dsa_timing_start", "dsa_timing_collect", "dsa_probe_row_gather", "dsa_probe_row_gather_sink_words",
 ]
@@ -63,6 +64,12 @@ def _load() -> ctypes.CDLL:
         "dsa_sparse_mla_decode_noalloc": [P, pool_p, pt_p, P, I64, I32, I32, I32, I32, F, P, P, P],
         "dsa_sparse_mla_prefill": [P, pool_p, pt_p, chunk_p, P, I64, I32, I32, I32, I32, I32, F, P, P, P, SZ,
                                    P],
+        "dsa_mla_up_project": [pool_p, P, I32, P, P],
+        "dsa_mla_absorb_q": [P, P, I32, I32, P, P],
+        "dsa_mla_unabsorb_o": [P, P, I32, I32, P, P],
+        "dsa_sparse_mla_prefill_mha": [P, pool_p, P, pt_p, chunk_p, P, I64, I32, I32, I32, F, P, P, P, SZ, P],
+        "dsa_mla_prefill_heads": [P, P, P, pool_p, P, pt_p, chunk_p, P, I64, I32, I32, I32, F, I64, P, P,
+                                  ctypes.POINTER(I32), P, SZ, P],
         "dsa_index_cache_init": [cache_p, P, I64, I32, I32, I32],
         "dsa_index_cache_publish": [cache_p, ctypes.c_uint64],
         "dsa_index_cache_get": [cache_p, ctypes.c_uint64, I32, ctypes.POINTER(ctypes.c_void_p)],

@@ -275,6 +275,197 @@ dsa_status dsa_sparse_mla_prefill(const void* q, const dsa_pool* kv, const dsa_p
   return launched(dsa::launch_mla(a, (hipStream_t)stream), "sparse MLA prefill launch");
 }
 
+// ---------------------------------------------------------------------------------------
+// MLA modes: the projections, MHA-mode attention and the length switch.  Dims are GLM-5's:
+// latent 512 + rope 64, NoPE 192 (query-key head 256), value head 128.
+namespace {
+
+constexpr int kDl = 512, kDr = 64, kDn = 192, kDqk = 256, kDv = 128, kDkv = 320;
+
+dsa_status check_heads(int32_t H) {
+  if (H < 1 || H > 128) return fail(DSA_ERR_UNSUPPORTED, "H = %d outside [1, 128]", H);
+  return DSA_OK;
+}
+
+dsa_status check_latent_pool(const dsa_pool* kv) {
+  dsa_status s = check_pool(kv, "kv", kDl + kDr);
+  if (s) return s;
+  if (kv->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "the MLA modes are instantiated for bf16 pools");
+  return DSA_OK;
+}
+
+hipError_t absorb(const void* q_mha, const void* w_uk, int32_t T, int32_t H, void* q_abs, hipStream_t st) {
+  dsa::GemmArgs g{q_mha, (int64_t)H * kDqk, kDqk, w_uk, kDn, (int64_t)kDl * kDn, q_abs, (int64_t)H * (kDl + kDr),
+                  kDl + kDr, T, kDl, kDn, H, "gemm_absorb_q"};
+  hipError_t e = dsa::launch_gemm_nt(g, st);
+  if (e != hipSuccess) return e;
+  return dsa::launch_copy_rows((const uint16_t*)q_mha + kDn, kDqk, (uint16_t*)q_abs + kDl, kDl + kDr, (int64_t)T * H,
+                               kDr / 8, st);
+}
+
+hipError_t unabsorb(const void* o_lat, const void* w_kv, int32_t T, int32_t H, void* o, hipStream_t st) {
+  dsa::GemmArgs g{o_lat, (int64_t)H * kDl, kDl, (const uint16_t*)w_kv + (int64_t)kDn * kDl, kDl,
+                  (int64_t)kDkv * kDl, o, (int64_t)H * kDv, kDv, T, kDv, kDl, H, "gemm_unabsorb_o"};
+  return dsa::launch_gemm_nt(g, st);
+}
+
+int64_t chunk_max_len(const dsa_chunk* c, int32_t T) {
+  int64_t mx = 0;
+  for (int32_t t = 0; t < T; ++t) mx = c->q_pos_host[t] + 1 > mx ? c->q_pos_host[t] + 1 : mx;
+  return mx;
+}
+
+// MQA-mode workspace: q_abs [T][H][576] and o_lat [T][H][512] bf16, then the sparse MLA's.
+size_t heads_mqa_bytes(int32_t T, int32_t k, int32_t H) {
+  const size_t q = (size_t)T * H * (kDl + kDr) * 2, o = (size_t)T * H * kDl * 2;
+  return (q + o + 255) / 256 * 256 + dsa::mla_workspace_bytes(T, k, H, kDl, true);
+}
+
+}  // namespace
+
+dsa_status dsa_mla_up_project(const dsa_pool* kv, const void* w_kv, int32_t H, void* kv_mha, void* stream) {
+  dsa_status s = check_latent_pool(kv);
+  if (s) return s;
+  if ((s = check_heads(H))) return s;
+  if (!w_kv || !kv_mha) return fail(DSA_ERR_INVALID, "w_kv/kv_mha is NULL");
+  if (!aligned16(w_kv) || !aligned16(kv_mha)) return fail(DSA_ERR_INVALID, "w_kv/kv_mha not 16-byte aligned");
+  const int64_t rows = kv->num_blocks * DSA_BLOCK;
+  if ((rows + 127) / 128 > 65535) return fail(DSA_ERR_UNSUPPORTED, "pool of %lld rows too large", (long long)rows);
+  dsa::GemmArgs g{kv->data, kDl + kDr, 0, w_kv, kDl, 0, kv_mha, (int64_t)H * kDkv, 0, (int)rows, H * kDkv, kDl, 1,
+                  "gemm_up_project"};
+  return launched(dsa::launch_gemm_nt(g, (hipStream_t)stream), "up-projection launch");
+}
+
+dsa_status dsa_mla_absorb_q(const void* q_mha, const void* w_uk, int32_t T, int32_t H, void* q_abs, void* stream) {
+  dsa_status s = check_heads(H);
+  if (s) return s;
+  if (T < 0) return fail(DSA_ERR_INVALID, "T = %d < 0", T);
+  if (T == 0) return ok();
+  if (!q_mha || !w_uk || !q_abs) return fail(DSA_ERR_INVALID, "q_mha/w_uk/q_abs is NULL");
+  if (!aligned16(q_mha) || !aligned16(w_uk) || !aligned16(q_abs)) return fail(DSA_ERR_INVALID, "pointer not 16-byte aligned");
+  if ((T + 127) / 128 > 65535) return fail(DSA_ERR_UNSUPPORTED, "T = %d too large", T);
+  return launched(absorb(q_mha, w_uk, T, H, q_abs, (hipStream_t)stream), "query absorption launch");
+}
+
+dsa_status dsa_mla_unabsorb_o(const void* o_lat, const void* w_kv, int32_t T, int32_t H, void* o, void* stream) {
+  dsa_status s = check_heads(H);
+  if (s) return s;
+  if (T < 0) return fail(DSA_ERR_INVALID, "T = %d < 0", T);
+  if (T == 0) return ok();
+  if (!o_lat || !w_kv || !o) return fail(DSA_ERR_INVALID, "o_lat/w_kv/o is NULL");
+  if (!aligned16(o_lat) || !aligned16(w_kv) || !aligned16(o)) return fail(DSA_ERR_INVALID, "pointer not 16-byte aligned");
+  if ((T + 127) / 128 > 65535) return fail(DSA_ERR_UNSUPPORTED, "T = %d too large", T);
+  return launched(unabsorb(o_lat, w_kv, T, H, o, (hipStream_t)stream), "value up-projection launch");
+}
+
+namespace {
+
+// Arguments both modes share.
+dsa_status check_modes(const void* q_mha, const dsa_pool* kv, const dsa_page_table* pt, const dsa_chunk* chunk,
+                       const int32_t* idx, int64_t ld_idx, int32_t T, int32_t k, int32_t H, float sm_scale,
+                       const void* out) {
+  dsa_status s = check_latent_pool(kv);
+  if (s) return s;
+  if ((s = check_heads(H))) return s;
+  if ((s = check_pt(pt))) return s;
+  if ((s = check_tokens(chunk, T, pt, true))) return s;
+  if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_UNSUPPORTED, "k = %d outside [1, %d]", k, DSA_MAX_K);
+  if (ld_idx < k) return fail(DSA_ERR_INVALID, "ld_idx %lld < k %d", (long long)ld_idx, k);
+  if (!isfinite(sm_scale)) return fail(DSA_ERR_INVALID, "sm_scale is not finite");
+  if (T == 0) return DSA_OK;
+  if (!q_mha || !idx || !out) return fail(DSA_ERR_INVALID, "q/idx/out is NULL");
+  if (!aligned16(q_mha) || !aligned16(out)) return fail(DSA_ERR_INVALID, "q/out not 16-byte aligned");
+  return DSA_OK;
+}
+
+// What MHA mode's kernel needs beyond that (T > 0).
+dsa_status check_mha_only(const void* kv_mha, const dsa_chunk* chunk, int32_t T) {
+  if (!kv_mha) return fail(DSA_ERR_INVALID, "kv_mha is NULL");
+  if (!aligned16(kv_mha)) return fail(DSA_ERR_INVALID, "kv_mha not 16-byte aligned");
+  // a workgroup takes 128 consecutive tokens of one request
+  for (int32_t t = 0; t < T; ++t)
+    if (chunk->q_row_host[t] != chunk->q_row_host[t - t % 128])
+      return fail(DSA_ERR_UNSUPPORTED, "MHA mode: tokens %d and %d of one 128-token tile belong to different "
+                  "requests", t - t % 128, t);
+  const int64_t mx = chunk_max_len(chunk, T);
+  if (mx > 64 * dsa::kMhaMaxWords)
+    return fail(DSA_ERR_UNSUPPORTED, "MHA mode: a token sees %lld positions, more than %d", (long long)mx,
+                64 * dsa::kMhaMaxWords);
+  return DSA_OK;
+}
+
+dsa::MhaArgs mha_args(const void* q_mha, const dsa_pool* kv, const void* kv_mha, const dsa_page_table* pt,
+                      const dsa_chunk* chunk, const int32_t* idx, int64_t ld_idx, int32_t T, int32_t k, int32_t H,
+                      float sm_scale, void* out, float* lse, void* ws) {
+  return dsa::MhaArgs{q_mha, kv_mha, kv->data, kv->num_blocks, pt->block_table, pt->max_blocks, chunk->q_row,
+                      chunk->q_pos, idx, ld_idx, k, T, H, chunk_max_len(chunk, T), sm_scale, out, lse, ws};
+}
+
+}  // namespace
+
+dsa_status dsa_sparse_mla_prefill_mha(const void* q_mha, const dsa_pool* kv, const void* kv_mha,
+                                      const dsa_page_table* pt, const dsa_chunk* chunk, const int32_t* idx,
+                                      int64_t ld_idx, int32_t T, int32_t k, int32_t H, float sm_scale, void* out,
+                                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status s = check_modes(q_mha, kv, pt, chunk, idx, ld_idx, T, k, H, sm_scale, out);
+  if (s) return s;
+  if (T == 0) return ok();
+  if ((s = check_mha_only(kv_mha, chunk, T))) return s;
+  const size_t need = dsa::mha_workspace_bytes(T, chunk_max_len(chunk, T));
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID, "workspace not 16-byte aligned");
+  return launched(dsa::launch_mla_mha(mha_args(q_mha, kv, kv_mha, pt, chunk, idx, ld_idx, T, k, H, sm_scale, out,
+                                               lse, ws), (hipStream_t)stream),
+                  "MHA-mode attention launch");
+}
+
+dsa_status dsa_mla_prefill_heads(const void* q_mha, const void* w_uk, const void* w_kv, const dsa_pool* kv,
+                                 const void* kv_mha, const dsa_page_table* pt, const dsa_chunk* chunk,
+                                 const int32_t* idx, int64_t ld_idx, int32_t T, int32_t k, int32_t H, float sm_scale,
+                                 int64_t mha_max_len, void* out, float* lse, int32_t* mode, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!w_uk || !w_kv) return fail(DSA_ERR_INVALID, "w_uk/w_kv is NULL");
+  if (!aligned16(w_uk) || !aligned16(w_kv)) return fail(DSA_ERR_INVALID, "w_uk/w_kv not 16-byte aligned");
+  if (mha_max_len < 0) return fail(DSA_ERR_INVALID, "mha_max_len %lld < 0", (long long)mha_max_len);
+  dsa_status s = check_modes(q_mha, kv, pt, chunk, idx, ld_idx, T, k, H, sm_scale, out);
+  if (s) return s;
+  if (T == 0) {
+    if (mode) *mode = 0;
+    return ok();
+  }
+  const int64_t mx = chunk_max_len(chunk, T);
+  const bool use_mha = kv_mha && mx <= mha_max_len;
+  if (use_mha) {
+    if ((s = check_mha_only(kv_mha, chunk, T))) return s;
+  } else {
+    if (H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "MQA mode runs H = 64 or 128, got %d", H);
+    if ((T + 127) / 128 > 65535) return fail(DSA_ERR_UNSUPPORTED, "T = %d too large", T);
+  }
+  const size_t need = use_mha ? dsa::mha_workspace_bytes(T, mx) : heads_mqa_bytes(T, k, H);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID, "workspace not 16-byte aligned");
+  if (mode) *mode = use_mha ? 1 : 0;
+  const hipStream_t st = (hipStream_t)stream;
+  if (use_mha)
+    return launched(dsa::launch_mla_mha(mha_args(q_mha, kv, kv_mha, pt, chunk, idx, ld_idx, T, k, H, sm_scale, out,
+                                                 lse, ws), st),
+                    "MHA-mode attention launch");
+  // MQA mode: absorb W_UK into the query, sparse MLA over the latent rows, then W_UV
+  uint8_t* w = (uint8_t*)ws;
+  void* q_abs = w;
+  void* o_lat = w + (size_t)T * H * (kDl + kDr) * 2;
+  void* mla_ws = w + ((size_t)T * H * (kDl + kDr) * 2 + (size_t)T * H * kDl * 2 + 255) / 256 * 256;
+  hipError_t e = absorb(q_mha, w_uk, T, H, q_abs, st);
+  if (e != hipSuccess) return launched(e, "query absorption launch");
+  dsa::MlaArgs a{q_abs, kv->data, kv->num_blocks, pt->block_table, pt->seq_len, pt->max_blocks, pt->batch,
+                 chunk->q_row, chunk->q_pos, idx, ld_idx, T, k, H, kDl, kDr, sm_scale, true, o_lat, lse, mla_ws};
+  e = dsa::launch_mla(a, st);
+  if (e != hipSuccess) return launched(e, "sparse MLA launch");
+  return launched(unabsorb(o_lat, w_kv, T, H, out, st), "value up-projection launch");
+}
+
 dsa_status dsa_index_cache_init(dsa_index_cache* c, int32_t* idx, int64_t ld, int32_t rows, int32_t k,
                                 int32_t group) {
   if (!c || !idx) return fail(DSA_ERR_INVALID, "cache/idx is NULL");
@@ -314,6 +505,11 @@ size_t dsa_workspace_bytes(int32_t op, int32_t rows, int64_t max_len, int32_t k,
   if (rows <= 0 || k <= 0) return 0;
   if (op == DSA_OP_TOPK) return dsa::topk_workspace_bytes(rows, max_len, k);
   if (op == DSA_OP_MLA) return dsa::mla_workspace_bytes(rows, k, H, Dl, true);
+  if (op == DSA_OP_MLA_MHA) return dsa::mha_workspace_bytes(rows, max_len);
+  if (op == DSA_OP_MLA_HEADS) {
+    const size_t a = dsa::mha_workspace_bytes(rows, max_len), b = heads_mqa_bytes(rows, k, H);
+    return a > b ? a : b;
+  }
   return 0;
 }
 

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 21
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -306,3 +306,66 @@ def test_probe_rejects():
     assert L.LIB.dsa_probe_row_gather(FAKE + 8, 10, FAKE, 100, 0, FAKE2, None) == L.DSA_ERR_INVALID
     assert L.LIB.dsa_probe_row_gather(FAKE, 10, FAKE, 100, 2, FAKE2, None) == L.DSA_ERR_INVALID
     assert L.LIB.dsa_probe_row_gather_sink_words(4097) == 3 * 256
+
+
+def _heads_call(fn="mha", **kw):
+    a = dict(q=FAKE, pool=pool(row=576), kv_mha=FAKE2, pt=pt(lens=[200, 255]), chunk=chunk([0, 0], [3, 4]),
+             idx=FAKE, ld_idx=2048, T=2, k=2048, H=64, scale=0.0625, out=FAKE, lse=None, ws=FAKE2, wsb=1 << 40,
+             thr=1 << 20)
+    a.update(kw)
+    pp = ctypes.byref(a["pool"]) if a["pool"] else None
+    tp = ctypes.byref(a["pt"]) if a["pt"] else None
+    cp = ctypes.byref(a["chunk"]) if a["chunk"] else None
+    if fn == "mha":
+        return L.LIB.dsa_sparse_mla_prefill_mha(a["q"], pp, a["kv_mha"], tp, cp, a["idx"], a["ld_idx"], a["T"], a["k"],
+                                                a["H"], a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+    mode = ctypes.c_int32(-1)
+    return L.LIB.dsa_mla_prefill_heads(a["q"], FAKE, FAKE2, pp, a["kv_mha"], tp, cp, a["idx"], a["ld_idx"], a["T"],
+                                       a["k"], a["H"], a["scale"], a["thr"], a["out"], a["lse"], ctypes.byref(mode),
+                                       a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("fn", ["mha", "heads"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), L.DSA_ERR_INVALID),
+    (dict(pool=pool(L.DSA_F32, row=576)), L.DSA_ERR_UNSUPPORTED),      # bf16 only
+    (dict(pool=pool(row=512)), L.DSA_ERR_INVALID),                     # latent rows are 512 + 64
+    (dict(H=0), L.DSA_ERR_UNSUPPORTED),
+    (dict(H=129), L.DSA_ERR_UNSUPPORTED),
+    (dict(chunk=chunk([0, 1], [3, 255])), L.DSA_ERR_INVALID),          # q_pos beyond its request
+    (dict(k=4096, ld_idx=4096), L.DSA_ERR_UNSUPPORTED),
+    (dict(ws=None), L.DSA_ERR_WORKSPACE),
+    (dict(out=FAKE + 2), L.DSA_ERR_INVALID),
+    (dict(pt=pt(seq_len_host=False)), L.DSA_ERR_INVALID),
+])
+def test_mla_modes_reject(fn, kw, status):
+    assert _heads_call(fn, **kw) == status
+
+
+def test_mha_mode_limits():
+    # a 128-token tile mixing two requests, and a token seeing more than 65536 positions
+    mixed = chunk([0] * 100 + [1] * 100, [5] * 200)
+    assert _heads_call("mha", T=200, chunk=mixed) == L.DSA_ERR_UNSUPPORTED
+    big = pt(max_blocks=2048, lens=[70000, 10])
+    assert _heads_call("mha", pt=big, chunk=chunk([0, 1], [69999, 3])) == L.DSA_ERR_UNSUPPORTED
+    assert _heads_call("mha", kv_mha=None) == L.DSA_ERR_INVALID
+    # the switch takes MQA mode there instead: H = 32 is not an MQA-mode instance
+    assert _heads_call("heads", H=32, thr=0) == L.DSA_ERR_UNSUPPORTED
+    assert _heads_call("heads", T=200, chunk=mixed, thr=0, H=32) == L.DSA_ERR_UNSUPPORTED
+
+
+def test_projection_rejects():
+    lib = L.LIB
+    assert lib.dsa_mla_up_project(ctypes.byref(pool(L.DSA_F32, row=576)), FAKE, 64, FAKE2, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_mla_up_project(ctypes.byref(pool(row=576)), None, 64, FAKE2, None) == L.DSA_ERR_INVALID
+    assert lib.dsa_mla_up_project(ctypes.byref(pool(row=576)), FAKE, 0, FAKE2, None) == L.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_mla_absorb_q(FAKE, FAKE2, -1, 64, FAKE, None) == L.DSA_ERR_INVALID
+    assert lib.dsa_mla_absorb_q(FAKE, None, 4, 64, FAKE, None) == L.DSA_ERR_INVALID
+    assert lib.dsa_mla_absorb_q(None, None, 0, 64, None, None) == L.DSA_OK      # empty: nothing enqueued
+    assert lib.dsa_mla_unabsorb_o(FAKE + 2, FAKE2, 4, 64, FAKE, None) == L.DSA_ERR_INVALID
+    assert lib.dsa_mla_unabsorb_o(FAKE, FAKE2, 4, 200, FAKE, None) == L.DSA_ERR_UNSUPPORTED
+    # workspace sizes: one 64-bit mask word per token and 64 positions; MQA mode's q_abs and
+    # latent output
+    assert lib.dsa_workspace_bytes(L.DSA_OP_MLA_MHA, 2048, 5120, 2048, 64, 512) == 2048 * 80 * 8
+    mqa = 2048 * 64 * 576 * 2 + 2048 * 64 * 512 * 2
+    assert lib.dsa_workspace_bytes(L.DSA_OP_MLA_HEADS, 2048, 5120, 2048, 64, 512) == mqa
