@@ -17,6 +17,8 @@ dsa_timing_start/collect) and the CPU oracle timed on a bounded sample of the sa
 workload's tokens.
 
 Two helper modes turn rocprofv3 output into the text summaries kept under profiles/:
+    --mla-modes                 MLA's MQA mode against its MHA mode on a 2048-token prefill
+                                chunk at context lengths 2.3K .. 16K
     --gather-ceiling            random 1152-byte row gathers with the sparse MLA's loads
                                 from pools in L2, Infinity Cache and HBM (--steps launches)
     --copy-calibration MIB      only copies MIB MiB device-to-device (--steps times),
@@ -398,6 +400,92 @@ def run_gather_ceiling(args):
     print(json.dumps(res), flush=True)
 
 
+# MLA's two modes on a prefill chunk: context lengths swept, chunk length
+MODE_CONTEXTS = [2304, 3072, 4096, 5120, 6144, 8192, 12288, 16384]
+MODE_CHUNK = 2048
+
+
+def mla_mode_ratios(H=64, dl=512, dr=64, dn=192, dv=128):
+    """Per token and head: MHA mode's cache bytes against the latent row's, and MQA mode's
+    FLOPs per (query, key) pair against MHA mode's (bf16)."""
+    latent = (dl + dr) * 2
+    return {"mha_cache_bytes_per_position": H * (dn + dv) * 2 + dr * 2,
+            "mha_bytes_with_rope_per_head": H * (dn + dr + dv) * 2,
+            "latent_bytes_per_position": latent,
+            "memory_ratio": H * (dn + dv) * 2 / latent + dr * 2 / latent,
+            "memory_ratio_rope_per_head": H * (dn + dr + dv) * 2 / latent,
+            "mqa_flop_per_pair": 2 * (dl + dr) + 2 * dl, "mha_flop_per_pair": 2 * (dn + dr) + 2 * dv,
+            "flop_ratio": (2 * (dl + dr) + 2 * dl) / (2 * (dn + dr) + 2 * dv),
+            "flop_ratio_deepseek_dims": (2 * (dl + dr) + 2 * dl) / (2 * (128 + dr) + 2 * 128)}
+
+
+def run_mla_modes(args, emit=True):
+    """Both modes of MLA on a MODE_CHUNK-token prefill chunk at the end of each context
+    length: MQA mode (query absorption, sparse MLA over the latent rows, value
+    up-projection) against MHA mode (selection mask, masked dense attention over the per-head
+    up-projected keys and values); the up-projection of the context into the MHA cache is
+    timed on its own.  Kernel times from HIP events in each dispatch."""
+    import torch
+    import dsa_inputs as I
+    import sparse_attention_19_amd as D
+    from sparse_attention_19_amd import pipeline as P
+    dev = torch.device("cuda:0")
+    T, H, k = MODE_CHUNK, 64, 2048
+    reps = max(3, min(args.steps, 10))
+    rows = []
+    for n in MODE_CONTEXTS:
+        cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], seed=31, ctx=n, prefill_tokens=T, mha=True,
+                       sm_scale=1.0 / 16)
+        inp = I.make_inputs(cfg, dev)
+        pt, ch = P.page_table(inp), P.chunk(inp)
+        ld = inp["block_table"].shape[1] * 64
+        scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        D.dsa_indexer_scores(inp["q_idx"], inp["w"], inp["k_pool"], pt, scores, chunk=ch)
+        D.dsa_topk(scores, ch.q_pos, ch.q_pos_host, k, idx, n_add=1, ws=D.workspace(D.DSA_OP_TOPK, T, ld, k, 0, 0, dev))
+        pool = inp["kv_pools"][0]
+        kv_mha = torch.empty((pool.shape[0] * 64, H, 320), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = D.workspace(D.DSA_OP_MLA_HEADS, T, n, k, H, 512, dev)
+        timed = {}
+        for label, fn in (("up_project", lambda: D.dsa_mla_up_project(pool, inp["w_kv"], kv_mha)),
+                          ("mha", lambda: D.dsa_mla_prefill_heads(inp["q_mha"], inp["w_uk"], inp["w_kv"], pool, kv_mha,
+                                                                  pt, ch, idx, k, 1.0 / 16, 1 << 20, out, lse, ws=ws)),
+                          ("mqa", lambda: D.dsa_mla_prefill_heads(inp["q_mha"], inp["w_uk"], inp["w_kv"], pool, kv_mha,
+                                                                  pt, ch, idx, k, 1.0 / 16, 0, out, lse, ws=ws))):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            D.dsa_timing_start(reps * 8)
+            for _ in range(reps):
+                fn()
+            launches = D.dsa_timing_collect()
+            per = {}
+            for name, t in launches:
+                per[name] = per.get(name, 0.0) + t / reps
+            timed[label] = per
+        row = {"context": n, "chunk_tokens": T,
+               "mqa_ms": round(sum(timed["mqa"].values()), 4), "mha_ms": round(sum(timed["mha"].values()), 4),
+               "up_project_ms": round(sum(timed["up_project"].values()), 4),
+               "mqa_kernels_ms": {a: round(b, 4) for a, b in timed["mqa"].items()},
+               "mha_kernels_ms": {a: round(b, 4) for a, b in timed["mha"].items()}}
+        rows.append(row)
+        if emit:
+            print(f"[modes] n={n}: MQA {row['mqa_ms']:.3f} ms, MHA {row['mha_ms']:.3f} ms "
+                  f"(+ up-projection of the context {row['up_project_ms']:.3f} ms)", flush=True)
+        del inp, scores, idx, kv_mha, out, lse, ws
+        torch.cuda.empty_cache()
+    cross = next((r["context"] for r in rows if r["mha_ms"] >= r["mqa_ms"]), None)
+    cross_p = next((r["context"] for r in rows if r["mha_ms"] + r["up_project_ms"] >= r["mqa_ms"]), None)
+    res = {"metric": "MLA mode time per prefill chunk (MQA vs MHA)", "unit": "ms", "rows": rows,
+           "first_context_where_mqa_wins": cross, "same_counting_the_context_up_projection": cross_p,
+           "ratios": mla_mode_ratios()}
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
+
+
 # workloads of the report: (config name, overrides, what it is)
 REPORT_WORKLOADS = [
     ("tiny_fp32", {}, "1 token, L = 256, fp32 (parity case)"),
@@ -668,6 +756,8 @@ def main():
     ap.add_argument("--no-index-share", action="store_true",
                     help="every layer runs its own indexer and top-k (the plain-DSA comparison)")
     ap.add_argument("--report", action="store_true", help="every workload; writes REPORT.md")
+    ap.add_argument("--mla-modes", action="store_true",
+                    help="MLA's MQA and MHA modes on a prefill chunk across context lengths")
     ap.add_argument("--gather-ceiling", action="store_true",
                     help="random-row gather bandwidth per pool size (L2, Infinity Cache, HBM)")
     ap.add_argument("--report-cpu-budget", type=float, default=8.0, help="oracle seconds per workload")
@@ -707,6 +797,8 @@ def main():
         return run_report(args)
     if args.gather_ceiling:
         return run_gather_ceiling(args)
+    if args.mla_modes:
+        return run_mla_modes(args)
     run_bench(args)
 
 

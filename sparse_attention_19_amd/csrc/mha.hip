@@ -17,9 +17,10 @@
 // ceil(len / 64) 64-bit words (word w, bit b: position 64w + b).
 // mla_mha_kernel: one workgroup per (128 tokens of one request, head); 4 waves of 32 tokens
 // (two 16-row tiles on 16x16x32 MFMAs); per 64-key tile, K [64][256] and V [64][128] are
-// staged in LDS (the next tile's loads in flight in registers), S = Q K^T, mask, online
-// softmax (running max with rescale), P through LDS, O += P V with V fragments read
-// transposed (ds_read_b64_tr_b16).
+// staged in LDS (the next tile's loads and mask words in flight in registers), S = Q K^T
+// with the next k-step's K fragments read ahead, mask, online softmax (row reductions on
+// DPP; O rescaled only when a row's max moves), P through LDS transposed, O += P V with the
+// P and V fragments read transposed (ds_read_b64_tr_b16).
 #include <math.h>
 
 #include "common.h"
@@ -35,7 +36,7 @@ constexpr int kKeys = 64;            // keys per tile (one page)
 constexpr int kThreads = 256;
 constexpr int kKRow = kDqk + 8;      // LDS K row, elements (528 bytes)
 constexpr int kVRow = kDv + 8;       // LDS V row, elements (272 bytes)
-constexpr int kPRow = kKeys + 8;     // LDS P row, elements (144 bytes)
+constexpr int kPtRow = 32 + 8;       // LDS row of P transposed (a key's 32 tokens), elements (80 bytes)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -64,29 +65,47 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int* __restrict__ i
 
 // One key tile in registers: K chunks (16 B) id = tid + 256 i, i < 8: key id / 32, chunk
 // id % 32 (chunks < 24 from the up-projected NoPE keys, the rest from the latent row's rope
-// dims); V chunks id = tid + 256 i, i < 4: key id / 16, chunk id % 16.
+// dims); V chunks id = tid + 256 i, i < 4: key id / 16, chunk id % 16; and the selection
+// mask words of this lane's 8 token rows for the tile.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+typedef const __attribute__((address_space(1))) u32x4* gu32x4;
+
 struct MhaTile {
   u32x4 k[8], v[4];
+  uint64_t mw[2][4];
+  int last;   // the tile's last key any token sees (-1: none)
 };
 
-__device__ __forceinline__ void load_mha_tile(MhaTile& r, const uint16_t* kv, const uint16_t* lat, int64_t row0,
-                                              bool ok, int H, int h) {
-  const int tid = threadIdx.x;
+// A whole tile is one page: a block-table entry outside the pool reads the pool's first
+// page, and its mask words are cleared so none of its keys takes part.
+__device__ __forceinline__ void load_mha_tile(MhaTile& r, gbytes kv, gbytes lat, int64_t row0, bool ok, int H, int h,
+                                              const uint64_t* mask, int words, int kt, int t0, int T, int last_pos) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = (lane >> 4) & 3;
+  r.last = ok ? min(last_pos - kKeys * kt, kKeys - 1) : -1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int id = tid + kThreads * i, key = id >> 5, c = id & 31;
     const int64_t row = row0 + key;
-    const uint16_t* src = c < 24 ? kv + (row * H + h) * kDkv + 8 * c : lat + row * (kDl + kDr) + kDl + 8 * (c - 24);
-    r.k[i] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+    const gbytes src = c < 24 ? kv + ((row * H + h) * kDkv + 8 * c) * 2 : lat + (row * (kDl + kDr) + kDl + 8 * (c - 24)) * 2;
+    r.k[i] = *(gu32x4)src;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int id = tid + kThreads * i, key = id >> 4, c = id & 15;
-    const uint16_t* src = kv + ((row0 + key) * H + h) * kDkv + kDn + 8 * c;
-    r.v[i] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+    r.v[i] = *(gu32x4)(kv + (((row0 + key) * H + h) * kDkv + kDn + 8 * c) * 2);
   }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 32 * wave + 16 * rt + 4 * g + i;
+      r.mw[rt][i] = (ok && t < T) ? mask[(int64_t)t * words + kt] : 0ull;
+    }
 }
 
+// Value rows past the last key any token sees are stored as zeros: the unused tail of a
+// request's last page holds whatever the cache left there, and P = 0 times a NaN there would
+// still be NaN.  (Keys need no such care: masked logits are replaced, not multiplied.)
 __device__ __forceinline__ void store_mha_tile(const MhaTile& r, uint16_t (*Ks)[kKRow], uint16_t (*Vs)[kVRow]) {
   const int tid = threadIdx.x;
 #pragma unroll
@@ -97,9 +116,26 @@ __device__ __forceinline__ void store_mha_tile(const MhaTile& r, uint16_t (*Ks)[
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int id = tid + kThreads * i;
-    *reinterpret_cast<u32x4*>(&Vs[id >> 4][8 * (id & 15)]) = r.v[i];
+    *reinterpret_cast<u32x4*>(&Vs[id >> 4][8 * (id & 15)]) = (id >> 4) <= r.last ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
   }
 }
+
+// Max / sum over the 16 lanes of a row (lanes with the same lane / 16), in every lane: DPP
+// row rotations, no LDS.
+#define DSA_ROR(v, n) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + (n), 0xf, 0xf, false))
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, DSA_ROR(v, 1));
+  v = fmaxf(v, DSA_ROR(v, 2));
+  v = fmaxf(v, DSA_ROR(v, 4));
+  return fmaxf(v, DSA_ROR(v, 8));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += DSA_ROR(v, 1);
+  v += DSA_ROR(v, 2);
+  v += DSA_ROR(v, 4);
+  return v + DSA_ROR(v, 8);
+}
+#undef DSA_ROR
 
 // grid (heads, token tiles) in XCD order: workgroup L runs on XCD L % 8, which takes heads
 // L % 8 (mod 8), each with all its token tiles in a row, so the tiles running together on
@@ -111,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeys][kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kKeys][kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][32][kPRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[4][kKeys][kPtRow];   // per wave: P transposed [key][token]
   __shared__ int s_pos;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int L = blockIdx.x, x = L & 7, j = L >> 3;
@@ -126,6 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   __syncthreads();
   const int ntiles = min(s_pos / kKeys + 1, words);
   const int* bt_row = block_table + (int64_t)b * max_blocks;
+  const gbytes kvg = (gbytes)kv, latg = (gbytes)lat;
 
   // Q fragments: tile rt = 0, 1 of the wave's 32 tokens, k-step s: token 32 wave + 16 rt +
   // c16, dims 32 s + 8 g .. +7
@@ -158,77 +195,99 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   MhaTile r;
   bool ok;
   int64_t row0 = tile_row0(0, ok);
-  load_mha_tile(r, kv, lat, row0, ok, H, h);
+  load_mha_tile(r, kvg, latg, row0, ok, H, h, mask, words, 0, t0, T, s_pos);
   for (int kt = 0; kt < ntiles; ++kt) {
     store_mha_tile(r, Ks, Vs);
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      row0 = tile_row0(kt + 1, ok);
-      load_mha_tile(r, kv, lat, row0, ok, H, h);
-    }
-    // mask words of this lane's 8 token rows
     uint64_t mw[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 32 * wave + 16 * rt + 4 * g + i;
-        mw[rt][i] = t < T ? mask[(int64_t)t * words + kt] : 0ull;
-      }
-    // S = Q K^T: [token][key], key n-tile nt = keys 16 nt .. +15
+      for (int i = 0; i < 4; ++i) mw[rt][i] = r.mw[rt][i];
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      row0 = tile_row0(kt + 1, ok);
+      load_mha_tile(r, kvg, latg, row0, ok, H, h, mask, words, kt + 1, t0, T, s_pos);
+    }
+    // S = Q K^T: [token][key], key n-tile nt = keys 16 nt .. +15; the K fragments of the
+    // next k-step are read while this one's MFMAs run
     f32x4 sacc[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) sacc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 kf[2][4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int nt = 0; nt < 4; ++nt) kf[0][nt] = *reinterpret_cast<const bf16x8*>(&Ks[16 * nt + c16][8 * g]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          kf[(s + 1) & 1][nt] = *reinterpret_cast<const bf16x8*>(&Ks[16 * nt + c16][32 * (s + 1) + 8 * g]);
+      }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[16 * nt + c16][32 * s + 8 * g]);
-        sacc[0][nt] = mfma16(qf[0][s], kf, sacc[0][nt]);
-        sacc[1][nt] = mfma16(qf[1][s], kf, sacc[1][nt]);
+        sacc[0][nt] = mfma16(qf[0][s], kf[s & 1][nt], sacc[0][nt]);
+        sacc[1][nt] = mfma16(qf[1][s], kf[s & 1][nt], sacc[1][nt]);
       }
-    // online softmax per token row (log2 units), P to LDS
+    }
+    // online softmax per token row (log2 units); P to LDS transposed, 4 token rows per 8-byte
+    // store.  O is rescaled only when some row's max moved (wave-uniform test).
+    float alpha[2][4];
+    bool moved = false;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float xs[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const bool in = (mw[rt][i] >> (16 * nt + c16)) & 1ull;
-          xs[nt] = in ? sacc[rt][nt][i] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, xs[nt]);
+          sacc[rt][nt][i] = in ? sacc[rt][nt][i] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sacc[rt][nt][i]);
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+        mx = row16_max(mx);
         const float mn = fmaxf(m[rt][i], mx);
-        const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[rt][i] - mn);
+        alpha[rt][i] = (mn == -INFINITY) ? 1.f : exp2f(m[rt][i] - mn);
+        moved |= alpha[rt][i] != 1.f;
         float ps = 0.f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const float p = (mn == -INFINITY) ? 0.f : exp2f(xs[nt] - mn);
+          const float p = (mn == -INFINITY) ? 0.f : exp2f(sacc[rt][nt][i] - mn);
+          sacc[rt][nt][i] = p;
           ps += p;
-          Ps[wave][16 * rt + 4 * g + i][16 * nt + c16] = f2bf_bits(p);
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off, kWave);
-        l[rt][i] = l[rt][i] * alpha + ps;
+        l[rt][i] = l[rt][i] * alpha[rt][i] + row16_sum(ps);
         m[rt][i] = mn;
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt) o[rt][vt][i] *= alpha;
       }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t lo = (uint32_t)f2bf_bits(sacc[rt][nt][0]) | ((uint32_t)f2bf_bits(sacc[rt][nt][1]) << 16);
+        const uint32_t hi = (uint32_t)f2bf_bits(sacc[rt][nt][2]) | ((uint32_t)f2bf_bits(sacc[rt][nt][3]) << 16);
+        *reinterpret_cast<uint2*>(&Pt[wave][16 * nt + c16][16 * rt + 4 * g]) = make_uint2(lo, hi);
+      }
+    }
+    if (__ballot(moved) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[rt][vt][i] *= alpha[rt][i];
+    }
     wave_lds_fence();
-    // O += P V: P fragments (token 16 rt + c16, keys 32 s2 + 8 g .. +7), V fragments by
-    // transposing reads (v dims 16 vt + c16, the same keys)
+    // O += P V: P fragments (token 16 rt + c16, keys 32 s2 + 8 g .. +7) and V fragments (v dims
+    // 16 vt + c16, the same keys), both by transposing reads
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       bf16x8 pa[2];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        pa[rt] = *reinterpret_cast<const bf16x8*>(&Ps[wave][16 * rt + c16][32 * s2 + 8 * g]);
+      for (int rt = 0; rt < 2; ++rt) {
+        const s16x4 lo = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + (c16 >> 2)][16 * rt + 4 * (c16 & 3)]);
+        const s16x4 hi = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + 4 + (c16 >> 2)][16 * rt + 4 * (c16 & 3)]);
+        const short __attribute__((ext_vector_type(8))) p8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        pa[rt] = __builtin_bit_cast(bf16x8, p8);
+      }
 #pragma unroll
       for (int vt = 0; vt < 8; ++vt) {
         const s16x4 lo = lds_read_tr16(&Vs[32 * s2 + 8 * g + (c16 >> 2)][16 * vt + 4 * (c16 & 3)]);

@@ -75,10 +75,21 @@ def check(inp, out, lse, tokens, heads, idx=None):
         assert d <= 2e-3, f"token {t}: lse diff {d:.3g}"
 
 
+def poison_page_tails(inp, value=float("nan")):
+    """Fill the unused slots of each request's last page (positions >= its length) of the
+    latent pool with a non-finite value: a cache leaves them unwritten."""
+    pool = inp["kv_pools"][0]
+    for b, n in enumerate(inp["seq_len_host"].tolist()):
+        if n % 64:
+            phys = int(inp["block_table"][b, n // 64])
+            pool[phys, n % 64:] = value
+
+
 def test_mha_mode_against_oracle():
     # tokens on both sides of k (dense up to position 2047), three 128-token tiles, the last
-    # one partial
+    # one partial; NaN in the unused tail of the request's last page
     inp = mha_inputs(ctx=2400, T=330)
+    poison_page_tails(inp)
     T, H = 330, 64
     pt, ch, idx = select(inp)
     kv_mha = up_projected(inp)
@@ -87,6 +98,7 @@ def test_mha_mode_against_oracle():
     ws = D.workspace(D.DSA_OP_MLA_MHA, T, 2400, 2048, H, 512, DEV)
     D.dsa_sparse_mla_prefill_mha(inp["q_mha"], inp["kv_pools"][0], kv_mha, pt, ch, idx, 2048, 1.0 / 16, out, lse, ws=ws)
     torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     log("[gpu] MHA mode: every token on heads 0 and 63")
     check(inp, out, lse, range(T), [0, 63], idx)
     log("[gpu] MHA mode: all heads of a few tokens")
