@@ -53,3 +53,13 @@ def test_indexshare_indexer_cut():
     assert shared["mla"] == pytest.approx(cfg.layers * single["mla"])
     cut = 1.0 - shared["indexer"] / (cfg.layers * single["indexer"])
     assert cut == pytest.approx(expected)
+
+
+def test_mla_mode_ratios():
+    params, expected = FIG["mha_memory_ratio"]
+    H, dn, dr, dv, d = (int(params[x]) for x in ("H", "dn", "dr", "dv", "d"))
+    r = bench.mla_mode_ratios(H=H, dl=d, dr=dr, dn=dn, dv=dv)
+    assert math.floor(r["memory_ratio_rope_per_head"]) == expected
+    params, expected = FIG["mqa_flop_ratio_max"]
+    r = bench.mla_mode_ratios(dn=int(params["dn"]), dr=int(params["dr"]), dv=int(params["dv"]), dl=int(params["d"]))
+    assert round(r["flop_ratio"], 1) == pytest.approx(expected)
