@@ -372,3 +372,55 @@ def check_mha(impl, seed=5):
 
 
 ALL_CHECKS += [check_mha]
+
+
+# ------------------------------------------------------------------ MHA-mode composition used by the GPU tests
+
+def mha_composition_inputs():
+    """Tiny CPU prefill chunks drawn with MHA-mode inputs (2 heads of 192 + 64 query-key and
+    128 value dims over 512 + 64 latent rows): one whose tokens select 64 of ~300 positions,
+    one whose tokens see fewer positions than k (dense)."""
+    import torch
+    import dsa_inputs as I
+    base = I.shrink(I.CONFIGS["prefill_4096_at_128k"], ctx=300, prefill_tokens=5, Hi=4, Di=32, idx_range=3,
+                    w_max=2, H=2, identity_pages=False, mha=True, sm_scale=1.0 / 16)
+    return [I.make_inputs(I.shrink(base, k=64)), I.make_inputs(I.shrink(base, seed=13, k=512))]
+
+
+def check_mha_composition(impl=None, inputs=None):
+    """oracle/run.py's expected_token_mha against a from-scratch composition on every token:
+    the selection of _brute_token, then per head the up-projected keys [latent . w_uk[h],
+    rope] and values latent . w_uv[h] of each selected row (row by row), Python-float
+    logits with the query's first 192 dims on the NoPE part and last 64 on the rope part, and
+    a Python softmax."""
+    from oracle import run as R
+    for inp in (inputs or mha_composition_inputs()):
+        cfg = inp["cfg"]
+        wuk = inp["w_uk"].float().double().numpy()
+        wuv = inp["w_uv"].float().double().numpy()
+        pool = inp["kv_pools"][0].float()
+        for t in range(inp["q_idx"].shape[0]):
+            got = R.expected_token_mha(inp, t)
+            _, idx, _ = _brute_token(inp, t, [])
+            assert got["idx"].tolist() == idx, (cfg.name, t)
+            sel = [s for s in idx if s >= 0]
+            bt = inp["block_table"][int(inp["q_row"][t])].tolist()
+            rows = [pool[bt[s // 64], s % 64].double().numpy() for s in sel]
+            q = inp["q_mha"][t].float().double().tolist()
+            for h in range(cfg.H):
+                lg, vs = [], []
+                for r in rows:
+                    lat, rope = r[:cfg.Dl], r[cfg.Dl:]
+                    key = [float(lat @ wuk[h][:, j]) for j in range(wuk.shape[2])] + [float(x) for x in rope]
+                    vs.append([float(lat @ wuv[h][:, j]) for j in range(wuv.shape[2])])
+                    lg.append(cfg.sm_scale * sum(a * b for a, b in zip(q[h], key)))
+                m = max(lg)
+                e = [math.exp(x - m) for x in lg]
+                z = sum(e)
+                want = [sum(e[i] * vs[i][j] for i in range(len(e))) / z for j in range(len(vs[0]))]
+                assert np.allclose(got["out"][h], want, rtol=1e-10, atol=1e-10), (cfg.name, t, h)
+                assert abs(got["lse"][h] - (m + math.log(z))) < 1e-10, (cfg.name, t, h)
+
+
+ALL_CHECKS += [check_mha_composition]
+

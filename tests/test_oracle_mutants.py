@@ -195,3 +195,51 @@ def test_mutant_is_caught(name):
     setattr(impl, attr, fn)
     with pytest.raises(AssertionError):
         check(impl)
+
+
+# ---- MHA-mode composition (oracle/run.py expected_token_mha): mistakes planted in copies of it
+
+def _mha_token(inp, t, visible=None, swap_q=False, unfiltered=False, values_from_keys=False):
+    from oracle import run as R
+    cfg = inp["cfg"]
+    b = int(inp["q_row"][t])
+    n = (visible or O.visible_count)(int(inp["q_pos"][t]))
+    bt = inp["block_table"][b].cpu().numpy()
+    scores = O.indexer_scores(R.to_f64(inp["q_idx"][t]), R.to_f64(inp["w"][t]), R.request_rows(inp["k_pool"], bt, n))
+    idx = O.topk_positions(scores, n, cfg.k)
+    rows = R.selected_rows(inp["kv_pools"][0], bt, idx if unfiltered else idx[idx >= 0])
+    q = R.to_f64(inp["q_mha"][t])
+    dn = inp["w_uk"].shape[2]
+    qn, qr = (q[:, q.shape[1] - dn:], q[:, :q.shape[1] - dn]) if swap_q else (q[:, :dn], q[:, dn:])
+    wuv = R.to_f64(inp["w_uk"])[:, :, :inp["w_uv"].shape[2]] if values_from_keys else R.to_f64(inp["w_uv"])
+    out, lse = O.mla_mha(qn, qr, rows[:, :cfg.Dl], rows[:, cfg.Dl:], R.to_f64(inp["w_uk"]), wuv, cfg.sm_scale)
+    return dict(out=out, lse=lse, idx=idx, n=n)
+
+
+MHA_COMPOSITION_MUTANTS = {
+    "mha_token_sees_before_own": lambda inp, t: _mha_token(inp, t, visible=_sees_before_own),
+    "mha_token_query_halves_swapped": lambda inp, t: _mha_token(inp, t, swap_q=True),
+    "mha_token_padding_rows_attended": lambda inp, t: _mha_token(inp, t, unfiltered=True),
+    "mha_token_values_from_key_weights": lambda inp, t: _mha_token(inp, t, values_from_keys=True),
+}
+
+
+@pytest.fixture(scope="module")
+def mha_inputs():
+    return P.mha_composition_inputs()
+
+
+@pytest.mark.parametrize("name", sorted(MHA_COMPOSITION_MUTANTS))
+def test_mha_composition_mutant_is_caught(name, mha_inputs, monkeypatch):
+    from oracle import run as R
+    monkeypatch.setattr(R, "expected_token_mha", MHA_COMPOSITION_MUTANTS[name])
+    with pytest.raises(AssertionError):
+        P.check_mha_composition(inputs=mha_inputs)
+
+
+def test_mha_composition_copy_passes(mha_inputs, monkeypatch):
+    """The unmutated copy passes, so each failure above comes from its planted mistake."""
+    from oracle import run as R
+    monkeypatch.setattr(R, "expected_token_mha", _mha_token)
+    P.check_mha_composition(inputs=mha_inputs)
+
