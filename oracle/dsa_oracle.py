@@ -17,6 +17,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * absorbed (MQA-mode) MLA: logits use all Dl+Dr dims of the latent row, the value is
     the first Dl (latent) dims
   * -0.0 scores are canonicalised to +0.0
+  * the HBM working set's "least recently used" over a step's selected set: hits stay,
+    misses take free slots first, then the least recently used unselected entries, in
+    ascending position order; the step's positions become the most recent, ascending
 
 Pinning status (tests/test_oracle_pins.py, tests/test_oracle_mutants.py): every function
 below, and the composition in oracle/run.py that the GPU tests compare against, is pinned
@@ -188,3 +191,49 @@ def decode_token(q_idx, w, key_rows, q, kv_rows, n, k, Dl, sm_scale):
     scores, idx, [(out, lse)] = group_token(q_idx, w, key_rows, n, k, [(q, lambda pos: kv_rows[pos])],
                                             Dl, sm_scale)
     return scores, idx, out, lse
+
+
+# --------------------------------------------------------------------------- HBM working set
+
+def working_set_init(slots: int) -> dict:
+    """An empty device working set of `slots` latent rows for one request (remio.ai,
+    "GLM-5.3のスパースアテンションは計算量を削減するが、HBM需要は残る", section HiSparse:
+    a small working set of KV entries stays on the GPU, the whole history sits in pinned
+    host memory).  State: pos_of[slot] = the position the slot holds (-1: free); order = the
+    slots from least to most recently used (free slots first, by index); slot_of = position
+    -> slot for the resident positions."""
+    return {"pos_of": [-1] * slots, "order": list(range(slots)), "slot_of": {}}
+
+
+def working_set_step(state: dict, sel) -> tuple:
+    """One decode step of the working set for a request's selection `sel` (its selected
+    positions, ascending; same section: a selected position not on the device is loaded
+    from host memory, and least-recently-used entries are evicted to keep the working set
+    bounded).
+
+    Reading of "least recently used" for a set of positions used together: the selected
+    positions already resident are hits and are not evicted; each miss takes, in ascending
+    position order, the next slot of the recency order that holds no hit (free slots first,
+    then the least recently used entries); afterwards this step's positions are the most
+    recent, in ascending position order.
+
+    Returns (slots, loads, evicted): the slot of each selected position (in sel's order),
+    the (position, slot) pairs to load from host memory, and the positions evicted."""
+    pos_of, order, slot_of = state["pos_of"], state["order"], state["slot_of"]
+    sel = [int(p) for p in sel]
+    hit_slots = {slot_of[p] for p in sel if p in slot_of}
+    misses = [p for p in sel if p not in slot_of]
+    candidates = [s for s in order if s not in hit_slots]
+    if len(misses) > len(candidates):
+        raise ValueError("the working set holds fewer slots than the selection")
+    loads, evicted = [], []
+    for p, s in zip(misses, candidates):
+        if pos_of[s] >= 0:
+            evicted.append(pos_of[s])
+            del slot_of[pos_of[s]]
+        pos_of[s] = p
+        slot_of[p] = s
+        loads.append((p, s))
+    slots = [slot_of[p] for p in sel]
+    state["order"] = candidates[len(misses):] + slots
+    return slots, loads, evicted

@@ -22,7 +22,8 @@ def real_impl():
                                  mla_absorbed=O.mla_absorbed, logical_rows=O.logical_rows,
                                  decode_token=O.decode_token, bf16_bits_to_f64=O.bf16_bits_to_f64,
                                  visible_count=O.visible_count, group_token=O.group_token,
-                                 mla_mha=O.mla_mha)
+                                 mla_mha=O.mla_mha, working_set_init=O.working_set_init,
+                                 working_set_step=O.working_set_step)
 
 
 # ------------------------------------------------------------------ indexer
@@ -424,3 +425,114 @@ def check_mha_composition(impl=None, inputs=None):
 
 ALL_CHECKS += [check_mha_composition]
 
+
+
+# ------------------------------------------------------------------ HBM working set (LRU)
+
+def _brute_lru(S, steps):
+    """The working set from its plain definition: every slot carries the time it was last
+    used, (step, rank of its position in that step's ascending selection), a free slot
+    (-1, slot index); a step's misses, in ascending position order, take the non-hit slots
+    with the oldest times.  Yields (slots, loads, evicted, order) per step."""
+    last = {s: (-1, s) for s in range(S)}
+    holds = {}                       # slot -> position
+    where = {}                       # position -> slot
+    for t, sel in enumerate(steps):
+        hits = {where[p] for p in sel if p in where}
+        misses = [p for p in sel if p not in where]
+        free = sorted((s for s in range(S) if s not in hits), key=lambda s: last[s])
+        if len(misses) > len(free):
+            raise ValueError("too small")
+        loads, evicted = [], []
+        for p, s in zip(misses, free):
+            if s in holds:
+                evicted.append(holds[s])
+                del where[holds[s]]
+            holds[s] = p
+            where[p] = s
+            loads.append((p, s))
+        for r, p in enumerate(sel):
+            last[where[p]] = (t, r)
+        yield [where[p] for p in sel], loads, evicted, sorted(range(S), key=lambda s: last[s])
+
+
+def _lru_sequences(rng):
+    """Selection sequences over a small universe with a drift between steps (some positions
+    kept, some new), including repeats, empty steps and full-size selections."""
+    cases = []
+    for S, size, universe, steps in [(4, 3, 9, 12), (7, 7, 20, 10), (64, 40, 300, 15), (16, 5, 16, 20)]:
+        seq, prev = [], []
+        for _ in range(steps):
+            n = int(rng.integers(0, size + 1))
+            keep = [p for p in prev if rng.random() < 0.6][:n]
+            new = [int(p) for p in rng.permutation(universe)[:n] if p not in keep][:n - len(keep)]
+            cur = sorted(set(keep + new))
+            seq.append(cur)
+            prev = cur
+        seq.append(list(seq[-1]))            # the same selection twice
+        cases.append((S, seq))
+    return cases
+
+
+def check_working_set(impl, seed=7):
+    rng = np.random.default_rng(seed)
+    for S, seq in _lru_sequences(rng):
+        st = impl.working_set_init(S)
+        for sel, (b_slots, b_loads, b_evicted, b_order) in zip(seq, _brute_lru(S, seq)):
+            before = dict(st["slot_of"])
+            slots, loads, evicted = impl.working_set_step(st, sel)
+            assert slots == b_slots and loads == b_loads and evicted == b_evicted, (S, sel)
+            assert st["order"] == b_order, (S, sel)
+            # invariants: every selected position resident; the maps are inverse; loads are
+            # exactly the selected positions that were not resident; evictions are unselected
+            assert all(p in st["slot_of"] for p in sel)
+            assert sorted(st["order"]) == list(range(S))
+            assert all(st["pos_of"][s] == p for p, s in st["slot_of"].items())
+            assert sum(1 for p in st["pos_of"] if p >= 0) == len(st["slot_of"]) <= S
+            assert [p for p, _ in loads] == [p for p in sel if p not in before]
+            assert not set(evicted) & set(sel)
+        # the repeated last selection loaded nothing
+        assert loads == []
+    # special cases: a history that fits never evicts; disjoint full-size selections evict
+    # everything every step; a selection larger than the working set is refused
+    st = impl.working_set_init(10)
+    for sel in ([0, 1, 2], [3, 4], [0, 5, 6, 7, 8, 9], [1, 2, 3]):
+        _, _, ev = impl.working_set_step(st, sel)
+        assert ev == []
+    st = impl.working_set_init(3)
+    impl.working_set_step(st, [0, 1, 2])
+    for base in (10, 20, 30):
+        _, loads, ev = impl.working_set_step(st, [base, base + 1, base + 2])
+        assert len(loads) == 3 and len(ev) == 3
+    try:
+        impl.working_set_step(impl.working_set_init(2), [1, 2, 3])
+        raise AssertionError("a selection larger than the working set was accepted")
+    except ValueError:
+        pass
+
+
+def check_working_set_exact(impl, seed=8):
+    """The working set changes where rows live, not what attention computes: rows copied
+    into device slots by each step's loads, read back through the step's slot list, are the
+    selected rows, and attention over them equals attention over the full cache, bit for
+    bit, step after step."""
+    rng = np.random.default_rng(seed)
+    n, D, Dl, S, k = 200, 12, 8, 24, 16
+    cache = rng.standard_normal((n, D))           # the history, in host memory
+    q = rng.standard_normal((3, D))
+    device = np.full((S, D), np.nan)              # slots start with nothing valid
+    st = impl.working_set_init(S)
+    prev = []
+    for _ in range(12):
+        keep = [p for p in prev if rng.random() < 0.7]
+        sel = sorted(set(keep) | set(int(p) for p in rng.permutation(n)[:k - len(keep)]))[:k]
+        slots, loads, _ = impl.working_set_step(st, sel)
+        for p, s in loads:
+            device[s] = cache[p]
+        got = impl.mla_absorbed(q, device[slots], Dl, 0.3)
+        want = impl.mla_absorbed(q, cache[sel], Dl, 0.3)
+        assert all(np.array_equal(a, b) for a, b in zip(got, want))
+        prev = sel
+
+
+ALL_CHECKS += [check_working_set, check_working_set_exact]

@@ -159,6 +159,39 @@ def _layers_use_pool0(q_idx, w, key_rows, n, k, layers, Dl, sm_scale):
     return _GROUP(q_idx, w, key_rows, n, k, [(q, r0) for q, _ in layers], Dl, sm_scale)
 
 
+def _ws_step_variant(evict_mru=False, evict_hits=False, recent_descending=False, keep_stale=False,
+                     misses_reversed=False):
+    def step(state, sel):
+        pos_of, order, slot_of = state["pos_of"], state["order"], state["slot_of"]
+        sel = [int(p) for p in sel]
+        pre = {p: slot_of[p] for p in sel if p in slot_of}
+        hit_slots = set(pre.values())
+        misses = [p for p in sel if p not in slot_of]
+        cands = list(order) if evict_hits else [s for s in order if s not in hit_slots]
+        if evict_mru:
+            cands = cands[::-1]
+        if misses_reversed:
+            misses = misses[::-1]
+        if len(misses) > len(cands):
+            raise ValueError("too small")
+        loads, evicted = [], []
+        for p, s in zip(misses, cands):
+            if pos_of[s] >= 0:
+                evicted.append(pos_of[s])
+                if not keep_stale:
+                    del slot_of[pos_of[s]]
+            pos_of[s] = p
+            slot_of[p] = s
+            loads.append((p, s))
+        # the slots of hits as looked up before the loads (a hit evicted by a load keeps the
+        # slot it had, which now holds another position)
+        slots = [pre[p] if p in pre else slot_of[p] for p in sel]
+        rest = [s for s in order if s not in set(slots)]
+        state["order"] = rest + (slots[::-1] if recent_descending else slots)
+        return slots, loads, evicted
+    return step
+
+
 MUTANTS = {
     "indexer_no_relu": ("indexer_scores", _no_relu, P.check_indexer),
     "indexer_relu_after_weight": ("indexer_scores", _relu_after_weight, P.check_indexer),
@@ -185,6 +218,15 @@ MUTANTS = {
     "mha_keys_without_rope": ("mla_mha", _mha_keys_without_rope, P.check_mha),
     "mha_value_dims_reversed": ("mla_mha", _mha_value_dims_reversed, P.check_mha),
     "mha_no_scale": ("mla_mha", _mha_no_scale, P.check_mha),
+    "working_set_evicts_most_recent": ("working_set_step", _ws_step_variant(evict_mru=True), P.check_working_set),
+    "working_set_evicts_hits": ("working_set_step", _ws_step_variant(evict_hits=True), P.check_working_set),
+    "working_set_recent_descending": ("working_set_step", _ws_step_variant(recent_descending=True),
+                                      P.check_working_set),
+    "working_set_keeps_stale_map": ("working_set_step", _ws_step_variant(keep_stale=True), P.check_working_set),
+    "working_set_misses_reversed": ("working_set_step", _ws_step_variant(misses_reversed=True),
+                                    P.check_working_set),
+    "working_set_exact_keeps_stale_map": ("working_set_step", _ws_step_variant(keep_stale=True),
+                                          P.check_working_set_exact),
 }
 
 
