@@ -22,6 +22,7 @@ import dataclasses
 import math
 from typing import Dict, List, Optional
 
+import numpy as np
 import torch
 
 BLOCK = 64  # tokens per page of every paged cache
@@ -249,3 +250,36 @@ def make_inputs(cfg: Config, device="cpu") -> dict:
         inp["w_kv"] = torch.cat([wuk.transpose(1, 2), wuv.transpose(1, 2)], dim=1).contiguous()
         inp["q_mha"] = _normal(cfg, _T_QMHA, 0, (T, cfg.H, MHA_DN + MHA_DR), cfg.dtype, device)
     return inp
+
+
+def selection_steps(lengths: List[int], k: int, steps: int, keep: float, seed: int) -> torch.Tensor:
+    """Seeded selections of `steps` consecutive decode steps, as the top-k writes them
+    ([steps][B][k] int32 CPU: ascending positions, then -1): a request of n <= k positions
+    selects all of them; a longer one keeps each position of its previous selection with
+    probability `keep` and fills up to k with positions drawn uniformly from the rest.
+    Drift between steps stands in for the slowly moving queries of consecutive decode
+    steps; the pages give no rate."""
+    rng = np.random.default_rng(seed)
+    out = torch.full((steps, len(lengths), k), -1, dtype=torch.int32)
+    prev = [None] * len(lengths)
+    for t in range(steps):
+        for b, n in enumerate(lengths):
+            if n <= k:
+                sel = np.arange(n)
+            else:
+                kept = prev[b][rng.random(k) < keep] if prev[b] is not None else np.empty(0, np.int64)
+                pool = np.setdiff1d(np.arange(n), kept, assume_unique=True)
+                sel = np.sort(np.concatenate([kept, rng.choice(pool, k - len(kept), replace=False)]))
+            prev[b] = sel
+            out[t, b, :len(sel)] = torch.from_numpy(sel.astype(np.int32))
+    return out
+
+
+def drift_queries(q_idx: torch.Tensor, frac: float, seed: int, idx_range: int = 4) -> torch.Tensor:
+    """q_idx with a fraction `frac` of its entries drawn again from U{-idx_range..idx_range}:
+    the indexer queries of a later decode step, whose selection then overlaps the earlier
+    one's in part (the pages give no rate for this; it is a knob of the synthetic inputs)."""
+    g = torch.Generator(device=q_idx.device).manual_seed(seed)
+    fresh = torch.randint(-idx_range, idx_range + 1, q_idx.shape, generator=g, device=q_idx.device).to(q_idx.dtype)
+    pick = torch.rand(q_idx.shape, generator=g, device=q_idx.device) < frac
+    return torch.where(pick, fresh, q_idx).contiguous()

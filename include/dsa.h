@@ -282,6 +282,71 @@ dsa_status dsa_index_cache_publish(dsa_index_cache* c, uint64_t step);
 dsa_status dsa_index_cache_get(const dsa_index_cache* c, uint64_t step, int32_t layer_in_group,
                                const int32_t** idx);
 
+/*
+ * HBM working set of latent rows for decode  [remio.ai GLM-5.3 explainer, §HiSparse: the
+ * GPU keeps a bounded least-recently-used working set of KV entries while the whole
+ * history sits in pinned host memory; selected entries missing from HBM are loaded from
+ * it, so attention is unchanged; SemiAnalysis, introduction: the loads overlap layer by
+ * layer; remio.ai, §IndexShare: layers sharing an index reuse the fetched entries].
+ *
+ * A working set gives each of `batch` requests `slots` rows of HBM.  Its state lives in
+ * three caller-owned device arrays:
+ *   slot_of [batch][max_len]  the slot holding position p of request b, -1 if not resident
+ *   pos_of  [batch][slots]    the position slot s holds, -1 if free
+ *   order   [batch][slots]    the request's slots from least to most recently used
+ * One decode step (one query token per request, token b of request b):
+ *   dsa_working_set_plan   takes the step's selection idx (as dsa_topk writes it: per row,
+ *                          strictly ascending positions, then -1; the row ends at its
+ *                          first entry that breaks this) and updates the state: selected
+ *                          positions already resident are hits; each miss, in ascending
+ *                          position order, takes the next slot of the recency order that
+ *                          holds no hit (free slots first, then the least recently used
+ *                          entries), evicting the position it held; this step's positions
+ *                          then become the most recent, in ascending position order.
+ *                          Writes slot_idx [batch][ld_slot] (entry j: the slot of idx
+ *                          entry j, -1 past the selection), loads [batch][k][2] (the
+ *                          (position, slot) pairs to load, in ascending position order)
+ *                          and load_count [batch].  All device.
+ *   dsa_working_set_fetch  copies the rows to load of one layer from that layer's history
+ *                          (host_kv: a paged pool in PINNED host memory -- allocated with
+ *                          hipHostMalloc or torch's pin_memory -- addressed by pt exactly as
+ *                          the device pool it replaces) into dev_kv, the layer's working-set
+ *                          pool in device memory: request b's slot s is row b * slots + s,
+ *                          i.e. block (b * slots + s) / 64.  The GPU reads host memory
+ *                          directly.  A history row whose block is outside [0, num_blocks)
+ *                          arrives as zeros.
+ * The sparse MLA then reads the working set through dsa_sparse_mla_decode with dev_kv, the
+ * slot list as its index list and the working set's page table: block_table[b][j] =
+ * b * slots / 64 + j for j < slots / 64, seq_len[b] = slots (slots > k, so the list is
+ * always used).  Every layer of an IndexShare group shares one plan (its selection, so
+ * its slots) and fetches its own rows; the fetch of layer l + 1 may run on a second stream
+ * while layer l attends.
+ *   dsa_working_set_reset  empties every request's working set (a fill kernel; no memset).
+ * Limits: slots a multiple of 64, k < slots <= 16384, k <= 2048, batch <= 65535,
+ * max_len = the page table's max_blocks * 64 for the fetch (checked); dev_kv holds
+ * batch * slots rows; host_kv and dev_kv are bf16 pools of 576-element rows.  Calls on
+ * one working set must be ordered on the stream(s); the plan is not re-entrant.
+ * DSA_ERR_INVALID for NULL pointers, bad sizes, host_kv not in pinned host memory (checked
+ * with hipPointerGetAttributes) or a device pool too small; DSA_ERR_UNSUPPORTED outside
+ * the limits.
+ */
+typedef struct {
+  int32_t* slot_of;   /* device [batch][max_len] */
+  int32_t* pos_of;    /* device [batch][slots] */
+  int32_t* order;     /* device [batch][slots] */
+  int32_t batch;
+  int32_t slots;
+  int64_t max_len;
+} dsa_working_set;
+
+dsa_status dsa_working_set_reset(const dsa_working_set* ws, void* stream);
+dsa_status dsa_working_set_plan(const dsa_working_set* ws, const int32_t* idx, int64_t ld_idx, int32_t k,
+                                int32_t* slot_idx, int64_t ld_slot, int32_t* loads, int32_t* load_count,
+                                void* stream);
+dsa_status dsa_working_set_fetch(const dsa_working_set* ws, const dsa_pool* host_kv, const dsa_page_table* pt,
+                                 const int32_t* loads, const int32_t* load_count, int32_t k,
+                                 const dsa_pool* dev_kv, void* stream);
+
 /* Workspace bytes an operation needs for `rows` query tokens (0 = none).  max_len is the
  * score row stride `ld` for DSA_OP_TOPK, the most positions a token sees (max q_pos + 1)
  * for DSA_OP_MLA_MHA and DSA_OP_MLA_HEADS, and is ignored for DSA_OP_MLA.  For DSA_OP_MLA

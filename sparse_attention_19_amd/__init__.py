@@ -15,7 +15,7 @@ import torch
 
 from ._lib import (DSA_BF16, DSA_BLOCK, DSA_ERR_INVALID, DSA_F32, DSA_MAX_K, DSA_OP_MLA, DSA_OP_MLA_HEADS,
                    DSA_OP_MLA_MHA, DSA_OP_TOPK, LIB,
-                   LIB_PATH, DsaChunk, DsaError, DsaIndexCache, DsaPageTable, DsaPool, check)
+                   LIB_PATH, DsaChunk, DsaError, DsaIndexCache, DsaPageTable, DsaPool, DsaWorkingSet, check)
 
 __all__ = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc",
@@ -24,6 +24,7 @@ __all__ = [
     "IndexCache", "PageTable", "Chunk", "dsa_workspace_bytes", "workspace", "DsaError", "LIB_PATH",
     "DSA_OP_TOPK", "DSA_OP_MLA",
     "dsa_timing_start", "dsa_timing_collect", "dsa_probe_row_gather",
+    "WorkingSet", "dsa_working_set_reset", "dsa_working_set_plan", "dsa_working_set_fetch",
 ]
 
 _DT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
@@ -254,6 +255,65 @@ class IndexCache:
         check(LIB.dsa_index_cache_get(ctypes.byref(self.c), step, layer_in_group, ctypes.byref(p)))
         assert p.value == self.idx.data_ptr()
         return self.idx
+
+
+class WorkingSet:
+    """dsa_working_set: the HBM working set of `slots` latent rows per request, its state in
+    three device int32 tensors allocated here with torch (slot_of [batch][max_len], pos_of and
+    order [batch][slots]), emptied by dsa_working_set_reset on the current stream.
+
+    page_table() is the table through which the sparse MLA reads the working-set pool:
+    request b's slots are blocks b * slots / 64 .. and every slot is visible."""
+
+    def __init__(self, batch: int, slots: int, max_len: int, device):
+        self.slot_of = torch.empty((batch, max_len), dtype=torch.int32, device=device)
+        self.pos_of = torch.empty((batch, slots), dtype=torch.int32, device=device)
+        self.order = torch.empty((batch, slots), dtype=torch.int32, device=device)
+        self.batch, self.slots, self.max_len = batch, slots, max_len
+        self.c = DsaWorkingSet(self.slot_of.data_ptr(), self.pos_of.data_ptr(), self.order.data_ptr(), batch, slots,
+                               max_len)
+        dsa_working_set_reset(self)
+
+    def page_table(self) -> PageTable:
+        dev = self.slot_of.device
+        nb = self.slots // DSA_BLOCK
+        bt = (torch.arange(self.batch, dtype=torch.int32, device=dev)[:, None] * nb
+              + torch.arange(nb, dtype=torch.int32, device=dev)[None, :]).contiguous()
+        lens_host = torch.full((self.batch,), self.slots, dtype=torch.int32)
+        return PageTable(bt, lens_host.to(dev), lens_host)
+
+
+def dsa_working_set_reset(ws: WorkingSet, stream=None) -> None:
+    check(LIB.dsa_working_set_reset(ctypes.byref(ws.c), _stream(stream, ws.slot_of)))
+
+
+def dsa_working_set_plan(ws: WorkingSet, idx, k, slot_idx, loads, load_count, stream=None) -> None:
+    """One decode step of the working set for selection idx [batch][>= k]: writes slot_idx
+    [batch][>= k], loads [batch][k][2] and load_count [batch] (device int32)."""
+    if loads.dim() != 3 or loads.shape[2] != 2 or loads.shape[0] != ws.batch or loads.shape[1] != k:
+        raise ValueError("loads must be [batch][k][2]")
+    if load_count.numel() != ws.batch or slot_idx.shape[0] != ws.batch or idx.shape[0] != ws.batch:
+        raise ValueError("idx, slot_idx and load_count need one row per request")
+    check(LIB.dsa_working_set_plan(ctypes.byref(ws.c), _dev(idx, "idx", torch.int32), idx.shape[1], k,
+                                   _dev(slot_idx, "slot_idx", torch.int32), slot_idx.shape[1],
+                                   _dev(loads, "loads", torch.int32), _dev(load_count, "load_count", torch.int32),
+                                   _stream(stream, idx)))
+
+
+def dsa_working_set_fetch(ws: WorkingSet, host_kv: torch.Tensor, pt: PageTable, loads, load_count, k,
+                          dev_kv: torch.Tensor, stream=None) -> None:
+    """Copy the planned rows of one layer from its history host_kv (a pinned CPU tensor
+    [num_blocks][64][576] bf16) into dev_kv (device [batch * slots / 64][64][576] bf16)."""
+    if not isinstance(host_kv, torch.Tensor) or host_kv.is_cuda or not host_kv.is_pinned():
+        raise ValueError("host_kv must be a pinned host (CPU) tensor")
+    if host_kv.dim() != 3 or host_kv.shape[1] != DSA_BLOCK or host_kv.dtype not in _DT or not host_kv.is_contiguous():
+        raise ValueError(f"host_kv must be a contiguous [num_blocks][{DSA_BLOCK}][row_dim] tensor")
+    if loads.dim() != 3 or loads.shape[0] != ws.batch or loads.shape[1] != k or loads.shape[2] != 2:
+        raise ValueError("loads must be [batch][k][2]")
+    hp = DsaPool(host_kv.data_ptr(), host_kv.shape[0], DSA_BLOCK, host_kv.shape[2], _DT[host_kv.dtype])
+    check(LIB.dsa_working_set_fetch(ctypes.byref(ws.c), ctypes.byref(hp), ctypes.byref(pt.c),
+                                    _dev(loads, "loads", torch.int32), _dev(load_count, "load_count", torch.int32), k,
+                                    ctypes.byref(_pool(dev_kv, "dev_kv")), _stream(stream, dev_kv)))
 
 
 def dsa_probe_row_gather(pool: torch.Tensor, rows: torch.Tensor, sink: Optional[torch.Tensor] = None,

@@ -18,7 +18,7 @@ DSA_F32, DSA_BF16 = 0, 1
 DSA_OP_TOPK, DSA_OP_MLA, DSA_OP_MLA_MHA, DSA_OP_MLA_HEADS = 0, 1, 2, 3
 DSA_BLOCK = 64
 DSA_MAX_K = 2048
-ABI_VERSION = b"dsa-gfx950 0.2.0"   # argument layout this binding marshals for
+ABI_VERSION = b"dsa-gfx950 0.3.0"   # argument layout this binding marshals for
 
 EXPORTS = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc",
@@ -26,6 +26,7 @@ EXPORTS = [
     "dsa_sparse_mla_prefill_mha", "dsa_mla_prefill_heads", "dsa_index_cache_init", "dsa_index_cache_publish", "dsa_index_cache_get",
     "dsa_workspace_bytes", "dsa_status_string", "dsa_last_error", "dsa_version",
     "dsa_timing_start", "dsa_timing_collect", "dsa_probe_row_gather", "dsa_probe_row_gather_sink_words",
+    "dsa_working_set_reset", "dsa_working_set_plan", "dsa_working_set_fetch",
 ]
 
 
@@ -44,6 +45,11 @@ class DsaChunk(ctypes.Structure):
                 ("q_row_host", ctypes.c_void_p), ("q_pos_host", ctypes.c_void_p)]
 
 
+class DsaWorkingSet(ctypes.Structure):
+    _fields_ = [("slot_of", ctypes.c_void_p), ("pos_of", ctypes.c_void_p), ("order", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("slots", ctypes.c_int32), ("max_len", ctypes.c_int64)]
+
+
 class DsaIndexCache(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("group", ctypes.c_int32), ("valid", ctypes.c_int32),
@@ -56,7 +62,7 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     pool_p, pt_p, cache_p = ctypes.POINTER(DsaPool), ctypes.POINTER(DsaPageTable), ctypes.POINTER(DsaIndexCache)
-    chunk_p = ctypes.POINTER(DsaChunk)
+    chunk_p, ws_p = ctypes.POINTER(DsaChunk), ctypes.POINTER(DsaWorkingSet)
     sig = {
         "dsa_indexer_scores": [P, P, pool_p, pt_p, chunk_p, I32, I32, I32, P, I64, P],
         "dsa_topk": [P, I64, P, P, I32, I32, I32, P, I64, P, SZ, P],
@@ -81,6 +87,9 @@ def _load() -> ctypes.CDLL:
         "dsa_timing_collect": [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(F), I32],
         "dsa_probe_row_gather": [P, I64, P, I64, I32, P, P],
         "dsa_probe_row_gather_sink_words": [I64],
+        "dsa_working_set_reset": [ws_p, P],
+        "dsa_working_set_plan": [ws_p, P, I64, I32, P, I64, P, P, P],
+        "dsa_working_set_fetch": [ws_p, pool_p, pt_p, P, P, I32, pool_p, P],
     }
     missing = [n for n in sig if not hasattr(lib, n)]
     if missing:

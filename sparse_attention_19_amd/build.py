@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libdsa.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["indexer.hip", "topk.hip", "mla.hip", "gemm.hip", "mha.hip", "probe.hip", "dsa_abi.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "mla.hip", "gemm.hip", "mha.hip", "probe.hip", "hisparse.hip", "dsa_abi.cpp"]
 
 # Packed fp32 ops are disabled for every device pass (-packed-fp32-ops): the compiler
 # otherwise forms v_pk_* fp32 instructions on its own.

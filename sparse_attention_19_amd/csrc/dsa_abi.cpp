@@ -527,7 +527,98 @@ const char* dsa_status_string(dsa_status s) {
 
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
-const char* dsa_version(void) { return "dsa-gfx950 0.2.0"; }
+const char* dsa_version(void) { return "dsa-gfx950 0.3.0"; }
+
+// ---- HBM working set of latent rows (hisparse.hip)
+
+namespace {
+
+constexpr int kLatentRow = 576;
+
+dsa_status check_ws(const dsa_working_set* ws) {
+  if (!ws) return fail(DSA_ERR_INVALID, "working set is NULL");
+  if (!ws->slot_of || !ws->pos_of || !ws->order)
+    return fail(DSA_ERR_INVALID, "working set: slot_of/pos_of/order is NULL");
+  if (ws->batch < 1 || ws->batch > 65535)
+    return fail(DSA_ERR_UNSUPPORTED, "working set: batch %d outside [1, 65535]", ws->batch);
+  if (ws->slots < DSA_BLOCK || ws->slots > dsa::kWsMaxSlots || ws->slots % DSA_BLOCK)
+    return fail(DSA_ERR_UNSUPPORTED, "working set: slots %d not a multiple of %d in [%d, %d]", ws->slots, DSA_BLOCK,
+                DSA_BLOCK, dsa::kWsMaxSlots);
+  if (ws->max_len < 1 || ws->max_len > INT32_MAX)
+    return fail(DSA_ERR_INVALID, "working set: max_len %lld outside [1, %d]", (long long)ws->max_len, INT32_MAX);
+  return DSA_OK;
+}
+
+dsa_status check_ws_k(const dsa_working_set* ws, int32_t k) {
+  if (k < 1 || k > dsa::kWsMaxK) return fail(DSA_ERR_UNSUPPORTED, "k = %d outside [1, %d]", k, dsa::kWsMaxK);
+  if (k >= ws->slots)
+    return fail(DSA_ERR_UNSUPPORTED, "working set: slots %d must exceed k = %d", ws->slots, k);
+  return DSA_OK;
+}
+
+dsa::WorkingSetArgs ws_args(const dsa_working_set* ws) {
+  return dsa::WorkingSetArgs{ws->slot_of, ws->pos_of, ws->order, ws->batch, ws->slots, ws->max_len};
+}
+
+}  // namespace
+
+dsa_status dsa_working_set_reset(const dsa_working_set* ws, void* stream) {
+  dsa_status s = check_ws(ws);
+  if (s) return s;
+  return launched(dsa::launch_ws_reset(ws_args(ws), (hipStream_t)stream), "working-set reset launch");
+}
+
+dsa_status dsa_working_set_plan(const dsa_working_set* ws, const int32_t* idx, int64_t ld_idx, int32_t k,
+                                int32_t* slot_idx, int64_t ld_slot, int32_t* loads, int32_t* load_count,
+                                void* stream) {
+  dsa_status s = check_ws(ws);
+  if (s) return s;
+  if ((s = check_ws_k(ws, k))) return s;
+  if (!idx || !slot_idx || !loads || !load_count)
+    return fail(DSA_ERR_INVALID, "idx/slot_idx/loads/load_count is NULL");
+  if (ld_idx < k || ld_slot < k)
+    return fail(DSA_ERR_INVALID, "ld_idx %lld / ld_slot %lld < k %d", (long long)ld_idx, (long long)ld_slot, k);
+  if (((uintptr_t)loads & 7u) != 0) return fail(DSA_ERR_INVALID, "loads not 8-byte aligned");
+  return launched(dsa::launch_ws_plan(ws_args(ws), idx, ld_idx, k, slot_idx, ld_slot, loads, load_count,
+                                      (hipStream_t)stream),
+                  "working-set plan launch");
+}
+
+dsa_status dsa_working_set_fetch(const dsa_working_set* ws, const dsa_pool* host_kv, const dsa_page_table* pt,
+                                 const int32_t* loads, const int32_t* load_count, int32_t k,
+                                 const dsa_pool* dev_kv, void* stream) {
+  dsa_status s = check_ws(ws);
+  if (s) return s;
+  if ((s = check_ws_k(ws, k))) return s;
+  if ((s = check_pool(host_kv, "host_kv", kLatentRow))) return s;
+  if ((s = check_pool(dev_kv, "dev_kv", kLatentRow))) return s;
+  if (host_kv->dtype != DSA_BF16 || dev_kv->dtype != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "the working set holds bf16 latent rows");
+  if (dev_kv->num_blocks * DSA_BLOCK < (int64_t)ws->batch * ws->slots)
+    return fail(DSA_ERR_INVALID, "dev_kv: %lld rows, the working set needs batch * slots = %lld",
+                (long long)(dev_kv->num_blocks * DSA_BLOCK), (long long)ws->batch * ws->slots);
+  if ((s = check_pt(pt))) return s;
+  if (pt->batch != ws->batch)
+    return fail(DSA_ERR_INVALID, "page table batch %d, working set batch %d", pt->batch, ws->batch);
+  if ((int64_t)pt->max_blocks * DSA_BLOCK != ws->max_len)
+    return fail(DSA_ERR_INVALID, "working set max_len %lld, page table covers %lld positions",
+                (long long)ws->max_len, (long long)pt->max_blocks * DSA_BLOCK);
+  if (!loads || !load_count) return fail(DSA_ERR_INVALID, "loads/load_count is NULL");
+  if (((uintptr_t)loads & 7u) != 0) return fail(DSA_ERR_INVALID, "loads not 8-byte aligned");
+  // the history must be pinned host memory the GPU can read: its device address comes from
+  // the runtime (the same pointer under unified addressing)
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, host_kv->data);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DSA_ERR_INVALID, "host_kv: not memory the HIP runtime knows (%s)", hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeHost || !attr.devicePointer)
+    return fail(DSA_ERR_INVALID, "host_kv: not pinned host memory (memory type %d)", (int)attr.type);
+  return launched(dsa::launch_ws_fetch(ws_args(ws), attr.devicePointer, host_kv->num_blocks, pt->block_table,
+                                       pt->max_blocks, loads, load_count, k, dev_kv->data, (hipStream_t)stream),
+                  "working-set fetch launch");
+}
 
 dsa_status dsa_probe_row_gather(const void* pool, int64_t nrows, const int32_t* rows, int64_t nlist,
                                 int32_t lines, uint32_t* sink, void* stream) {

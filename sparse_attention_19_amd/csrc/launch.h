@@ -122,4 +122,21 @@ int64_t probe_gather_workgroups(int64_t nlist);
 hipError_t launch_probe_row_gather(const void* pool, int64_t nrows, const int* rows, int64_t nlist, bool lines,
                                    uint32_t* sink, hipStream_t stream);
 
+// HBM working set of latent rows (hisparse.hip)
+constexpr int kWsMaxSlots = 16384;   // slots per request
+constexpr int kWsMaxK = 2048;
+struct WorkingSetArgs {
+  int* slot_of;      // [batch][max_len]
+  int* pos_of;       // [batch][slots]
+  int* order;        // [batch][slots]
+  int batch, slots;
+  int64_t max_len;
+};
+hipError_t launch_ws_reset(const WorkingSetArgs& a, hipStream_t stream);
+hipError_t launch_ws_plan(const WorkingSetArgs& a, const int* idx, int64_t ld_idx, int k, int* slot_idx,
+                          int64_t ld_slot, int* loads, int* load_count, hipStream_t stream);
+hipError_t launch_ws_fetch(const WorkingSetArgs& a, const void* host, int64_t host_blocks, const int* block_table,
+                           int max_blocks, const int* loads, const int* load_count, int k, void* dev,
+                           hipStream_t stream);
+
 }  // namespace dsa

@@ -14,8 +14,9 @@ from typing import List, Optional
 
 import torch
 
-from . import (DSA_OP_MLA, DSA_OP_TOPK, Chunk, IndexCache, PageTable, dsa_indexer_scores,
-               dsa_sparse_mla_decode, dsa_sparse_mla_prefill, dsa_topk, workspace)
+from . import (DSA_OP_MLA, DSA_OP_TOPK, Chunk, IndexCache, PageTable, WorkingSet, dsa_indexer_scores,
+               dsa_sparse_mla_decode, dsa_sparse_mla_prefill, dsa_topk, dsa_working_set_fetch,
+               dsa_working_set_plan, workspace)
 
 
 @dataclasses.dataclass
@@ -73,6 +74,67 @@ def prefill_step(q_idx, w, k_pool, kv_pools, qs, pt: PageTable, chunk: Chunk, k,
         idx = buf.idx if layer == 0 else buf.cache.get(step, layer)
         dsa_sparse_mla_prefill(q, kv, pt, chunk, idx, k, sm_scale, buf.outs[layer], buf.lses[layer],
                                ws=buf.ws_mla)
+
+
+@dataclasses.dataclass
+class WorkingSetBuffers:
+    """Decode through an HBM working set of latent rows (remio.ai GLM-5.3 explainer,
+    §HiSparse): the selection's rows are loaded from each layer's history in pinned host
+    memory into that layer's working-set pool, then attended to there."""
+    ws: WorkingSet
+    pt: PageTable                   # the working set's page table (request b's slots)
+    slot_idx: torch.Tensor          # [T][k] int32, the MLA's index list into the slots
+    loads: torch.Tensor             # [T][k][2] int32 (position, slot) to load
+    load_count: torch.Tensor        # [T] int32
+    dev_pools: List[torch.Tensor]   # per layer [T * slots / 64][64][row_dim]
+    fetch_stream: Optional[torch.cuda.Stream]   # None: loads and attention in one stream
+    fetched: List[torch.cuda.Event]
+
+
+def alloc_working_set(batch: int, slots: int, max_len: int, k: int, layers: int, row_dim: int, dtype, device,
+                      overlap: bool = True) -> WorkingSetBuffers:
+    ws = WorkingSet(batch, slots, max_len, device)
+    return WorkingSetBuffers(
+        ws=ws, pt=ws.page_table(),
+        slot_idx=torch.empty((batch, k), dtype=torch.int32, device=device),
+        loads=torch.empty((batch, k, 2), dtype=torch.int32, device=device),
+        load_count=torch.empty((batch,), dtype=torch.int32, device=device),
+        dev_pools=[torch.empty((batch * slots // 64, 64, row_dim), dtype=dtype, device=device)
+                   for _ in range(layers)],
+        fetch_stream=torch.cuda.Stream(device=device) if overlap else None,   # default priority
+        fetched=[torch.cuda.Event() for _ in range(layers)],
+    )
+
+
+def decode_step_working_set(q_idx, w, k_pool, host_pools, qs, pt: PageTable, k, sm_scale, buf: StepBuffers,
+                            wb: WorkingSetBuffers) -> None:
+    """One decode token per request through the layers of an IndexShare group whose latent
+    caches live in pinned host memory (host_pools): the indexer and top-k over the device
+    key cache, one working-set plan for the group's shared selection, then per layer the
+    loads of its missing rows and its attention over the working set.  With a fetch stream
+    the loads of layer l + 1 run while layer l attends (SemiAnalysis, introduction: the
+    layer-wise overlap HiSparse takes from HiCache)."""
+    dsa_indexer_scores(q_idx, w, k_pool, pt, buf.scores)
+    dsa_topk(buf.scores, pt.seq_len, pt.seq_len_host, k, buf.idx, n_add=0, ws=buf.ws_topk)
+    dsa_working_set_plan(wb.ws, buf.idx, k, wb.slot_idx, wb.loads, wb.load_count)
+    cur = torch.cuda.current_stream(q_idx.device)
+    if wb.fetch_stream is None:
+        for layer, (host, q) in enumerate(zip(host_pools, qs)):
+            dsa_working_set_fetch(wb.ws, host, pt, wb.loads, wb.load_count, k, wb.dev_pools[layer])
+            dsa_sparse_mla_decode(q, wb.dev_pools[layer], wb.pt, wb.slot_idx, k, sm_scale, buf.outs[layer],
+                                  buf.lses[layer], ws=buf.ws_mla)
+        return
+    planned = torch.cuda.Event()
+    planned.record(cur)
+    wb.fetch_stream.wait_event(planned)
+    for layer, host in enumerate(host_pools):
+        dsa_working_set_fetch(wb.ws, host, pt, wb.loads, wb.load_count, k, wb.dev_pools[layer],
+                              stream=wb.fetch_stream)
+        wb.fetched[layer].record(wb.fetch_stream)
+    for layer, q in enumerate(qs):
+        cur.wait_event(wb.fetched[layer])
+        dsa_sparse_mla_decode(q, wb.dev_pools[layer], wb.pt, wb.slot_idx, k, sm_scale, buf.outs[layer],
+                              buf.lses[layer], ws=buf.ws_mla)
 
 
 def page_table(inp: dict) -> PageTable:

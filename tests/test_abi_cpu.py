@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 24
     assert sorted(L.EXPORTS) == names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -369,3 +369,78 @@ def test_projection_rejects():
     assert lib.dsa_workspace_bytes(L.DSA_OP_MLA_MHA, 2048, 5120, 2048, 64, 512) == 2048 * 80 * 8
     mqa = 2048 * 64 * 576 * 2 + 2048 * 64 * 512 * 2
     assert lib.dsa_workspace_bytes(L.DSA_OP_MLA_HEADS, 2048, 5120, 2048, 64, 512) == mqa
+
+
+# ---- HBM working set
+
+FAKE3 = 0x30000
+
+
+def wset(batch=2, slots=4096, max_len=256, arrays=True):
+    return L.DsaWorkingSet(FAKE if arrays else None, FAKE2, FAKE3, batch, slots, max_len)
+
+
+def plan_call(**kw):
+    a = dict(ws=wset(), idx=FAKE, ld_idx=2048, k=2048, slot_idx=FAKE2, ld_slot=2048, loads=FAKE3, load_count=FAKE)
+    a.update(kw)
+    return L.LIB.dsa_working_set_plan(ctypes.byref(a["ws"]) if a["ws"] else None, a["idx"], a["ld_idx"], a["k"],
+                                      a["slot_idx"], a["ld_slot"], a["loads"], a["load_count"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), L.DSA_ERR_INVALID),
+    (dict(ws=wset(arrays=False)), L.DSA_ERR_INVALID),
+    (dict(ws=wset(batch=0)), L.DSA_ERR_UNSUPPORTED),
+    (dict(ws=wset(batch=70000)), L.DSA_ERR_UNSUPPORTED),
+    (dict(ws=wset(slots=4000)), L.DSA_ERR_UNSUPPORTED),
+    (dict(ws=wset(slots=32768)), L.DSA_ERR_UNSUPPORTED),
+    (dict(ws=wset(slots=2048)), L.DSA_ERR_UNSUPPORTED),          # slots must exceed k
+    (dict(ws=wset(max_len=0)), L.DSA_ERR_INVALID),
+    (dict(k=0), L.DSA_ERR_UNSUPPORTED),
+    (dict(k=4096), L.DSA_ERR_UNSUPPORTED),
+    (dict(idx=None), L.DSA_ERR_INVALID),
+    (dict(slot_idx=None), L.DSA_ERR_INVALID),
+    (dict(loads=None), L.DSA_ERR_INVALID),
+    (dict(load_count=None), L.DSA_ERR_INVALID),
+    (dict(ld_idx=100), L.DSA_ERR_INVALID),
+    (dict(ld_slot=100), L.DSA_ERR_INVALID),
+    (dict(loads=FAKE3 + 4), L.DSA_ERR_INVALID),
+])
+def test_working_set_plan_rejects(kw, status):
+    assert plan_call(**kw) == status
+
+
+def test_working_set_reset_rejects():
+    assert L.LIB.dsa_working_set_reset(None, None) == L.DSA_ERR_INVALID
+    assert L.LIB.dsa_working_set_reset(ctypes.byref(wset(slots=100)), None) == L.DSA_ERR_UNSUPPORTED
+
+
+def fetch_call(**kw):
+    a = dict(ws=wset(batch=2, max_len=256), host=pool(row=576, nblk=100), pt=pt(batch=2, max_blocks=4), loads=FAKE3,
+             load_count=FAKE, k=2048, dev=pool(row=576, nblk=128, data=FAKE2))
+    a.update(kw)
+    ref = lambda x: ctypes.byref(x) if x is not None else None   # noqa: E731
+    return L.LIB.dsa_working_set_fetch(ref(a["ws"]), ref(a["host"]), ref(a["pt"]), a["loads"], a["load_count"], a["k"],
+                                       ref(a["dev"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), L.DSA_ERR_INVALID),
+    (dict(k=4096), L.DSA_ERR_UNSUPPORTED),
+    (dict(host=None), L.DSA_ERR_INVALID),
+    (dict(host=pool(row=512, nblk=100)), L.DSA_ERR_INVALID),
+    (dict(host=pool(row=576, nblk=100, dtype=L.DSA_F32)), L.DSA_ERR_UNSUPPORTED),
+    (dict(dev=None), L.DSA_ERR_INVALID),
+    (dict(dev=pool(row=576, nblk=127, data=FAKE2)), L.DSA_ERR_INVALID),     # fewer than batch * slots rows
+    (dict(pt=None), L.DSA_ERR_INVALID),
+    (dict(pt=pt(batch=3, max_blocks=4)), L.DSA_ERR_INVALID),               # batch differs from the working set
+    (dict(pt=pt(batch=2, max_blocks=5)), L.DSA_ERR_INVALID),               # covers other positions than max_len
+    (dict(pt=pt(batch=2, max_blocks=4, lens=[300, 10])), L.DSA_ERR_INVALID),
+    (dict(loads=None), L.DSA_ERR_INVALID),
+    (dict(load_count=None), L.DSA_ERR_INVALID),
+    (dict(loads=FAKE3 + 4), L.DSA_ERR_INVALID),
+    (dict(), L.DSA_ERR_INVALID),     # every size is right, but the history is not pinned host memory
+])
+def test_working_set_fetch_rejects(kw, status):
+    assert fetch_call(**kw) == status
+

@@ -1,0 +1,155 @@
+"""The HBM working set of latent rows (HiSparse) on the GPU against the oracle.
+
+The plan kernel's state after each step -- the slot of every selected entry, the rows to
+load, and the slot_of / pos_of / order arrays -- must equal the oracle's working set bit
+for bit on seeded selection sequences.  Attention through the working set (rows loaded from
+pinned host memory) must equal attention over the full device cache: bit for bit for the
+requests whose selection is a top-k list (same rows in the same order), and within the bf16
+bar against the oracle everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as I
+from oracle import dsa_oracle as O
+from oracle import run as R
+
+pytestmark = pytest.mark.gpu
+
+import sparse_attention_19_amd as D  # noqa: E402  (fails loudly if the library is missing)
+from sparse_attention_19_amd import pipeline as P  # noqa: E402
+
+DEV = "cuda"
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def check_state(ws, states, sels, slot_idx, loads, load_count, step):
+    """The working set's device state and one plan's outputs against the oracle's, request
+    by request (the oracle's states are advanced here)."""
+    slot_of, pos_of, order = ws.slot_of.cpu(), ws.pos_of.cpu(), ws.order.cpu()
+    slot_idx, loads, load_count = slot_idx.cpu(), loads.cpu(), load_count.cpu()
+    k = slot_idx.shape[1]
+    for b, st in enumerate(states):
+        sel = [p for p in sels[b].tolist() if p >= 0]
+        slots, exp_loads, _ = O.working_set_step(st, sel)
+        got_slots = slot_idx[b].tolist()
+        assert got_slots[:len(sel)] == slots, f"step {step} request {b}: slots differ"
+        assert all(s == -1 for s in got_slots[len(sel):k]), f"step {step} request {b}: padding"
+        m = int(load_count[b])
+        assert m == len(exp_loads), f"step {step} request {b}: {m} loads, oracle {len(exp_loads)}"
+        assert [tuple(x) for x in loads[b, :m].tolist()] == exp_loads, f"step {step} request {b}: loads differ"
+        assert pos_of[b].tolist() == st["pos_of"], f"step {step} request {b}: pos_of differs"
+        assert order[b].tolist() == st["order"], f"step {step} request {b}: order differs"
+        want = torch.full((ws.max_len,), -1, dtype=torch.int32)
+        for p, s in st["slot_of"].items():
+            want[p] = s
+        assert torch.equal(slot_of[b], want), f"step {step} request {b}: slot_of differs"
+
+
+@pytest.mark.parametrize("lengths,k,slots,steps,keep", [
+    ([3000, 5000, 700, 2100, 9000, 257], 256, 512, 10, 0.7),   # sparse and dense rows, small k
+    ([70000, 40000, 1500], 2048, 4096, 6, 0.8),                 # the path's k at long contexts
+    ([20000, 2049], 2048, 16384, 4, 0.5),                       # the largest working set
+])
+def test_plan_matches_oracle(lengths, k, slots, steps, keep):
+    max_len = (max(lengths) + 63) // 64 * 64
+    seq = I.selection_steps(lengths, k, steps, keep, seed=len(lengths) * 7 + k)
+    # a repeated selection (all hits) and a fresh one (mostly misses) close the sequence
+    seq = torch.cat([seq, seq[-1:], I.selection_steps(lengths, k, 1, 0.0, seed=99)])
+    ws = D.WorkingSet(len(lengths), slots, max_len, DEV)
+    states = [O.working_set_init(slots) for _ in lengths]
+    B = len(lengths)
+    slot_idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    loads = torch.empty((B, k, 2), dtype=torch.int32, device=DEV)
+    load_count = torch.empty((B,), dtype=torch.int32, device=DEV)
+    for t in range(seq.shape[0]):
+        log(f"[gpu] working set {lengths} k={k} slots={slots}: step {t}")
+        idx = seq[t].to(DEV)
+        D.dsa_working_set_plan(ws, idx, k, slot_idx, loads, load_count)
+        torch.cuda.synchronize()
+        check_state(ws, states, seq[t], slot_idx, loads, load_count, t)
+    assert int(load_count.sum()) > 0
+
+
+def test_plan_ends_selection_at_a_broken_row():
+    """Entries after the first one that is not a position above its predecessor are not
+    part of the selection (as the top-k never writes them)."""
+    k, slots = 64, 128
+    ws = D.WorkingSet(2, slots, 4096, DEV)
+    rows = torch.full((2, k), -1, dtype=torch.int32)
+    rows[0, :10] = torch.arange(10) * 3
+    rows[0, 10] = 5                    # not above its predecessor: the selection ends here
+    rows[0, 11:20] = torch.arange(100, 109)
+    rows[1, :5] = torch.tensor([1, 2, 3, 3, 4])   # a repeat ends it too
+    slot_idx = torch.empty((2, k), dtype=torch.int32, device=DEV)
+    loads = torch.empty((2, k, 2), dtype=torch.int32, device=DEV)
+    load_count = torch.empty((2,), dtype=torch.int32, device=DEV)
+    D.dsa_working_set_plan(ws, rows.to(DEV), k, slot_idx, loads, load_count)
+    torch.cuda.synchronize()
+    states = [O.working_set_init(slots) for _ in range(2)]
+    check_state(ws, states, torch.stack([torch.cat([rows[0, :10], torch.full((k - 10,), -1, dtype=torch.int32)]),
+                                         torch.cat([rows[1, :3], torch.full((k - 3,), -1, dtype=torch.int32)])]),
+                slot_idx, loads, load_count, 0)
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_decode_through_working_set(overlap):
+    cfg = I.shrink(I.CONFIGS["indexshare_decode_4layer"], batch=5, ctx_range=(3000, 20000), extra_dense=(1500, 700),
+                   layers=2, seed=41)
+    inp = I.make_inputs(cfg, DEV)
+    T, k = inp["q_idx"].shape[0], cfg.k
+    pt = P.page_table(inp)
+    ld = inp["block_table"].shape[1] * 64
+    hosts = [torch.empty(p.shape, dtype=p.dtype, pin_memory=True) for p in inp["kv_pools"]]
+    for h, p in zip(hosts, inp["kv_pools"]):
+        h.copy_(p)
+    wb = P.alloc_working_set(T, 4096, ld, k, cfg.layers, cfg.row_dim, cfg.dtype, DEV, overlap=overlap)
+    ref = P.alloc_buffers(T, ld, k, cfg.H, cfg.Dl, cfg.layers, cfg.dtype, DEV)
+    buf = P.alloc_buffers(T, ld, k, cfg.H, cfg.Dl, cfg.layers, cfg.dtype, DEV)
+    lens = inp["seq_len_host"].tolist()
+    q0 = inp["q_idx"]
+    total_loads = []
+    for step in range(4):
+        log(f"[gpu] decode through the working set (overlap={overlap}), step {step}")
+        inp["q_idx"] = q0 if step == 0 else I.drift_queries(q0, 0.02 * step, seed=step)
+        P.decode_step(inp["q_idx"], inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], pt, k, cfg.sm_scale, ref,
+                      step=step)
+        P.decode_step_working_set(inp["q_idx"], inp["w"], inp["k_pool"], hosts, inp["q"], pt, k, cfg.sm_scale, buf,
+                                  wb)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.idx, ref.idx)
+        total_loads.append(int(wb.load_count.sum()))
+        for layer in range(cfg.layers):
+            for t in range(T):
+                if lens[t] > k:   # a top-k list: the same rows in the same order, so the same bits
+                    assert torch.equal(buf.outs[layer][t], ref.outs[layer][t]), (step, layer, t)
+                    assert torch.equal(buf.lses[layer][t], ref.lses[layer][t]), (step, layer, t)
+            # every resident row of the working set holds its position's latent row
+            slot_of = wb.ws.slot_of.cpu()
+            bt = inp["block_table"].cpu()
+            dev = wb.dev_pools[layer].reshape(T, 4096, -1)
+            for t in range(T):
+                pos = torch.nonzero(slot_of[t] >= 0).flatten()
+                slots = slot_of[t, pos].long()
+                rows = (bt[t, pos // 64].long() * 64 + pos % 64)
+                want = inp["kv_pools"][layer].reshape(-1, cfg.row_dim)[rows.to(DEV)]
+                assert torch.equal(dev[t, slots.to(DEV)], want), (step, layer, t)
+        for t in range(T):
+            exp = R.expected_token(inp, t)
+            for layer in range(cfg.layers):
+                got = R.to_f64(buf.outs[layer][t])
+                e = float((np.abs(got - exp["out"][layer]).max(1) / np.abs(exp["out"][layer]).max(1)).max())
+                assert e <= 2e-2, (step, layer, t, e)
+                assert np.abs(buf.lses[layer][t].cpu().double().numpy() - exp["lse"][layer]).max() <= 2e-3
+    # the first step loads every selected row; drifting queries reuse most of the set
+    assert total_loads[0] == sum(min(n, k) for n in lens)
+    assert all(x < total_loads[0] for x in total_loads[1:])
+    log(f"[gpu] rows loaded per step: {total_loads}")
