@@ -16,9 +16,12 @@ with HIP events recorded on the kernel's own stream by the library,
 dsa_timing_start/collect) and the CPU oracle timed on a bounded sample of the same
 workload's tokens.
 
-Two helper modes turn rocprofv3 output into the text summaries kept under profiles/:
+Other modes (each prints JSON; none is the bench line):
     --mla-modes                 MLA's MQA mode against its MHA mode on a 2048-token prefill
                                 chunk at context lengths 2.3K .. 16K
+    --hisparse                  decode with every layer's latent cache in pinned host memory
+                                and an HBM working set per request (loads over PCIe,
+                                overlapped layer by layer), at several query drifts
     --gather-ceiling            random 1152-byte row gathers with the sparse MLA's loads
                                 from pools in L2, Infinity Cache and HBM (--steps launches)
     --copy-calibration MIB      only copies MIB MiB device-to-device (--steps times),
@@ -487,6 +490,114 @@ def run_mla_modes(args, emit=True):
     return res
 
 
+# the HBM working set (HiSparse): drift of the indexer queries per step, working-set slots
+HISPARSE_DRIFTS = [0.003, 0.01, 0.03]
+HISPARSE_SLOTS = 4096
+
+
+def run_hisparse(args):
+    """Decode of the 4-layer IndexShare workload with each layer's latent cache in pinned host
+    memory and a working set of HISPARSE_SLOTS rows per request in HBM (dsa_working_set_*):
+    per step the indexer and top-k over the device key cache, one plan for the group, then
+    per layer the loads of its missing rows (PCIe) and its attention over the working set,
+    the loads of layer l + 1 overlapped with the attention of layer l on a second stream.
+    The indexer queries drift between steps (a fraction of their entries drawn again), so
+    consecutive selections overlap in part; each drift is one row of the result.  Timed
+    against the same steps with every layer's cache in HBM, and with the loads serialised."""
+    import torch
+    import dsa_inputs as I
+    import sparse_attention_19_amd as D
+    from sparse_attention_19_amd import pipeline as P
+    dev = torch.device("cuda:0")
+    cfg = I.CONFIGS[args.config]
+    if cfg.prefill_tokens or cfg.dtype != torch.bfloat16:
+        raise SystemExit("--hisparse runs a bf16 decode workload")
+    inp = I.make_inputs(cfg, dev)
+    pt = P.page_table(inp)
+    T, k, L = inp["q_idx"].shape[0], cfg.k, cfg.layers
+    ld = inp["block_table"].shape[1] * 64
+    print(f"[hisparse] pinning {L} histories of {inp['kv_pools'][0].numel() * 2 / 1e9:.2f} GB", flush=True)
+    hosts = []
+    for p in inp["kv_pools"]:
+        h = torch.empty(p.shape, dtype=p.dtype, pin_memory=True)
+        h.copy_(p)
+        hosts.append(h)
+    buf = P.alloc_buffers(T, ld, k, cfg.H, cfg.Dl, L, cfg.dtype, dev)
+    wbs = {ov: P.alloc_working_set(T, HISPARSE_SLOTS, ld, k, L, cfg.row_dim, cfg.dtype, dev, overlap=ov)
+           for ov in (True, False)}
+    lens = inp["seq_len_host"].tolist()
+    selected = sum(min(n, k) for n in lens)
+    warm, K = max(args.warmup, 3), args.steps
+    res = {"metric": "decode tokens/s with latent caches in pinned host memory and an HBM working set",
+           "unit": "tokens/s", "workload": cfg.name, "slots_per_request": HISPARSE_SLOTS, "steps": K,
+           "working_set_bytes_per_layer": T * HISPARSE_SLOTS * cfg.row_dim * 2,
+           "history_bytes_per_layer": inp["kv_pools"][0].numel() * 2, "rows_selected_per_step": selected,
+           "drifts": []}
+
+    def queries(frac):
+        qs, q = [], inp["q_idx"]
+        for i in range(warm + K):
+            q = q if i == 0 else I.drift_queries(q, frac, seed=1000 + i)
+            qs.append(q)
+        return qs
+
+    def run(qs, mode, timed):
+        wb = wbs.get(mode)
+        if wb is not None:
+            D.dsa_working_set_reset(wb.ws)
+        loads = []
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i, q in enumerate(qs):
+            if i == warm:
+                torch.cuda.synchronize()
+                start.record()
+            if mode == "hbm":
+                P.decode_step(q, inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], pt, k, cfg.sm_scale, buf, step=i)
+            else:
+                P.decode_step_working_set(q, inp["w"], inp["k_pool"], hosts, inp["q"], pt, k, cfg.sm_scale, buf, wb)
+                if not timed and i >= warm:
+                    loads.append(wb.load_count.clone())
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K, loads
+
+    for frac in HISPARSE_DRIFTS:
+        qs = queries(frac)
+        _, loads = run(qs, True, timed=False)
+        rows = sum(int(x.sum()) for x in loads) / len(loads)
+        ms_hbm, _ = run(qs, "hbm", timed=True)
+        ms_ov, _ = run(qs, True, timed=True)
+        ms_ser, _ = run(qs, False, timed=True)
+        # per-kernel times of the overlapped mode (events in each dispatch, on its stream)
+        D.dsa_working_set_reset(wbs[True].ws)
+        for q in qs[:warm]:
+            P.decode_step_working_set(q, inp["w"], inp["k_pool"], hosts, inp["q"], pt, k, cfg.sm_scale, buf, wbs[True])
+        torch.cuda.synchronize()
+        D.dsa_timing_start(K * (8 + 3 * L))
+        for q in qs[warm:]:
+            P.decode_step_working_set(q, inp["w"], inp["k_pool"], hosts, inp["q"], pt, k, cfg.sm_scale, buf, wbs[True])
+        per = {}
+        for name, t in D.dsa_timing_collect():
+            c = per.setdefault(name, [0, 0.0])
+            c[0] += 1
+            c[1] += t
+        fetch_ms = per.get("ws_fetch_kernel", [1, 0.0])[1] / max(1, per.get("ws_fetch_kernel", [1, 0.0])[0])
+        row = {"drift": frac, "rows_loaded_per_step": round(rows, 1), "load_fraction": round(rows / selected, 4),
+               "pcie_bytes_per_step": int(rows * cfg.row_dim * 2 * L),
+               "ms_per_step_all_in_hbm": round(ms_hbm, 4), "ms_per_step_overlapped": round(ms_ov, 4),
+               "ms_per_step_serial": round(ms_ser, 4), "tokens_per_s_overlapped": round(T / (ms_ov * 1e-3), 1),
+               "fetch_kernel_us": round(fetch_ms * 1e3, 2),
+               "fetch_gbs": round(rows * cfg.row_dim * 2 / (fetch_ms * 1e-3) / 1e9, 2) if fetch_ms > 0 else None,
+               "kernels_us_per_launch": {n: round(c[1] / c[0] * 1e3, 2) for n, c in per.items()}}
+        res["drifts"].append(row)
+        print(f"[hisparse] drift {frac}: {row['load_fraction'] * 100:.1f} % of the selected rows loaded per step "
+              f"({row['rows_loaded_per_step']:.0f} rows x {L} layers); step {ms_ov:.3f} ms overlapped, "
+              f"{ms_ser:.3f} ms serial, {ms_hbm:.3f} ms with every cache in HBM; fetch {row['fetch_kernel_us']} us "
+              f"per layer ({row['fetch_gbs']} GB/s)", flush=True)
+    print(json.dumps(res), flush=True)
+    return res
+
+
 # workloads of the report: (config name, overrides, what it is)
 REPORT_WORKLOADS = [
     ("tiny_fp32", {}, "1 token, L = 256, fp32 (parity case)"),
@@ -806,6 +917,8 @@ def main():
     ap.add_argument("--report", action="store_true", help="every workload; writes REPORT.md")
     ap.add_argument("--mla-modes", action="store_true",
                     help="MLA's MQA and MHA modes on a prefill chunk across context lengths")
+    ap.add_argument("--hisparse", action="store_true",
+                    help="decode with the latent caches in pinned host memory and an HBM working set")
     ap.add_argument("--gather-ceiling", action="store_true",
                     help="random-row gather bandwidth per pool size (L2, Infinity Cache, HBM)")
     ap.add_argument("--report-path", default=os.path.join(ROOT, "REPORT.md"), help="where --report writes")
@@ -848,6 +961,8 @@ def main():
         return run_gather_ceiling(args)
     if args.mla_modes:
         return run_mla_modes(args)
+    if args.hisparse:
+        return run_hisparse(args)
     run_bench(args)
 
 

@@ -183,40 +183,43 @@ __global__ __launch_bounds__(kPlanThreads) void ws_plan_kernel(const int* __rest
   if (tid == 0) load_count[b] = m;
 }
 
-// grid (ceil(k / 16), batch): workgroup (c, b) copies loads 16c .. 16c + 15 of request b
-// (when it has that many) from the host history to their slots; 72 16-byte chunks per row.
-__global__ __launch_bounds__(kFetchThreads) void ws_fetch_kernel(const uint8_t* __restrict__ host,
-                                                                 int64_t host_blocks,
-                                                                 const int* __restrict__ block_table,
-                                                                 int max_blocks, const int2* __restrict__ loads,
-                                                                 const int* __restrict__ load_count, int k,
-                                                                 int slots, uint8_t* __restrict__ dev) {
-  const int b = blockIdx.y, r0 = blockIdx.x * kFetchRows;
+// grid (gx, batch): the workgroups (x, b) of request b copy its loads in chunks of 16 rows,
+// chunk c by workgroup c mod gx; 72 16-byte chunks per row, 16-byte loads of system memory
+// straight into registers.  At most 64 registers per lane: a fetch wave then fits on a SIMD
+// beside a sparse-MLA wave (436 registers), so the loads of the next layer run on the CUs
+// the attention of this layer occupies instead of holding CUs it is waiting for.
+__global__ __launch_bounds__(kFetchThreads) __attribute__((amdgpu_num_vgpr(64))) void ws_fetch_kernel(
+    const uint8_t* __restrict__ host, int64_t host_blocks, const int* __restrict__ block_table, int max_blocks,
+    const int2* __restrict__ loads, const int* __restrict__ load_count, int k, int slots, uint8_t* __restrict__ dev) {
+  const int b = blockIdx.y;
   const int m = min(load_count[b], k);
-  if (r0 >= m) return;
-  const int nrows = min(kFetchRows, m - r0);
-  u32x4 v[kFetchLoads];
-  int64_t dst[kFetchLoads];
+  const int nchunks = (m + kFetchRows - 1) / kFetchRows;
+  for (int c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int r0 = c * kFetchRows, nrows = min(kFetchRows, m - r0);
+    u32x4 v[kFetchLoads];
+    int dst[kFetchLoads];   // slot * 72 + 16-byte chunk of the request's working set, -1: none
 #pragma unroll
-  for (int i = 0; i < kFetchLoads; ++i) {
-    const int c = threadIdx.x + kFetchThreads * i;
-    dst[i] = -1;
-    v[i] = u32x4{0u, 0u, 0u, 0u};
-    if (c < nrows * kRowChunks) {
-      const int r = c / kRowChunks, ch = c - r * kRowChunks;
-      const int2 e = loads[(int64_t)b * k + r0 + r];
-      const int pos = e.x, s = e.y;
-      if (s >= 0 && s < slots) {
-        dst[i] = ((int64_t)b * slots + s) * kRowBytes + 16 * ch;
-        const int blk = (pos >= 0 && (pos >> 6) < max_blocks) ? block_table[(int64_t)b * max_blocks + (pos >> 6)] : -1;
-        if (blk >= 0 && blk < host_blocks)   // else the slot gets zeros
-          v[i] = *(gu32x4)(host + ((int64_t)blk * kBlock + (pos & (kBlock - 1))) * kRowBytes + 16 * ch);
+    for (int i = 0; i < kFetchLoads; ++i) {
+      const int q = threadIdx.x + kFetchThreads * i;
+      dst[i] = -1;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (q < nrows * kRowChunks) {
+        const int r = q / kRowChunks, ch = q - r * kRowChunks;
+        const int2 e = loads[(int64_t)b * k + r0 + r];
+        const int pos = e.x, s = e.y;
+        if (s >= 0 && s < slots) {
+          dst[i] = s * kRowChunks + ch;
+          const int blk = (pos >= 0 && (pos >> 6) < max_blocks) ? block_table[(int64_t)b * max_blocks + (pos >> 6)] : -1;
+          if (blk >= 0 && blk < host_blocks)   // else the slot gets zeros
+            v[i] = *(gu32x4)(host + ((int64_t)blk * kBlock + (pos & (kBlock - 1))) * kRowBytes + 16 * ch);
+        }
       }
     }
-  }
+    u32x4* const mine = reinterpret_cast<u32x4*>(dev + (int64_t)b * slots * kRowBytes);
 #pragma unroll
-  for (int i = 0; i < kFetchLoads; ++i)
-    if (dst[i] >= 0) *reinterpret_cast<u32x4*>(dev + dst[i]) = v[i];
+    for (int i = 0; i < kFetchLoads; ++i)
+      if (dst[i] >= 0) mine[dst[i]] = v[i];
+  }
 }
 
 }  // namespace
@@ -244,7 +247,10 @@ hipError_t launch_ws_fetch(const WorkingSetArgs& a, const void* host, int64_t ho
                            int max_blocks, const int* loads, const int* load_count, int k, void* dev,
                            hipStream_t stream) {
   const KernelEvents ev("ws_fetch_kernel");
-  const dim3 grid((unsigned)((k + kFetchRows - 1) / kFetchRows), (unsigned)a.batch);
+  // about 256 workgroups in all, at most one per 16-row chunk of a request's loads
+  const int per_request = a.batch >= 256 ? 1 : (256 / a.batch < 16 ? 256 / a.batch : 16);
+  const int chunks = (k + kFetchRows - 1) / kFetchRows;
+  const dim3 grid((unsigned)(per_request < chunks ? per_request : chunks), (unsigned)a.batch);
   hipExtLaunchKernelGGL(ws_fetch_kernel, grid, dim3(kFetchThreads), 0, stream, ev.start, ev.stop, 0,
                         (const uint8_t*)host, host_blocks, block_table, max_blocks,
                         reinterpret_cast<const int2*>(loads), load_count, k, a.slots, (uint8_t*)dev);
