@@ -65,49 +65,67 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int* __restrict__ i
 
 // One key tile in registers: K chunks (16 B) id = tid + 256 i, i < 8: key id / 32, chunk
 // id % 32 (chunks < 24 from the up-projected NoPE keys, the rest from the latent row's rope
-// dims); V chunks id = tid + 256 i, i < 4: key id / 16, chunk id % 16; and the selection
-// mask words of this lane's 8 token rows for the tile.
+// dims); V chunks id = tid + 256 i, i < 4: key id / 16, chunk id % 16; and (threads below
+// 128) the selection mask word of token tid for the tile.
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 typedef const __attribute__((address_space(1))) u32x4* gu32x4;
+typedef const __attribute__((address_space(1))) uint64_t* gu64;
 
 struct MhaTile {
   u32x4 k[8], v[4];
-  uint64_t mw[2][4];
+  uint64_t mw;
   int last;   // the tile's last key any token sees (-1: none)
 };
 
+// Per-thread load addresses, fixed for the whole kernel: the thread's chunk of key 0 of
+// page 0 and the byte strides from there (per key row of the page, per page row).  The
+// chunk of K a thread loads is fixed (tid % 32), so is whether it comes from kv_mha or from
+// the latent pool.
+struct MhaAddr {
+  gbytes k0, v0;
+  int64_t k_rowb, v_rowb;   // bytes per pool row (position) for the thread's K / V source
+  gu64 m0;                  // mask word of token t0 + tid (threads below 128), tile 0
+};
+
+__device__ __forceinline__ MhaAddr mha_addr(gbytes kv, gbytes lat, int H, int h, const uint64_t* mask, int words,
+                                            int t0, int T) {
+  const int tid = threadIdx.x, c = tid & 31, ck = tid & 15;
+  MhaAddr a;
+  const int64_t kv_rowb = (int64_t)H * kDkv * 2;
+  if (c < 24) {
+    a.k_rowb = kv_rowb;
+    a.k0 = kv + (int64_t)(tid >> 5) * kv_rowb + ((int64_t)h * kDkv + 8 * c) * 2;
+  } else {
+    a.k_rowb = (kDl + kDr) * 2;
+    a.k0 = lat + (int64_t)(tid >> 5) * a.k_rowb + (kDl + 8 * (c - 24)) * 2;
+  }
+  a.v_rowb = kv_rowb;
+  a.v0 = kv + (int64_t)(tid >> 4) * kv_rowb + ((int64_t)h * kDkv + kDn + 8 * ck) * 2;
+  a.m0 = (gu64)mask + (int64_t)min(t0 + tid, T - 1) * words;
+  return a;
+}
+
 // A whole tile is one page: a block-table entry outside the pool reads the pool's first
 // page, and its mask words are cleared so none of its keys takes part.
-__device__ __forceinline__ void load_mha_tile(MhaTile& r, gbytes kv, gbytes lat, int64_t row0, bool ok, int H, int h,
-                                              const uint64_t* mask, int words, int kt, int t0, int T, int last_pos) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = (lane >> 4) & 3;
+__device__ __forceinline__ void load_mha_tile(MhaTile& r, const MhaAddr& a, int64_t row0, bool ok, int kt, int t0,
+                                              int T, int last_pos) {
+  const int tid = threadIdx.x;
   r.last = ok ? min(last_pos - kKeys * kt, kKeys - 1) : -1;
+  const gbytes kb = a.k0 + row0 * a.k_rowb, vb = a.v0 + row0 * a.v_rowb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int id = tid + kThreads * i, key = id >> 5, c = id & 31;
-    const int64_t row = row0 + key;
-    const gbytes src = c < 24 ? kv + ((row * H + h) * kDkv + 8 * c) * 2 : lat + (row * (kDl + kDr) + kDl + 8 * (c - 24)) * 2;
-    r.k[i] = *(gu32x4)src;
-  }
+  for (int i = 0; i < 8; ++i) r.k[i] = *(gu32x4)(kb + 8 * i * a.k_rowb);   // keys 8 i + tid / 32
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + kThreads * i, key = id >> 4, c = id & 15;
-    r.v[i] = *(gu32x4)(kv + (((row0 + key) * H + h) * kDkv + kDn + 8 * c) * 2);
-  }
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 32 * wave + 16 * rt + 4 * g + i;
-      r.mw[rt][i] = (ok && t < T) ? mask[(int64_t)t * words + kt] : 0ull;
-    }
+  for (int i = 0; i < 4; ++i) r.v[i] = *(gu32x4)(vb + 16 * i * a.v_rowb);  // keys 16 i + tid / 16
+  r.mw = (ok && tid < kQ && t0 + tid < T) ? a.m0[kt] : 0ull;
 }
 
 // Value rows past the last key any token sees are stored as zeros: the unused tail of a
 // request's last page holds whatever the cache left there, and P = 0 times a NaN there would
 // still be NaN.  (Keys need no such care: masked logits are replaced, not multiplied.)
-__device__ __forceinline__ void store_mha_tile(const MhaTile& r, uint16_t (*Ks)[kKRow], uint16_t (*Vs)[kVRow]) {
+__device__ __forceinline__ void store_mha_tile(const MhaTile& r, uint16_t (*Ks)[kKRow], uint16_t (*Vs)[kVRow],
+                                               uint64_t* Ms) {
   const int tid = threadIdx.x;
+  if (tid < kQ) Ms[tid] = r.mw;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int id = tid + kThreads * i;
@@ -118,6 +136,13 @@ __device__ __forceinline__ void store_mha_tile(const MhaTile& r, uint16_t (*Ks)[
     const int id = tid + kThreads * i;
     *reinterpret_cast<u32x4*>(&Vs[id >> 4][8 * (id & 15)]) = (id >> 4) <= r.last ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
   }
+}
+
+// Two floats as packed bf16 (round to nearest even): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), h2));
 }
 
 // Max / sum over the 16 lanes of a row (lanes with the same lane / 16), in every lane: DPP
@@ -148,6 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeys][kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kKeys][kVRow];
   __shared__ __attribute__((aligned(16))) uint16_t Pt[4][kKeys][kPtRow];   // per wave: P transposed [key][token]
+  __shared__ uint64_t Ms[kQ];   // the tile's mask word of each of the workgroup's tokens
   __shared__ int s_pos;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int L = blockIdx.x, x = L & 7, j = L >> 3;
@@ -192,22 +218,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     ok = phys >= 0 && phys < num_blocks;
     return (int64_t)(ok ? phys : 0) * kKeys;
   };
+  const MhaAddr ad = mha_addr(kvg, latg, H, h, mask, words, t0, T);
   MhaTile r;
   bool ok;
   int64_t row0 = tile_row0(0, ok);
-  load_mha_tile(r, kvg, latg, row0, ok, H, h, mask, words, 0, t0, T, s_pos);
+  load_mha_tile(r, ad, row0, ok, 0, t0, T, s_pos);
   for (int kt = 0; kt < ntiles; ++kt) {
-    store_mha_tile(r, Ks, Vs);
+    store_mha_tile(r, Ks, Vs, Ms);
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      row0 = tile_row0(kt + 1, ok);
+      load_mha_tile(r, ad, row0, ok, kt + 1, t0, T, s_pos);
+    }
+    // this lane's mask words (token rows 32 wave + 16 rt + 4 g + i), pre-shifted to its key
+    // column c16: bit 16 nt is key 16 nt + c16
     uint64_t mw[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mw[rt][i] = r.mw[rt][i];
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      row0 = tile_row0(kt + 1, ok);
-      load_mha_tile(r, kvg, latg, row0, ok, H, h, mask, words, kt + 1, t0, T, s_pos);
-    }
+      for (int i = 0; i < 4; ++i) mw[rt][i] = Ms[32 * wave + 16 * rt + 4 * g + i] >> c16;
     // S = Q K^T: [token][key], key n-tile nt = keys 16 nt .. +15; the K fragments of the
     // next k-step are read while this one's MFMAs run
     f32x4 sacc[2][4];
@@ -233,27 +262,47 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     }
     // online softmax per token row (log2 units); P to LDS transposed, 4 token rows per 8-byte
     // store.  O is rescaled only when some row's max moved (wave-uniform test).
+    // a tile whose 64 keys every token of the wave selected (the dense rows, most of a short
+    // context) needs no masking: a wave-uniform test
+    uint64_t all = ~0ull;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) all &= mw[rt][i];
+    constexpr uint64_t kLaneKeys = 0x0001000100010001ull;   // this lane's 4 keys after the shift
+    if (__ballot((all & kLaneKeys) != kLaneKeys) == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[rt][nt][i] *= scale_log2;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sacc[rt][nt][i] = ((mw[rt][i] >> (16 * nt)) & 1ull) ? sacc[rt][nt][i] * scale_log2 : -INFINITY;
+    }
     float alpha[2][4];
     bool moved = false;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const bool in = (mw[rt][i] >> (16 * nt + c16)) & 1ull;
-          sacc[rt][nt][i] = in ? sacc[rt][nt][i] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sacc[rt][nt][i]);
-        }
+        float mx = fmaxf(fmaxf(sacc[rt][0][i], sacc[rt][1][i]), fmaxf(sacc[rt][2][i], sacc[rt][3][i]));
         mx = row16_max(mx);
         const float mn = fmaxf(m[rt][i], mx);
-        alpha[rt][i] = (mn == -INFINITY) ? 1.f : exp2f(m[rt][i] - mn);
+        // a row with nothing seen yet keeps mn = -inf: its p are exp2(-inf) = 0 against 0
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        alpha[rt][i] = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m[rt][i] - ms);
         moved |= alpha[rt][i] != 1.f;
         float ps = 0.f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const float p = (mn == -INFINITY) ? 0.f : exp2f(sacc[rt][nt][i] - mn);
+          const float p = __builtin_amdgcn_exp2f(sacc[rt][nt][i] - ms);
           sacc[rt][nt][i] = p;
           ps += p;
         }
@@ -262,8 +311,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const uint32_t lo = (uint32_t)f2bf_bits(sacc[rt][nt][0]) | ((uint32_t)f2bf_bits(sacc[rt][nt][1]) << 16);
-        const uint32_t hi = (uint32_t)f2bf_bits(sacc[rt][nt][2]) | ((uint32_t)f2bf_bits(sacc[rt][nt][3]) << 16);
+        const uint32_t lo = pack_bf16(sacc[rt][nt][0], sacc[rt][nt][1]);
+        const uint32_t hi = pack_bf16(sacc[rt][nt][2], sacc[rt][nt][3]);
         *reinterpret_cast<uint2*>(&Pt[wave][16 * nt + c16][16 * rt + 4 * g]) = make_uint2(lo, hi);
       }
     }
