@@ -15,12 +15,13 @@
 //
 // mha_mask_kernel: one workgroup per token turns its selection list into a bitmask of
 // ceil(len / 64) 64-bit words (word w, bit b: position 64w + b).
-// mla_mha_kernel: one workgroup per (128 tokens of one request, head); 4 waves of 32 tokens
-// (two 16-row tiles on 16x16x32 MFMAs); per 64-key tile, K [64][256] and V [64][128] are
-// staged in LDS (the next tile's loads and mask words in flight in registers), S = Q K^T
-// with the next k-step's K fragments read ahead, mask, online softmax (row reductions on
-// DPP; O rescaled only when a row's max moves), P through LDS transposed, O += P V with the
-// P and V fragments read transposed (ds_read_b64_tr_b16).
+// mla_mha_kernel: one workgroup per (128 tokens of one request, head); 8 waves of 16 tokens
+// (one 16-row tile on 16x16x32 MFMAs, two waves per SIMD); per 64-key tile, K [64][256] and V [64][128] are
+// staged in double-buffered LDS (the next tile's loads in flight in registers), S = Q K^T
+// with the next k-step's K fragments read ahead, mask (skipped for tiles every token of the
+// wave selected whole), online softmax (row reductions on DPP; a row's reference max moves
+// only when passed by more than 2^8, so O is rarely rescaled), P through LDS transposed,
+// O += P V with the P and V fragments read transposed (ds_read_b64_tr_b16).
 #include <math.h>
 
 #include "common.h"
@@ -33,12 +34,21 @@ namespace {
 constexpr int kDl = 512, kDn = 192, kDr = 64, kDqk = 256, kDv = 128, kDkv = 320;
 constexpr int kQ = 128;              // query tokens per workgroup
 constexpr int kKeys = 64;            // keys per tile (one page)
-constexpr int kThreads = 256;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kTokW = kQ / kWaves;   // query tokens per wave (one 16-row MFMA tile)
+constexpr int kKLoads = kKeys * (kDqk / 8) / kThreads;   // 16-byte K chunks per thread per tile (4)
+constexpr int kVLoads = kKeys * (kDv / 8) / kThreads;    // and V chunks (2)
 constexpr int kKRow = kDqk + 8;      // LDS K row, elements (528 bytes)
 constexpr int kVRow = kDv + 8;       // LDS V row, elements (272 bytes)
-constexpr int kPtRow = 32 + 8;       // LDS row of P transposed (a key's 32 tokens), elements (80 bytes)
+constexpr int kPtRow = kTokW + 8;    // LDS row of P transposed (a key's 16 tokens), elements (48 bytes)
+static_assert(kTokW == 16, "one 16-row MFMA tile per wave");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// A row's reference max is its first valid tile's max and stays fixed: probabilities up to
+// 2^32 above it are exact enough in bf16 (relative rounding) and far from overflow in the
+// fp32 sums, so O is never rescaled inside the loop.  A logit more than 32 (log2 units)
+// above the reference sends the workgroup through a second pass from each row's final max.
+constexpr float kSlack = 32.f;
 
 __global__ __launch_bounds__(256) void mha_mask_kernel(const int* __restrict__ idx, int64_t ld_idx, int k,
                                                        const int* __restrict__ q_pos, int words,
@@ -63,16 +73,16 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int* __restrict__ i
     mask[(int64_t)t * words + w] = (uint64_t)bits[2 * w] | ((uint64_t)bits[2 * w + 1] << 32);
 }
 
-// One key tile in registers: K chunks (16 B) id = tid + 256 i, i < 8: key id / 32, chunk
+// One key tile in registers: K chunks (16 B) id = tid + 512 i, i < 4: key id / 32, chunk
 // id % 32 (chunks < 24 from the up-projected NoPE keys, the rest from the latent row's rope
-// dims); V chunks id = tid + 256 i, i < 4: key id / 16, chunk id % 16; and (threads below
+// dims); V chunks id = tid + 512 i, i < 2: key id / 16, chunk id % 16; and (threads below
 // 128) the selection mask word of token tid for the tile.
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 typedef const __attribute__((address_space(1))) u32x4* gu32x4;
 typedef const __attribute__((address_space(1))) uint64_t* gu64;
 
 struct MhaTile {
-  u32x4 k[8], v[4];
+  u32x4 k[kKLoads], v[kVLoads];
   uint64_t mw;
   int last;   // the tile's last key any token sees (-1: none)
 };
@@ -113,9 +123,11 @@ __device__ __forceinline__ void load_mha_tile(MhaTile& r, const MhaAddr& a, int6
   r.last = ok ? min(last_pos - kKeys * kt, kKeys - 1) : -1;
   const gbytes kb = a.k0 + row0 * a.k_rowb, vb = a.v0 + row0 * a.v_rowb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.k[i] = *(gu32x4)(kb + 8 * i * a.k_rowb);   // keys 8 i + tid / 32
+  for (int i = 0; i < kKLoads; ++i)   // keys (kThreads / 32) i + tid / 32
+    r.k[i] = *(gu32x4)(kb + (kThreads / 32) * i * a.k_rowb);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = *(gu32x4)(vb + 16 * i * a.v_rowb);  // keys 16 i + tid / 16
+  for (int i = 0; i < kVLoads; ++i)   // keys (kThreads / 16) i + tid / 16
+    r.v[i] = *(gu32x4)(vb + (kThreads / 16) * i * a.v_rowb);
   r.mw = (ok && tid < kQ && t0 + tid < T) ? a.m0[kt] : 0ull;
 }
 
@@ -127,12 +139,12 @@ __device__ __forceinline__ void store_mha_tile(const MhaTile& r, uint16_t (*Ks)[
   const int tid = threadIdx.x;
   if (tid < kQ) Ms[tid] = r.mw;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kKLoads; ++i) {
     const int id = tid + kThreads * i;
     *reinterpret_cast<u32x4*>(&Ks[id >> 5][8 * (id & 31)]) = r.k[i];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kVLoads; ++i) {
     const int id = tid + kThreads * i;
     *reinterpret_cast<u32x4*>(&Vs[id >> 4][8 * (id & 15)]) = (id >> 4) <= r.last ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
   }
@@ -147,33 +159,53 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // Max / sum over the 16 lanes of a row (lanes with the same lane / 16), in every lane: DPP
 // row rotations, no LDS.
-#define DSA_ROR(v, n) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + (n), 0xf, 0xf, false))
+// Each step is one VALU instruction with a DPP row rotation of its first operand (row
+// rotations read and write every lane of the row).  Written as inline asm: the compiler
+// splits fmaxf over a DPP value into a lane move, a NaN-quieting max and the max.  The
+// s_nop gives the two wait states a DPP read needs after a VALU write of its source.
+#define DSA_DPP_STEP(op, v, n)                                                                      \
+  {                                                                                                \
+    float t_;                                                                                      \
+    asm volatile("s_nop 1\n\t" op " %0, %1, %1 row_ror:" #n " row_mask:0xf bank_mask:0xf"         \
+                 : "=v"(t_)                                                                        \
+                 : "v"(v));                                                                        \
+    v = t_;                                                                                        \
+  }
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, DSA_ROR(v, 1));
-  v = fmaxf(v, DSA_ROR(v, 2));
-  v = fmaxf(v, DSA_ROR(v, 4));
-  return fmaxf(v, DSA_ROR(v, 8));
+  DSA_DPP_STEP("v_max_f32_dpp", v, 1)
+  DSA_DPP_STEP("v_max_f32_dpp", v, 2)
+  DSA_DPP_STEP("v_max_f32_dpp", v, 4)
+  DSA_DPP_STEP("v_max_f32_dpp", v, 8)
+  return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-  v += DSA_ROR(v, 1);
-  v += DSA_ROR(v, 2);
-  v += DSA_ROR(v, 4);
-  return v + DSA_ROR(v, 8);
+  DSA_DPP_STEP("v_add_f32_dpp", v, 1)
+  DSA_DPP_STEP("v_add_f32_dpp", v, 2)
+  DSA_DPP_STEP("v_add_f32_dpp", v, 4)
+  DSA_DPP_STEP("v_add_f32_dpp", v, 8)
+  return v;
 }
-#undef DSA_ROR
+#undef DSA_DPP_STEP
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
 
 // grid (heads, token tiles) in XCD order: workgroup L runs on XCD L % 8, which takes heads
 // L % 8 (mod 8), each with all its token tiles in a row, so the tiles running together on
-// one XCD read the same head's keys and values from its L2.
+// one XCD read the same head's keys and values from its L2.  8 waves of 16 tokens: every
+// wave stays within 256 registers, so the two waves of a SIMD hide each other's MFMA, LDS
+// and exp latencies.
 __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ lat,
     int64_t num_blocks, const int* __restrict__ block_table, int max_blocks, const int* __restrict__ q_row,
     const int* __restrict__ q_pos, int T, int H, int tiles, const uint64_t* __restrict__ mask, int words,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeys][kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kKeys][kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Pt[4][kKeys][kPtRow];   // per wave: P transposed [key][token]
-  __shared__ uint64_t Ms[kQ];   // the tile's mask word of each of the workgroup's tokens
+  // K, V and the mask words are double-buffered (tile kt in buffer kt % 2), so one barrier
+  // per tile separates a buffer's stores from its readers and its readers from its next
+  // stores two tiles later
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kKeys][kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs2[2][kKeys][kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[kWaves][kKeys][kPtRow];   // per wave: P transposed [key][token]
+  __shared__ uint64_t Ms2[2][kQ];   // the tile's mask word of each of the workgroup's tokens
   __shared__ int s_pos;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int L = blockIdx.x, x = L & 7, j = L >> 3;
@@ -190,28 +222,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   const int* bt_row = block_table + (int64_t)b * max_blocks;
   const gbytes kvg = (gbytes)kv, latg = (gbytes)lat;
 
-  // Q fragments: tile rt = 0, 1 of the wave's 32 tokens, k-step s: token 32 wave + 16 rt +
-  // c16, dims 32 s + 8 g .. +7
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int t = min(t0 + 32 * wave + 16 * rt + c16, T - 1);
+  // Q fragments of the wave's 16 tokens, k-step s: token 16 wave + c16, dims 32 s + 8 g .. +7
+  bf16x8 qf[8];
+  {
+    const int t = min(t0 + kTokW * wave + c16, T - 1);
     const uint16_t* src = q + ((int64_t)t * H + h) * kDqk + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[rt][s] = *reinterpret_cast<const bf16x8*>(src + 32 * s);
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(src + 32 * s);
   }
-  // this lane's C rows: token 32 wave + 16 rt + 4 g + i
-  float m[2][4], l[2][4];
-  f32x4 o[2][8];
+  // this lane's C rows: token 16 wave + 4 g + i; m = the row's reference max (log2 units),
+  // mf = its largest logit so far
+  float m[4], mf[4], l[4];
+  f32x4 o[8];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m[rt][i] = -INFINITY;
-      l[rt][i] = 0.f;
-    }
-#pragma unroll
-    for (int vt = 0; vt < 8; ++vt) o[rt][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    mf[i] = -INFINITY;
   }
   auto tile_row0 = [&](int kt, bool& ok) {
     const int phys = bt_row[kt];
@@ -221,29 +247,38 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   const MhaAddr ad = mha_addr(kvg, latg, H, h, mask, words, t0, T);
   MhaTile r;
   bool ok;
-  int64_t row0 = tile_row0(0, ok);
+  int64_t row0;
+  for (int pass = 0; pass < 2; ++pass) {
+  bool ovf = false;   // some row of this lane passed its reference max by more than kSlack
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (pass == 1) m[i] = mf[i];   // the second pass starts from the final max
+    l[i] = 0.f;
+  }
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt) o[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  row0 = tile_row0(0, ok);
   load_mha_tile(r, ad, row0, ok, 0, t0, T, s_pos);
   for (int kt = 0; kt < ntiles; ++kt) {
+    uint16_t (*const Ks)[kKRow] = Ks2[kt & 1];
+    uint16_t (*const Vs)[kVRow] = Vs2[kt & 1];
+    uint64_t* const Ms = Ms2[kt & 1];
     store_mha_tile(r, Ks, Vs, Ms);
     __syncthreads();
     if (kt + 1 < ntiles) {
       row0 = tile_row0(kt + 1, ok);
       load_mha_tile(r, ad, row0, ok, kt + 1, t0, T, s_pos);
     }
-    // this lane's mask words (token rows 32 wave + 16 rt + 4 g + i), pre-shifted to its key
-    // column c16: bit 16 nt is key 16 nt + c16
-    uint64_t mw[2][4];
+    // this lane's mask words (token rows 16 wave + 4 g + i), pre-shifted to its key column
+    // c16: bit 16 nt is key 16 nt + c16
+    uint64_t mw[4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mw[rt][i] = Ms[32 * wave + 16 * rt + 4 * g + i] >> c16;
+    for (int i = 0; i < 4; ++i) mw[i] = Ms[kTokW * wave + 4 * g + i] >> c16;
     // S = Q K^T: [token][key], key n-tile nt = keys 16 nt .. +15; the K fragments of the
     // next k-step are read while this one's MFMAs run
-    f32x4 sacc[2][4];
+    f32x4 sacc[4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sacc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 4; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 kf[2][4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) kf[0][nt] = *reinterpret_cast<const bf16x8*>(&Ks[16 * nt + c16][8 * g]);
@@ -255,114 +290,87 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
           kf[(s + 1) & 1][nt] = *reinterpret_cast<const bf16x8*>(&Ks[16 * nt + c16][32 * (s + 1) + 8 * g]);
       }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        sacc[0][nt] = mfma16(qf[0][s], kf[s & 1][nt], sacc[0][nt]);
-        sacc[1][nt] = mfma16(qf[1][s], kf[s & 1][nt], sacc[1][nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt) sacc[nt] = mfma16(qf[s], kf[s & 1][nt], sacc[nt]);
     }
-    // online softmax per token row (log2 units); P to LDS transposed, 4 token rows per 8-byte
-    // store.  O is rescaled only when some row's max moved (wave-uniform test).
     // a tile whose 64 keys every token of the wave selected (the dense rows, most of a short
     // context) needs no masking: a wave-uniform test
-    uint64_t all = ~0ull;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) all &= mw[rt][i];
+    uint64_t all = mw[0] & mw[1] & mw[2] & mw[3];
     constexpr uint64_t kLaneKeys = 0x0001000100010001ull;   // this lane's 4 keys after the shift
     if (__ballot((all & kLaneKeys) != kLaneKeys) == 0) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sacc[rt][nt][i] *= scale_log2;
+        for (int i = 0; i < 4; ++i) sacc[nt][i] *= scale_log2;
     } else {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sacc[rt][nt][i] = ((mw[rt][i] >> (16 * nt)) & 1ull) ? sacc[rt][nt][i] * scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; ++i)
+          sacc[nt][i] = ((mw[i] >> (16 * nt)) & 1ull) ? sacc[nt][i] * scale_log2 : -INFINITY;
     }
-    float alpha[2][4];
-    bool moved = false;
+    // softmax per token row (log2 units) against the row's fixed reference; P to LDS
+    // transposed, 4 token rows per 8-byte store
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = fmaxf(fmaxf(sacc[rt][0][i], sacc[rt][1][i]), fmaxf(sacc[rt][2][i], sacc[rt][3][i]));
-        mx = row16_max(mx);
-        const float mn = fmaxf(m[rt][i], mx);
-        // a row with nothing seen yet keeps mn = -inf: its p are exp2(-inf) = 0 against 0
-        const float ms = (mn == -INFINITY) ? 0.f : mn;
-        alpha[rt][i] = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m[rt][i] - ms);
-        moved |= alpha[rt][i] != 1.f;
-        float ps = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float p = __builtin_amdgcn_exp2f(sacc[rt][nt][i] - ms);
-          sacc[rt][nt][i] = p;
-          ps += p;
-        }
-        l[rt][i] = l[rt][i] * alpha[rt][i] + row16_sum(ps);
-        m[rt][i] = mn;
-      }
+    for (int i = 0; i < 4; ++i) {
+      float mx = max2(max2(sacc[0][i], sacc[1][i]), max2(sacc[2][i], sacc[3][i]));
+      mx = row16_max(mx);
+      // the first valid tile sets the reference; later tiles only check against it (a row
+      // with nothing seen yet keeps -inf, and its p are exp2(-inf) = 0 against 0)
+      if (m[i] == -INFINITY) m[i] = mx;
+      ovf |= mx > m[i] + kSlack;
+      mf[i] = max2(mf[i], mx);
+      const float ms = (m[i] == -INFINITY) ? 0.f : m[i];
+      float ps = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const uint32_t lo = pack_bf16(sacc[rt][nt][0], sacc[rt][nt][1]);
-        const uint32_t hi = pack_bf16(sacc[rt][nt][2], sacc[rt][nt][3]);
-        *reinterpret_cast<uint2*>(&Pt[wave][16 * nt + c16][16 * rt + 4 * g]) = make_uint2(lo, hi);
+        const float p = __builtin_amdgcn_exp2f(sacc[nt][i] - ms);
+        sacc[nt][i] = p;
+        ps += p;
       }
+      l[i] += row16_sum(ps);
     }
-    if (__ballot(moved) != 0) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[rt][vt][i] *= alpha[rt][i];
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint32_t lo = pack_bf16(sacc[nt][0], sacc[nt][1]);
+      const uint32_t hi = pack_bf16(sacc[nt][2], sacc[nt][3]);
+      *reinterpret_cast<uint2*>(&Pt[wave][16 * nt + c16][4 * g]) = make_uint2(lo, hi);
     }
     wave_lds_fence();
-    // O += P V: P fragments (token 16 rt + c16, keys 32 s2 + 8 g .. +7) and V fragments (v dims
+    // O += P V: P fragments (token c16, keys 32 s2 + 8 g .. +7) and V fragments (v dims
     // 16 vt + c16, the same keys), both by transposing reads
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 pa[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const s16x4 lo = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + (c16 >> 2)][16 * rt + 4 * (c16 & 3)]);
-        const s16x4 hi = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + 4 + (c16 >> 2)][16 * rt + 4 * (c16 & 3)]);
+      bf16x8 pa;
+      {
+        const s16x4 lo = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + (c16 >> 2)][4 * (c16 & 3)]);
+        const s16x4 hi = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + 4 + (c16 >> 2)][4 * (c16 & 3)]);
         const short __attribute__((ext_vector_type(8))) p8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        pa[rt] = __builtin_bit_cast(bf16x8, p8);
+        pa = __builtin_bit_cast(bf16x8, p8);
       }
 #pragma unroll
       for (int vt = 0; vt < 8; ++vt) {
         const s16x4 lo = lds_read_tr16(&Vs[32 * s2 + 8 * g + (c16 >> 2)][16 * vt + 4 * (c16 & 3)]);
         const s16x4 hi = lds_read_tr16(&Vs[32 * s2 + 8 * g + 4 + (c16 >> 2)][16 * vt + 4 * (c16 & 3)]);
         const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-        o[0][vt] = mfma16(pa[0], vf, o[0][vt]);
-        o[1][vt] = mfma16(pa[1], vf, o[1][vt]);
+        o[vt] = mfma16(pa, __builtin_bit_cast(bf16x8, v8), o[vt]);
       }
     }
-    __syncthreads();   // Ks / Vs are rewritten next
+  }
+  // a second pass only when some row passed its reference (the vote is also the barrier
+  // after which the second pass may rewrite the tile buffers)
+  if (!__syncthreads_or(ovf)) break;
   }
   // out = O / l (bf16), lse
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + kTokW * wave + 4 * g + i;
+    if (t >= T) continue;
+    const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
+    uint16_t* dst = out + ((int64_t)t * H + h) * kDv + c16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 32 * wave + 16 * rt + 4 * g + i;
-      if (t >= T) continue;
-      const float inv = l[rt][i] > 0.f ? 1.f / l[rt][i] : 0.f;
-      uint16_t* dst = out + ((int64_t)t * H + h) * kDv + c16;
-#pragma unroll
-      for (int vt = 0; vt < 8; ++vt) dst[16 * vt] = f2bf_bits(o[rt][vt][i] * inv);
-      if (lse && c16 == 0)
-        lse[(int64_t)t * H + h] = l[rt][i] > 0.f ? (m[rt][i] + log2f(l[rt][i])) * kLn2 : -INFINITY;
-    }
+    for (int vt = 0; vt < 8; ++vt) dst[16 * vt] = f2bf_bits(o[vt][i] * inv);
+    if (lse && c16 == 0) lse[(int64_t)t * H + h] = l[i] > 0.f ? (m[i] + log2f(l[i])) * kLn2 : -INFINITY;
+  }
 }
 
 }  // namespace
