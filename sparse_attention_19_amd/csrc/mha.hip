@@ -191,7 +191,7 @@ __device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgc
 
 // grid (heads, token tiles) in XCD order: workgroup L runs on XCD L % 8, which takes heads
 // L % 8 (mod 8), each with all its token tiles in a row, so the tiles running together on
-// one XCD read the same head's keys and values from its L2.  8 waves of 16 tokens: every
+// one XCD read the same head's keys and values from its L2 (latest token tile first).  8 waves of 16 tokens: every
 // wave stays within 256 registers, so the two waves of a SIMD hide each other's MFMA, LDS
 // and exp latencies.
 __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
@@ -209,7 +209,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   __shared__ int s_pos;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int L = blockIdx.x, x = L & 7, j = L >> 3;
-  const int h = 8 * (j / tiles) + x, qt = j % tiles;
+  // a head's token tiles go out last first: later tokens see more keys, so the longest
+  // workgroups start first and the short ones fill in behind them
+  const int h = 8 * (j / tiles) + x, qt = tiles - 1 - j % tiles;
   if (h >= H) return;
   const int t0 = kQ * qt;
   const int b = q_row[t0];   // every token of the tile belongs to this request (checked on the host)
