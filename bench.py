@@ -621,7 +621,7 @@ def _fmt_frac(x):
     return "-" if x is None else f"{100 * x:.1f} %"
 
 
-def write_report(results, host, gpu_name, path, gather=None, modes=None):
+def write_report(results, host, gpu_name, path, gather=None, modes=None, hisparse=None):
     L = []
     w = L.append
     w("# DSA hot path on one MI355X: measured report")
@@ -753,6 +753,25 @@ def write_report(results, host, gpu_name, path, gather=None, modes=None):
           f"({rt['memory_ratio_rope_per_head']:.1f}x, the pages' 42x; {rt['memory_ratio']:.1f}x with the rope dims "
           f"kept once), and MQA mode spends {rt['flop_ratio']:.2f}x the FLOPs per query-key pair with GLM-5's "
           f"dims ({rt['flop_ratio_deepseek_dims']:.1f}x with DeepSeek-V3.2's, the pages' 'up to 3.4x').")
+    if hisparse:
+        w("")
+        w("## HBM working set (HiSparse)")
+        w("")
+        w(f"`python bench.py --hisparse`: `{hisparse['workload']}` with every layer's latent cache "
+          f"({hisparse['history_bytes_per_layer'] / 1e9:.2f} GB per layer) in pinned host memory and "
+          f"{hisparse['slots_per_request']} slots per request in HBM ({hisparse['working_set_bytes_per_layer'] / 1e6:.0f} "
+          "MB per layer); the indexer queries drift between steps, so consecutive selections overlap in part.")
+        w("")
+        w("| query drift | rows loaded / selected | step, loads overlapped | loads serialised | every cache in HBM "
+          "| tokens/s (overlapped) | fetch per layer |")
+        w("|---|---|---|---|---|---|---|")
+        for r in hisparse["drifts"]:
+            w(f"| {r['drift']} | {100 * r['load_fraction']:.1f} % | {r['ms_per_step_overlapped']:.3f} ms | "
+              f"{r['ms_per_step_serial']:.3f} ms | {r['ms_per_step_all_in_hbm']:.3f} ms | "
+              f"{r['tokens_per_s_overlapped']:,.0f} | {r['fetch_kernel_us']:.1f} us, {r['fetch_gbs']:.1f} GB/s |")
+        w("")
+        w("The loads over PCIe set the step: the pages' trade of HBM capacity for I/O on top-k misses "
+          "(remio.ai explainer, section HiSparse), here with no other layer work to hide the loads behind.")
     with open(path, "w") as fh:
         fh.write("\n".join(L) + "\n")
 
@@ -776,7 +795,11 @@ def run_report(args):
     print("[report] MLA modes ...", flush=True)
     args.steps = 5
     modes = run_mla_modes(args)
-    write_report(results, host_cpu(), torch.cuda.get_device_name(0), args.report_path, gather, modes)
+    torch.cuda.empty_cache()
+    print("[report] HBM working set ...", flush=True)
+    args.steps, args.warmup, args.config = 20, 5, "indexshare_decode_4layer"
+    hisparse = run_hisparse(args)
+    write_report(results, host_cpu(), torch.cuda.get_device_name(0), args.report_path, gather, modes, hisparse)
     print(f"[report] wrote {args.report_path}", flush=True)
 
 
@@ -806,6 +829,66 @@ def _db(d):
 def _short(name):
     m = re.search(r"dsa::.*?(\w+_kernel)\b", name or "")
     return m.group(1) if m else (name or "")[:40]
+
+
+def summarize_json(args):
+    """Text summary (for profiles/) of the JSON line a --mla-modes, --gather-ceiling or
+    --hisparse run printed (the last JSON line of the file given)."""
+    line = [l for l in open(args.summarize_json) if l.startswith("{")][-1]
+    d = json.loads(line)
+    out = []
+    if d["metric"].startswith("MLA mode time"):
+        out.append("# MLA's two modes on one MI355X: a 2048-token prefill chunk at the end of each context length")
+        out.append(f"# command : {args.command or 'python bench.py --mla-modes --steps 5'}")
+        out.append("# MQA mode: query absorption (gemm_absorb_q + copy of the rope dims), sparse MLA over the latent rows")
+        out.append("#           (mla_bf16_kernel), value up-projection (gemm_unabsorb_o)")
+        out.append("# MHA mode: selection mask (mha_mask_kernel) + masked dense attention over the per-head up-projected")
+        out.append("#           keys and values (mla_mha_kernel); the up-projection of the whole context (gemm_up_project)")
+        out.append("#           is timed on its own; kernel times from HIP events in each dispatch, ms per chunk")
+        out.append(" context   MQA ms   MHA ms  up-proj ms")
+        for r in d["rows"]:
+            out.append(f"{r['context']:8d} {r['mqa_ms']:8.3f} {r['mha_ms']:8.3f} {r['up_project_ms']:11.3f}")
+        rt = d["ratios"]
+        out.append(f"# first context where MQA mode is faster: {d['first_context_where_mqa_wins']} (counting the "
+                   f"context's up-projection: {d['same_counting_the_context_up_projection']})")
+        out.append(f"# per position and layer: MHA cache {rt['mha_cache_bytes_per_position']} B (rope shared) / "
+                   f"{rt['mha_bytes_with_rope_per_head']} B (rope per head) against {rt['latent_bytes_per_position']} B "
+                   f"of latent -> {rt['memory_ratio']:.1f}x / {rt['memory_ratio_rope_per_head']:.1f}x")
+        out.append(f"# FLOP per (query, key, head): MQA {rt['mqa_flop_per_pair']}, MHA {rt['mha_flop_per_pair']} -> "
+                   f"{rt['flop_ratio']:.2f}x (DeepSeek-V3.2's 128 + 64 / 128 dims: {rt['flop_ratio_deepseek_dims']:.2f}x)")
+    elif d["metric"].startswith("random 1152-byte row gather"):
+        out.append("# Random 1152-byte row gather ceiling of one MI355X (measurement aid, not part of the method)")
+        out.append(f"# command        : {args.command or 'python bench.py --gather-ceiling --steps 7'}")
+        out.append(f"# what it runs   : dsa_probe_row_gather over {d['list_rows']} uniform random rows "
+                   f"({d['bytes_per_launch'] / 1e9:.2f} GB per launch), median launch time from HIP events in the")
+        out.append("#                  dispatch; 'MLA loads' = the sparse MLA's own load pattern (16 B per lane of 16 rows")
+        out.append("#                  per instruction, half a 128-byte line per row), 'whole lines' = 8 rows x 128 B")
+        out.append("        pool   MLA loads GB/s   whole lines GB/s  what")
+        for q in d["pools"]:
+            out.append(f"{q['pool_bytes'] / 2**20:10.1f}MB {q['mla_loads']['gbs']:16.1f} {q['whole_lines']['gbs']:18.1f}  "
+                       f"{q['what']}")
+    elif d["metric"].startswith("decode tokens/s with latent caches in pinned host memory"):
+        out.append("# Decode through an HBM working set of latent rows (every layer's latent cache in pinned host memory)")
+        out.append(f"# command : {args.command or 'python bench.py --hisparse --steps 20 --warmup 5'}")
+        out.append(f"# workload: {d['workload']}, one selection per step shared by the IndexShare group; the indexer")
+        out.append("#           queries drift between steps (a fraction of their entries drawn again);")
+        out.append(f"#           {d['slots_per_request']} working-set slots per request: "
+                   f"{d['working_set_bytes_per_layer'] / 1e6:.1f} MB of HBM per layer against "
+                   f"{d['history_bytes_per_layer'] / 1e9:.2f} GB of history per layer in pinned host memory")
+        out.append("# timed   : torch events around the steps; kernel times from HIP events in each dispatch")
+        out.append("#           (dsa_timing_*) over the same steps run again")
+        out.append(" drift  loaded/selected  rows/step/layer  all-in-HBM ms  overlapped ms  serial ms  fetch us/layer  fetch GB/s")
+        for r in d["drifts"]:
+            out.append(f"{r['drift']:6.3f}  {r['load_fraction'] * 100:14.1f} %  {r['rows_loaded_per_step']:15.0f}  "
+                       f"{r['ms_per_step_all_in_hbm']:13.3f}  {r['ms_per_step_overlapped']:13.3f}  "
+                       f"{r['ms_per_step_serial']:9.3f}  {r['fetch_kernel_us']:14.1f}  {r['fetch_gbs']:10.1f}")
+        out.append("# per-kernel us per launch (overlapped mode):")
+        for r in d["drifts"]:
+            out.append(f"#   drift {r['drift']}: " + ", ".join(f"{k} {v}" for k, v in r["kernels_us_per_launch"].items()))
+    else:
+        raise SystemExit(f"no summary for metric {d['metric']!r}")
+    out.append("JSON " + line.strip())
+    print("\n".join(out))
 
 
 def summarize_trace(args):
@@ -929,6 +1012,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-traffic", action="store_true")
     ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--summarize-json", metavar="FILE", help="text summary of a --mla-modes / --gather-ceiling / "
+                    "--hisparse output")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     ap.add_argument("--kernel")
@@ -948,6 +1033,8 @@ def main():
         return summarize_traffic(args)
     if args.summarize_counters:
         return summarize_counters(args)
+    if args.summarize_json:
+        return summarize_json(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures "
               f"the path on one MI355X; how it would shard over several is described, not run.",
