@@ -153,3 +153,38 @@ def test_decode_through_working_set(overlap):
     assert total_loads[0] == sum(min(n, k) for n in lens)
     assert all(x < total_loads[0] for x in total_loads[1:])
     log(f"[gpu] rows loaded per step: {total_loads}")
+
+
+def test_working_set_many_requests_small_k():
+    """300 requests (more than the fetch's 256 workgroups spread over requests), k = 64 and the
+    smallest working set (k + 64 slots): plan against the oracle, attention through the
+    working set against the all-HBM path, over three steps."""
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], batch=300, ctx_range=(40, 700), k=64, seed=43)
+    inp = I.make_inputs(cfg, DEV)
+    T, k, slots = inp["q_idx"].shape[0], cfg.k, 128
+    pt = P.page_table(inp)
+    ld = inp["block_table"].shape[1] * 64
+    host = torch.empty(inp["kv_pools"][0].shape, dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(inp["kv_pools"][0])
+    wb = P.alloc_working_set(T, slots, ld, k, 1, cfg.row_dim, cfg.dtype, DEV, overlap=False)
+    ref = P.alloc_buffers(T, ld, k, cfg.H, cfg.Dl, 1, cfg.dtype, DEV)
+    buf = P.alloc_buffers(T, ld, k, cfg.H, cfg.Dl, 1, cfg.dtype, DEV)
+    states = [O.working_set_init(slots) for _ in range(T)]
+    lens = inp["seq_len_host"].tolist()
+    q0 = inp["q_idx"]
+    for step in range(3):
+        log(f"[gpu] 300 requests through a {slots}-slot working set, step {step}")
+        q = q0 if step == 0 else I.drift_queries(q0, 0.05 * step, seed=50 + step)
+        inp["q_idx"] = q
+        P.decode_step(q, inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], pt, k, cfg.sm_scale, ref)
+        P.decode_step_working_set(q, inp["w"], inp["k_pool"], [host], inp["q"], pt, k, cfg.sm_scale, buf, wb)
+        torch.cuda.synchronize()
+        # the oracle's own selection drives its working set
+        sel = torch.from_numpy(np.stack([R.expected_token(inp, t, layers=[])["idx"] for t in range(T)]))
+        assert torch.equal(buf.idx.cpu(), sel)
+        check_state(wb.ws, states, sel, wb.slot_idx, wb.loads, wb.load_count, step)
+        sparse = torch.tensor([n > k for n in lens], device=DEV)
+        assert torch.equal(buf.outs[0][sparse], ref.outs[0][sparse])
+        assert torch.equal(buf.lses[0][sparse], ref.lses[0][sparse])
+        got, want = R.to_f64(buf.outs[0][~sparse].reshape(-1, cfg.Dl)), R.to_f64(ref.outs[0][~sparse].reshape(-1, cfg.Dl))
+        assert float((np.abs(got - want).max(1) / np.abs(want).max(1)).max()) <= 2e-2
