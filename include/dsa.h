@@ -328,7 +328,8 @@ dsa_status dsa_index_cache_get(const dsa_index_cache* c, uint64_t step, int32_t 
  * one working set must be ordered on the stream(s); the plan is not re-entrant.
  * DSA_ERR_INVALID for NULL pointers, bad sizes, host_kv not in pinned host memory (checked
  * with hipPointerGetAttributes) or a device pool too small; DSA_ERR_UNSUPPORTED outside
- * the limits.
+ * the limits, or when the GPU maps the pinned history at an address other than its host
+ * address (the fetch reads it at the host address).
  */
 typedef struct {
   int32_t* slot_of;   /* device [batch][max_len] */

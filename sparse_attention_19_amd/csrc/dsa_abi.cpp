@@ -615,7 +615,13 @@ dsa_status dsa_working_set_fetch(const dsa_working_set* ws, const dsa_pool* host
   }
   if (attr.type != hipMemoryTypeHost || !attr.devicePointer)
     return fail(DSA_ERR_INVALID, "host_kv: not pinned host memory (memory type %d)", (int)attr.type);
-  return launched(dsa::launch_ws_fetch(ws_args(ws), attr.devicePointer, host_kv->num_blocks, pt->block_table,
+  // the kernel reads the history at its host address: pinned memory the GPU maps at the same
+  // address (as the runtime reports it for the queried pointer or for its allocation)
+  const bool same_address = attr.devicePointer == host_kv->data ||
+                            (attr.hostPointer != nullptr && attr.hostPointer == attr.devicePointer);
+  if (!same_address)
+    return fail(DSA_ERR_UNSUPPORTED, "host_kv: pinned memory the GPU maps at another address");
+  return launched(dsa::launch_ws_fetch(ws_args(ws), host_kv->data, host_kv->num_blocks, pt->block_table,
                                        pt->max_blocks, loads, load_count, k, dev_kv->data, (hipStream_t)stream),
                   "working-set fetch launch");
 }
