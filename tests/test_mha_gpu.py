@@ -173,3 +173,26 @@ def test_projections_against_float64():
     want_kv = np.concatenate([np.einsum("rc,hcj->rhj", lat[:, :512], wuk), np.einsum("rc,hcv->rhv", lat[:, :512], wuv)],
                              axis=2)
     assert rel_rows(f(kv_mha).reshape(-1, 320), want_kv.reshape(-1, 320)) <= 1e-2
+
+
+def test_128_heads_both_modes():
+    """DeepSeek-V3.2's 128 heads: MHA mode and MQA mode (two 64-head groups of the sparse
+    MLA between the projections) against the oracle, and against each other."""
+    inp = mha_inputs(ctx=2300, T=200, H=128, seed=24)
+    T, H = 200, 128
+    pt, ch, idx = select(inp)
+    kv_mha = up_projected(inp)
+    ws = D.workspace(D.DSA_OP_MLA_HEADS, T, 2300, 2048, H, 512, DEV)
+    outs = {}
+    for thr, want in ((1 << 20, 1), (0, 0)):
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+        mode = D.dsa_mla_prefill_heads(inp["q_mha"], inp["w_uk"], inp["w_kv"], inp["kv_pools"][0], kv_mha, pt, ch,
+                                       idx, 2048, 1.0 / 16, thr, out, lse, ws=ws)
+        torch.cuda.synchronize()
+        assert mode == want
+        log(f"[gpu] 128 heads, mode {mode}")
+        check(inp, out, lse, [0, 63, 64, 127, 128, 199], [0, 1, 63, 64, 65, 127], idx)
+        outs[mode] = out
+    a, b = R.to_f64(outs[1].reshape(-1, 128)), R.to_f64(outs[0].reshape(-1, 128))
+    assert rel_rows(a, b) <= 2e-2
