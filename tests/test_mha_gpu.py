@@ -196,3 +196,20 @@ def test_128_heads_both_modes():
         outs[mode] = out
     a, b = R.to_f64(outs[1].reshape(-1, 128)), R.to_f64(outs[0].reshape(-1, 128))
     assert rel_rows(a, b) <= 2e-2
+
+
+def test_mha_mode_at_its_longest_context():
+    """The longest context MHA mode takes (65536 positions, 1024 mask words per token): a
+    128-token tile at the end of it, checked on a few tokens and heads."""
+    inp = mha_inputs(ctx=65536, T=128, seed=25)
+    T, H = 128, 64
+    pt, ch, idx = select(inp)
+    kv_mha = up_projected(inp)
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    ws = D.workspace(D.DSA_OP_MLA_MHA, T, 65536, 2048, H, 512, DEV)
+    D.dsa_sparse_mla_prefill_mha(inp["q_mha"], inp["kv_pools"][0], kv_mha, pt, ch, idx, 2048, 1.0 / 16, out, lse, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    log("[gpu] MHA mode at 65536 positions")
+    check(inp, out, lse, [0, 77, 127], [0, 31, 63], idx)
