@@ -15,13 +15,16 @@
 //
 // mha_mask_kernel: one workgroup per token turns its selection list into a bitmask of
 // ceil(len / 64) 64-bit words (word w, bit b: position 64w + b).
-// mla_mha_kernel: one workgroup per (128 tokens of one request, head); 8 waves of 16 tokens
-// (one 16-row tile on 16x16x32 MFMAs, two waves per SIMD); per 64-key tile, K [64][256] and V [64][128] are
-// staged in double-buffered LDS (the next tile's loads in flight in registers), S = Q K^T
-// with the next k-step's K fragments read ahead, mask (skipped for tiles every token of the
-// wave selected whole), online softmax (row reductions on DPP; a row's reference max moves
-// only when passed by more than 2^8, so O is rarely rescaled), P through LDS transposed,
-// O += P V with the P and V fragments read transposed (ds_read_b64_tr_b16).
+// mla_mha_kernel: one workgroup per (128 tokens of one request, head); 8 waves, each 32 tokens
+// x one half (32 keys) of every 64-key tile, on 32x32x16 MFMAs.  Per tile, K [64][256] and
+// V [64][128] are staged in double-buffered LDS (the next tile's loads in flight in
+// registers).  A wave computes S^T = K Q^T (keys x tokens, Q^T held in registers), so each
+// lane holds one token's logits: the mask, the softmax row statistics (within the lane plus
+// one swap with the other half of the wave) and P never leave the registers, and P feeds
+// O^T += V^T P^T as the B operand directly, with V^T read transposed (ds_read_b64_tr_b16).
+// A row's reference max moves only when passed by more than 2^32, so O is never rescaled
+// inside the loop.  The two key halves of a token are two splits of its softmax, merged at
+// the end through LDS.
 #include <math.h>
 
 #include "common.h"
@@ -35,13 +38,15 @@ constexpr int kDl = 512, kDn = 192, kDr = 64, kDqk = 256, kDv = 128, kDkv = 320;
 constexpr int kQ = 128;              // query tokens per workgroup
 constexpr int kKeys = 64;            // keys per tile (one page)
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kTokW = kQ / kWaves;   // query tokens per wave (one 16-row MFMA tile)
+constexpr int kTokW = 32;            // query tokens per wave (the 32 columns of its MFMA tiles)
+constexpr int kKeyW = 32;            // keys of each tile per wave (its half of the tile)
 constexpr int kKLoads = kKeys * (kDqk / 8) / kThreads;   // 16-byte K chunks per thread per tile (4)
 constexpr int kVLoads = kKeys * (kDv / 8) / kThreads;    // and V chunks (2)
-constexpr int kKRow = kDqk + 8;      // LDS K row, elements (528 bytes)
-constexpr int kVRow = kDv + 8;       // LDS V row, elements (272 bytes)
-constexpr int kPtRow = kTokW + 8;    // LDS row of P transposed (a key's 16 tokens), elements (48 bytes)
-static_assert(kTokW == 16, "one 16-row MFMA tile per wave");
+// LDS rows: K 528 bytes (132 words: the 8 rows of a 16-byte read group start 4 banks
+// apart), V 288 bytes (72 words: the 4 rows of a transposing read group start 8 banks apart)
+constexpr int kKRow = kDqk + 8;
+constexpr int kVRow = kDv + 16;
+static_assert(kQ == (kWaves / 2) * kTokW && kKeys == 2 * kKeyW, "wave = 32 tokens x half of a tile");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A row's reference max is its first valid tile's max and stays fixed: probabilities up to
@@ -157,43 +162,33 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), h2));
 }
 
-// Max / sum over the 16 lanes of a row (lanes with the same lane / 16), in every lane: DPP
-// row rotations, no LDS.
-// Each step is one VALU instruction with a DPP row rotation of its first operand (row
-// rotations read and write every lane of the row).  Written as inline asm: the compiler
-// splits fmaxf over a DPP value into a lane move, a NaN-quieting max and the max.  The
-// s_nop gives the two wait states a DPP read needs after a VALU write of its source.
-#define DSA_DPP_STEP(op, v, n)                                                                      \
-  {                                                                                                \
-    float t_;                                                                                      \
-    asm volatile("s_nop 1\n\t" op " %0, %1, %1 row_ror:" #n " row_mask:0xf bank_mask:0xf"         \
-                 : "=v"(t_)                                                                        \
-                 : "v"(v));                                                                        \
-    v = t_;                                                                                        \
-  }
-__device__ __forceinline__ float row16_max(float v) {
-  DSA_DPP_STEP("v_max_f32_dpp", v, 1)
-  DSA_DPP_STEP("v_max_f32_dpp", v, 2)
-  DSA_DPP_STEP("v_max_f32_dpp", v, 4)
-  DSA_DPP_STEP("v_max_f32_dpp", v, 8)
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  DSA_DPP_STEP("v_add_f32_dpp", v, 1)
-  DSA_DPP_STEP("v_add_f32_dpp", v, 2)
-  DSA_DPP_STEP("v_add_f32_dpp", v, 4)
-  DSA_DPP_STEP("v_add_f32_dpp", v, 8)
-  return v;
-}
-#undef DSA_DPP_STEP
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 
+// Max / sum of a lane's value and the same lane's in the other half of the wave (lanes l and
+// l ^ 32 hold the same token), in both: one permlane32 swap.  Both halves add or compare the
+// same two values, so they end with the same result.
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // grid (heads, token tiles) in XCD order: workgroup L runs on XCD L % 8, which takes heads
 // L % 8 (mod 8), each with all its token tiles in a row, so the tiles running together on
-// one XCD read the same head's keys and values from its L2 (latest token tile first).  8 waves of 16 tokens: every
-// wave stays within 256 registers, so the two waves of a SIMD hide each other's MFMA, LDS
-// and exp latencies.
+// one XCD read the same head's keys and values from its L2 (latest token tile first).
+// Wave w: tokens 32 (w / 2) .. +31 of the workgroup's 128, keys 32 (w % 2) .. +31 of every
+// tile; lane l: token 32 (w / 2) + l % 32, lane half hb = l / 32.  Every wave stays within
+// 256 registers, so the two waves of a SIMD hide each other's MFMA, LDS and exp latencies.
+//   S^T (32 keys x 32 tokens): A = K rows from LDS (lane: key l % 32, dims 16 s + 8 hb ..
+//     +7 of k-step s), B = Q^T (lane: token l % 32, the same dims); C slot r of lane l is key
+//     8 (r / 4) + 4 hb + r % 4 of the wave's half, token l % 32.
+//   O^T (128 dims x 32 tokens) += V^T P^T per 16-key step p: B = P^T straight from the
+//     softmax (slots 8p .. 8p + 7 of the lane, i.e. keys 16 p + 8 (j / 4) + 4 hb + j % 4 for
+//     B slot j), A = V^T (lane: dim l % 32 of the 32-dim tile, the same keys) from two
+//     transposing reads; C slot r of lane l is dim 8 (r / 4) + 4 hb + r % 4, token l % 32.
 __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ lat,
     int64_t num_blocks, const int* __restrict__ block_table, int max_blocks, const int* __restrict__ q_row,
@@ -201,13 +196,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   // K, V and the mask words are double-buffered (tile kt in buffer kt % 2), so one barrier
   // per tile separates a buffer's stores from its readers and its readers from its next
-  // stores two tiles later
+  // stores two tiles later.  After the loop the K buffers hold the second key half's O^T.
   __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kKeys][kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t Vs2[2][kKeys][kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Pt[kWaves][kKeys][kPtRow];   // per wave: P transposed [key][token]
   __shared__ uint64_t Ms2[2][kQ];   // the tile's mask word of each of the workgroup's tokens
+  __shared__ float s_ml[kWaves / 2][2][kTokW];   // the second key half's (reference max, sum)
   __shared__ int s_pos;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  static_assert(sizeof(Ks2) >= (size_t)(kWaves / 2) * 64 * 64 * sizeof(float), "O^T exchange fits");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tg = wave >> 1, kh = wave & 1, c = lane & 31, hb = lane >> 5;
   const int L = blockIdx.x, x = L & 7, j = L >> 3;
   // a head's token tiles go out last first: later tokens see more keys, so the longest
   // workgroups start first and the short ones fill in behind them
@@ -224,23 +221,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   const int* bt_row = block_table + (int64_t)b * max_blocks;
   const gbytes kvg = (gbytes)kv, latg = (gbytes)lat;
 
-  // Q fragments of the wave's 16 tokens, k-step s: token 16 wave + c16, dims 32 s + 8 g .. +7
-  bf16x8 qf[8];
+  // Q^T fragments (B operand) of k-step s: token t0 + 32 tg + c, dims 16 s + 8 hb .. +7
+  bf16x8 qf[16];
   {
-    const int t = min(t0 + kTokW * wave + c16, T - 1);
-    const uint16_t* src = q + ((int64_t)t * H + h) * kDqk + 8 * g;
+    const int t = min(t0 + kTokW * tg + c, T - 1);
+    const uint16_t* src = q + ((int64_t)t * H + h) * kDqk + 8 * hb;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(src + 32 * s);
+    for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
   }
-  // this lane's C rows: token 16 wave + 4 g + i; m = the row's reference max (log2 units),
-  // mf = its largest logit so far
-  float m[4], mf[4], l[4];
-  f32x4 o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    mf[i] = -INFINITY;
-  }
+  // the lane's token, over this wave's key half: m = reference max (log2 units), mf = the
+  // largest logit so far, l = sum of p against m
+  float m = -INFINITY, mf = -INFINITY, l = 0.f;
+  f32x16 o[4];   // O^T, dims 32 dt .. +31
+  // per-lane LDS element offsets: the K rows of the A operand, and the transposing V reads
+  // (lane a = l % 16 of its 16-lane group reads key 4 hb + a / 4 (+ 8, + 16 p), dims
+  // 16 (c / 16) + 4 (a % 4) .. +3 (+ 32 dt) of the wave's key half)
+  const int k_off = (kKeyW * kh + c) * kKRow + 8 * hb;
+  const int v_off = (kKeyW * kh + 4 * hb + ((c & 15) >> 2)) * kVRow + 16 * (c >> 4) + 4 * (c & 3);
   auto tile_row0 = [&](int kt, bool& ok) {
     const int phys = bt_row[kt];
     ok = phys >= 0 && phys < num_blocks;
@@ -251,14 +248,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   bool ok;
   int64_t row0;
   for (int pass = 0; pass < 2; ++pass) {
-  bool ovf = false;   // some row of this lane passed its reference max by more than kSlack
+  bool ovf = false;   // the lane's token passed its reference max by more than kSlack
+  if (pass == 1) m = mf;   // the second pass starts from the final max
+  l = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (pass == 1) m[i] = mf[i];   // the second pass starts from the final max
-    l[i] = 0.f;
-  }
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-  for (int vt = 0; vt < 8; ++vt) o[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   row0 = tile_row0(0, ok);
   load_mha_tile(r, ad, row0, ok, 0, t0, T, s_pos);
   for (int kt = 0; kt < ntiles; ++kt) {
@@ -271,90 +267,63 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
       row0 = tile_row0(kt + 1, ok);
       load_mha_tile(r, ad, row0, ok, kt + 1, t0, T, s_pos);
     }
-    // this lane's mask words (token rows 16 wave + 4 g + i), pre-shifted to its key column
-    // c16: bit 16 nt is key 16 nt + c16
-    uint64_t mw[4];
+    // the token's mask bits for this wave's keys, shifted so that C slot r (key
+    // 8 (r / 4) + 4 hb + r % 4 of the half) is bit 8 (r / 4) + r % 4
+    const uint32_t mw = (uint32_t)(Ms[kTokW * tg + c] >> (kKeyW * kh + 4 * hb));
+    // S^T, one accumulator chain (the SIMD's other wave supplies a second); the K
+    // fragments of the next k-step are read while this one's MFMA runs
+    const uint16_t* kp = &Ks[0][0] + k_off;
+    f32x16 sa;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mw[i] = Ms[kTokW * wave + 4 * g + i] >> c16;
-    // S = Q K^T: [token][key], key n-tile nt = keys 16 nt .. +15; the K fragments of the
-    // next k-step are read while this one's MFMAs run
-    f32x4 sacc[4];
+    for (int i = 0; i < 16; ++i) sa[i] = 0.f;
+    bf16x8 ka[2];
+    ka[0] = *reinterpret_cast<const bf16x8*>(kp);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) kf[0][nt] = *reinterpret_cast<const bf16x8*>(&Ks[16 * nt + c16][8 * g]);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (s + 1 < 8) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          kf[(s + 1) & 1][nt] = *reinterpret_cast<const bf16x8*>(&Ks[16 * nt + c16][32 * (s + 1) + 8 * g]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sacc[nt] = mfma16(qf[s], kf[s & 1][nt], sacc[nt]);
+    for (int s = 0; s < 16; ++s) {
+      if (s + 1 < 16) ka[(s + 1) & 1] = *reinterpret_cast<const bf16x8*>(kp + 16 * (s + 1));
+      sa = mfma32(ka[s & 1], qf[s], sa);
     }
-    // a tile whose 64 keys every token of the wave selected (the dense rows, most of a short
-    // context) needs no masking: a wave-uniform test
-    uint64_t all = mw[0] & mw[1] & mw[2] & mw[3];
-    constexpr uint64_t kLaneKeys = 0x0001000100010001ull;   // this lane's 4 keys after the shift
-    if (__ballot((all & kLaneKeys) != kLaneKeys) == 0) {
+    // a tile half whose 32 keys every token of the wave selected (the dense rows, most of a
+    // short context) needs no masking: a wave-uniform test
+    float xs[16];
+    if (__ballot((mw & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) == 0) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[nt][i] *= scale_log2;
+      for (int i = 0; i < 16; ++i) xs[i] = sa[i] * scale_log2;
     } else {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sacc[nt][i] = ((mw[i] >> (16 * nt)) & 1ull) ? sacc[nt][i] * scale_log2 : -INFINITY;
+      for (int i = 0; i < 16; ++i)
+        xs[i] = ((mw >> (8 * (i >> 2) + (i & 3))) & 1u) ? sa[i] * scale_log2 : -INFINITY;
     }
-    // softmax per token row (log2 units) against the row's fixed reference; P to LDS
-    // transposed, 4 token rows per 8-byte store
+    // softmax of the lane's token against its fixed reference (the first tile with a valid
+    // key sets it; a token with nothing seen yet keeps -inf, and its p are exp2(-inf) = 0)
+    float mx = xs[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = max2(max2(sacc[0][i], sacc[1][i]), max2(sacc[2][i], sacc[3][i]));
-      mx = row16_max(mx);
-      // the first valid tile sets the reference; later tiles only check against it (a row
-      // with nothing seen yet keeps -inf, and its p are exp2(-inf) = 0 against 0)
-      if (m[i] == -INFINITY) m[i] = mx;
-      ovf |= mx > m[i] + kSlack;
-      mf[i] = max2(mf[i], mx);
-      const float ms = (m[i] == -INFINITY) ? 0.f : m[i];
-      float ps = 0.f;
+    for (int i = 1; i < 16; ++i) mx = max2(mx, xs[i]);
+    mx = half_max(mx);
+    if (m == -INFINITY) m = mx;
+    ovf |= mx > m + kSlack;
+    mf = max2(mf, mx);
+    const float ms = (m == -INFINITY) ? 0.f : m;
+    float ps = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float p = __builtin_amdgcn_exp2f(sacc[nt][i] - ms);
-        sacc[nt][i] = p;
-        ps += p;
-      }
-      l[i] += row16_sum(ps);
+    for (int i = 0; i < 16; ++i) {
+      xs[i] = __builtin_amdgcn_exp2f(xs[i] - ms);
+      ps += xs[i];
     }
+    l += half_sum(ps);
+    // O^T += V^T P^T, 16 keys per step
+    const uint16_t* vp = &Vs[0][0] + v_off;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint32_t lo = pack_bf16(sacc[nt][0], sacc[nt][1]);
-      const uint32_t hi = pack_bf16(sacc[nt][2], sacc[nt][3]);
-      *reinterpret_cast<uint2*>(&Pt[wave][16 * nt + c16][4 * g]) = make_uint2(lo, hi);
-    }
-    wave_lds_fence();
-    // O += P V: P fragments (token c16, keys 32 s2 + 8 g .. +7) and V fragments (v dims
-    // 16 vt + c16, the same keys), both by transposing reads
+    for (int p = 0; p < 2; ++p) {
+      const u32x4 pw = {pack_bf16(xs[8 * p], xs[8 * p + 1]), pack_bf16(xs[8 * p + 2], xs[8 * p + 3]),
+                        pack_bf16(xs[8 * p + 4], xs[8 * p + 5]), pack_bf16(xs[8 * p + 6], xs[8 * p + 7])};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 pa;
-      {
-        const s16x4 lo = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + (c16 >> 2)][4 * (c16 & 3)]);
-        const s16x4 hi = lds_read_tr16(&Pt[wave][32 * s2 + 8 * g + 4 + (c16 >> 2)][4 * (c16 & 3)]);
-        const short __attribute__((ext_vector_type(8))) p8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        pa = __builtin_bit_cast(bf16x8, p8);
-      }
-#pragma unroll
-      for (int vt = 0; vt < 8; ++vt) {
-        const s16x4 lo = lds_read_tr16(&Vs[32 * s2 + 8 * g + (c16 >> 2)][16 * vt + 4 * (c16 & 3)]);
-        const s16x4 hi = lds_read_tr16(&Vs[32 * s2 + 8 * g + 4 + (c16 >> 2)][16 * vt + 4 * (c16 & 3)]);
+      for (int dt = 0; dt < 4; ++dt) {
+        const s16x4 lo = lds_read_tr16(vp + 16 * p * kVRow + 32 * dt);
+        const s16x4 hi = lds_read_tr16(vp + (16 * p + 8) * kVRow + 32 * dt);
         const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[vt] = mfma16(pa, __builtin_bit_cast(bf16x8, v8), o[vt]);
+        o[dt] = mfma32(__builtin_bit_cast(bf16x8, v8), pb, o[dt]);
       }
     }
   }
@@ -362,17 +331,44 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   // after which the second pass may rewrite the tile buffers)
   if (!__syncthreads_or(ovf)) break;
   }
-  // out = O / l (bf16), lse
+  // merge the two key halves of every token: the second half's (m, l, O^T) through LDS
+  // (lane-major, conflict-free), then out = (O0 2^(m0 - M) + O1 2^(m1 - M)) / L as bf16
+  float* xo = reinterpret_cast<float*>(&Ks2[0][0][0]) + tg * (64 * 64);
+  if (kh == 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + kTokW * wave + 4 * g + i;
-    if (t >= T) continue;
-    const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
-    uint16_t* dst = out + ((int64_t)t * H + h) * kDv + c16;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int vt = 0; vt < 8; ++vt) dst[16 * vt] = f2bf_bits(o[vt][i] * inv);
-    if (lse && c16 == 0) lse[(int64_t)t * H + h] = l[i] > 0.f ? (m[i] + log2f(l[i])) * kLn2 : -INFINITY;
+      for (int i = 0; i < 16; ++i) xo[(16 * dt + i) * 64 + lane] = o[dt][i];
+    if (hb == 0) {
+      s_ml[tg][0][c] = m;
+      s_ml[tg][1][c] = l;
+    }
   }
+  __syncthreads();
+  if (kh == 1) return;
+  const int t = t0 + kTokW * tg + c;
+  if (t >= T) return;
+  const float m1 = s_ml[tg][0][c], l1 = s_ml[tg][1][c];
+  const float M = max2(m, m1);
+  const float w0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  const float w1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+  const float Lsum = l * w0 + l1 * w1;
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  const float a0 = w0 * inv, a1 = w1 * inv;
+  uint16_t* dst = out + ((int64_t)t * H + h) * kDv + 4 * hb;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r_ = 4 * qq + i;
+        v[i] = o[dt][r_] * a0 + xo[(16 * dt + r_) * 64 + lane] * a1;
+      }
+      *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * qq) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    }
+  if (lse && hb == 0) lse[(int64_t)t * H + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

@@ -213,3 +213,51 @@ def test_mha_mode_at_its_longest_context():
     assert torch.isfinite(out.float()).all()
     log("[gpu] MHA mode at 65536 positions")
     check(inp, out, lse, [0, 77, 127], [0, 31, 63], idx)
+
+
+def test_mha_mode_reference_max_moves_late():
+    """Latent rows of the context's second half scaled up 12x: a token's logits there (about
+    60, log2 units) pass the reference max its first tile sets (about 5) by more than 32, so
+    the kernel runs its second pass from each row's final max.  The up-projections are
+    selection matrices (each NoPE key and value dim copies one latent dim), so the bf16
+    per-head cache holds exactly the keys and values the oracle forms in float64: with logits
+    this large, a rounded key would move p by several percent and the comparison would test
+    the cache's rounding instead of the kernel."""
+    inp = mha_inputs(ctx=3000, T=256, seed=26)
+    T, H, ctx = 256, 64, 3000
+    g = torch.Generator().manual_seed(27)
+    wuk = torch.zeros((H, 512, 192))
+    wuv = torch.zeros((H, 512, 128))
+    for h in range(H):
+        d = torch.randperm(512, generator=g)
+        wuk[h, d[:192], torch.arange(192)] = 1.0
+        wuv[h, d[192:320], torch.arange(128)] = 1.0
+    inp["w_uk"] = wuk.to(torch.bfloat16).to(DEV)
+    inp["w_uv"] = wuv.to(torch.bfloat16).to(DEV)
+    inp["w_kv"] = torch.cat([inp["w_uk"].transpose(1, 2), inp["w_uv"].transpose(1, 2)], dim=1).contiguous()
+    pool = inp["kv_pools"][0]
+    bt = inp["block_table"].cpu()
+    pages = sorted({int(bt[0, j]) for j in range((ctx // 2) // 64 + 1, (ctx + 63) // 64)})
+    sel = torch.tensor(pages, dtype=torch.long, device=DEV)
+    pool[sel] = (pool[sel].float() * 12).to(pool.dtype)
+    pt, ch, idx = select(inp)
+    # the case is real: token 0, head 0 (float64, from the inputs, over the oracle's
+    # selection) -- its largest logit over the scaled pages against its largest over the
+    # unscaled first half, which bounds the reference max its first tiles set
+    lat = R.to_f64(pool).reshape(-1, 576)
+    pos = np.asarray(R.expected_token_mha(inp, 0, [0])["idx"])
+    rows = [int(bt[0, s // 64]) * 64 + s % 64 for s in pos.tolist()]
+    k_nope = lat[rows, :512] @ R.to_f64(inp["w_uk"][0])
+    q0 = R.to_f64(inp["q_mha"][0, 0])
+    lg = (k_nope @ q0[:192] + lat[rows, 512:] @ q0[192:]) / 16 * np.log2(np.e)
+    assert lg[pos >= (ctx // 2 // 64 + 1) * 64].max() > lg[pos < ctx // 2].max() + 32
+    kv_mha = up_projected(inp)
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    ws = D.workspace(D.DSA_OP_MLA_MHA, T, ctx, 2048, H, 512, DEV)
+    D.dsa_sparse_mla_prefill_mha(inp["q_mha"], pool, kv_mha, pt, ch, idx, 2048, 1.0 / 16, out, lse, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    log(f"[gpu] MHA mode, late max: {len(pages)} scaled pages")
+    check(inp, out, lse, range(0, T, 3), [0, 17, 63], idx)
+    check(inp, out, lse, [0, 129, 255], list(range(H)))
