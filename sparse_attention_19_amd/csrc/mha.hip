@@ -78,13 +78,16 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int* __restrict__ i
     mask[(int64_t)t * words + w] = (uint64_t)bits[2 * w] | ((uint64_t)bits[2 * w + 1] << 32);
 }
 
-// One key tile in registers: K chunks (16 B) id = tid + 512 i, i < 4: key id / 32, chunk
-// id % 32 (chunks < 24 from the up-projected NoPE keys, the rest from the latent row's rope
-// dims); V chunks id = tid + 512 i, i < 2: key id / 16, chunk id % 16; and (threads below
-// 128) the selection mask word of token tid for the tile.
+// One key tile in registers: K chunks (16 B) -- loads i < 3 take NoPE chunk id = tid + 512 i
+// (key id / 24, chunk id % 24) from the up-projected cache, load 3 takes rope chunk tid (key
+// tid / 8, chunk tid % 8) from the latent row; V chunks id = tid + 512 i, i < 2: key id / 16,
+// chunk id % 16; and (threads below 128) the selection mask word of token tid for the tile.
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 typedef const __attribute__((address_space(1))) u32x4* gu32x4;
 typedef const __attribute__((address_space(1))) uint64_t* gu64;
+constexpr int kNopeChunks = kDn / 8;   // 24
+static_assert(kKeys * kNopeChunks == 3 * kThreads && kKeys * (kDr / 8) == kThreads && kKLoads == 4,
+              "K tile: three NoPE loads and one rope load per thread");
 
 struct MhaTile {
   u32x4 k[kKLoads], v[kVLoads];
@@ -92,47 +95,45 @@ struct MhaTile {
   int last;   // the tile's last key any token sees (-1: none)
 };
 
-// Per-thread load addresses, fixed for the whole kernel: the thread's chunk of key 0 of
-// page 0 and the byte strides from there (per key row of the page, per page row).  The
-// chunk of K a thread loads is fixed (tid % 32), so is whether it comes from kv_mha or from
-// the latent pool.
+// Per-thread byte offsets of the thread's chunks within a page of the up-projected cache
+// (NoPE, V) or of the latent pool (rope), fixed for the whole kernel: a tile's loads are the
+// page's base (workgroup-uniform, in scalar registers) plus these 32-bit offsets.
 struct MhaAddr {
-  gbytes k0, v0;
-  int64_t k_rowb, v_rowb;   // bytes per pool row (position) for the thread's K / V source
-  gu64 m0;                  // mask word of token t0 + tid (threads below 128), tile 0
+  uint32_t kn[3], kr, v[kVLoads];
+  gu64 m0;   // mask word of token t0 + tid (threads below 128), tile 0
 };
 
-__device__ __forceinline__ MhaAddr mha_addr(gbytes kv, gbytes lat, int H, int h, const uint64_t* mask, int words,
-                                            int t0, int T) {
-  const int tid = threadIdx.x, c = tid & 31, ck = tid & 15;
+__device__ __forceinline__ MhaAddr mha_addr(int H, int h, const uint64_t* mask, int words, int t0, int T) {
+  const int tid = threadIdx.x;
+  const uint32_t kv_rowb = (uint32_t)H * kDkv * 2;
   MhaAddr a;
-  const int64_t kv_rowb = (int64_t)H * kDkv * 2;
-  if (c < 24) {
-    a.k_rowb = kv_rowb;
-    a.k0 = kv + (int64_t)(tid >> 5) * kv_rowb + ((int64_t)h * kDkv + 8 * c) * 2;
-  } else {
-    a.k_rowb = (kDl + kDr) * 2;
-    a.k0 = lat + (int64_t)(tid >> 5) * a.k_rowb + (kDl + 8 * (c - 24)) * 2;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int id = tid + kThreads * i;
+    a.kn[i] = (uint32_t)(id / kNopeChunks) * kv_rowb + (uint32_t)(h * kDkv + 8 * (id % kNopeChunks)) * 2;
   }
-  a.v_rowb = kv_rowb;
-  a.v0 = kv + (int64_t)(tid >> 4) * kv_rowb + ((int64_t)h * kDkv + kDn + 8 * ck) * 2;
+  a.kr = (uint32_t)(tid >> 3) * ((kDl + kDr) * 2) + (uint32_t)(kDl + 8 * (tid & 7)) * 2;
+#pragma unroll
+  for (int i = 0; i < kVLoads; ++i) {
+    const int id = tid + kThreads * i;
+    a.v[i] = (uint32_t)(id >> 4) * kv_rowb + (uint32_t)(h * kDkv + kDn + 8 * (id & 15)) * 2;
+  }
   a.m0 = (gu64)mask + (int64_t)min(t0 + tid, T - 1) * words;
   return a;
 }
 
 // A whole tile is one page: a block-table entry outside the pool reads the pool's first
-// page, and its mask words are cleared so none of its keys takes part.
-__device__ __forceinline__ void load_mha_tile(MhaTile& r, const MhaAddr& a, int64_t row0, bool ok, int kt, int t0,
-                                              int T, int last_pos) {
+// page, and its mask words are cleared so none of its keys takes part.  kv_page / lat_page:
+// the page's first row in the up-projected cache and in the latent pool.
+__device__ __forceinline__ void load_mha_tile(MhaTile& r, const MhaAddr& a, gbytes kv_page, gbytes lat_page, bool ok,
+                                              int kt, int t0, int T, int last_pos) {
   const int tid = threadIdx.x;
   r.last = ok ? min(last_pos - kKeys * kt, kKeys - 1) : -1;
-  const gbytes kb = a.k0 + row0 * a.k_rowb, vb = a.v0 + row0 * a.v_rowb;
 #pragma unroll
-  for (int i = 0; i < kKLoads; ++i)   // keys (kThreads / 32) i + tid / 32
-    r.k[i] = *(gu32x4)(kb + (kThreads / 32) * i * a.k_rowb);
+  for (int i = 0; i < 3; ++i) r.k[i] = *(gu32x4)(kv_page + a.kn[i]);
+  r.k[3] = *(gu32x4)(lat_page + a.kr);
 #pragma unroll
-  for (int i = 0; i < kVLoads; ++i)   // keys (kThreads / 16) i + tid / 16
-    r.v[i] = *(gu32x4)(vb + (kThreads / 16) * i * a.v_rowb);
+  for (int i = 0; i < kVLoads; ++i) r.v[i] = *(gu32x4)(kv_page + a.v[i]);
   r.mw = (ok && tid < kQ && t0 + tid < T) ? a.m0[kt] : 0ull;
 }
 
@@ -144,14 +145,23 @@ __device__ __forceinline__ void store_mha_tile(const MhaTile& r, uint16_t (*Ks)[
   const int tid = threadIdx.x;
   if (tid < kQ) Ms[tid] = r.mw;
 #pragma unroll
-  for (int i = 0; i < kKLoads; ++i) {
+  for (int i = 0; i < 3; ++i) {
     const int id = tid + kThreads * i;
-    *reinterpret_cast<u32x4*>(&Ks[id >> 5][8 * (id & 31)]) = r.k[i];
+    *reinterpret_cast<u32x4*>(&Ks[id / kNopeChunks][8 * (id % kNopeChunks)]) = r.k[i];
   }
+  *reinterpret_cast<u32x4*>(&Ks[tid >> 3][kDn + 8 * (tid & 7)]) = r.k[3];
+  if (r.last >= kKeys - 1) {   // the whole page is seen (workgroup-uniform)
 #pragma unroll
-  for (int i = 0; i < kVLoads; ++i) {
-    const int id = tid + kThreads * i;
-    *reinterpret_cast<u32x4*>(&Vs[id >> 4][8 * (id & 15)]) = (id >> 4) <= r.last ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kVLoads; ++i) {
+      const int id = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(&Vs[id >> 4][8 * (id & 15)]) = r.v[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
+      const int id = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(&Vs[id >> 4][8 * (id & 15)]) = (id >> 4) <= r.last ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
@@ -228,7 +238,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     const uint16_t* src = q + ((int64_t)t * H + h) * kDqk + 8 * hb;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(src + 16 * s);
+    // a negative scale becomes a positive one on -Q (exact: a sign flip)
+    if (scale_log2 < 0.f) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[s]) ^ 0x80008000u);
+    }
   }
+  // |scale| in log2 units, at least the smallest normal float: a zero scale gives every
+  // valid logit 0 and p = 1, and so does this one for any logit below 2^100 (x sl < 2^-26
+  // rounds exp2 to 1), while masked logits (-inf) stay -inf instead of 0 * inf = NaN
+  const float sl = fmaxf(fabsf(scale_log2), 1.17549435e-38f);
   // the lane's token, over this wave's key half: m = reference max (log2 units), mf = the
   // largest logit so far, l = sum of p against m
   float m = -INFINITY, mf = -INFINITY, l = 0.f;
@@ -238,15 +257,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   // 16 (c / 16) + 4 (a % 4) .. +3 (+ 32 dt) of the wave's key half)
   const int k_off = (kKeyW * kh + c) * kKRow + 8 * hb;
   const int v_off = (kKeyW * kh + 4 * hb + ((c & 15) >> 2)) * kVRow + 16 * (c >> 4) + 4 * (c & 3);
-  auto tile_row0 = [&](int kt, bool& ok) {
+  const MhaAddr ad = mha_addr(H, h, mask, words, t0, T);
+  const int64_t kv_pageb = (int64_t)kKeys * H * kDkv * 2, lat_pageb = (int64_t)kKeys * (kDl + kDr) * 2;
+  auto load_tile = [&](MhaTile& r, int kt) {
     const int phys = bt_row[kt];
-    ok = phys >= 0 && phys < num_blocks;
-    return (int64_t)(ok ? phys : 0) * kKeys;
+    const bool ok = phys >= 0 && phys < num_blocks;
+    const int64_t pg = ok ? phys : 0;
+    load_mha_tile(r, ad, kvg + pg * kv_pageb, latg + pg * lat_pageb, ok, kt, t0, T, s_pos);
   };
-  const MhaAddr ad = mha_addr(kvg, latg, H, h, mask, words, t0, T);
   MhaTile r;
-  bool ok;
-  int64_t row0;
   for (int pass = 0; pass < 2; ++pass) {
   bool ovf = false;   // the lane's token passed its reference max by more than kSlack
   if (pass == 1) m = mf;   // the second pass starts from the final max
@@ -255,18 +274,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  row0 = tile_row0(0, ok);
-  load_mha_tile(r, ad, row0, ok, 0, t0, T, s_pos);
+  load_tile(r, 0);
   for (int kt = 0; kt < ntiles; ++kt) {
     uint16_t (*const Ks)[kKRow] = Ks2[kt & 1];
     uint16_t (*const Vs)[kVRow] = Vs2[kt & 1];
     uint64_t* const Ms = Ms2[kt & 1];
     store_mha_tile(r, Ks, Vs, Ms);
     __syncthreads();
-    if (kt + 1 < ntiles) {
-      row0 = tile_row0(kt + 1, ok);
-      load_mha_tile(r, ad, row0, ok, kt + 1, t0, T, s_pos);
-    }
+    if (kt + 1 < ntiles) load_tile(r, kt + 1);
     // the token's mask bits for this wave's keys, shifted so that C slot r (key
     // 8 (r / 4) + 4 hb + r % 4 of the half) is bit 8 (r / 4) + r % 4
     const uint32_t mw = (uint32_t)(Ms[kTokW * tg + c] >> (kKeyW * kh + 4 * hb));
@@ -283,23 +298,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
       if (s + 1 < 16) ka[(s + 1) & 1] = *reinterpret_cast<const bf16x8*>(kp + 16 * (s + 1));
       sa = mfma32(ka[s & 1], qf[s], sa);
     }
-    // a tile half whose 32 keys every token of the wave selected (the dense rows, most of a
-    // short context) needs no masking: a wave-uniform test
+    // raw logits, -inf where the lane's token did not select the key (one sign-extended bit
+    // extract and one bit select); a tile half whose 32 keys every token of the wave
+    // selected (the dense rows, most of a short context) skips the mask: a wave-uniform test
     float xs[16];
     if (__ballot((mw & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xs[i] = sa[i] * scale_log2;
+      for (int i = 0; i < 16; ++i) xs[i] = sa[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        xs[i] = ((mw >> (8 * (i >> 2) + (i & 3))) & 1u) ? sa[i] * scale_log2 : -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)mw, 8 * (i >> 2) + (i & 3), 1);
+        xs[i] = __uint_as_float((__float_as_uint(sa[i]) & keep) | (0xFF800000u & ~keep));
+      }
     }
     // softmax of the lane's token against its fixed reference (the first tile with a valid
-    // key sets it; a token with nothing seen yet keeps -inf, and its p are exp2(-inf) = 0)
-    float mx = xs[0];
+    // key sets it; a token with nothing seen yet keeps -inf, and its p are exp2(-inf) = 0).
+    // The scale sl is positive (Q was negated for a negative one), so the largest scaled
+    // logit is the largest raw one scaled, and p = exp2(x sl - m) is one fma and one exp.
+    float mr = xs[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = max2(mx, xs[i]);
-    mx = half_max(mx);
+    for (int i = 1; i < 16; ++i) mr = max2(mr, xs[i]);
+    mr = half_max(mr);
+    const float mx = mr == -INFINITY ? -INFINITY : mr * sl;
     if (m == -INFINITY) m = mx;
     ovf |= mx > m + kSlack;
     mf = max2(mf, mx);
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mha_kernel(
     float ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      xs[i] = __builtin_amdgcn_exp2f(xs[i] - ms);
+      xs[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[i], sl, -ms));
       ps += xs[i];
     }
     l += half_sum(ps);

@@ -4,6 +4,8 @@ oracle (dsa_oracle.mla_mha over each token's selection).
 Bars as for the other attention outputs: normwise 2e-2 per (token, head) row for the bf16
 outputs, lse within 2e-3.  The oracle up-projects the selected rows per head in float64, so
 every token is checked on two heads and a few tokens on all heads."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -117,6 +119,25 @@ def test_mha_mode_two_requests_and_small_heads():
     D.dsa_sparse_mla_prefill_mha(inp["q_mha"], inp["kv_pools"][0], kv_mha, pt, ch, idx, 2048, 1.0 / 16, out, lse, ws=ws)
     torch.cuda.synchronize()
     check(inp, out, lse, range(0, T, 5), list(range(H)), idx)
+
+
+@pytest.mark.parametrize("sm_scale", [-1.0 / 16, 0.0])
+def test_mha_mode_negative_and_zero_scale(sm_scale):
+    """The kernel runs a negative scale as a positive one on -Q, and a zero scale as the
+    smallest normal one (every valid p = 1: the mean of the selected values, lse = log |S|)."""
+    inp = mha_inputs(ctx=2300, T=140, H=8, seed=28)
+    T, H = 140, 8
+    inp["cfg"] = dataclasses.replace(inp["cfg"], sm_scale=sm_scale)
+    pt, ch, idx = select(inp)
+    kv_mha = up_projected(inp)
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    ws = D.workspace(D.DSA_OP_MLA_MHA, T, 2300, 2048, H, 512, DEV)
+    D.dsa_sparse_mla_prefill_mha(inp["q_mha"], inp["kv_pools"][0], kv_mha, pt, ch, idx, 2048, sm_scale, out, lse,
+                                 ws=ws)
+    torch.cuda.synchronize()
+    log(f"[gpu] MHA mode, sm_scale {sm_scale}")
+    check(inp, out, lse, range(0, T, 3), list(range(H)), idx)
 
 
 def test_switch_runs_either_mode_to_the_same_result():
