@@ -460,6 +460,50 @@ def test_mla_ignores_non_finite_rows_outside_the_selection():
         check_token(inp, buf, t)
 
 
+# ------------------------------------------------------------------ seeded shape sweep
+
+def _sweep_shape(seed):
+    """One seeded draw of the path's shape parameters: k (1, values off the 32-row tile,
+    2048), 64 or 128 MLA heads, one or two layers of an IndexShare group, random pages."""
+    rng = np.random.default_rng(7000 + seed)
+    return dict(k=int(rng.choice([1, 17, 64, 100, 333, 2048])), H=int(rng.choice([64, 128])),
+                layers=int(rng.choice([1, 2])), hi=int(rng.choice([300, 2500, 7000])),
+                batch=int(rng.integers(1, 10)), T=int(rng.integers(1, 200)))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sweep_decode_shapes(seed):
+    """Decode through the whole path on a seeded draw of shapes (lengths from 1, so rows on
+    both sides of k): every token's scores, selection and outputs against the oracle."""
+    sh = _sweep_shape(seed)
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged"], seed=300 + seed, batch=sh["batch"], ctx_range=(1, sh["hi"]),
+                   H=sh["H"], k=sh["k"], layers=sh["layers"])
+    inp = I.make_inputs(cfg, DEV)
+    lens = inp["seq_len"].tolist()
+    log(f"[gpu] sweep decode {sh} lens {lens}")
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in range(len(lens)):
+        check_token(inp, buf, t)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_prefill_shapes(seed):
+    """A causal prefill chunk of a seeded length at the end of a seeded context, shapes as
+    for the decode sweep; spread tokens against the oracle."""
+    sh = _sweep_shape(100 + seed)
+    ctx = max(sh["T"], sh["hi"])
+    cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], seed=400 + seed, ctx=ctx, prefill_tokens=sh["T"], H=sh["H"],
+                   k=sh["k"], layers=sh["layers"], identity_pages=False)
+    inp = I.make_inputs(cfg, DEV)
+    log(f"[gpu] sweep prefill {sh} ctx {ctx}")
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    T = sh["T"]
+    for t in sorted({0, T - 1} | set(np.linspace(0, T - 1, min(T, 12)).round().astype(int).tolist())):
+        check_token(inp, buf, t)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def test_full_decode_b1_32k():
