@@ -18,7 +18,8 @@ workload's tokens.
 
 Other modes (each prints JSON; none is the bench line):
     --mla-modes                 MLA's MQA mode against its MHA mode on a 2048-token prefill
-                                chunk at context lengths 2.3K .. 16K
+                                chunk at context lengths 2.3K .. 16K (--mode-contexts N,N
+                                for others)
     --hisparse                  decode with every layer's latent cache in pinned host memory
                                 and an HBM working set per request (loads over PCIe,
                                 overlapped layer by layer), at several query drifts
@@ -437,7 +438,10 @@ def run_mla_modes(args, emit=True):
     T, H, k = MODE_CHUNK, 64, 2048
     reps = max(3, min(args.steps, 10))
     rows = []
-    for n in MODE_CONTEXTS:
+    contexts = [int(x) for x in str(getattr(args, "mode_contexts", "") or "").split(",") if x.strip()] or MODE_CONTEXTS
+    for n in contexts:
+        if n < T:
+            raise SystemExit(f"--mode-contexts: {n} is shorter than the {T}-token chunk")
         cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], seed=31, ctx=n, prefill_tokens=T, mha=True,
                        sm_scale=1.0 / 16)
         inp = I.make_inputs(cfg, dev)
@@ -1000,6 +1004,8 @@ def main():
     ap.add_argument("--report", action="store_true", help="every workload; writes REPORT.md")
     ap.add_argument("--mla-modes", action="store_true",
                     help="MLA's MQA and MHA modes on a prefill chunk across context lengths")
+    ap.add_argument("--mode-contexts", default=",".join(str(n) for n in MODE_CONTEXTS),
+                    help="context lengths of --mla-modes (comma-separated)")
     ap.add_argument("--hisparse", action="store_true",
                     help="decode with the latent caches in pinned host memory and an HBM working set")
     ap.add_argument("--gather-ceiling", action="store_true",
