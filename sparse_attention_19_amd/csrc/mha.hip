@@ -22,9 +22,10 @@
 // lane holds one token's logits: the mask, the softmax row statistics (within the lane plus
 // one swap with the other half of the wave) and P never leave the registers, and P feeds
 // O^T += V^T P^T as the B operand directly, with V^T read transposed (ds_read_b64_tr_b16).
-// A row's reference max moves only when passed by more than 2^32, so O is never rescaled
-// inside the loop.  The two key halves of a token are two splits of its softmax, merged at
-// the end through LDS.
+// A row's reference max is fixed by its first valid tile, so O is never rescaled inside the
+// loop; a logit more than 32 (log2 units) above it sends the workgroup through a second
+// pass.  The two key halves of a token are two splits of its softmax, merged at the end
+// through LDS.
 #include <math.h>
 
 #include "common.h"
