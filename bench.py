@@ -1042,8 +1042,8 @@ def main():
     if args.summarize_json:
         return summarize_json(args)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures "
-              f"the path on one MI355X; how it would shard over several is described, not run.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): it measures the path on "
+              f"one MI355X; how the path would shard over several GPUs is described, not run.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
