@@ -121,6 +121,24 @@ def test_mha_mode_two_requests_and_small_heads():
     check(inp, out, lse, range(0, T, 5), list(range(H)), idx)
 
 
+def test_mha_mode_odd_head_count():
+    """Five heads: the grid pads the head count to a multiple of 8 (one head per XCD in
+    turn), and the padding workgroups have nothing to do; a ragged 200-token chunk."""
+    inp = mha_inputs(ctx=2600, T=200, H=5, seed=29)
+    T, H = 200, 5
+    pt, ch, idx = select(inp)
+    kv_mha = up_projected(inp)
+    out = torch.full((T, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    ws = D.workspace(D.DSA_OP_MLA_MHA, T, 2600, 2048, H, 512, DEV)
+    D.dsa_sparse_mla_prefill_mha(inp["q_mha"], inp["kv_pools"][0], kv_mha, pt, ch, idx, 2048, 1.0 / 16, out, lse,
+                                 ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    log("[gpu] MHA mode, 5 heads")
+    check(inp, out, lse, range(0, T, 7), list(range(H)), idx)
+
+
 @pytest.mark.parametrize("sm_scale", [-1.0 / 16, 0.0])
 def test_mha_mode_negative_and_zero_scale(sm_scale):
     """The kernel runs a negative scale as a positive one on -Q, and a zero scale as the
