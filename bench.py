@@ -55,7 +55,7 @@ METRIC = "DSA decode tokens/s at 32K–128K ctx + achieved HBM GB/s fraction"
 KERNEL_SRC = {
     "indexer_decode_kernel": "indexer.hip", "indexer_prefill_kernel": "indexer.hip",
     "indexer_f32_kernel": "indexer.hip", "topk_prune_kernel": "topk.hip", "topk_select_kernel": "topk.hip",
-    "topk_onepass_kernel": "topk.hip",
+    "topk_onepass_kernel": "topk.hip", "topk_rowpass_kernel": "topk.hip",
     "mla_bf16_kernel": "mla.hip", "mla_combine_kernel": "mla.hip", "mla_f32_kernel": "mla.hip",
 }
 
@@ -117,6 +117,7 @@ def algorithmic(cfg, kernels_seen=()):
         "topk_prune_kernel": (tk_in, 0, "hbm"),
         "topk_select_kernel": (tk_out + (0 if prune else tk_in), 0, "hbm"),
         "topk_onepass_kernel": (tk_in + tk_out, 0, "hbm"),
+        "topk_rowpass_kernel": (tk_in + tk_out, 0, "hbm"),
         "mla_bf16_kernel": (mla_in + (0 if combine else mla_out), mla_f, mla_bound),
         "mla_combine_kernel": (mla_out, 0, "hbm"),
         "mla_f32_kernel": (mla_in + mla_out, mla_f, "hbm"),

@@ -146,9 +146,10 @@ dsa_status dsa_indexer_scores(const void* q_idx, const float* w, const dsa_pool*
  *                 0 <= n_valid[r] + n_add <= ld (checked before any launch)
  *   idx     device [rows][ld_idx] int32 (ld_idx >= k)
  *   ws/ws_bytes  workspace of dsa_workspace_bytes(DSA_OP_TOPK, rows, ld, k, 0, 0) bytes
- *                (for ld > 32768: per-row bounds and the (key, position) lists of the
- *                 positions whose scores are at or above a sampled bound; its contents on
- *                 entry do not matter; may be NULL when the size is 0)
+ *                (for ld > 32768 and fewer than 2048 rows: per-row bounds and the
+ *                 (key, position) lists of the positions whose scores are at or above a
+ *                 sampled bound; its contents on entry do not matter; may be NULL when
+ *                 the size is 0)
  * The result is deterministic (independent of scheduling).
  */
 dsa_status dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid,

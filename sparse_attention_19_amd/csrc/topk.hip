@@ -28,12 +28,14 @@
 //   ld <= 32768 : topk_onepass_kernel, one workgroup per row; the row goes through
 //                 coalesced loads into a padded LDS copy, from which the samples and the
 //                 candidates' keys are read.
-//   ld >  32768 : topk_prune_kernel (grid rows x G, 256 threads: several workgroups per row
-//                 when rows are few) computes tau redundantly in each workgroup, streams its
-//                 contiguous share of the row's 4096-position blocks and lists its
-//                 candidates as (key, position) pairs in position order;
+//   ld >  32768, fewer than 2048 rows : topk_prune_kernel (grid rows x G, 256 threads:
+//                 several workgroups per row) computes tau redundantly in each workgroup,
+//                 streams its contiguous share of the row's 4096-position blocks and lists
+//                 its candidates as (key, position) pairs in position order;
 //                 topk_select_kernel (one workgroup per row) reads the G lists as one and
 //                 selects.
+//   ld >  32768, 2048 rows or more : topk_rowpass_kernel, one workgroup per row streams
+//                 the row, lists its candidates in LDS and selects from there.
 // The result does not depend on scheduling.
 #include <algorithm>
 
@@ -549,6 +551,205 @@ __global__ __launch_bounds__(kSelThreads, 8) void topk_select_kernel(
   select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
 }
 
+constexpr int kRowSub = 2;                        // 4096-position sub-blocks per row-pass block
+constexpr int kRowBlock = kRowSub * kPBlock;      // positions per row-pass block
+constexpr int kRowWords = (kRowSub + 1) / 2;      // packed 16-bit candidate counts
+constexpr int kRowDepth = 0;                      // blocks prefetched beyond the next one
+static_assert(kPBlock == 4 * kSelThreads, "one float4 per thread per sub-block");
+
+// ld > kOnePass with enough rows to fill the GPU with one workgroup per row (the prune would
+// run one slice per row): the prune and the select in one workgroup, the candidate list in
+// LDS instead of memory.  tau comes from the samples as in the prune kernel; the row then
+// streams once in blocks of kRowSub sub-blocks of 4096 positions (thread t: positions
+// 4t .. 4t+3 of each sub-block, non-temporal 16-byte loads; the next block's loads go out
+// before the current block is listed); each block's candidates (key >= tau) take their
+// places in the list, in position order (sub-block, thread, position), from one block scan
+// of packed per-thread counts; then the exact select and the ordered compaction over the
+// list as in the select kernel.  A row whose candidates number fewer than k or more than
+// kCap selects streaming the whole row.
+__global__ __launch_bounds__(kSelThreads) void topk_rowpass_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                   const int* __restrict__ n_valid, int n_add, int k,
+                                                                   int* __restrict__ idx, int64_t ld_idx) {
+  __shared__ __attribute__((aligned(16))) SelSmem sm;
+  __shared__ uint32_t lkey[kCap];
+  __shared__ uint32_t lpos[kCap];
+  __shared__ uint32_t part[2][kRowWords][kSelWaves];   // per-wave packed counts (alternating blocks)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const int n = row_len(n_valid, n_add, ld, row);
+  int* out = idx + (int64_t)row * ld_idx;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kSelThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* src = scores + (int64_t)row * ld;
+  if (n <= kCap) {
+    select_direct(src, n, k, sm, out);
+    return;
+  }
+  const bool vec = ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0) && (ld & 3) == 0;
+  struct Vals {
+    f32x4 x[kRowSub];
+  };
+  // a block inside the row, 16-byte aligned: loads without conditions
+  auto load_full = [&](int b) {
+    Vals v;
+#pragma unroll
+    for (int u = 0; u < kRowSub; ++u)
+      v.x[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(src + b * kRowBlock + u * kPBlock + 4 * tid));
+    return v;
+  };
+  auto load_checked = [&](int b) {
+    Vals v;
+#pragma unroll
+    for (int u = 0; u < kRowSub; ++u) {
+      const int p = b * kRowBlock + u * kPBlock + 4 * tid;
+      if (vec && p + 3 < n) {
+        v.x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + p));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v.x[u][j] = p + j < n ? src[p + j] : 0.f;
+      }
+    }
+    return v;
+  };
+  uint32_t listed = 0u, mx = 0u, tau = 0u;
+  struct Keys {
+    uint32_t key[kRowSub][4];
+    uint32_t mask[kRowSub];
+  };
+  // keys of block b and which are candidates (key >= tau)
+  auto block_keys = [&](const Vals& v, int b) {
+    Keys c;
+#pragma unroll
+    for (int u = 0; u < kRowSub; ++u) {
+      const int p = b * kRowBlock + u * kPBlock + 4 * tid;
+      c.mask[u] = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c.key[u][j] = p + j < n ? order_key(v.x[u][j]) : 0u;
+        mx = max(mx, c.key[u][j]);
+        c.mask[u] |= (c.key[u][j] >= tau && c.key[u][j] != 0u ? 1u : 0u) << j;
+      }
+    }
+    return c;
+  };
+  // block b's candidates take their places in the list: the per-sub-block counts (at most
+  // 4 per thread, 4096 per sub-block) travel in pairs of 16-bit fields through one scan
+  auto list_block = [&](const Keys& c, int b) {
+    uint32_t cnt[kRowWords], incl[kRowWords];
+#pragma unroll
+    for (int w = 0; w < kRowWords; ++w) {
+      cnt[w] = (uint32_t)__popc(c.mask[2 * w]);
+      if (2 * w + 1 < kRowSub) cnt[w] |= (uint32_t)__popc(c.mask[2 * w + 1]) << 16;
+      incl[w] = wave_incl_add(cnt[w]);
+      if (lane == 63) part[b & 1][w][wave] = incl[w];
+    }
+    lds_barrier();
+    uint32_t base = listed;
+#pragma unroll
+    for (int w = 0; w < kRowWords; ++w) {
+      const uint32_t xi = wave_incl_add(lane < kSelWaves ? part[b & 1][w][lane] : 0u);
+      const uint32_t before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)xi, wave - 1) : 0u;
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)xi, kSelWaves - 1);
+      const uint32_t excl = before + incl[w] - cnt[w];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int u = 2 * w + h;
+        if (u < kRowSub) {
+          const int p = b * kRowBlock + u * kPBlock + 4 * tid;
+          const uint32_t first = base + ((excl >> (16 * h)) & 0xFFFFu);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t slot = first + (uint32_t)__popc(c.mask[u] & ((1u << j) - 1u));
+            if (((c.mask[u] >> j) & 1u) && slot < (uint32_t)kCap) {
+              lkey[slot] = c.key[u][j];
+              lpos[slot] = (uint32_t)(p + j);
+            }
+          }
+          base += (tot >> (16 * h)) & 0xFFFFu;
+        }
+      }
+    }
+    listed = base;
+  };
+  // the samples load first (every thread loads a run, threads past kRuns repeat one and
+  // drop it), then the first blocks: tau comes from the samples while the blocks are in
+  // flight (loads complete in order; the sample levels wait for LDS only)
+  // (4-byte loads whatever the alignment: a branch here would make the compiler wait for
+  // every load before the samples are used)
+  float sraw[4];
+  {
+    const int sp = sample_pos(tid & (kRuns - 1), n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sraw[j] = src[sp + j];
+  }
+  const int nb = (n + kRowBlock - 1) / kRowBlock;
+  // blocks read without conditions: all the row's full blocks when it is 16-byte aligned
+  // and holds more than kRowDepth of them, else none (the checked loop reads the row)
+  const int nfull = vec && n / kRowBlock > kRowDepth ? n / kRowBlock : 0;
+  auto sample_keys = [&](uint32_t (&smp)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) smp[j] = tid < kRuns ? order_key(sraw[j]) : 0u;
+  };
+  uint32_t smp[4];
+  if (nfull > 0) {   // workgroup-uniform; each path waits for its own loads only
+    Vals v[kRowDepth + 1];
+#pragma unroll
+    for (int d = 0; d <= kRowDepth; ++d) v[d] = load_full(d);
+    sample_keys(smp);
+    tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), sm.hist, sm.red);
+    // block b sits in v[b % (kRowDepth + 1)]; while every block of a group has a full block
+    // to prefetch the body holds no condition
+    int b0 = 0;
+    for (; b0 + 2 * kRowDepth + 1 < nfull; b0 += kRowDepth + 1) {
+#pragma unroll
+      for (int d = 0; d <= kRowDepth; ++d) {
+        const Keys c = block_keys(v[d], b0 + d);
+        v[d] = load_full(b0 + d + kRowDepth + 1);
+        list_block(c, b0 + d);
+      }
+    }
+    for (; b0 < nfull; b0 += kRowDepth + 1) {
+#pragma unroll
+      for (int d = 0; d <= kRowDepth; ++d) {
+        const int b = b0 + d;
+        if (b < nfull) {   // workgroup-uniform
+          const Keys c = block_keys(v[d], b);
+          if (b + kRowDepth + 1 < nfull) v[d] = load_full(b + kRowDepth + 1);
+          list_block(c, b);
+        }
+      }
+    }
+  } else {
+    sample_keys(smp);
+    tau = sample_tau<kSelWaves, 4>(smp, sample_rank(k, n), sm.hist, sm.red);
+  }
+  for (int b = nfull; b < nb; ++b) list_block(block_keys(load_checked(b), b), b);   // the row's end, unaligned rows
+  // the row's largest key; hist[0] clear for the selection; the list complete
+  mx = wave_max_u32(mx);
+  if (lane == 0) sm.red[1][wave] = mx;
+  if (tid < kHistWords / 4) reinterpret_cast<uint4*>(sm.hist[0])[tid] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  const uint32_t hi = wave_max_u32(lane < kSelWaves ? sm.red[1][lane] : 0u);
+  if (listed >= (uint32_t)k && listed <= (uint32_t)kCap) {
+    uint32_t key[kCR], pos[kCR];
+#pragma unroll
+    for (int r = 0; r < kCR; ++r) {
+      const uint32_t i = (uint32_t)(kCR * tid + r);
+      key[r] = i < listed ? lkey[i] : 0u;
+      pos[r] = i < listed ? lpos[i] : 0u;
+    }
+    Radix st;
+    const uint32_t theta = select_regs<kCR>(key, listed, tau, hi, (uint32_t)k, sm.hist, st);
+    compact<kCR>(key, theta, st.remaining, 0u, sm.wsum[1],
+                 [&](int r, uint32_t slot) { out[slot] = (int)pos[r]; });
+    return;
+  }
+  select_streamed(src, n, hi, k, sm, out);   // too few or too many candidates
+}
+
 // The whole selection in one workgroup per row, launched when ld <= kOnePass.  Rows of
 // kCap < n <= kOnePass: the scores go through coalesced loads into a padded LDS copy, from
 // which every thread reads its 32 consecutive keys (32t .. 32t+31), the samples are read,
@@ -700,7 +901,7 @@ TopkWs topk_ws(void* base, int rows, int64_t ld) {
 
 size_t topk_workspace_bytes(int rows, int64_t ld, int k) {
   (void)k;
-  if (ld <= kOnePass || rows <= 0) return 0;
+  if (ld <= kOnePass || rows <= 0 || prune_slices(rows, ld) == 1) return 0;   // one-pass, row-pass
   return topk_ws(nullptr, rows, ld).words * 4;
 }
 
@@ -712,6 +913,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int G = prune_slices(a.rows, a.ld);
+  if (G == 1) {   // a workgroup per row fills the GPU: prune and select in one pass
+    const KernelEvents ev("topk_rowpass_kernel");
+    hipExtLaunchKernelGGL(topk_rowpass_kernel, dim3(a.rows), dim3(kSelThreads), 0, stream, ev.start, ev.stop, 0,
+                          a.scores, a.ld, a.n_valid, a.n_add, a.k, a.idx, a.ld_idx);
+    return hipGetLastError();
+  }
   const TopkWs w = topk_ws(a.ws, a.rows, a.ld);
   {
     const KernelEvents ev("topk_prune_kernel");

@@ -228,13 +228,16 @@ def test_workspace_sizes():
     # longer rows, G = min(ceil(2048 / rows), blocks of 4096, 1024) prune workgroups per
     # row: tau per row (padded to 4 words), the largest key of each prune wave (4 per
     # workgroup), a candidate count per workgroup (padded) and 8192 (key, position) pairs
-    # per workgroup
+    # per workgroup; with G = 1 (2048 rows or more) one workgroup per row prunes and
+    # selects, its candidates in LDS: no workspace
     def words(rows, G):
         pad4 = lambda x: -(-x // 4) * 4
         return pad4(rows) + rows * G * 4 + pad4(rows * G) + rows * G * 8192 * 2
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 1, 40000, 2048, 0, 0) == words(1, 10) * 4
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 40, 131072, 2048, 0, 0) == words(40, 32) * 4
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 4096, 131072, 2048, 0, 0) == words(4096, 1) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 2047, 131072, 2048, 0, 0) == words(2047, 2) * 4
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 2048, 131072, 2048, 0, 0) == 0
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 4096, 131072, 2048, 0, 0) == 0
 
 
 def test_index_cache_host_logic():

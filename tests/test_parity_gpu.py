@@ -273,7 +273,8 @@ def test_topk_adversarial(k):
 def test_topk_many_rows(rows, ld):
     # relu-weighted sums like indexer scores, ragged lengths across the direct / pruned
     # boundaries; ld <= 32768 selects in one kernel, otherwise 300 rows prune with several
-    # workgroups per row (candidate bits) and 2500 with one (candidate lists)
+    # workgroups per row (candidate lists in memory) and 2500 with one workgroup per row
+    # that prunes and selects (candidate list in LDS)
     rng = np.random.default_rng(rows + ld)
     sc = np.maximum(rng.standard_normal((rows, ld)), 0.0) + 0.5 * np.maximum(rng.standard_normal((rows, ld)), 0.0)
     nv = rng.integers(0, ld + 1, rows)
@@ -281,10 +282,33 @@ def test_topk_many_rows(rows, ld):
     _topk_case(sc, nv.tolist(), 2048)
 
 
+def _sampled_heavy(rng, n, runs):
+    """Values in [0, 1) except 10.0 on the first `runs` of the 512 sample runs (4 positions
+    each, evenly spaced over the row): the sampled bound lands on 10.0 and lists
+    4 * runs candidates, fewer than k = 2048 for runs < 512."""
+    row = rng.random(n)
+    for i in range(runs):
+        p = 4 * ((i * (n // 4)) // 512)
+        row[p:p + 4] = 10.0
+    return row
+
+
+def _spread_tens(rng, n, count):
+    """Values in [0, 1) except 10.0 at `count` evenly spread positions: about a fifth of
+    the samples are 10.0, so the sampled bound lands on 10.0 and lists exactly `count`
+    candidates (8192 fills the candidate list, 8193 overflows it)."""
+    row = rng.random(n)
+    row[(np.arange(count) * n) // count] = 10.0
+    return row
+
+
 def _adversarial_rows(rng, ld, k):
-    """Rows that defeat the sampled bound (ties, two values, winners at the end) next to
-    ordinary ones."""
+    """Rows that defeat the sampled bound (ties, two values, winners at the end, too few or
+    too many candidates) next to ordinary ones."""
     return [
+        (_sampled_heavy(rng, ld, 300), ld),                                  # too few listed
+        (_spread_tens(rng, ld, 8192), ld),                                   # list just full
+        (_spread_tens(rng, ld, 8193), ld),                                   # one over
         (np.full(ld, 3.0), ld),                                               # all equal
         (rng.integers(0, 2, ld).astype(np.float64), ld),                     # two values
         (np.where(np.arange(ld) > ld - k - 3, 5.0, 1.0), ld),                # winners at the end
@@ -296,9 +320,9 @@ def _adversarial_rows(rng, ld, k):
 
 @pytest.mark.parametrize("ld", [40000, 40001])
 def test_topk_listed_rows_adversarial(ld):
-    # 2048 rows: one prune workgroup per row, candidates listed; most rows short (dense or
-    # direct), a few adversarial ones of full length.  ld = 40001 leaves the rows unaligned
-    # (scalar loads)
+    # 2048 rows: one workgroup per row prunes and selects, candidates listed in LDS; most
+    # rows short (dense or direct), a few adversarial ones of full length.  ld = 40001
+    # leaves the rows unaligned (scalar loads)
     rng = np.random.default_rng(ld)
     rows = 2048
     sc = rng.integers(0, 100, (rows, ld)).astype(np.float32)
@@ -311,7 +335,8 @@ def test_topk_listed_rows_adversarial(ld):
 
 @pytest.mark.parametrize("ld", [30001, 40001])
 def test_topk_unaligned_rows(ld):
-    # rows not 16-byte aligned: the one-pass kernel (ld <= 32768) and the bit-marking prune
+    # rows not 16-byte aligned: the one-pass kernel (ld <= 32768) and the prune with several
+    # workgroups per row
     rng = np.random.default_rng(ld)
     cases = _adversarial_rows(rng, ld, 64)
     sc = np.stack([r for r, _ in cases] + [rng.integers(0, 1000, ld).astype(np.float64)])
