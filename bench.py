@@ -57,6 +57,7 @@ KERNEL_SRC = {
     "indexer_f32_kernel": "indexer.hip", "topk_prune_kernel": "topk.hip", "topk_select_kernel": "topk.hip",
     "topk_onepass_kernel": "topk.hip", "topk_rowpass_kernel": "topk.hip",
     "mla_bf16_kernel": "mla.hip", "mla_combine_kernel": "mla.hip", "mla_f32_kernel": "mla.hip",
+    "mla_h128_kernel": "mla.hip",
 }
 
 
@@ -121,6 +122,7 @@ def algorithmic(cfg, kernels_seen=()):
         "mla_bf16_kernel": (mla_in + (0 if combine else mla_out), mla_f, mla_bound),
         "mla_combine_kernel": (mla_out, 0, "hbm"),
         "mla_f32_kernel": (mla_in + mla_out, mla_f, "hbm"),
+        "mla_h128_kernel": (mla_in + mla_out, mla_f, mla_bound),
     }
     # a step's HBM bytes: in prefill the tokens' selections overlap, and each latent row
     # is fetched from HBM once (later visits hit the caches), so count unique rows there

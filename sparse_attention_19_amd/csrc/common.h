@@ -112,6 +112,27 @@ __device__ __forceinline__ float rows4_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Two floats as packed bf16 (round to nearest even): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), h2));
+}
+
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
+// Max / sum of a lane's value and the same lane's in the other half of the wave (lanes l and
+// l ^ 32 hold the same row of an MFMA tile), in both: one permlane32 swap.  Both halves add
+// or compare the same two values, so they end with the same result.
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Minimum over the wave, in every lane (min a = ~max ~a keeps 0 the identity).
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
 

@@ -576,6 +576,187 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   }
 }
 
+// ---- 128 heads, one workgroup per token (no splits)
+//
+// The two 64-head groups of a token read the same selected rows.  mla_bf16_kernel runs them
+// as two workgroups that each gather every row; when a token needs no splits (enough tokens
+// to fill the GPU), this kernel serves all 128 heads from one gather instead: 4 waves of 32
+// heads share each 32-row tile, staged once in LDS, as K (all 576 dims) and as V (its first
+// 512 dims).  Per tile and wave, on 32x32x16 MFMAs:
+//   S^T (32 rows x 32 heads): A = K rows from LDS (lane: row l % 32, dims 16 s + 8 hb .. +7
+//     of k-step s), B = Q^T in registers (lane: head l % 32, the same dims); C slot r of
+//     lane l is row 8 (r / 4) + 4 hb + r % 4, head l % 32, so a head's softmax stays in
+//     lanes l and l ^ 32.
+//   O^T (512 dims x 32 heads) += V^T P^T per 16-row step p: B = P^T straight from the
+//     softmax (slots 8p .. 8p + 7: rows 16 p + 8 (j / 4) + 4 hb + j % 4), A = V^T from two
+//     transposing reads (lane: dim l % 32 of the 32-dim tile, the same rows); C slot r of
+//     lane l is dim 8 (r / 4) + 4 hb + r % 4, head l % 32.
+// The next tile's rows load into registers while the current one is used (one barrier per
+// tile).  Softmax: a head's reference max is set by its first tile with a valid row and
+// stays fixed; a logit more than kMaxSlack (log2 units) above it sends the workgroup
+// through a second pass from each head's final max (as in the 64-head kernel).
+constexpr int kH2 = 128;                           // heads per workgroup
+constexpr int kH2Steps = kRow / 16;                // 36 k-steps of 16 dims
+constexpr int kH2DimTiles = kDl / 32;              // 16 output tiles of 32 dims
+constexpr int kH2RowB = kRowBytes + 32;            // LDS row: 1184 bytes
+constexpr int kH2RowE = kH2RowB / 2;               // 592 elements
+constexpr int kH2Loads = kChunks / 8;              // 9 chunks per thread per tile: 8 threads a row
+static_assert(kH2 == 32 * kWaves && kMT * 8 == kThreads && kH2Loads * 8 == kChunks, "tile gather shape");
+// LDS rows are 1184 bytes (32 mod 128) and the 16-byte chunk c of row r sits at slot
+// c ^ ((r >> 2) & 1): the 8 rows of one 16-byte K read then start on 8 distinct 16-byte bank
+// groups, and the 4 rows x 32 bytes of one transposing V read on 4 distinct 32-byte groups.
+
+__global__ __launch_bounds__(kThreads, 1) void mla_h128_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
+    const int* __restrict__ block_table, const int* __restrict__ seq_len, int max_blocks, int batch,
+    const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
+    int64_t ld_idx, int k, float scale_log2, int T, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kMT][kH2RowE];
+  __shared__ int rowid[kMaxList];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 31, hb = lane >> 5;
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const int h = kH2 / kWaves * wave + c;   // the lane's head
+
+  // Q^T fragments: head h, dims 16 s + 8 hb .. +7 (their loads go out before the list's
+  // two round trips, which they do not depend on)
+  bf16x8 qf[kH2Steps];
+  {
+    const gbytes src = (gbytes)q + ((int64_t)t * kH2 + h) * kRowBytes + 16 * hb;
+#pragma unroll
+    for (int s = 0; s < kH2Steps; ++s) qf[s] = *(gbf16x8)(src + 32 * s);
+  }
+  int nent;
+  resolve_rows(t, 0, 1, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos, idx, ld_idx, k,
+               rowid, nent);
+  __syncthreads();
+  const int ntiles = (nent + kMT - 1) / kMT;
+
+  // tile gather: thread tid takes row tid / 8 of the tile, chunks tid % 8 + 8 j (j < 9)
+  const int grow = tid >> 3;
+  const int g_lds = grow * kH2RowB + 16 * ((tid & 7) ^ ((grow >> 2) & 1));   // + 128 j
+  u32x4 pf[kH2Loads];
+  auto load_tile = [&](int kt) {
+    const int rid = rowid[kt * kMT + grow];
+    const gbytes src = (rid >= 0 ? (gbytes)pool + (int64_t)rid * kRowBytes : (gbytes)kZeroRow) + 16 * (tid & 7);
+#pragma unroll
+    for (int j = 0; j < kH2Loads; ++j) pf[j] = *(const __attribute__((address_space(1))) u32x4*)(src + 128 * j);
+  };
+  auto store_tile = [&](int buf) {
+    uint8_t* dst = reinterpret_cast<uint8_t*>(&Ks2[buf][0][0]) + g_lds;
+#pragma unroll
+    for (int j = 0; j < kH2Loads; ++j) *reinterpret_cast<u32x4*>(dst + 128 * j) = pf[j];
+  };
+  // per-lane LDS element offsets: K rows of the A operand (row c, chunk 2 s + hb swizzled),
+  // and the transposing V reads (lane a = c % 16 of its 16-lane group: row 4 hb + a / 4 (+ 8,
+  // + 16 p), dims 16 (c / 16) + 4 (a % 4) .. +3 (+ 32 dt); rows 4 hb + ... all have swizzle
+  // bit hb)
+  const int k_off = c * kH2RowE + 8 * (hb ^ ((c >> 2) & 1));
+  const int a16 = c & 15;
+  const int v_off = (4 * hb + (a16 >> 2)) * kH2RowE + 16 * (c >> 4) + 8 * (((a16 & 3) >> 1) ^ hb) + 4 * (a16 & 1);
+
+  float m = -INFINITY, mf = -INFINITY, l = 0.f;   // the lane's head: reference max, largest, sum
+  f32x16 o[kH2DimTiles];
+  for (int pass = 0; pass < 2; ++pass) {
+    bool ovf = false;
+    if (pass == 1) m = mf;   // the second pass starts from the final max
+    l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < kH2DimTiles; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+    if (ntiles > 0) load_tile(0);
+    for (int kt = 0; kt < ntiles; ++kt) {
+      store_tile(kt & 1);
+      const uint32_t vmask = (uint32_t)__ballot(lane < 32 && rowid[kt * kMT + c] >= 0);
+      lds_barrier();
+      if (kt + 1 < ntiles) load_tile(kt + 1);
+      const uint16_t* Kb = &Ks2[kt & 1][0][0];
+      // S^T, one accumulator chain; the next k-step's K fragment is read while this one's
+      // MFMA runs
+      f32x16 sa;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sa[i] = 0.f;
+      {
+        const uint16_t* kp = Kb + k_off;
+        constexpr int kAhead = 3;   // K fragments read this many k-steps ahead of their MFMA
+        bf16x8 ka[kAhead + 1];
+#pragma unroll
+        for (int s = 0; s < kAhead; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+#pragma unroll
+        for (int s = 0; s < kH2Steps; ++s) {
+          if (s + kAhead < kH2Steps) ka[(s + kAhead) % (kAhead + 1)] = *reinterpret_cast<const bf16x8*>(kp + 16 * (s + kAhead));
+          sa = mfma32(ka[s % (kAhead + 1)], qf[s], sa);
+        }
+      }
+      // scaled logits, -inf for rows without a position (C slot i: row 8 (i / 4) + 4 hb + i % 4)
+      float xs[16];
+      const uint32_t vm = vmask >> (4 * hb);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = (vm >> (8 * (i >> 2) + (i & 3))) & 1u;
+        xs[i] = ok ? sa[i] * scale_log2 : -INFINITY;
+      }
+      float mr = xs[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mr = max2(mr, xs[i]);
+      mr = half_max(mr);
+      if (m == -INFINITY) m = mr;
+      ovf |= mr > m + kMaxSlack;
+      mf = max2(mf, mr);
+      const float ms = (m == -INFINITY) ? 0.f : m;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        xs[i] = __builtin_amdgcn_exp2f(xs[i] - ms);
+        ps += xs[i];
+      }
+      l += half_sum(ps);
+      // O^T += V^T P^T, 16 rows per step
+      const uint16_t* vp = Kb + v_off;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const u32x4 pw = {pack_bf16(xs[8 * p], xs[8 * p + 1]), pack_bf16(xs[8 * p + 2], xs[8 * p + 3]),
+                          pack_bf16(xs[8 * p + 4], xs[8 * p + 5]), pack_bf16(xs[8 * p + 6], xs[8 * p + 7])};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        // V^T fragments read kVAhead dims tiles ahead of their MFMA
+        constexpr int kVAhead = 2;
+        s16x4 vlo[kVAhead + 1], vhi[kVAhead + 1];
+#pragma unroll
+        for (int dt = 0; dt < kVAhead; ++dt) {
+          vlo[dt] = lds_read_tr16(vp + 16 * p * kH2RowE + 32 * dt);
+          vhi[dt] = lds_read_tr16(vp + (16 * p + 8) * kH2RowE + 32 * dt);
+        }
+#pragma unroll
+        for (int dt = 0; dt < kH2DimTiles; ++dt) {
+          if (dt + kVAhead < kH2DimTiles) {
+            vlo[(dt + kVAhead) % (kVAhead + 1)] = lds_read_tr16(vp + 16 * p * kH2RowE + 32 * (dt + kVAhead));
+            vhi[(dt + kVAhead) % (kVAhead + 1)] = lds_read_tr16(vp + (16 * p + 8) * kH2RowE + 32 * (dt + kVAhead));
+          }
+          const s16x4 lo = vlo[dt % (kVAhead + 1)], hi = vhi[dt % (kVAhead + 1)];
+          const short __attribute__((ext_vector_type(8))) v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[dt] = mfma32(__builtin_bit_cast(bf16x8, v8), pb, o[dt]);
+        }
+      }
+    }
+    // a second pass only when some head passed its reference (the vote is also the barrier
+    // after which the second pass may rewrite the tile buffers)
+    if (!__syncthreads_or(ovf)) break;
+  }
+  // out = O / l as bf16 (8-byte stores of 4 consecutive dims), lse in natural-log units
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* dst = out + ((int64_t)t * kH2 + h) * kDl + 4 * hb;
+#pragma unroll
+  for (int dt = 0; dt < kH2DimTiles; ++dt)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * qq) =
+          make_uint2(pack_bf16(o[dt][4 * qq] * inv, o[dt][4 * qq + 1] * inv),
+                     pack_bf16(o[dt][4 * qq + 2] * inv, o[dt][4 * qq + 3] * inv));
+  if (lse && hb == 0) lse[(int64_t)t * kH2 + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
 // Merge split partials (O_s normalized by its own l_s): m = max m_s, L = sum l_s 2^(m_s - m),
 // O = sum (l_s 2^(m_s - m) / L) O_s.
 // grid (T, H, Z); one wave per (token, head) and 1/Z of the output dims, in kNP passes of
@@ -781,6 +962,14 @@ hipError_t mla_scratch(void** ptr) {
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
+  if (a.bf16 && a.H == kH2 && mla_splits(a.T, a.k, a.H, true) == 1) {   // one gather for both head groups
+    const KernelEvents ev("mla_h128_kernel");
+    hipExtLaunchKernelGGL(mla_h128_kernel, dim3((unsigned)a.T), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
+                          (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks, a.block_table, a.seq_len,
+                          a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k, a.sm_scale * kLog2e, a.T,
+                          (uint16_t*)a.out, a.lse);
+    return hipGetLastError();
+  }
   if (a.bf16) {
     const int splits = mla_splits(a.T, a.k, a.H, true);
     const int groups = a.H / kH;

@@ -146,6 +146,65 @@ def test_bf16_prefill_h128():
         check_token(inp, buf, t, key_cache=kc)
 
 
+def test_bf16_prefill_h128_unsplit():
+    # 200 tokens x 128 heads need no splits: one workgroup per token serves both 64-head
+    # groups from one gather.  The chunk crosses n = k (dense rows ending mid-tile, then
+    # top-k rows)
+    cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], ctx=2200, prefill_tokens=200, H=128)
+    inp, buf = run_cfg(cfg)
+    kc = {}
+    for t in list(range(0, 200, 9)) + [47, 48, 151, 152, 199]:
+        check_token(inp, buf, t, key_cache=kc)
+
+
+def _scale_second_halves(inp, lens, factor):
+    """Scales the latent rows of the pages holding the second half of every context."""
+    bt = inp["block_table"].cpu()
+    phys = sorted({int(bt[b, j]) for b, n in enumerate(lens) for j in range((n // 2) // 64 + 1, (n + 63) // 64)})
+    sel = torch.tensor(phys, dtype=torch.long, device=DEV)
+    for pool in inp["kv_pools"]:
+        pool[sel] = (pool[sel].float() * factor).to(pool.dtype)
+    return len(phys)
+
+
+def test_mla_h128_running_max_moves_late():
+    # the late-max case of the 64-head test for the one-gather 128-head kernel (130 tokens,
+    # no splits): logits rise by far more than 32 (log2 units) after the first tiles, and the
+    # workgroup runs its second pass
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=130, ctx_range=(3000, 9000))
+    inp = I.make_inputs(cfg, DEV)
+    lens = inp["seq_len"].tolist()
+    npg = _scale_second_halves(inp, lens, 8)
+    inp["q"] = [(q.float() * 4).to(q.dtype) for q in inp["q"]]
+    log(f"[gpu] h128 late-max, {npg} scaled pages")
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in (0, 1, 37, 64, 100, 129):
+        check_token(inp, buf, t)
+
+
+def test_mla_h128_ignores_non_finite_rows_outside_the_selection():
+    # NaN / Inf in a block no request references, 130 tokens x 128 heads (one-gather kernel):
+    # the masked tail entries of short dense rows read zeros, not that block
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=130, ctx_range=(5, 3000))
+    inp = I.make_inputs(cfg, DEV)
+    pool = inp["k_pool"]
+    inp["k_pool"] = torch.cat([torch.zeros_like(pool[:1]), pool]).contiguous()
+    pools = []
+    for pool in inp["kv_pools"]:
+        junk = torch.full_like(pool[:1], float("nan"))
+        junk[0, ::2] = float("inf")
+        pools.append(torch.cat([junk, pool]).contiguous())
+    inp["kv_pools"] = pools
+    bt = inp["block_table"]
+    inp["block_table"] = torch.where(bt >= 0, bt + 1, bt).contiguous()
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(buf.outs[0].float()).all()
+    for t in (0, 5, 64, 77, 129):
+        check_token(inp, buf, t)
+
+
 def test_bf16_decode_edge_lengths():
     # n = 1, n = k, n = k + 1, n a multiple of 64, n = 64k + 1
     lens = [1, 2048, 2049, 4096, 4097, 63, 65, 2047]
