@@ -183,6 +183,16 @@ def test_mla_h128_running_max_moves_late():
         check_token(inp, buf, t)
 
 
+@pytest.mark.parametrize("sm_scale", [-1.0 / 16, 0.0])
+def test_mla_h128_negative_and_zero_scale(sm_scale):
+    # the one-gather 128-head kernel takes its max over scaled logits: a negative scale
+    # reverses which rows lead, a zero scale makes every selected row weigh the same
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=130, ctx_range=(1000, 4000), sm_scale=sm_scale)
+    inp, buf = run_cfg(cfg)
+    for t in (0, 63, 129):
+        check_token(inp, buf, t)
+
+
 def test_mla_h128_ignores_non_finite_rows_outside_the_selection():
     # NaN / Inf in a block no request references, 130 tokens x 128 heads (one-gather kernel):
     # the masked tail entries of short dense rows read zeros, not that block
