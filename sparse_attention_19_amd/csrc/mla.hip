@@ -579,8 +579,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
 // ---- 128 heads, one workgroup per token (no splits)
 //
 // The two 64-head groups of a token read the same selected rows.  mla_bf16_kernel runs them
-// as two workgroups that each gather every row; when a token needs no splits (enough tokens
-// to fill the GPU), this kernel serves all 128 heads from one gather instead: 4 waves of 32
+// as two workgroups that each gather every row; with more than 128 tokens (no splits, and
+// more than one round of those workgroups), this kernel serves all 128 heads from one
+// gather instead: 4 waves of 32
 // heads share each 32-row tile, staged once in LDS, as K (all 576 dims) and as V (its first
 // 512 dims).  Per tile and wave, on 32x32x16 MFMAs:
 //   S^T (32 rows x 32 heads): A = K rows from LDS (lane: row l % 32, dims 16 s + 8 hb .. +7
@@ -962,7 +963,11 @@ hipError_t mla_scratch(void** ptr) {
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
-  if (a.bf16 && a.H == kH2 && mla_splits(a.T, a.k, a.H, true) == 1) {   // one gather for both head groups
+  // one gather for both head groups, once the two-group form would need more than one round
+  // of 256 workgroups (T > 128): with fewer tokens that form fills the chip and is faster
+  // (measured at 100 and 128 tokens: 114 and 115 us against 138 and 142), with more it
+  // is slower (129 and 256 tokens: 218 and 234 us against 141 and 172)
+  if (a.bf16 && a.H == kH2 && (int64_t)a.T * (kH2 / kH) > 256) {
     const KernelEvents ev("mla_h128_kernel");
     hipExtLaunchKernelGGL(mla_h128_kernel, dim3((unsigned)a.T), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
                           (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks, a.block_table, a.seq_len,

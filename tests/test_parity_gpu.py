@@ -127,7 +127,19 @@ def test_bf16_decode_h128_split():
 
 
 def test_bf16_decode_h128_unsplit():
-    # 130 tokens x 2 head groups fill the GPU without splitting: normalized output path
+    # 120 tokens x 2 head groups fill the GPU in one round without splitting: the two-group
+    # kernel's normalized output path
+    cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=120, ctx_range=(1500, 5000))
+    inp = I.make_inputs(cfg, DEV)
+    buf = P.run_inputs(inp)
+    torch.cuda.synchronize()
+    for t in (0, 1, 64, 65, 118, 119):
+        check_token(inp, buf, t)
+
+
+def test_bf16_decode_h128_one_gather():
+    # 130 tokens: past one round of two-group workgroups, the one-gather kernel serves all
+    # 128 heads of a token
     cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=130, ctx_range=(1500, 5000))
     inp = I.make_inputs(cfg, DEV)
     buf = P.run_inputs(inp)
@@ -147,9 +159,8 @@ def test_bf16_prefill_h128():
 
 
 def test_bf16_prefill_h128_unsplit():
-    # 200 tokens x 128 heads need no splits: one workgroup per token serves both 64-head
-    # groups from one gather.  The chunk crosses n = k (dense rows ending mid-tile, then
-    # top-k rows)
+    # 200 tokens x 128 heads: one workgroup per token serves both 64-head groups from one
+    # gather.  The chunk crosses n = k (dense rows ending mid-tile, then top-k rows)
     cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], ctx=2200, prefill_tokens=200, H=128)
     inp, buf = run_cfg(cfg)
     kc = {}
@@ -168,8 +179,8 @@ def _scale_second_halves(inp, lens, factor):
 
 
 def test_mla_h128_running_max_moves_late():
-    # the late-max case of the 64-head test for the one-gather 128-head kernel (130 tokens,
-    # no splits): logits rise by far more than 32 (log2 units) after the first tiles, and the
+    # the late-max case of the 64-head test for the one-gather 128-head kernel (130
+    # tokens): logits rise by far more than 32 (log2 units) after the first tiles, and the
     # workgroup runs its second pass
     cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=130, ctx_range=(3000, 9000))
     inp = I.make_inputs(cfg, DEV)
