@@ -122,7 +122,7 @@ def algorithmic(cfg, kernels_seen=()):
         "mla_bf16_kernel": (mla_in + (0 if combine else mla_out), mla_f, mla_bound),
         "mla_combine_kernel": (mla_out, 0, "hbm"),
         "mla_f32_kernel": (mla_in + mla_out, mla_f, "hbm"),
-        "mla_h128_kernel": (mla_in + mla_out, mla_f, mla_bound),
+        "mla_h128_kernel": (mla_in + (0 if combine else mla_out), mla_f, mla_bound),
     }
     # a step's HBM bytes: in prefill the tokens' selections overlap, and each latent row
     # is fetched from HBM once (later visits hit the caches), so count unique rows there
@@ -319,7 +319,8 @@ def measure(cfg, steps, warmup, copies=0, cpu_budget=12.0):
     # decode: the indexer's key stream and the MLA's latent-row gather (with the combine that
     # finishes its output), algorithmic bytes over those kernels' time per step
     decode_hbm = None
-    gather = [n for n in ("indexer_decode_kernel", "mla_bf16_kernel", "mla_combine_kernel") if n in kern]
+    gather = [n for n in ("indexer_decode_kernel", "mla_bf16_kernel", "mla_h128_kernel", "mla_combine_kernel")
+              if n in kern]
     if not cfg.prefill_tokens and cfg.dtype.itemsize == 2 and gather:
         b = sum(alg[n][0] * kern[n]["launches_per_step"] for n in gather)
         t = sum(kern[n]["ms_per_step"] for n in gather) * 1e-3

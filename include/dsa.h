@@ -186,7 +186,7 @@ dsa_status dsa_sparse_mla_decode(const void* q, const dsa_pool* kv, const dsa_pa
  * allocation).  Same arguments, results and errors as dsa_sparse_mla_decode, bit for
  * bit; the split partials go to a device array the library holds on each GPU it runs on
  * (dsa_workspace_bytes(DSA_OP_MLA, B, 0, k, H, Dl) bytes of it; every supported shape
- * fits its 16,908,288 bytes, a larger need returns DSA_ERR_WORKSPACE).  It calls no
+ * fits its 33,816,576 bytes, a larger need returns DSA_ERR_WORKSPACE).  It calls no
  * allocating routine.  The first call on a device looks the array's address up with that
  * device current, so `stream` must belong to the current device.  All calls on one GPU
  * share its array: calls whose work overlaps on that GPU (different streams, or threads

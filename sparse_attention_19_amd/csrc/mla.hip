@@ -576,12 +576,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bf16_kernel(
   }
 }
 
-// ---- 128 heads, one workgroup per token (no splits)
+// ---- 128 heads, one workgroup per (token, split) for all heads
 //
 // The two 64-head groups of a token read the same selected rows.  mla_bf16_kernel runs them
-// as two workgroups that each gather every row; with more than 128 tokens (no splits, and
-// more than one round of those workgroups), this kernel serves all 128 heads from one
-// gather instead: 4 waves of 32
+// as two workgroups that each gather every row; from 64 tokens on (mla_one_gather), this
+// kernel serves all 128 heads from one gather instead: 4 waves of 32
 // heads share each 32-row tile, staged once in LDS, as K (all 576 dims) and as V (its first
 // 512 dims).  Per tile and wave, on 32x32x16 MFMAs:
 //   S^T (32 rows x 32 heads): A = K rows from LDS (lane: row l % 32, dims 16 s + 8 hb .. +7
@@ -611,13 +610,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_h128_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t num_blocks,
     const int* __restrict__ block_table, const int* __restrict__ seq_len, int max_blocks, int batch,
     const int* __restrict__ q_row, const int* __restrict__ q_pos, const int* __restrict__ idx,
-    int64_t ld_idx, int k, float scale_log2, int T, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int64_t ld_idx, int k, float scale_log2, int T, int splits, int xcd, uint16_t* __restrict__ out,
+    float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kMT][kH2RowE];
   __shared__ int rowid[kMaxList];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 31, hb = lane >> 5;
-  const int t = blockIdx.x;
-  if (t >= T) return;
+  int t, sp, z;
+  work_item(blockIdx.x, splits, 1, T, xcd != 0, t, sp, z);
+  if (t >= T) return;   // past the last token (whole workgroup)
   const int h = kH2 / kWaves * wave + c;   // the lane's head
 
   // Q^T fragments: head h, dims 16 s + 8 hb .. +7 (their loads go out before the list's
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_h128_kernel(
     for (int s = 0; s < kH2Steps; ++s) qf[s] = *(gbf16x8)(src + 32 * s);
   }
   int nent;
-  resolve_rows(t, 0, 1, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos, idx, ld_idx, k,
+  resolve_rows(t, sp, splits, block_table, seq_len, max_blocks, batch, num_blocks, q_row, q_pos, idx, ld_idx, k,
                rowid, nent);
   __syncthreads();
   const int ntiles = (nent + kMT - 1) / kMT;
@@ -745,9 +746,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_h128_kernel(
     // after which the second pass may rewrite the tile buffers)
     if (!__syncthreads_or(ovf)) break;
   }
-  // out = O / l as bf16 (8-byte stores of 4 consecutive dims), lse in natural-log units
+  // O / l as bf16 (8-byte stores of 4 consecutive dims): splits == 1 to the output, lse in
+  // natural-log units; else the split's partial O to the workspace with its (max, sum) in
+  // log2 units, laid out as the 64-head kernel's ([token][split][head]) for the combine
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* dst = out + ((int64_t)t * kH2 + h) * kDl + 4 * hb;
+  const int64_t row = splits == 1 ? (int64_t)t * kH2 + h : ((int64_t)t * splits + sp) * kH2 + h;
+  uint16_t* dst = (splits == 1 ? out : ws_o) + row * kDl + 4 * hb;
 #pragma unroll
   for (int dt = 0; dt < kH2DimTiles; ++dt)
 #pragma unroll
@@ -755,7 +759,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_h128_kernel(
       *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * qq) =
           make_uint2(pack_bf16(o[dt][4 * qq] * inv, o[dt][4 * qq + 1] * inv),
                      pack_bf16(o[dt][4 * qq + 2] * inv, o[dt][4 * qq + 3] * inv));
-  if (lse && hb == 0) lse[(int64_t)t * kH2 + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  if (hb == 0) {
+    if (splits == 1) {
+      if (lse) lse[row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    } else {
+      ws_ml[row * 2 + 0] = m;
+      ws_ml[row * 2 + 1] = l;
+    }
+  }
 }
 
 // Merge split partials (O_s normalized by its own l_s): m = max m_s, L = sum l_s 2^(m_s - m),
@@ -924,20 +935,38 @@ int combine_slices(int T, int H, int splits) {
 }
 static_assert((32 + 3) / 4 * 1 <= kCombSlots, "32 splits fit at Z = kPasses");
 
+// 128 heads: the one-gather kernel (one workgroup per (token, split) for all heads) from 64
+// tokens on, else the two-group form (mla_bf16_kernel, one workgroup per (token, split,
+// 64-head group)).  MLA + combine, decode_b64_paged_h128 at other batch sizes, one-gather
+// against two-group: 25.8 / 17.3 us at 1 token, 33.9 / 21.2 at 8, 46.0 / 42.6 at 32,
+// 65.0 / 68.7 at 64, 95.9 / 110.1 at 100, 106.6 / 114.8 at 128 (218 us two-group from 129
+// tokens on, when its workgroups need a second round).
+bool mla_one_gather(int T, int H, bool bf16) { return bf16 && H == kH2 && T >= 64; }
+
+// Splits of the one-gather kernel: as many (token, split) workgroups as fit in one round on
+// the 256 CUs, at most 32 and never more than the list has tiles.
+int mla_h128_splits(int T, int k) {
+  const int tiles = (k + kMT - 1) / kMT;
+  int s = T > 0 ? 256 / T : 1;
+  s = s < 1 ? 1 : (s > 32 ? 32 : s);
+  return s < tiles ? s : tiles;
+}
+
 // Split partials: O [T][splits][H][Dl] bf16, then (max, sum) [T][splits][H][2] fp32.
 size_t mla_workspace_bytes(int T, int k, int H, int Dl, bool bf16) {
-  const int s = mla_splits(T, k, H, bf16);
+  const int s = mla_one_gather(T, H, bf16) ? mla_h128_splits(T, k) : mla_splits(T, k, H, bf16);
   if (s <= 1) return 0;
   return (size_t)T * s * H * (2 * (size_t)Dl + 2 * sizeof(float));
 }
 
 // ---- split partials without a caller workspace (dsa_sparse_mla_decode_noalloc)
-// At most 256 (token, split, head group) work items carry partials (mla_splits keeps
-// T * splits * groups <= 256 whenever splits > 1), each 64 heads x (512 bf16 + 2 fp32):
+// At most 256 work items carry partials whenever splits > 1: (token, split, head group)
+// items of 64 heads (mla_splits keeps T * splits * groups <= 256), or (token, split) items
+// of the one-gather kernel's 128 heads (T * splits <= 256), each head 512 bf16 + 2 fp32:
 // the largest workspace any call needs.  Every GPU the library runs on holds one copy of this
 // array until the process ends; host code reaches it only through the address
 // hipGetSymbolAddress gives for the current device.
-constexpr size_t kScratchBytes = (size_t)256 * kH * (2 * kDl + 2 * sizeof(float));
+constexpr size_t kScratchBytes = (size_t)256 * kH2 * (2 * kDl + 2 * sizeof(float));
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -963,24 +992,21 @@ hipError_t mla_scratch(void** ptr) {
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
-  // one gather for both head groups, once the two-group form would need more than one round
-  // of 256 workgroups (T > 128): with fewer tokens that form fills the chip and is faster
-  // (measured at 100 and 128 tokens: 114 and 115 us against 138 and 142), with more it
-  // is slower (129 and 256 tokens: 218 and 234 us against 141 and 172)
-  if (a.bf16 && a.H == kH2 && (int64_t)a.T * (kH2 / kH) > 256) {
-    const KernelEvents ev("mla_h128_kernel");
-    hipExtLaunchKernelGGL(mla_h128_kernel, dim3((unsigned)a.T), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
-                          (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks, a.block_table, a.seq_len,
-                          a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k, a.sm_scale * kLog2e, a.T,
-                          (uint16_t*)a.out, a.lse);
-    return hipGetLastError();
-  }
+  const bool one_gather = mla_one_gather(a.T, a.H, a.bf16);
   if (a.bf16) {
-    const int splits = mla_splits(a.T, a.k, a.H, true);
+    const int splits = one_gather ? mla_h128_splits(a.T, a.k) : mla_splits(a.T, a.k, a.H, true);
     const int groups = a.H / kH;
     uint16_t* ws_o = (uint16_t*)a.ws;
     float* ws_ml = ws_o ? (float*)(ws_o + (size_t)a.T * splits * a.H * kDl) : nullptr;
     const bool xcd = a.T >= 8;
+    if (one_gather) {
+      const int64_t items = (int64_t)(xcd ? (a.T + 7) / 8 * 8 : a.T) * splits;
+      const KernelEvents ev("mla_h128_kernel");
+      hipExtLaunchKernelGGL(mla_h128_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, ev.start, ev.stop, 0,
+                            (const uint8_t*)a.q, (const uint8_t*)a.pool, a.num_blocks, a.block_table, a.seq_len,
+                            a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k, a.sm_scale * kLog2e,
+                            a.T, splits, (int)xcd, (uint16_t*)a.out, a.lse, ws_o, ws_ml);
+    } else {
     const int64_t items = (int64_t)(xcd ? (a.T + 7) / 8 * 8 : a.T) * splits * groups;
     {
       const KernelEvents ev("mla_bf16_kernel");
@@ -991,6 +1017,7 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
                             a.seq_len, a.max_blocks, a.batch, a.q_row, a.q_pos, a.idx, a.ld_idx, a.k,
                             a.sm_scale * kLog2e, splits, groups, a.T, (int)xcd, a.H, (uint16_t*)a.out, a.lse,
                             ws_o, ws_ml);
+    }
     }
     if (splits > 1) {
       const int Z = combine_slices(a.T, a.H, splits);

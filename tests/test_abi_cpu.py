@@ -217,12 +217,17 @@ def test_workspace_sizes():
     assert one == 32 * 64 * per
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 4096, 0, 2048, 64, 512) == 0
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 0, 0, 2048, 64, 512) == 0
-    # 128 heads run as two 64-head workgroups per (token, split): one token still splits 32
-    # ways (64 workgroups), 64 tokens split 2 ways, 128 tokens do not split
+    # 128 heads below 64 tokens run as two 64-head workgroups per (token, split): one token
+    # still splits 32 ways (64 workgroups), 32 tokens 4 ways; from 64 tokens on one workgroup
+    # per (token, split) serves all 128 heads, splits = 256 / tokens: 64 tokens split 4 ways,
+    # 128 tokens 2 ways, 256 tokens do not split
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 1, 0, 2048, 128, 512) == 32 * 128 * per
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 128, 512) == 64 * 2 * 128 * per
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 32, 0, 2048, 128, 512) == 32 * 4 * 128 * per
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 63, 0, 2048, 128, 512) == 63 * 2 * 128 * per
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 128, 512) == 64 * 4 * 128 * per
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 64, 0, 2048, 64, 512) == 64 * 4 * 64 * per
-    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 128, 0, 2048, 128, 512) == 0
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 128, 0, 2048, 128, 512) == 128 * 2 * 128 * per
+    assert L.LIB.dsa_workspace_bytes(L.DSA_OP_MLA, 256, 0, 2048, 128, 512) == 0
     # rows of at most 32768 positions are selected in one workgroup: no workspace
     assert L.LIB.dsa_workspace_bytes(L.DSA_OP_TOPK, 64, 32768, 2048, 0, 0) == 0
     # longer rows, G = min(ceil(2048 / rows), blocks of 4096, 1024) prune workgroups per
@@ -293,9 +298,9 @@ def test_noalloc_decode_rejects(kw, status):
 
 
 def test_noalloc_scratch_holds_every_workspace():
-    # the library's scratch array (16,908,288 bytes) covers the split partials of every
-    # batch size, head count and list width the bf16 decode accepts
-    scratch = 256 * 64 * (512 * 2 + 2 * 4)
+    # the library's scratch array (33,816,576 bytes: 256 work items of 128 heads) covers the
+    # split partials of every batch size, head count and list width the bf16 decode accepts
+    scratch = 256 * 128 * (512 * 2 + 2 * 4)
     for H in (64, 128):
         for k in (1, 31, 32, 33, 500, 2047, 2048):
             for T in list(range(1, 300)) + [511, 512, 1000, 4096, 100000]:

@@ -126,9 +126,9 @@ def test_bf16_decode_h128_split():
         check_token(inp, buf, t)
 
 
-def test_bf16_decode_h128_unsplit():
-    # 120 tokens x 2 head groups fill the GPU in one round without splitting: the two-group
-    # kernel's normalized output path
+def test_bf16_decode_h128_one_gather_split():
+    # 120 tokens: one workgroup per (token, split) for all 128 heads, 2 splits merged by the
+    # combine kernel
     cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=120, ctx_range=(1500, 5000))
     inp = I.make_inputs(cfg, DEV)
     buf = P.run_inputs(inp)
@@ -138,8 +138,7 @@ def test_bf16_decode_h128_unsplit():
 
 
 def test_bf16_decode_h128_one_gather():
-    # 130 tokens: past one round of two-group workgroups, the one-gather kernel serves all
-    # 128 heads of a token
+    # 130 tokens: one workgroup per token for all 128 heads, no split (normalized output)
     cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=130, ctx_range=(1500, 5000))
     inp = I.make_inputs(cfg, DEV)
     buf = P.run_inputs(inp)
@@ -625,7 +624,8 @@ def test_full_decode_b64_paged_every_token():
 
 
 def test_full_decode_b64_paged_h128_every_token():
-    # 128 MLA heads at full size: 64 tokens x 2 head groups, split in two
+    # 128 MLA heads at full size: 64 tokens, one workgroup per (token, split) for all heads,
+    # 4 splits
     inp, buf = run_cfg(I.CONFIGS["decode_b64_paged_h128"])
     lens = inp["seq_len"].tolist()
     for t in range(len(lens)):

@@ -45,6 +45,9 @@ def test_noalloc_matches_workspace_entry_point_twice():
 
 
 def test_noalloc_h128():
-    cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=5, ctx_range=(1000, 6000))
-    inp, buf, out, lse, T = _case(cfg)
-    assert torch.equal(out, buf.outs[0]) and torch.equal(lse, buf.lses[0])
+    # 5 tokens: two 64-head workgroups per (token, split); 64 tokens: one workgroup per
+    # (token, split) for all 128 heads, 4 splits (the largest partials the array holds)
+    for batch in (5, 64):
+        cfg = I.shrink(I.CONFIGS["decode_b64_paged_h128"], batch=batch, ctx_range=(1000, 6000))
+        inp, buf, out, lse, T = _case(cfg)
+        assert torch.equal(out, buf.outs[0]) and torch.equal(lse, buf.lses[0]), batch
