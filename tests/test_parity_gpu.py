@@ -193,6 +193,19 @@ def test_mla_h128_running_max_moves_late():
         check_token(inp, buf, t)
 
 
+@pytest.mark.parametrize("k", [1, 17, 100, 333])
+def test_mla_h128_one_gather_small_k(k):
+    # the one-gather kernel with lists shorter than a tile or ending mid-tile, and with
+    # splits (96 tokens: 2 splits where the list has 2 tiles or more): a 96-token chunk at
+    # the end of a 1200-position context, every row sparse once n > k
+    cfg = I.shrink(I.CONFIGS["prefill_4096_at_128k"], seed=500 + k, ctx=1200, prefill_tokens=96, H=128, k=k,
+                   identity_pages=False)
+    inp, buf = run_cfg(cfg)
+    kc = {}
+    for t in (0, 31, 64, 95):
+        check_token(inp, buf, t, key_cache=kc)
+
+
 @pytest.mark.parametrize("sm_scale", [-1.0 / 16, 0.0])
 def test_mla_h128_negative_and_zero_scale(sm_scale):
     # the one-gather 128-head kernel takes its max over scaled logits: a negative scale
@@ -410,6 +423,21 @@ def test_topk_listed_rows_adversarial(ld):
         sc[100 * i + 7] = r
         nv[100 * i + 7] = n
     _topk_case(sc, nv.tolist(), 2048)
+
+
+def test_topk_row_pass_block_edges():
+    # 2048 rows (one workgroup per row streams it in 8192-position blocks): lengths at the
+    # block edges -- one position into a block, whole blocks with no partial end, the 32768
+    # edge, a ragged end -- next to short rows (dense, or selected without a bound)
+    rng = np.random.default_rng(77)
+    ld = 40000
+    rows = 2048
+    sc = rng.standard_normal((rows, ld)).astype(np.float32)
+    sc[1::5] = rng.integers(0, 40, (len(range(1, rows, 5)), ld))   # heavy ties on some rows
+    edges = [8193, 8200, 16383, 16384, 16385, 24576, 24577, 32767, 32768, 32769, 39999, 40000,
+             2048, 2049, 8192, 0, 1]
+    nv = [edges[i % len(edges)] for i in range(rows)]
+    _topk_case(sc, nv, 2048)
 
 
 @pytest.mark.parametrize("ld", [30001, 40001])
