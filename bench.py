@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the DSA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config indexshare_decode_4layer]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config indexshare_decode_4layer] [--graph]
     python bench.py --report            every workload, written to REPORT.md
 
 A step is one pass of the whole path (lightning indexer -> top-k -> sparse MLA, plus the
@@ -243,9 +243,11 @@ def cpu_baseline(inp, budget_s=12.0, seed=0):
 
 # --------------------------------------------------------------------------- benchmark
 
-def measure(cfg, steps, warmup, copies=0, cpu_budget=12.0):
+def measure(cfg, steps, warmup, copies=0, cpu_budget=12.0, graph=False):
     """Time `steps` whole steps of a workload (after `warmup`), then each kernel on its own
-    over further steps, and (cpu_budget > 0) the oracle on a sample of its tokens."""
+    over further steps, and (cpu_budget > 0) the oracle on a sample of its tokens.  graph:
+    the timed steps are replays of one captured HIP graph per input copy (pipeline.StepGraph)
+    instead of eager library calls."""
     import torch
     import dsa_inputs as I
     import sparse_attention_19_amd as D
@@ -270,8 +272,16 @@ def measure(cfg, steps, warmup, copies=0, cpu_budget=12.0):
         c = i % copies
         P.run_inputs(inputs[c], buf, step=i, pt=pts[c], ch=chs[c])
 
+    graphs = [P.StepGraph(inputs[c], buf, pt=pts[c], ch=chs[c]) for c in range(copies)] if graph else None
+
+    def timed_step(i):
+        if graphs is None:
+            step(i)
+        else:
+            graphs[i % copies].replay()
+
     for i in range(warmup):
-        step(i)
+        timed_step(i)
     torch.cuda.synchronize()
 
     # timed region: K whole steps back to back, no per-kernel instrumentation
@@ -279,7 +289,7 @@ def measure(cfg, steps, warmup, copies=0, cpu_budget=12.0):
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        step(warmup + i)
+        timed_step(warmup + i)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -337,7 +347,8 @@ def measure(cfg, steps, warmup, copies=0, cpu_budget=12.0):
         "config": {"workload": cfg.name, "requests": len(I.context_lengths(cfg)), "ctx": cfg.ctx,
                    "query_tokens": T, "k": cfg.k, "indexer_heads_x_dim": f"{cfg.Hi}x{cfg.Di}",
                    "mla_heads_x_dim": f"{cfg.H}x({cfg.Dl}+{cfg.Dr})", "layers": cfg.layers,
-                   "index_share": cfg.index_share, "rotated_input_copies": copies},
+                   "index_share": cfg.index_share, "rotated_input_copies": copies,
+                   "launch": "hip_graph" if graph else "eager"},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_gbs": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "decode_hbm": decode_hbm,
@@ -347,7 +358,7 @@ def measure(cfg, steps, warmup, copies=0, cpu_budget=12.0):
     }
     if cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(inputs[0], budget_s=cpu_budget)
-    del inputs, buf
+    del inputs, buf, graphs
     torch.cuda.empty_cache()
     return res
 
@@ -357,7 +368,8 @@ def run_bench(args):
     cfg = I.CONFIGS[args.config]
     if args.no_index_share:
         cfg = I.shrink(cfg, index_share=False)
-    res = measure(cfg, args.steps, args.warmup, args.copies, 0.0 if args.no_cpu_baseline else 12.0)
+    res = measure(cfg, args.steps, args.warmup, args.copies, 0.0 if args.no_cpu_baseline else 12.0,
+                  graph=args.graph)
     print(json.dumps(res), flush=True)
 
 
@@ -1003,6 +1015,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="indexshare_decode_4layer")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the whole step captured as one HIP graph per input copy")
     ap.add_argument("--no-index-share", action="store_true",
                     help="every layer runs its own indexer and top-k (the plain-DSA comparison)")
     ap.add_argument("--report", action="store_true", help="every workload; writes REPORT.md")

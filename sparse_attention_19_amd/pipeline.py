@@ -166,3 +166,38 @@ def run_inputs(inp: dict, buf: Optional[StepBuffers] = None, step: int = 0, pt: 
         decode_step(inp["q_idx"], inp["w"], inp["k_pool"], inp["kv_pools"], inp["q"], pt, cfg.k, cfg.sm_scale,
                     buf, step, share=cfg.index_share)
     return buf
+
+
+class StepGraph:
+    """One whole step of an input set captured once as a HIP graph (torch.cuda.CUDAGraph
+    records a HIP graph on ROCm) and replayed with a single launch call: the indexer, the
+    top-k and every layer's sparse MLA (and split combine) as graph nodes, with no per-kernel
+    host work at replay time.
+
+    The library enqueues kernel launches only (no memset, copy or allocation nodes), on
+    torch's current stream, which is the capture stream inside torch.cuda.graph.  What the
+    host does per call happens once, at capture: argument checks, kernel and split choices
+    from the host lengths, and the IndexShare cache's step stamp.  A replay therefore
+    repeats the captured step over the same buffers: new inputs are written into those
+    tensors in place, with the same lengths and page layout (the host lengths decide the
+    launch shapes)."""
+
+    def __init__(self, inp: dict, buf: StepBuffers, step: int = 0, pt: Optional[PageTable] = None,
+                 ch: Optional[Chunk] = None):
+        self.inp, self.buf = inp, buf
+        self.pt = pt or page_table(inp)
+        self.ch = ch if ch is not None or not inp["cfg"].prefill_tokens else chunk(inp)
+        # one eager step on a side stream first (torch's capture recipe: whatever is set up
+        # lazily on first use happens outside the capture)
+        side = torch.cuda.Stream(device=inp["q_idx"].device)   # default priority
+        side.wait_stream(torch.cuda.current_stream(inp["q_idx"].device))
+        with torch.cuda.stream(side):
+            run_inputs(inp, buf, step, self.pt, self.ch)
+        torch.cuda.current_stream(inp["q_idx"].device).wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            run_inputs(inp, buf, step, self.pt, self.ch)
+
+    def replay(self) -> StepBuffers:
+        self.graph.replay()
+        return self.buf
