@@ -641,7 +641,7 @@ def _fmt_frac(x):
     return "-" if x is None else f"{100 * x:.1f} %"
 
 
-def write_report(results, host, gpu_name, path, gather=None, modes=None, hisparse=None):
+def write_report(results, host, gpu_name, path, gather=None, modes=None, hisparse=None, graphs=None):
     L = []
     w = L.append
     w("# DSA hot path on one MI355X: measured report")
@@ -688,6 +688,17 @@ def write_report(results, host, gpu_name, path, gather=None, modes=None, hispars
               f"{k['launches_per_step']:.0f} | {1e3 * k['avg_ms']:.1f} | {k['achieved']:.0f} {k['unit']} | "
               f"{_fmt_frac(k['frac'])} |")
     w("")
+    if graphs:
+        w("## Launch: eager calls against one captured HIP graph")
+        w("")
+        w("The same step, timed the same way (100 steps after 10), launched by eager library calls or "
+          "replayed as one HIP graph captured per input copy (`pipeline.StepGraph`, `bench.py --graph`).")
+        w("")
+        w("| workload | eager ms/step | HIP graph ms/step |")
+        w("|---|---|---|")
+        for name, eager_ms, graph_ms in graphs:
+            w(f"| `{name}` | {eager_ms:.4f} | {graph_ms:.4f} |")
+        w("")
     share = [r for r in results if r["config"]["workload"] == "indexshare_decode_4layer"]
     if len(share) == 2:
         on = next(r for r in share if r["config"]["index_share"])
@@ -809,6 +820,14 @@ def run_report(args):
         r["what"] = what
         results.append(r)
         print(json.dumps(r), flush=True)
+    print("[report] HIP graph replays ...", flush=True)
+    graphs = []
+    for r in results:
+        c = r["config"]
+        if c["index_share"] and c["workload"] in ("decode_b1_32k", "decode_b64_paged", "indexshare_decode_4layer"):
+            g = measure(I.CONFIGS[c["workload"]], 100, 10, 0, 0.0, graph=True)
+            graphs.append((c["workload"], r["ms_per_step"], g["ms_per_step"]))
+            print(json.dumps(g), flush=True)
     print("[report] gather ceiling ...", flush=True)
     args.steps = 7
     gather = run_gather_ceiling(args)
@@ -819,7 +838,8 @@ def run_report(args):
     print("[report] HBM working set ...", flush=True)
     args.steps, args.warmup, args.config = 20, 5, "indexshare_decode_4layer"
     hisparse = run_hisparse(args)
-    write_report(results, host_cpu(), torch.cuda.get_device_name(0), args.report_path, gather, modes, hisparse)
+    write_report(results, host_cpu(), torch.cuda.get_device_name(0), args.report_path, gather, modes, hisparse,
+                 graphs)
     print(f"[report] wrote {args.report_path}", flush=True)
 
 
